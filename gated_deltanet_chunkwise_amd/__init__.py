@@ -1,0 +1,30 @@
+"""MI355X (gfx950) Gated DeltaNet chunkwise forward pass.
+
+Thin Python binding of libgdn.so (C ABI in include/gdn.h).  It only marshals
+arguments: every step of the forward pass runs in the library's HIP kernels.
+PyTorch is used for device memory and streams.  Importing the package does not
+load the library; the first call does, and raises if it was not built
+(``python -m gated_deltanet_chunkwise_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    GDN_BF16,
+    GDN_F32,
+    GdnError,
+    GdnForward,
+    Params,
+    WorkspaceLayout,
+    check,
+    fwd,
+    lib_path,
+    load_library,
+    make_params,
+    status_string,
+    workspace_layout,
+    workspace_size,
+)
+
+__all__ = [
+    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "Params", "WorkspaceLayout",
+    "check", "fwd", "lib_path", "load_library", "make_params", "status_string",
+    "workspace_layout", "workspace_size",
+]

@@ -1,0 +1,191 @@
+"""ctypes binding of libgdn.so: same entry points as include/gdn.h.
+
+Argument marshalling only.  No fallback: if the library is missing or the
+device is not a GPU, calls raise.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libgdn.so")
+_LIB = None
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
+           "gdn_fwd", "gdn_status_string")
+
+
+class Params(ctypes.Structure):
+    """gdn_params_t."""
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    """gdn_workspace_layout_t."""
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("gamma", "beta", "w", "kt", "u", "hc", "vn", "chunk_map", "seq_slot", "total")] + [
+                    ("num_slots", ctypes.c_int32), ("num_seqs", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, where="gdn_fwd"):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load_library(path=None):
+    """Load libgdn.so (raises OSError if it has not been built)."""
+    global _LIB
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise OSError("libgdn.so not found at %s; build it with "
+                          "`python -m gated_deltanet_chunkwise_amd.build`" % _LIB_PATH)
+        _LIB = _declare(ctypes.CDLL(_LIB_PATH))
+    return _LIB
+
+
+def _declare(lib):
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    P = ctypes.POINTER(Params)
+    lib.gdn_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_fwd_workspace_size.argtypes = [P, ctypes.c_int]
+    lib.gdn_fwd_workspace_layout.restype = ctypes.c_int
+    lib.gdn_fwd_workspace_layout.argtypes = [P, ctypes.c_int, ctypes.POINTER(WorkspaceLayout)]
+    lib.gdn_fwd_check.restype = ctypes.c_int
+    lib.gdn_fwd_check.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t]
+    lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_fwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    return lib
+
+
+def status_string(status):
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+def make_params(B, T, H, HV, K, V, dtype, num_seqs=0, scale=1.0):
+    return Params(int(B), int(T), int(H), int(HV), int(K), int(V), int(num_seqs), int(dtype),
+                  float(scale))
+
+
+def workspace_size(params, packed=False):
+    return int(load_library().gdn_fwd_workspace_size(ctypes.byref(params), int(bool(packed))))
+
+
+def workspace_layout(params, packed=False):
+    lay = WorkspaceLayout()
+    st = load_library().gdn_fwd_workspace_layout(ctypes.byref(params), int(bool(packed)),
+                                                 ctypes.byref(lay))
+    if st:
+        raise GdnError(st, "gdn_fwd_workspace_layout")
+    return lay
+
+
+def check(params, ptrs, workspace_bytes):
+    """gdn_fwd_check with raw integer pointers (12 of them, gdn_fwd's order)."""
+    return int(load_library().gdn_fwd_check(ctypes.byref(params), *ptrs, int(workspace_bytes)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrapper
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
+
+
+class GdnForward:
+    """A planned forward pass: outputs and workspace allocated once, so that
+    calling it launches the kernels and allocates nothing.
+
+    Shapes follow include/gdn.h: q, k [B,T,H,K]; v [B,T,HV,V]; g_raw, beta
+    [B,T,HV] fp32; A_log, dt_bias [HV] fp32; cu_seqlens [N+1] int64 (B == 1);
+    initial_state [N,HV,K,V] fp32.
+    """
+
+    def __init__(self, B, T, H, HV, K, V, dtype, device, num_seqs=None, scale=1.0,
+                 final_state=True):
+        torch = _torch()
+        self.packed = num_seqs is not None
+        self.N = num_seqs if self.packed else B
+        self.params = make_params(B, T, H, HV, K, V, _dtype_code(dtype),
+                                  num_seqs if self.packed else 0, scale)
+        self.lib = load_library()
+        self.layout = workspace_layout(self.params, self.packed)  # raises on bad sizes
+        self.ws_bytes = int(self.layout.total)
+        # 256-byte aligned (torch's caching allocator aligns blocks to at least 512)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.o = torch.empty((B, T, HV, V), dtype=dtype, device=device)
+        self.final_state = (torch.empty((self.N, HV, K, V), dtype=torch.float32, device=device)
+                            if final_state else None)
+
+    def __call__(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
+                 initial_state=None, stream=None):
+        torch = _torch()
+        if (cu_seqlens is not None) != self.packed:
+            raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
+        for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta),
+                        ("A_log", A_log), ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
+                        ("initial_state", initial_state)):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        st = self.lib.gdn_fwd(
+            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
+            _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
+            _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
+            ctypes.c_void_p(stream.cuda_stream))
+        if st:
+            raise GdnError(st)
+        return self.o, self.final_state
+
+
+def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_state=None,
+        scale=1.0, output_final_state=True):
+    """One forward pass; allocates o, final_state and the workspace with torch.
+
+    Returns (o [B,T,HV,V] in q's dtype, final_state [N,HV,K,V] fp32 or None).
+    """
+    torch = _torch()
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T):
+        raise ValueError("shape mismatch between q, k and v")
+    if g_raw.shape != (B, T, HV) or beta.shape != (B, T, HV):
+        raise ValueError("g_raw and beta must be [B,T,HV]")
+    if g_raw.dtype != torch.float32 or beta.dtype != torch.float32 or A_log.dtype != torch.float32:
+        raise TypeError("g_raw, beta, A_log (and dt_bias) must be float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int64:
+        raise TypeError("cu_seqlens must be int64")
+    num_seqs = None if cu_seqlens is None else cu_seqlens.numel() - 1
+    plan = GdnForward(B, T, H, HV, K, V, q.dtype, q.device, num_seqs=num_seqs, scale=scale,
+                      final_state=output_final_state)
+    return plan(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state)

@@ -1,0 +1,225 @@
+// gdn_api.hip -- host side of libgdn: argument validation, workspace layout
+// and the launch sequence.  See include/gdn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+struct Plan {
+  gdn::Geo geo;
+  gdn_workspace_layout_t lay;
+  bool varlen;
+  int64_t ntok;  // tokens in q/k/v/o
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shapes and sizes only (no pointers).
+gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (p->B < 0 || p->T < 0 || p->H <= 0 || p->HV <= 0 || p->K <= 0 || p->V <= 0) return GDN_ERR_SHAPE;
+  if (p->HV % p->H) return GDN_ERR_SHAPE;
+  if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDN_ERR_UNSUPPORTED;
+  if (varlen && (p->B != 1 || p->num_seqs < 0)) return GDN_ERR_SHAPE;
+  const int64_t N = varlen ? p->num_seqs : p->B;
+  const int64_t NT = ((int64_t)p->T + gdn::kChunk - 1) / gdn::kChunk;
+  const int64_t slots = varlen ? (int64_t)p->T / gdn::kChunk + N : (int64_t)p->B * NT;
+  const int64_t ntok = varlen ? (int64_t)p->T : (int64_t)p->B * p->T;
+  // Index arithmetic uses int32 for slots, units and tokens within a packed batch.
+  const int64_t units = N * p->HV * (p->V / 16);
+  if (slots > INT32_MAX / 2 || units > INT32_MAX || N + 1 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+
+  Plan pl{};
+  pl.varlen = varlen;
+  pl.ntok = ntok;
+  gdn::Geo& g = pl.geo;
+  g.B = p->B; g.T = p->T; g.H = p->H; g.HV = p->HV; g.K = p->K; g.V = p->V;
+  g.N = (int)N; g.G = p->HV / p->H; g.NT = (int)NT; g.slots = (int)slots; g.scale = p->scale;
+
+  const size_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+  const size_t hsl = (size_t)p->HV * (size_t)slots;  // (head, slot) pairs
+  gdn_workspace_layout_t& L = pl.lay;
+  size_t off = 0;
+  L.gamma = off; off = align_up(off + hsl * gdn::kChunk * 4);
+  L.beta = off;  off = align_up(off + hsl * gdn::kChunk * 4);
+  L.w = off;     off = align_up(off + hsl * gdn::kChunk * p->K * esz);
+  L.kt = off;    off = align_up(off + hsl * gdn::kChunk * p->K * esz);
+  L.u = off;     off = align_up(off + hsl * gdn::kChunk * p->V * esz);
+  L.hc = off;    off = align_up(off + hsl * (size_t)p->K * p->V * esz);
+  L.vn = off;    off = align_up(off + hsl * gdn::kChunk * p->V * esz);
+  L.chunk_map = off; off = align_up(off + (varlen ? (size_t)slots * 16 : 0));
+  L.seq_slot = off;  off = align_up(off + (varlen ? (size_t)(N + 1) * 4 : 0));
+  L.total = off;
+  L.num_slots = (int32_t)slots;
+  L.num_seqs = (int32_t)N;
+  *out = pl;
+  return GDN_OK;
+}
+
+gdn_status_t check_all(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                       const float* g_raw, const float* beta, const float* A_log,
+                       const float* dt_bias, const int64_t* cu_seqlens,
+                       const float* initial_state, const void* o, const float* final_state,
+                       const void* workspace, size_t workspace_bytes, Plan* plan) {
+  if (!p) return GDN_ERR_NULL;
+  gdn_status_t st = make_plan(p, cu_seqlens != nullptr, plan);
+  if (st != GDN_OK) return st;
+  const bool tokens = plan->ntok > 0;
+  if (tokens && (!q || !k || !v || !g_raw || !beta || !A_log || !o)) return GDN_ERR_NULL;
+  if (plan->lay.total > 0 && !workspace) return GDN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(g_raw, 4) || !aligned(beta, 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(initial_state, 4) || !aligned(final_state, 4))
+    return GDN_ERR_ALIGN;
+  if (!aligned(cu_seqlens, 8) || !aligned(workspace, kWsAlign)) return GDN_ERR_ALIGN;
+  if (workspace_bytes < plan->lay.total) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+// hipLaunchKernel with the argument tuple converted to the kernel's own types.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args&&... args) {
+  std::tuple<KArgs...> t(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto&... a) {
+        void* argv[] = {(void*)&a...};
+        return hipLaunchKernel((const void*)kern, grid, block, argv, 0, s);
+      },
+      t);
+}
+
+template <typename E, int K, int V, bool VARLEN>
+gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
+                 const float* beta, const float* A_log, const float* dt_bias,
+                 const int64_t* cu_seqlens, const float* h0, void* o, float* fin, void* ws,
+                 hipStream_t s) {
+  using gdn::Frag;
+  using gdn::Quad;
+  const gdn::Geo& geo = pl.geo;
+  const gdn_workspace_layout_t& L = pl.lay;
+  char* w = static_cast<char*>(ws);
+  float* gam = reinterpret_cast<float*>(w + L.gamma);
+  float* bet = reinterpret_cast<float*>(w + L.beta);
+  Frag<E>* wf = reinterpret_cast<Frag<E>*>(w + L.w);
+  Frag<E>* ktf = reinterpret_cast<Frag<E>*>(w + L.kt);
+  Quad<E>* uf = reinterpret_cast<Quad<E>*>(w + L.u);
+  Frag<E>* hcf = reinterpret_cast<Frag<E>*>(w + L.hc);
+  Frag<E>* vnf = reinterpret_cast<Frag<E>*>(w + L.vn);
+  int4* cmap = VARLEN ? reinterpret_cast<int4*>(w + L.chunk_map) : nullptr;
+  int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
+  const E* qe = static_cast<const E*>(q);
+  const E* ke = static_cast<const E*>(k);
+  const E* ve = static_cast<const E*>(v);
+  E* oe = static_cast<E*>(o);
+
+  if (geo.N == 0) return GDN_OK;
+  hipError_t err = hipSuccess;
+  auto ok = [&](hipError_t e) {
+    if (e != hipSuccess && err == hipSuccess) err = e;
+  };
+  if (VARLEN) ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
+                        geo.slots, cmap, seq_slot));
+  if (geo.slots > 0) {
+    ok(launch(gdn::gdn_prologue_kernel<VARLEN>, dim3(geo.slots), dim3(256), s, geo, g_raw, beta,
+              A_log, dt_bias, cmap, gam, bet));
+    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo, ke,
+              ve, cmap, gam, bet, wf, ktf, uf));
+  }
+  ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(geo.N * geo.HV * (V / 16)), dim3(64), s,
+            geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+  if (geo.slots > 0)
+    ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo,
+              qe, ke, cmap, gam, hcf, vnf, oe));
+  return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename E, int K, int V>
+gdn_status_t run_v(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
+                   const float* beta, const float* A_log, const float* dt_bias,
+                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s) {
+  return pl.varlen ? run<E, K, V, true>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s)
+                   : run<E, K, V, false>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+}
+
+template <typename E>
+gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
+                   const float* beta, const float* A_log, const float* dt_bias,
+                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s) {
+  const int K = pl.geo.K, V = pl.geo.V;
+  if (K == 128 && V == 128) return run_v<E, 128, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+  if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+  if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+  return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_fwd_workspace_size(const gdn_params_t* p, int packed) {
+  Plan pl;
+  if (!p) return 0;
+  return make_plan(p, packed != 0, &pl) == GDN_OK ? pl.lay.total : 0;
+}
+
+gdn_status_t gdn_fwd_workspace_layout(const gdn_params_t* p, int packed,
+                                      gdn_workspace_layout_t* out) {
+  if (!p || !out) return GDN_ERR_NULL;
+  Plan pl;
+  gdn_status_t st = make_plan(p, packed != 0, &pl);
+  if (st == GDN_OK) *out = pl.lay;
+  return st;
+}
+
+gdn_status_t gdn_fwd_check(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                           const float* g_raw, const float* beta, const float* A_log,
+                           const float* dt_bias, const int64_t* cu_seqlens,
+                           const float* initial_state, const void* o, const float* final_state,
+                           const void* workspace, size_t workspace_bytes) {
+  Plan pl;
+  return check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                   final_state, workspace, workspace_bytes, &pl);
+}
+
+gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                     const float* g_raw, const float* beta, const float* A_log,
+                     const float* dt_bias, const int64_t* cu_seqlens, const float* initial_state,
+                     void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Plan pl;
+  gdn_status_t st = check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
+                              o, final_state, workspace, workspace_bytes, &pl);
+  if (st != GDN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == GDN_BF16)
+    return run_e<gdn::bf16>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                            final_state, workspace, s);
+  return run_e<float>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                      final_state, workspace, s);
+}
+
+const char* gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid shape";
+    case GDN_ERR_DTYPE: return "unsupported dtype";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size (K and V must be 64 or 128)";
+    case GDN_ERR_ALIGN: return "misaligned pointer";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

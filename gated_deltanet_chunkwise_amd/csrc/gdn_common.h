@@ -1,0 +1,130 @@
+// gdn_common.h -- gfx950 device helpers shared by the GDN kernels.
+//
+// MFMA fragments.  All contractions use 16x16 output tiles.  An output tile
+// ("D tile", f32x4 per lane) holds D[4*g + r][lane % 16] in element r, with
+// g = lane / 16: four consecutive rows of one column.
+//
+// Reductions run over blocks of 32 indices ("k32 blocks").  A k32 operand
+// fragment holds, per lane, 8 values at the k offsets
+//     kslot(g, i) = 4*g + i          for i = 0..3
+//                   16 + 4*g + (i-4) for i = 4..7
+// of the block, for the lane's row (A operand: row lane%16) or column
+// (B operand: column lane%16).  Any k order gives the same sum as long as the
+// A and B fragments agree; this one has the property that two D tiles covering
+// rows 0..15 and 16..31 of a block ARE a k32 fragment (element i<4 from the
+// first tile, i>=4 from the second), so a product's output feeds the next
+// product's reduction straight from registers with no LDS round trip.
+//
+//   bf16:  one v_mfma_f32_16x16x32_bf16 per k32 block (8 bf16 per lane).
+//   fp32:  eight v_mfma_f32_16x16x4_f32, the s-th taking element s of both
+//          fragments (k rows {kslot(g, s) : g = 0..3}, which are distinct).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;  // tokens per chunk
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <typename E> struct Frag;
+template <> struct Frag<bf16> { bf16x8 x; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+// Four consecutive elements (one D-tile lane's column segment), stored.
+template <typename E> struct Quad;
+template <> struct Quad<bf16> { bf16x4 x; };
+template <> struct Quad<float> { f32x4 x; };
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  return __builtin_convertvector(v, bf16x4);
+}
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) { return __builtin_convertvector(v, f32x4); }
+
+template <typename E> __device__ __forceinline__ Quad<E> make_quad(f32x4 v);
+template <> __device__ __forceinline__ Quad<bf16> make_quad<bf16>(f32x4 v) { return {to_bf16x4(v)}; }
+template <> __device__ __forceinline__ Quad<float> make_quad<float>(f32x4 v) { return {v}; }
+__device__ __forceinline__ f32x4 quad_f32(const Quad<bf16>& q) { return to_f32x4(q.x); }
+__device__ __forceinline__ f32x4 quad_f32(const Quad<float>& q) { return q.x; }
+
+// Two D tiles (rows 0..15 and 16..31 of a k32 block) -> a k32 fragment.
+template <typename E> __device__ __forceinline__ Frag<E> frag_from_tiles(f32x4 d0, f32x4 d1);
+template <> __device__ __forceinline__ Frag<bf16> frag_from_tiles<bf16>(f32x4 d0, f32x4 d1) {
+  bf16x4 a = to_bf16x4(d0), b = to_bf16x4(d1);
+  return {__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)};
+}
+template <> __device__ __forceinline__ Frag<float> frag_from_tiles<float>(f32x4 d0, f32x4 d1) {
+  return {d0, d1};
+}
+
+// k32 fragment from a row-major matrix row: `row` points at element 32*kb of
+// the lane's row (A operand) or column-as-row (B operand).  Works for LDS and
+// global pointers; both 4-element pieces must be 8-byte (bf16) / 16-byte
+// (fp32) aligned.
+__device__ __forceinline__ Frag<bf16> frag_from_row(const bf16* row) {
+  const int g = lane_id() >> 4;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 4 * g);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 16 + 4 * g);
+  return {__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)};
+}
+__device__ __forceinline__ Frag<float> frag_from_row(const float* row) {
+  const int g = lane_id() >> 4;
+  return {*reinterpret_cast<const f32x4*>(row + 4 * g),
+          *reinterpret_cast<const f32x4*>(row + 16 + 4 * g)};
+}
+
+// acc += A * B over one k32 block.
+__device__ __forceinline__ void mma_k32(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x, b.x, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_k32(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[s], b.lo[s], acc, 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
+}
+
+// Plain fp32 16x16x4 MFMA (A[m=lane%16][k=lane/16], B[k=lane/16][n=lane%16]).
+__device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Chunk geometry shared by all kernels (passed by value).
+struct Geo {
+  int B, T, H, HV, K, V, N;  // N = number of sequences
+  int G;                     // HV / H: value heads per key head
+  int NT;                    // chunks per sequence without cu_seqlens
+  int slots;                 // chunk slots
+  float scale;
+};
+
+// Chunk slot -> (sequence, absolute first token, length).  Returns false for
+// an unused slot (packed sequences only).
+template <bool VARLEN>
+__device__ __forceinline__ bool chunk_of_slot(const Geo& geo, const int4* cmap, int slot,
+                                              int& n, int64_t& t0, int& len) {
+  if constexpr (VARLEN) {
+    int4 e = cmap[slot];
+    n = e.x;
+    t0 = e.y;
+    len = e.z;
+    return e.z > 0;
+  } else {
+    n = slot / geo.NT;
+    int c = slot - n * geo.NT;
+    t0 = (int64_t)n * geo.T + (int64_t)c * kChunk;
+    len = min(kChunk, geo.T - c * kChunk);
+    return true;
+  }
+}
+
+}  // namespace gdn

@@ -1,0 +1,560 @@
+// gdn_kernels.h -- gfx950 kernels of the GDN chunkwise forward pass.
+//
+// Pipeline (one stream, no host sync):
+//   chunk map  (packed sequences only)  cu_seqlens -> chunk slot table
+//   prologue   g = -exp(A_log) softplus(g_raw + dt_bias); chunk-local cumsum
+//              G (times log2 e) and beta, both stored [HV][slot][64]: stride 1
+//              along T, the relayout the G_T_CONTIG page does with a host
+//              transpose, fused here into the producing kernel.
+//   WY         per (slot, hv): A = strictly_lower(beta_i k_i.k_j e^{G_i-G_j}),
+//              T = (I+A)^-1, w = T diag(beta e^G) K, u = T diag(beta) V and
+//              kd^T = (diag(e^{G_last-G}) K)^T.
+//   chain      per (sequence, hv, 16 value columns): sequential over chunks,
+//              state H (K x 16 fp32) in registers:
+//                 v_new = u - w H;  H <- e^{G_last} H + kd^T v_new
+//              stores the chunk-start state and v_new for the output stage.
+//   output     per (slot, hv): o = scale [ diag(e^G) Q H_c + (Q K^T * causal *
+//              e^{G_i-G_j}) v_new ]  (the chunk_fwd_o stage of the Ascend GDN
+//              blog, with its inter-chunk q.S and intra-chunk masked QK^T terms).
+//
+// Intermediates are stored "fragment-major": every per-chunk tensor is laid
+// out in the exact per-lane order in which its consumer feeds it to the MFMA
+// (see gdn_common.h), so producer stores and consumer loads are single
+// 8/16/32-byte accesses per lane, contiguous across the wave.
+#pragma once
+#include "gdn_common.h"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// Small vector helpers: 8 consecutive elements, loaded/stored as 16/32 bytes.
+__device__ __forceinline__ void ld8(const bf16* p, float (&e)[8]) {
+  bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = (float)t[j];
+}
+__device__ __forceinline__ void ld8(const float* p, float (&e)[8]) {
+  f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { e[j] = a[j]; e[4 + j] = b[j]; }
+}
+__device__ __forceinline__ void st8(bf16* p, const float (&e)[8]) {
+  bf16x8 t;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t[j] = (bf16)e[j];
+  *reinterpret_cast<bf16x8*>(p) = t;
+}
+__device__ __forceinline__ void st8(float* p, const float (&e)[8]) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{e[0], e[1], e[2], e[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{e[4], e[5], e[6], e[7]};
+}
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<bf16x4*>(p) = to_bf16x4(f32x4{a, b, c, d});
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Multiply element i of a k32 fragment by s[i] (in fp32, rounded back once).
+__device__ __forceinline__ Frag<bf16> frag_scale(const Frag<bf16>& f, const float (&s)[8]) {
+  f32x4 lo = to_f32x4(__builtin_shufflevector(f.x, f.x, 0, 1, 2, 3));
+  f32x4 hi = to_f32x4(__builtin_shufflevector(f.x, f.x, 4, 5, 6, 7));
+  lo *= f32x4{s[0], s[1], s[2], s[3]};
+  hi *= f32x4{s[4], s[5], s[6], s[7]};
+  return frag_from_tiles<bf16>(lo, hi);
+}
+__device__ __forceinline__ Frag<float> frag_scale(const Frag<float>& f, const float (&s)[8]) {
+  return {f.lo * f32x4{s[0], s[1], s[2], s[3]}, f.hi * f32x4{s[4], s[5], s[6], s[7]}};
+}
+
+// k offset (0..31) of fragment element i for lane group g.
+__device__ __forceinline__ int kslot(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
+
+// ---------------------------------------------------------------------------
+// Chunk map for packed sequences (G_T_CONTIG page, "varlen checklist": int64
+// offsets, chunk positions relative to each sequence start).  One workgroup.
+// Offsets are clamped to [0, T] and made non-decreasing (running maximum), so
+// the table never addresses outside the buffers even for malformed input;
+// for valid input this is the identity.  Writes cmap[slot] = (seq, first
+// token, length, 0) for used slots, (-1, 0, 0, 0) for the rest, and
+// seq_slot[n] = first slot of sequence n, seq_slot[N] = slots used.
+__global__ __launch_bounds__(256) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu, int N,
+                                                            int T, int slots,
+                                                            int4* __restrict__ cmap,
+                                                            int* __restrict__ seq_slot) {
+  __shared__ int64_t smax[256];
+  __shared__ int ssum[256];
+  __shared__ int64_t carry_b;
+  __shared__ int carry_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    carry_b = min(max(cu[0], (int64_t)0), (int64_t)T);
+    carry_s = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < N; base += 256) {
+    const int n = base + tid;
+    smax[tid] = (n < N) ? min(max(cu[n + 1], (int64_t)0), (int64_t)T) : (int64_t)0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int64_t y = tid >= off ? smax[tid - off] : (int64_t)0;
+      __syncthreads();
+      smax[tid] = max(smax[tid], y);
+      __syncthreads();
+    }
+    const int64_t cb = carry_b;
+    const int64_t e = max(smax[tid], cb);
+    const int64_t b = tid == 0 ? cb : max(smax[tid - 1], cb);
+    const int len = (n < N) ? (int)(e - b) : 0;
+    const int nch = (len + kChunk - 1) / kChunk;
+    ssum[tid] = nch;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int y = tid >= off ? ssum[tid - off] : 0;
+      __syncthreads();
+      ssum[tid] += y;
+      __syncthreads();
+    }
+    const int s0 = carry_s + ssum[tid] - nch;
+    if (n < N) {
+      seq_slot[n] = min(s0, slots);
+      for (int c = 0; c < nch; ++c) {
+        const int s = s0 + c;
+        if (s < slots) cmap[s] = make_int4(n, (int)(b + (int64_t)kChunk * c), min(kChunk, len - kChunk * c), 0);
+      }
+    }
+    __syncthreads();
+    if (tid == 255) {
+      carry_b = max(smax[255], cb);
+      carry_s += ssum[255];
+    }
+    __syncthreads();
+  }
+  const int used = min(carry_s, slots);
+  for (int s = used + tid; s < slots; s += 256) cmap[s] = make_int4(-1, 0, 0, 0);
+  if (tid == 0) seq_slot[N] = used;
+}
+
+// ---------------------------------------------------------------------------
+// Gate prologue.  One workgroup per chunk slot.  The 64 x HV tiles of g_raw and
+// beta are read coalesced (HV contiguous) into LDS, then one wave per head
+// evaluates the gate in fp32 (softplus threshold 20 as in the KDA gate guide,
+// "core computation logic"), scans along the 64 tokens and writes the
+// chunk's row for that head: stride 1 along T.
+// Padding past a chunk's end: g = 0 (so G stays at its last value) and beta = 0.
+template <bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_prologue_kernel(Geo geo, const float* __restrict__ g_raw,
+                                                           const float* __restrict__ beta,
+                                                           const float* __restrict__ A_log,
+                                                           const float* __restrict__ dt_bias,
+                                                           const int4* __restrict__ cmap,
+                                                           float* __restrict__ gam,
+                                                           float* __restrict__ bet) {
+  constexpr int HG = 32;  // heads per LDS pass
+  __shared__ float sa[kChunk][HG + 1];
+  __shared__ float sb[kChunk][HG + 1];
+  const int slot = blockIdx.x;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int HV = geo.HV, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int hb = 0; hb < HV; hb += HG) {
+    const int nh = min(HG, HV - hb);
+    __syncthreads();
+    for (int i = tid; i < len * nh; i += 256) {
+      const int t = i / nh, j = i - t * nh;
+      const int64_t src = (t0 + t) * HV + hb + j;
+      sa[t][j] = g_raw[src];
+      sb[t][j] = beta[src];
+    }
+    __syncthreads();
+    for (int j = wave; j < nh; j += 4) {
+      const int hv = hb + j;
+      float g = 0.f, b = 0.f;
+      if (lane < len) {
+        const float x = sa[lane][j] + (dt_bias ? dt_bias[hv] : 0.f);
+        const float sp = x > 20.f ? x : log1pf(expf(x));
+        g = -expf(A_log[hv]) * sp;
+        b = sb[lane][j];
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off, 64);
+        if (lane >= off) g += y;
+      }
+      const size_t o = ((size_t)hv * geo.slots + slot) * kChunk + lane;
+      gam[o] = g * kLog2e;
+      bet[o] = b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WY representation.  One workgroup (4 waves) per (chunk slot, value head).
+//
+// LDS: K natural [64][K] (later reused for T_w, T_u), K^T [K][64], V^T [V][64],
+// A and T (fp32 [64][64]).  Rows past the chunk end are zero.
+//
+// T = (I + A)^-1 is unit lower triangular.  Its 16x16 diagonal blocks are
+// found by forward substitution (one lane per column), the off-diagonal
+// blocks block-row by block-row:  T_rc = -T_rr sum_{m=c}^{r-1} A_rm T_mc,
+// on fp32 MFMAs.
+//
+// Outputs (fragment-major, dtype E):
+//   wf  [hv][slot][ct<4][kb<K/32][lane]   A operand of  w H        (rows c, k over K)
+//   ktf [hv][slot][mt<K/16][cb<2][lane]   A operand of  kd^T v_new (rows K, k over c)
+//   uf  [hv][slot][vt<V/16][ct<4][lane]   D tile (4 values) of u   (rows c, column v)
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
+                                                     const E* __restrict__ vg,
+                                                     const int4* __restrict__ cmap,
+                                                     const float* __restrict__ gam,
+                                                     const float* __restrict__ bet,
+                                                     Frag<E>* __restrict__ wf,
+                                                     Frag<E>* __restrict__ ktf,
+                                                     Quad<E>* __restrict__ uf) {
+  constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
+  constexpr int KS = K + P;          // K natural row stride
+  constexpr int CS = kChunk + P;     // K^T, V^T, T_w, T_u row stride
+  constexpr int FS = kChunk + 4;     // A, T row stride (fp32)
+  constexpr int R0 = (kChunk * KS > 2 * kChunk * CS) ? kChunk * KS : 2 * kChunk * CS;
+  __shared__ __align__(16) E r0[R0];
+  __shared__ __align__(16) E Kt[K * CS];
+  __shared__ __align__(16) E Vt[V * CS];
+  __shared__ __align__(16) float As[kChunk * FS];
+  __shared__ __align__(16) float Ts[kChunk * FS];
+  __shared__ float sg[kChunk], sb[kChunk];
+  E* const Ks = r0;
+  E* const Tw = r0;
+  E* const Tu = r0 + kChunk * CS;
+
+  const int slot = blockIdx.x, hv = blockIdx.y;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+
+  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
+  else if (tid < 2 * kChunk) sb[tid - kChunk] = bet[hs * kChunk + tid - kChunk];
+
+  // K tile: 4x8 micro-tiles, stored natural and transposed.
+  for (int m = tid; m < 16 * (K / 8); m += 256) {
+    const int rb = 4 * (m / (K / 8)), c0 = 8 * (m % (K / 8));
+    float e[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (rb + r < len) ld8(kg + ((t0 + rb + r) * geo.H + h) * K + c0, e[r]);
+      else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
+      }
+      st8(Ks + (rb + r) * KS + c0, e[r]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st4(Kt + (c0 + j) * CS + rb, e[0][j], e[1][j], e[2][j], e[3][j]);
+  }
+  // V tile, transposed only.
+  for (int m = tid; m < 16 * (V / 8); m += 256) {
+    const int rb = 4 * (m / (V / 8)), c0 = 8 * (m % (V / 8));
+    float e[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (rb + r < len) ld8(vg + ((t0 + rb + r) * geo.HV + hv) * V + c0, e[r]);
+      else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st4(Vt + (c0 + j) * CS + rb, e[0][j], e[1][j], e[2][j], e[3][j]);
+  }
+  __syncthreads();
+
+  // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)); wave w owns row tile w.
+  for (int jt = 0; jt <= wave; ++jt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb)
+      mma_k32(acc, frag_from_row(Ks + (16 * wave + lc) * KS + 32 * kb),
+              frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * wave + 4 * g + r, col = 16 * jt + lc;
+      As[row * FS + col] = col < row ? sb[row] * acc[r] * fast_exp2(sg[row] - sg[col]) : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // Diagonal blocks of T by forward substitution; zero the blocks above them.
+  {
+    const int b = wave;
+    if (lane < 16) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) s -= As[(16 * b + i) * FS + 16 * b + m] * x[m];
+        x[i] = s;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Ts[(16 * b + i) * FS + 16 * b + lane] = x[i];
+    }
+    const int wcols = 16 * (3 - b);
+    for (int idx = lane; idx < 16 * wcols; idx += 64)
+      Ts[(16 * b + idx / wcols) * FS + 16 * (b + 1) + idx % wcols] = 0.f;
+  }
+  __syncthreads();
+
+  // Off-diagonal blocks, one block row at a time.
+  for (int r = 1; r < 4; ++r) {
+    if (wave < r) {
+      const int c = wave;
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+      for (int m = c; m < r; ++m)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          X = mfma_f32_4(As[(16 * r + lc) * FS + 16 * m + 4 * ks + g],
+                         Ts[(16 * m + 4 * ks + g) * FS + 16 * c + lc], X);
+      // Y = T_rr X, with X's D tile used directly as the B operand:
+      // MFMA q reduces over k = 4*g + q for lane group g.
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Y = mfma_f32_4(Ts[(16 * r + lc) * FS + 16 * r + 4 * g + q], X[q], Y);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Ts[(16 * r + 4 * g + q) * FS + 16 * c + lc] = -Y[q];
+    }
+    __syncthreads();
+  }
+
+  // T_w = T diag(beta e^G), T_u = T diag(beta) in the operand dtype.
+  for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
+    const int i = idx >> 6, j = idx & 63;
+    const float t = Ts[i * FS + j] * sb[j];
+    Tw[i * CS + j] = (E)(t * fast_exp2(sg[j]));
+    Tu[i * CS + j] = (E)t;
+  }
+  __syncthreads();
+
+  // w^T = K^T T_w^T: wave w owns chunk-row tile ct = w; D tile (mt) holds
+  // w[16ct + lane%16][16mt + 4g + r], so tile pairs are the chain's A fragments.
+  {
+    const int ct = wave;
+    f32x4 acc[K / 16];
+#pragma unroll
+    for (int mt = 0; mt < K / 16; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        mma_k32(acc[mt], frag_from_row(Kt + (16 * mt + lc) * CS + 32 * cb),
+                frag_from_row(Tw + (16 * ct + lc) * CS + 32 * cb));
+    }
+    Frag<E>* dst = wf + (hs * 4 + ct) * (K / 32) * 64;
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) dst[kb * 64 + lane] = frag_from_tiles<E>(acc[2 * kb], acc[2 * kb + 1]);
+  }
+  // u = T_u V: wave w owns chunk-row tile ct = w.
+  {
+    const int ct = wave;
+    Quad<E>* dst = uf + hs * (V / 16) * 4 * 64;
+#pragma unroll
+    for (int vt = 0; vt < V / 16; ++vt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        mma_k32(acc, frag_from_row(Tu + (16 * ct + lc) * CS + 32 * cb),
+                frag_from_row(Vt + (16 * vt + lc) * CS + 32 * cb));
+      dst[(vt * 4 + ct) * 64 + lane] = make_quad<E>(acc);
+    }
+  }
+  // kd^T = (diag(e^{G_last - G}) K)^T as A fragments over the chunk index.
+  {
+    Frag<E>* dst = ktf + hs * (K / 16) * 2 * 64;
+    const float gl = sg[kChunk - 1];
+    for (int f = wave; f < (K / 16) * 2; f += 4) {
+      const int mt = f >> 1, cb = f & 1;
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = fast_exp2(gl - sg[32 * cb + kslot(g, i)]);
+      dst[f * 64 + lane] = frag_scale(frag_from_row(Kt + (16 * mt + lc) * CS + 32 * cb), s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inter-chunk state pass.  One wave per (sequence, value head, 16 value
+// columns); the K x 16 fp32 state lives in registers as K/16 D tiles
+// (rows k, column v).  Per chunk, in order:
+//   store H_c (the chunk-start state) for the output stage,
+//   v_new = u - w H_c            (B operand: the state tiles, paired),
+//   store v_new,
+//   H <- e^{G_last} H + kd^T v_new (B operand: the v_new tiles, paired).
+// Outputs (fragment-major, dtype E):
+//   hcf [hv][slot][vt][kb<K/32][lane]  A operand of H_c^T q^T (rows v, k over K)
+//   vnf [hv][slot][vt][cb<2][lane]     A operand of v_new^T P^T (rows v, k over c)
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* __restrict__ wf,
+                                                       const Frag<E>* __restrict__ ktf,
+                                                       const Quad<E>* __restrict__ uf,
+                                                       const float* __restrict__ gam,
+                                                       const int* __restrict__ seq_slot,
+                                                       const float* __restrict__ h0,
+                                                       float* __restrict__ fin,
+                                                       Frag<E>* __restrict__ hcf,
+                                                       Frag<E>* __restrict__ vnf) {
+  constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
+  const int unit = blockIdx.x;
+  const int vt = unit % NV, nh = unit / NV;
+  const int hv = nh % geo.HV, n = nh / geo.HV;
+  if (n >= geo.N) return;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int lane = lane_id(), g = lane >> 4, lc = lane & 15;
+  const int v = 16 * vt + lc;
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+
+  f32x4 Hs[KT];
+#pragma unroll
+  for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Hs[mt][r] = h0 ? h0[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] : 0.f;
+
+  for (int s = s0; s < s1; ++s) {
+    const size_t hs = (size_t)hv * geo.slots + s;
+    Frag<E> hb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      hb[kb] = frag_from_tiles<E>(Hs[2 * kb], Hs[2 * kb + 1]);
+      hcf[((hs * NV + vt) * KB + kb) * 64 + lane] = hb[kb];
+    }
+    f32x4 vn[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) mma_k32(p, wf[((hs * 4 + ct) * KB + kb) * 64 + lane], hb[kb]);
+      vn[ct] = quad_f32(uf[((hs * NV + vt) * 4 + ct) * 64 + lane]) - p;
+    }
+    Frag<E> vb[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      vb[cb] = frag_from_tiles<E>(vn[2 * cb], vn[2 * cb + 1]);
+      vnf[((hs * NV + vt) * 2 + cb) * 64 + lane] = vb[cb];
+    }
+    const float dec = fast_exp2(gam[hs * kChunk + kChunk - 1]);
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      Hs[mt] *= dec;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) mma_k32(Hs[mt], ktf[((hs * KT + mt) * 2 + cb) * 64 + lane], vb[cb]);
+    }
+  }
+  if (fin) {
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Output.  One workgroup (4 waves) per (chunk slot, value head), computing
+// o^T (V x 64) so that the state and v_new fragments written by the chain are
+// the A operands and rows of Q / P^T are the B operands:
+//   P^T = K Q^T * [j <= i] * e^{G_i - G_j}   (wave w: token tile i = w)
+//   o^T = e^{G_i} (H_c^T Q^T) + v_new^T P^T, times scale  (wave w: value tiles w, w+4)
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __restrict__ qg,
+                                                         const E* __restrict__ kg,
+                                                         const int4* __restrict__ cmap,
+                                                         const float* __restrict__ gam,
+                                                         const Frag<E>* __restrict__ hcf,
+                                                         const Frag<E>* __restrict__ vnf,
+                                                         E* __restrict__ og) {
+  constexpr int P = 16 / sizeof(E), KS = K + P, NV = V / 16, KB = K / 32;
+  __shared__ __align__(16) E Qs[kChunk * KS];
+  __shared__ __align__(16) E Ks[kChunk * KS];
+  __shared__ __align__(16) Frag<E> Pb[4][2][64];
+  __shared__ float sg[kChunk];
+
+  const int slot = blockIdx.x, hv = blockIdx.y;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+
+  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
+  for (int m = tid; m < kChunk * (K / 8); m += 256) {
+    const int row = m / (K / 8), c0 = 8 * (m % (K / 8));
+    float eq[8], ek[8];
+    if (row < len) {
+      ld8(qg + ((t0 + row) * geo.H + h) * K + c0, eq);
+      ld8(kg + ((t0 + row) * geo.H + h) * K + c0, ek);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) eq[j] = ek[j] = 0.f;
+    }
+    st8(Qs + row * KS + c0, eq);
+    st8(Ks + row * KS + c0, ek);
+  }
+  __syncthreads();
+
+  {
+    const int it = wave;
+    f32x4 pt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt <= it) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mma_k32(pt[jt], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
+                  frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
+        const int i = 16 * it + lc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * g + r;
+          pt[jt][r] = j <= i ? pt[jt][r] * fast_exp2(sg[i] - sg[j]) : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) Pb[it][jb][lane] = frag_from_tiles<E>(pt[2 * jb], pt[2 * jb + 1]);
+  }
+  __syncthreads();
+
+  for (int vt = wave; vt < NV; vt += 4) {
+    Frag<E> hc[KB], vn[2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hc[kb] = hcf[((hs * NV + vt) * KB + kb) * 64 + lane];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) vn[jb] = vnf[((hs * NV + vt) * 2 + jb) * 64 + lane];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[kb], frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
+      acc *= fast_exp2(sg[16 * it + lc]);
+#pragma unroll
+      for (int jb = 0; jb <= (it >> 1); ++jb) mma_k32(acc, vn[jb], Pb[it][jb][lane]);
+      acc *= geo.scale;
+      const int i = 16 * it + lc;
+      if (i < len) {
+        E* dst = og + ((t0 + i) * geo.HV + hv) * V + 16 * vt + 4 * g;
+        st4(dst, acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+  }
+}
+
+}  // namespace gdn

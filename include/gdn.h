@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of libgdn, the MI355X (gfx950) Gated DeltaNet chunkwise
+ * forward pass.
+ *
+ * The operation.  For every sequence and value head the library evaluates the
+ * gated delta rule (the "stateful linear recurrent layer" of the Ascend GDN
+ * blog, section "GDN sequence structure and Triton introduction": linear
+ * attention + gating + the delta rule, one fixed-size state per head updated
+ * token by token):
+ *
+ *     g_t = -exp(A_log[hv]) * softplus(g_raw_t + dt_bias[hv])
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * The gate is the per-head scalar case of the KDA gate guide (MindSpeed-Ops
+ * issue page, "core computation logic"), softplus(x) = x for x > 20 and
+ * log(1 + exp(x)) otherwise, evaluated in fp32 ("numerical stability": fp32
+ * inside, cast at the output).  The state S_t (V x K) is exposed as its
+ * transpose H = S^T: initial_state / final_state are [N][HV][K][V] fp32 with
+ * element [n][hv][i][j] = S[j][i].
+ *
+ * It is computed chunkwise (chunks of 64 tokens, aligned to every sequence
+ * start, last chunk of a sequence possibly shorter) by four gfx950 kernels
+ * on the caller's stream: gate prologue + chunk-local cumsum (stride-1 along T,
+ * the layout fix of the G_T_CONTIG page, "fix: host transpose + stride-1
+ * pointer", done inside the kernel instead of on the host), the per-chunk WY
+ * representation, the sequential inter-chunk state pass, and the chunk
+ * output.  A fifth kernel builds the chunk map when cu_seqlens is given.
+ *
+ * Layouts (all contiguous, row-major, device memory):
+ *   q, k           [B][T][H][K]   dtype (GDN_BF16 or GDN_F32)
+ *   v              [B][T][HV][V]  dtype
+ *   g_raw, beta    [B][T][HV]     fp32 (beta already in (0,1); no activation applied)
+ *   A_log          [HV]           fp32
+ *   dt_bias        [HV]           fp32, may be NULL (treated as 0)
+ *   cu_seqlens     [N+1]          int64, may be NULL; see below
+ *   initial_state  [N][HV][K][V]  fp32, may be NULL (zero state)
+ *   o              [B][T][HV][V]  dtype (written)
+ *   final_state    [N][HV][K][V]  fp32, may be NULL (written)
+ *   workspace      gdn_fwd_workspace_size() bytes, 256-byte aligned
+ * Value head hv reads query/key head hv / (HV/H).
+ *
+ * Packed sequences (the G_T_CONTIG page, "varlen checklist"): with cu_seqlens
+ * given, B must be 1, T is the packed total, and sequence n covers tokens
+ * cu_seqlens[n] .. cu_seqlens[n+1]-1.  Offsets are int64.  Precondition
+ * (not checked, to avoid a device-to-host sync): cu_seqlens[0] == 0,
+ * cu_seqlens[N] == T, non-decreasing.  Offsets that break it are clamped on the
+ * device so that no access leaves the buffers; the results are then undefined.
+ * Empty sequences are allowed (final state = initial state).
+ *
+ * Ownership.  The caller owns every buffer.  The library never allocates,
+ * frees or synchronizes; gdn_fwd only enqueues kernels on `stream` (a
+ * hipStream_t, NULL = default stream) and returns.  It keeps no global mutable
+ * state and may be called concurrently on different streams with different
+ * workspaces.  Outputs and workspace must not overlap any input.
+ *
+ * Errors.  gdn_fwd validates every argument on the host first (the same checks
+ * as gdn_fwd_check); on failure it returns the status and enqueues nothing.
+ * A failed kernel launch returns GDN_ERR_LAUNCH.  Nothing is printed, thrown
+ * or aborted across the ABI.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* negative size, HV % H != 0, cu_seqlens with B != 1, ... */
+  GDN_ERR_DTYPE = 3,       /* dtype is not GDN_F32 or GDN_BF16 */
+  GDN_ERR_UNSUPPORTED = 4, /* K or V not in {64, 128}, or a size beyond the int32 index range */
+  GDN_ERR_ALIGN = 5,       /* a pointer is not aligned as required below */
+  GDN_ERR_WORKSPACE = 6,   /* workspace smaller than gdn_fwd_workspace_size() */
+  GDN_ERR_LAUNCH = 7       /* a kernel launch failed */
+} gdn_status_t;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+typedef struct {
+  int32_t B;        /* sequences (fixed length), or 1 with cu_seqlens */
+  int32_t T;        /* tokens per sequence, or the packed total with cu_seqlens */
+  int32_t H;        /* query/key heads */
+  int32_t HV;       /* value heads, a multiple of H */
+  int32_t K;        /* key/query head dim: 64 or 128 */
+  int32_t V;        /* value head dim: 64 or 128 */
+  int32_t num_seqs; /* N with cu_seqlens; ignored (N = B) without */
+  int32_t dtype;    /* gdn_dtype_t of q, k, v and o */
+  float scale;      /* multiplies every o_t; 1.0 gives o_t = S_t q_t */
+} gdn_params_t;
+
+/* Byte offsets of the intermediates inside the workspace, for inspection.
+ * Every per-chunk buffer is indexed by a chunk slot: slot = n*ceil(T/64) + c
+ * without cu_seqlens, or the position of the chunk in sequence order with
+ * cu_seqlens (num_slots = floor(T/64) + N is an upper bound there).
+ *   gamma [HV][num_slots][64] fp32  chunk-local cumsum of g, times log2(e)
+ *   beta  [HV][num_slots][64] fp32  beta in the same layout (0 past a chunk's end)
+ *   w, kt, u, hc, vn                 MFMA-fragment-ordered dtype tensors (see
+ *                                    the kernel sources for the lane order)
+ *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32 (cu_seqlens only) */
+typedef struct {
+  size_t gamma, beta, w, kt, u, hc, vn, chunk_map, seq_slot, total;
+  int32_t num_slots;
+  int32_t num_seqs;
+} gdn_workspace_layout_t;
+
+/* Workspace bytes gdn_fwd needs for these parameters (0 if they are invalid).
+ * `packed` != 0 for a call that will pass cu_seqlens.  Pure host function. */
+size_t gdn_fwd_workspace_size(const gdn_params_t *p, int packed);
+
+/* Fill *out with the workspace layout (`packed` as above).  Pure host function. */
+gdn_status_t gdn_fwd_workspace_layout(const gdn_params_t *p, int packed,
+                                      gdn_workspace_layout_t *out);
+
+/* Validate a gdn_fwd call without touching the GPU or dereferencing any device
+ * pointer: sizes, dtype, NULL-ness and alignment (q, k, v, o: 16 bytes;
+ * g_raw, beta, A_log, dt_bias, initial_state, final_state: 4 bytes;
+ * cu_seqlens: 8 bytes; workspace: 256 bytes) and workspace_bytes. */
+gdn_status_t gdn_fwd_check(const gdn_params_t *p, const void *q, const void *k,
+                           const void *v, const float *g_raw, const float *beta,
+                           const float *A_log, const float *dt_bias,
+                           const int64_t *cu_seqlens, const float *initial_state,
+                           const void *o, const float *final_state,
+                           const void *workspace, size_t workspace_bytes);
+
+/* The forward pass (see the top of this file).  Enqueues the kernels on
+ * `stream` (hipStream_t) and returns without waiting. */
+gdn_status_t gdn_fwd(const gdn_params_t *p, const void *q, const void *k, const void *v,
+                     const float *g_raw, const float *beta, const float *A_log,
+                     const float *dt_bias, const int64_t *cu_seqlens,
+                     const float *initial_state, void *o, float *final_state,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *gdn_status_string(gdn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

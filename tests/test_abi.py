@@ -1,0 +1,149 @@
+"""The C ABI boundary on the CPU: the library loads, exports every entry point
+include/gdn.h declares, and validates arguments without touching a GPU (no
+device pointer is ever dereferenced by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_chunkwise_amd as gdn
+from gated_deltanet_chunkwise_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EWS, ELAUNCH = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_binding.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gdn.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    seen = set()
+    for s in range(8):
+        msg = gdn.status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert gdn.status_string(99) == "unknown status"
+
+
+def P(**kw):
+    d = dict(B=2, T=200, H=4, HV=8, K=128, V=64, dtype=gdn.GDN_BF16, num_seqs=0, scale=1.0)
+    d.update(kw)
+    return gdn.make_params(**d)
+
+
+def ptrs(**over):
+    """12 fake, aligned, never-dereferenced addresses in gdn_fwd's order."""
+    names = ["q", "k", "v", "g_raw", "beta", "A_log", "dt_bias", "cu_seqlens",
+             "initial_state", "o", "final_state", "workspace"]
+    base = {n: 0x10000 * (i + 1) for i, n in enumerate(names)}
+    base["cu_seqlens"] = None
+    base.update(over)
+    return [base[n] for n in names]
+
+
+def test_valid_call_checks_ok():
+    p = P()
+    ws = gdn.workspace_size(p)
+    assert gdn.check(p, ptrs(), ws) == OK
+    assert gdn.check(p, ptrs(initial_state=None, final_state=None, dt_bias=None), ws) == OK
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g_raw", "beta", "A_log", "o", "workspace"])
+def test_required_pointer_null(name):
+    p = P()
+    assert gdn.check(p, ptrs(**{name: None}), gdn.workspace_size(p)) == ENULL
+
+
+@pytest.mark.parametrize("name,addr", [("q", 0x10008), ("o", 0x10004), ("v", 0x10002),
+                                       ("g_raw", 0x10002), ("beta", 0x10001),
+                                       ("A_log", 0x10003), ("initial_state", 0x10002),
+                                       ("final_state", 0x10001), ("workspace", 0x10080)])
+def test_misaligned(name, addr):
+    p = P()
+    assert gdn.check(p, ptrs(**{name: addr}), gdn.workspace_size(p)) == EALIGN
+
+
+def test_workspace_too_small():
+    p = P()
+    assert gdn.check(p, ptrs(), gdn.workspace_size(p) - 1) == EWS
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(HV=6), ESHAPE),            # HV % H != 0
+    (dict(H=0), ESHAPE),
+    (dict(T=-1), ESHAPE),
+    (dict(B=-2), ESHAPE),
+    (dict(K=96), EUNSUP),
+    (dict(V=256), EUNSUP),
+    (dict(K=32), EUNSUP),
+    (dict(dtype=7), EDTYPE),
+])
+def test_bad_shapes(kw, status):
+    p = P(**kw)
+    assert gdn.check(p, ptrs(), 1 << 40) == status
+    assert gdn.workspace_size(p) == 0
+
+
+def test_packed_rules():
+    # cu_seqlens needs B == 1
+    assert gdn.check(P(num_seqs=3), ptrs(cu_seqlens=0x90000), 1 << 40) == ESHAPE
+    p = P(B=1, T=1000, num_seqs=3)
+    ws = gdn.workspace_size(p, packed=True)
+    assert gdn.check(p, ptrs(cu_seqlens=0x90000), ws) == OK
+    assert gdn.check(p, ptrs(cu_seqlens=0x90004), ws) == EALIGN
+    assert gdn.check(p, ptrs(cu_seqlens=0x90000), ws - 256) == EWS
+
+
+def test_empty_token_batch_needs_no_token_pointers():
+    p = P(T=0)
+    null = dict(q=None, k=None, v=None, g_raw=None, beta=None, A_log=None, o=None)
+    assert gdn.check(p, ptrs(**null), gdn.workspace_size(p)) == OK
+
+
+def test_workspace_layout():
+    for dtype, esz in ((gdn.GDN_BF16, 2), (gdn.GDN_F32, 4)):
+        for packed in (False, True):
+            B = 1 if packed else 3
+            p = P(B=B, T=1000, dtype=dtype, num_seqs=5 if packed else 0)
+            lay = gdn.workspace_layout(p, packed)
+            slots = 1000 // 64 + 5 if packed else B * ((1000 + 63) // 64)
+            assert lay.num_slots == slots
+            HV, K, V = 8, 128, 64
+            hsl = HV * slots
+            offs = [lay.gamma, lay.beta, lay.w, lay.kt, lay.u, lay.hc, lay.vn, lay.chunk_map,
+                    lay.seq_slot, lay.total]
+            assert all(o % 256 == 0 for o in offs)
+            assert offs == sorted(offs)
+            assert lay.beta - lay.gamma >= hsl * 64 * 4
+            assert lay.kt - lay.w >= hsl * 64 * K * esz
+            assert lay.u - lay.kt >= hsl * 64 * K * esz
+            assert lay.hc - lay.u >= hsl * 64 * V * esz
+            assert lay.vn - lay.hc >= hsl * K * V * esz
+            assert lay.chunk_map - lay.vn >= hsl * 64 * V * esz
+            if packed:
+                assert lay.seq_slot - lay.chunk_map >= slots * 16
+                assert lay.total - lay.seq_slot >= (5 + 1) * 4
+            assert lay.total == gdn.workspace_size(p, packed)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_binding, "_LIB", None)
+    monkeypatch.setattr(_binding, "_LIB_PATH", "/nonexistent/libgdn.so")
+    with pytest.raises(OSError):
+        _binding.load_library()

@@ -1,0 +1,128 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Small cases are compared in full; the full-size workloads (run in the same
+launch configuration bench.py times) are compared on sampled (sequence,
+value head) units whose o rows and final state the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_chunkwise_amd as gdn
+from gated_deltanet_chunkwise_amd.inputs import make_inputs, workload_inputs
+from gpu_helpers import assert_close, oracle_unit, run_gpu, run_oracle, say, unit_slices
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = "bf16", "fp32"
+
+
+def check_full(inp, tag):
+    say("case", tag, inp.shape)
+    o, fin = run_gpu(inp)
+    o_r, fin_r = run_oracle(inp)
+    dt = inp.q.dtype
+    assert_close(o, o_r, dt, tag + " o")
+    assert_close(fin, fin_r, dt, tag + " final")
+
+
+def test_tiny_fp32_workload():
+    check_full(workload_inputs("tiny_fp32"), "tiny_fp32")
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_ragged_gqa_h0(dtype, K, V):
+    # 300 = 4 full chunks + a 44-token tail; 2 value heads per key head; h0 != 0
+    inp = make_inputs(B=2, T=300, H=2, HV=4, K=K, V=V, dtype=dtype, seed=100 + K + V, h0=True,
+                      scale=0.75)
+    check_full(inp, "ragged_gqa_h0_%s_K%d_V%d" % (dtype, K, V))
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("T", [1, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 512])
+def test_block_edge_lengths(dtype, T):
+    # the block-edge lengths of the KDA gate precision sweep (page 4)
+    inp = make_inputs(B=2, T=T, H=2, HV=2, K=128, V=128, dtype=dtype, seed=200 + T)
+    check_full(inp, "edge_T%d_%s" % (T, dtype))
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_packed_edge_lengths(dtype):
+    lengths = [1, 63, 64, 65, 130, 0, 200, 64, 3]
+    inp = make_inputs(B=1, T=sum(lengths), H=2, HV=4, K=128, V=128, dtype=dtype, seed=300,
+                      lengths=lengths, h0=True)
+    check_full(inp, "packed_edges_%s" % dtype)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_slow_decay_long_memory(dtype):
+    # A_log in (-6, -3): chunk-level decays near 1, so the state carries across chunks
+    inp = make_inputs(B=1, T=1024, H=2, HV=2, K=128, V=128, dtype=dtype, seed=400,
+                      A_log_range=(-6.0, -3.0), h0=True)
+    check_full(inp, "slow_decay_%s" % dtype)
+
+
+def test_pages_workload_full():
+    # B=2, T=2048, H=HV=8, K=V=128 bf16: small enough to compare every unit
+    check_full(workload_inputs("pages_bf16"), "pages_bf16")
+
+
+def test_empty_and_zero_length():
+    # T = 0 with an initial state: o is empty and the final state equals h0
+    inp = make_inputs(B=2, T=0, H=1, HV=2, K=64, V=64, dtype=BF, seed=5, h0=True)
+    o, fin = run_gpu(inp)
+    assert o.shape == (2, 0, 2, 64)
+    assert np.array_equal(fin, inp.h0.numpy().astype(np.float64))
+
+
+def test_deterministic():
+    inp = make_inputs(B=1, T=700, H=2, HV=2, K=128, V=128, dtype=BF, seed=6, h0=True)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_and_resume_matches_one_call():
+    # the final state is a checkpoint: run [0, s) then [s, T) from it
+    inp = make_inputs(B=1, T=640, H=2, HV=2, K=128, V=128, dtype=F32, seed=7,
+                      A_log_range=(-5.0, -3.0))
+    o, fin = run_gpu(inp)
+    s = 300
+    import dataclasses
+    first = dataclasses.replace(inp, q=inp.q[:, :s], k=inp.k[:, :s], v=inp.v[:, :s],
+                                g_raw=inp.g_raw[:, :s], beta=inp.beta[:, :s])
+    o1, f1 = run_gpu(first)
+    second = dataclasses.replace(inp, q=inp.q[:, s:], k=inp.k[:, s:], v=inp.v[:, s:],
+                                 g_raw=inp.g_raw[:, s:], beta=inp.beta[:, s:],
+                                 h0=torch.from_numpy(f1).float())
+    o2, f2 = run_gpu(second)
+    assert_close(np.concatenate([o1, o2], axis=1), o, torch.float32, "resume o")
+    assert_close(f2, fin, torch.float32, "resume final")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled units
+
+def sampled_units(inp, count, seed):
+    s = inp.shape
+    rng = np.random.default_rng(seed)
+    total = s["N"] * s["HV"]
+    pick = sorted(set(rng.choice(total, size=min(count, total), replace=False).tolist()))
+    return [divmod(u, s["HV"]) for u in pick]
+
+
+@pytest.mark.parametrize("name,count", [("wide_bf16_h0", 6), ("packed_bf16", 8),
+                                        ("long_gqa_bf16", 4)])
+def test_full_size_workload_sampled(name, count):
+    inp = workload_inputs(name)
+    say("case", name, inp.shape)
+    o, fin = run_gpu(inp)
+    dt = inp.q.dtype
+    for n, hv in sampled_units(inp, count, seed=len(name)):
+        o_r, f_r = oracle_unit(inp, n, hv)
+        _, (b, sl) = unit_slices(inp, n, hv)
+        assert_close(o[b, sl, hv], o_r, dt, "%s o[n=%d,hv=%d]" % (name, n, hv))
+        assert_close(fin[n, hv], f_r, dt, "%s final[n=%d,hv=%d]" % (name, n, hv))
+    # every element written (outputs are NaN-filled before the call) and finite
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(fin))

@@ -1,0 +1,149 @@
+"""Per-kernel parity: decode the intermediates the kernels leave in the
+workspace (chunk-local cumsum, WY factors w/u, decayed keys, chunk-start
+states, v_new) and compare each with the chunkwise oracle's intermediates.
+
+The fragment orders decoded here are the ones the kernels document: a k32
+fragment holds, for lane l (g = l // 16), the k offsets
+4g + i (i < 4) and 16 + 4g + (i - 4) (i >= 4) of a 32-wide block; a D tile
+holds rows 4g + r of column l % 16.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_chunkwise_amd.inputs import make_inputs
+from gpu_helpers import f64, metrics, run_gpu, say
+import oracle
+from oracle import chunkwise
+
+pytestmark = pytest.mark.gpu
+
+LANE = np.arange(64)
+G_OF_LANE = LANE // 16
+LC = LANE % 16
+KSLOT = np.array([[4 * g + i if i < 4 else 12 + 4 * g + i for i in range(8)] for g in range(4)])
+
+
+def read(ws, off, count, dtype):
+    nbytes = count * (2 if dtype == torch.bfloat16 else 4)
+    raw = ws[off:off + nbytes]
+    return raw.view(dtype).float().cpu().numpy().astype(np.float64)
+
+
+def decode_w(buf, HV, slots, K):
+    """wf [hv][slot][ct<4][kb<K/32][lane][8] -> w[hv][slot][c][kk]."""
+    f = buf.reshape(HV, slots, 4, K // 32, 64, 8)
+    out = np.zeros((HV, slots, 64, K))
+    for ct in range(4):
+        for kb in range(K // 32):
+            for i in range(8):
+                out[:, :, 16 * ct + LC, 32 * kb + KSLOT[G_OF_LANE, i]] = f[:, :, ct, kb, :, i]
+    return out
+
+
+def decode_kt(buf, HV, slots, K):
+    """ktf [hv][slot][mt<K/16][cb<2][lane][8] -> kd[hv][slot][c][kk]."""
+    f = buf.reshape(HV, slots, K // 16, 2, 64, 8)
+    out = np.zeros((HV, slots, 64, K))
+    for mt in range(K // 16):
+        for cb in range(2):
+            for i in range(8):
+                out[:, :, 32 * cb + KSLOT[G_OF_LANE, i], 16 * mt + LC] = f[:, :, mt, cb, :, i]
+    return out
+
+
+def decode_u(buf, HV, slots, V):
+    """uf [hv][slot][vt][ct<4][lane][4] -> u[hv][slot][c][v]."""
+    f = buf.reshape(HV, slots, V // 16, 4, 64, 4)
+    out = np.zeros((HV, slots, 64, V))
+    for vt in range(V // 16):
+        for ct in range(4):
+            for r in range(4):
+                out[:, :, 16 * ct + 4 * G_OF_LANE + r, 16 * vt + LC] = f[:, :, vt, ct, :, r]
+    return out
+
+
+def decode_hc(buf, HV, slots, K, V):
+    """hcf [hv][slot][vt][kb][lane][8] -> H[hv][slot][kk][v]."""
+    f = buf.reshape(HV, slots, V // 16, K // 32, 64, 8)
+    out = np.zeros((HV, slots, K, V))
+    for vt in range(V // 16):
+        for kb in range(K // 32):
+            for i in range(8):
+                out[:, :, 32 * kb + KSLOT[G_OF_LANE, i], 16 * vt + LC] = f[:, :, vt, kb, :, i]
+    return out
+
+
+def decode_vn(buf, HV, slots, V):
+    """vnf [hv][slot][vt][cb<2][lane][8] -> v_new[hv][slot][c][v]."""
+    f = buf.reshape(HV, slots, V // 16, 2, 64, 8)
+    out = np.zeros((HV, slots, 64, V))
+    for vt in range(V // 16):
+        for cb in range(2):
+            for i in range(8):
+                out[:, :, 32 * cb + KSLOT[G_OF_LANE, i], 16 * vt + LC] = f[:, :, vt, cb, :, i]
+    return out
+
+
+def cmp(x, r, tol, what):
+    m = metrics(x, r)
+    say("  %-22s rel_l2=%.3e max_abs=%.3e" % (what, m["rel_l2"], m["max_abs"]))
+    assert np.all(np.isfinite(x)), what
+    assert m["rel_l2"] <= tol, (what, m)
+
+
+@pytest.mark.parametrize("dtype,tol", [("fp32", 2e-5), ("bf16", 1.5e-2)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_intermediates(dtype, tol, packed):
+    K = V = 128
+    if packed:
+        lengths = [70, 0, 64, 66]
+        inp = make_inputs(B=1, T=sum(lengths), H=1, HV=2, K=K, V=V, dtype=dtype, seed=9,
+                          lengths=lengths, h0=True, A_log_range=(-4.0, 0.0))
+    else:
+        inp = make_inputs(B=2, T=200, H=1, HV=2, K=K, V=V, dtype=dtype, seed=8, h0=True,
+                          A_log_range=(-4.0, 0.0))
+    say("case intermediates", dtype, "packed" if packed else "fixed", inp.shape)
+    plans = []
+    run_gpu(inp, plans)
+    plan = plans[0]
+    lay = plan.layout
+    s = inp.shape
+    HV, slots = s["HV"], lay.num_slots
+    ws = plan.workspace
+    et = inp.q.dtype
+    gam = read(ws, lay.gamma, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
+    bet = read(ws, lay.beta, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
+    w = decode_w(read(ws, lay.w, HV * slots * 64 * K, et), HV, slots, K)
+    kd = decode_kt(read(ws, lay.kt, HV * slots * 64 * K, et), HV, slots, K)
+    u = decode_u(read(ws, lay.u, HV * slots * 64 * V, et), HV, slots, V)
+    hc = decode_hc(read(ws, lay.hc, HV * slots * K * V, et), HV, slots, K, V)
+    vn = decode_vn(read(ws, lay.vn, HV * slots * 64 * V, et), HV, slots, V)
+
+    q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)
+    g = oracle.gate(f64(inp.g_raw), f64(inp.A_log), f64(inp.dt_bias))
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    _, _, kept = chunkwise.fwd(q, k, v, g, f64(inp.beta), cu_seqlens=cu, h0=f64(inp.h0),
+                               keep=True)
+    # chunk slots in sequence order
+    slot = 0
+    for n in range(s["N"]):
+        steps = kept[(n, 0)]
+        for c in range(len(steps)):
+            for hv in range(HV):
+                st = kept[(n, hv)][c]
+                L = len(st["G"])
+                tag = "n%d c%d hv%d" % (n, c, hv)
+                cmp(gam[hv, slot, :L], st["G"] * math.log2(math.e), 1e-5, tag + " gamma")
+                assert np.allclose(gam[hv, slot, L:], gam[hv, slot, L - 1]), tag + " gamma pad"
+                assert np.all(bet[hv, slot, L:] == 0), tag + " beta pad"
+                cmp(w[hv, slot, :L], st["w"], tol, tag + " w")
+                cmp(u[hv, slot, :L], st["u"], tol, tag + " u")
+                cmp(kd[hv, slot, :L], st["kdecay"], tol, tag + " kdecay")
+                cmp(hc[hv, slot], st["H0"], tol, tag + " chunk-start state")
+                cmp(vn[hv, slot, :L], st["v_new"], tol, tag + " v_new")
+                for name, arr in (("w", w), ("u", u), ("kd", kd), ("vn", vn)):
+                    assert not np.any(arr[hv, slot, L:]), tag + " %s rows past the end" % name
+            slot += 1
