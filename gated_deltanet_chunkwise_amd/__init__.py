@@ -11,7 +11,9 @@ from ._binding import (  # noqa: F401
     GDN_F32,
     GdnError,
     GdnForward,
+    NUM_STAGES,
     Params,
+    STAGES,
     WorkspaceLayout,
     check,
     fwd,
@@ -24,7 +26,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "Params", "WorkspaceLayout",
+    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "WorkspaceLayout",
     "check", "fwd", "lib_path", "load_library", "make_params", "status_string",
     "workspace_layout", "workspace_size",
 ]

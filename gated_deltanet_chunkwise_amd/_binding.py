@@ -14,7 +14,9 @@ GDN_F32 = 0
 GDN_BF16 = 1
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
-           "gdn_fwd", "gdn_status_string")
+           "gdn_fwd", "gdn_fwd_timed", "gdn_status_string")
+NUM_STAGES = 5
+STAGES = ("chunk_map", "prologue", "wy", "chain", "output")
 
 
 class Params(ctypes.Structure):
@@ -66,6 +68,8 @@ def _declare(lib):
     lib.gdn_fwd_check.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t]
     lib.gdn_fwd.restype = ctypes.c_int
     lib.gdn_fwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp]
+    lib.gdn_fwd_timed.restype = ctypes.c_int
+    lib.gdn_fwd_timed.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp, ctypes.c_void_p]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -145,7 +149,9 @@ class GdnForward:
                             if final_state else None)
 
     def __call__(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
-                 initial_state=None, stream=None):
+                 initial_state=None, stream=None, events=None):
+        """Launch on `stream` (default: torch's current stream).  `events`: optional
+        ctypes array of NUM_STAGES + 1 hipEvent_t recorded around the stages."""
         torch = _torch()
         if (cu_seqlens is not None) != self.packed:
             raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
@@ -156,14 +162,39 @@ class GdnForward:
                 raise ValueError("%s must be a contiguous GPU tensor" % name)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
-        st = self.lib.gdn_fwd(
-            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
-            _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
-            _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
-            ctypes.c_void_p(stream.cuda_stream))
+        args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
+                _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
+                _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
+                ctypes.c_void_p(stream.cuda_stream))
+        if events is None:
+            st = self.lib.gdn_fwd(*args)
+        else:
+            st = self.lib.gdn_fwd_timed(*args, ctypes.cast(events, ctypes.c_void_p))
         if st:
             raise GdnError(st)
         return self.o, self.final_state
+
+    def bind(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
+             initial_state=None, stream=None):
+        """Marshal the arguments once; returns a zero-argument callable that
+        launches the pass (for hot loops: no per-call Python checks)."""
+        torch = _torch()
+        self(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream)  # validate
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
+                _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
+                _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
+                ctypes.c_void_p(stream.cuda_stream))
+        keep = (q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state)
+        fn = self.lib.gdn_fwd
+
+        def launch():
+            keep  # the tensors stay alive as long as the callable
+            st = fn(*args)
+            if st:
+                raise GdnError(st)
+        return launch
 
 
 def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_state=None,

@@ -102,7 +102,7 @@ template <typename E, int K, int V, bool VARLEN>
 gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                  const float* beta, const float* A_log, const float* dt_bias,
                  const int64_t* cu_seqlens, const float* h0, void* o, float* fin, void* ws,
-                 hipStream_t s) {
+                 hipStream_t s, void* const* events) {
   using gdn::Frag;
   using gdn::Quad;
   const gdn::Geo& geo = pl.geo;
@@ -122,44 +122,57 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   const E* ve = static_cast<const E*>(v);
   E* oe = static_cast<E*>(o);
 
-  if (geo.N == 0) return GDN_OK;
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) {
     if (e != hipSuccess && err == hipSuccess) err = e;
   };
-  if (VARLEN) ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
-                        geo.slots, cmap, seq_slot));
-  if (geo.slots > 0) {
+  auto mark = [&](int i) {
+    if (events) ok(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
+  };
+  mark(0);
+  const bool work = geo.N > 0;
+  if (VARLEN && work)
+    ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
+              geo.slots, cmap, seq_slot));
+  mark(1);
+  if (work && geo.slots > 0)
     ok(launch(gdn::gdn_prologue_kernel<VARLEN>, dim3(geo.slots), dim3(256), s, geo, g_raw, beta,
               A_log, dt_bias, cmap, gam, bet));
+  mark(2);
+  if (work && geo.slots > 0)
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo, ke,
               ve, cmap, gam, bet, wf, ktf, uf));
-  }
-  ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(geo.N * geo.HV * (V / 16)), dim3(64), s,
-            geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
-  if (geo.slots > 0)
+  mark(3);
+  if (work)
+    ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(geo.N * geo.HV * (V / 16)), dim3(64),
+              s, geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+  mark(4);
+  if (work && geo.slots > 0)
     ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo,
               qe, ke, cmap, gam, hcf, vnf, oe));
+  mark(5);
   return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 template <typename E, int K, int V>
 gdn_status_t run_v(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                    const float* beta, const float* A_log, const float* dt_bias,
-                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s) {
-  return pl.varlen ? run<E, K, V, true>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s)
-                   : run<E, K, V, false>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s,
+                   void* const* ev) {
+  return pl.varlen ? run<E, K, V, true>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev)
+                   : run<E, K, V, false>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
 }
 
 template <typename E>
 gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                    const float* beta, const float* A_log, const float* dt_bias,
-                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s) {
+                   const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s,
+                   void* const* ev) {
   const int K = pl.geo.K, V = pl.geo.V;
-  if (K == 128 && V == 128) return run_v<E, 128, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
-  if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
-  if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
-  return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s);
+  if (K == 128 && V == 128) return run_v<E, 128, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
+  if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
+  if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
+  return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
 }
 
 }  // namespace
@@ -191,11 +204,12 @@ gdn_status_t gdn_fwd_check(const gdn_params_t* p, const void* q, const void* k, 
                    final_state, workspace, workspace_bytes, &pl);
 }
 
-gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const void* v,
-                     const float* g_raw, const float* beta, const float* A_log,
-                     const float* dt_bias, const int64_t* cu_seqlens, const float* initial_state,
-                     void* o, float* final_state, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+gdn_status_t gdn_fwd_timed(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                           const float* g_raw, const float* beta, const float* A_log,
+                           const float* dt_bias, const int64_t* cu_seqlens,
+                           const float* initial_state, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* events) {
   Plan pl;
   gdn_status_t st = check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
                               o, final_state, workspace, workspace_bytes, &pl);
@@ -203,9 +217,18 @@ gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->dtype == GDN_BF16)
     return run_e<gdn::bf16>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
-                            final_state, workspace, s);
+                            final_state, workspace, s, events);
   return run_e<float>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
-                      final_state, workspace, s);
+                      final_state, workspace, s, events);
+}
+
+gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                     const float* g_raw, const float* beta, const float* A_log,
+                     const float* dt_bias, const int64_t* cu_seqlens, const float* initial_state,
+                     void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return gdn_fwd_timed(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                       final_state, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* gdn_status_string(gdn_status_t s) {

@@ -136,6 +136,25 @@ gdn_status_t gdn_fwd(const gdn_params_t *p, const void *q, const void *k, const 
                      const float *initial_state, void *o, float *final_state,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Number of stages gdn_fwd_timed brackets with events: chunk map, gate
+ * prologue, WY, state pass, output. */
+#define GDN_NUM_STAGES 5
+
+/* gdn_fwd that also records timing events on `stream`, for profiling:
+ * events[0] before the first kernel and events[i] right after stage i
+ * (1..GDN_NUM_STAGES, order as above; a stage that does not run for these
+ * arguments, e.g. the chunk map without cu_seqlens, records its event at the
+ * same point as the previous one).  `events` holds GDN_NUM_STAGES + 1 hipEvent_t
+ * created by the caller; NULL makes this identical to gdn_fwd.  Same
+ * validation and errors as gdn_fwd; a failed event record returns
+ * GDN_ERR_LAUNCH. */
+gdn_status_t gdn_fwd_timed(const gdn_params_t *p, const void *q, const void *k,
+                           const void *v, const float *g_raw, const float *beta,
+                           const float *A_log, const float *dt_bias,
+                           const int64_t *cu_seqlens, const float *initial_state, void *o,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream, void *const *events);
+
 /* Static description of a status code. */
 const char *gdn_status_string(gdn_status_t s);
 
