@@ -2,6 +2,7 @@
 // and the launch sequence.  See include/gdn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <tuple>
 #include <utility>
@@ -23,6 +24,22 @@ struct Plan {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Compute units of the current device (cached per device id; a benign race
+// at worst stores the same value twice).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 // Shapes and sizes only (no pointers).
 gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   if (!p) return GDN_ERR_NULL;
@@ -37,7 +54,8 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   const int64_t ntok = varlen ? (int64_t)p->T : (int64_t)p->B * p->T;
   // Index arithmetic uses int32 for slots, units and tokens within a packed batch.
   const int64_t units = N * p->HV * (p->V / 16);
-  if (slots > INT32_MAX / 2 || units > INT32_MAX || N + 1 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  if (slots > INT32_MAX / 2 || slots * p->HV > INT32_MAX || units > INT32_MAX || N + 1 > INT32_MAX)
+    return GDN_ERR_UNSUPPORTED;
 
   Plan pl{};
   pl.varlen = varlen;
@@ -140,15 +158,23 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               A_log, dt_bias, cmap, gam, bet));
   mark(2);
   if (work && geo.slots > 0)
-    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo, ke,
+    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo, ke,
               ve, cmap, gam, bet, wf, ktf, uf));
   mark(3);
-  if (work)
-    ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(geo.N * geo.HV * (V / 16)), dim3(64),
-              s, geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+  if (work) {
+    // One CU per state-pass unit when they fit: the LDS-ring variant; otherwise
+    // many units share a CU and the register-buffered variant is used.
+    const int units = geo.N * geo.HV * (V / 16);
+    if (units <= device_cus())
+      ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN>, dim3(units), dim3(192), s, geo, wf,
+                ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+    else
+      ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo, wf, ktf,
+                uf, gam, seq_slot, h0, fin, hcf, vnf));
+  }
   mark(4);
   if (work && geo.slots > 0)
-    ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots, geo.HV), dim3(256), s, geo,
+    ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo,
               qe, ke, cmap, gam, hcf, vnf, oe));
   mark(5);
   return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;

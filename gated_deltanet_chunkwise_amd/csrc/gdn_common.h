@@ -127,4 +127,20 @@ __device__ __forceinline__ bool chunk_of_slot(const Geo& geo, const int4* cmap, 
   }
 }
 
+// Block id -> (value head, index within the head), such that every block of a
+// head lands on one XCD when HV is a multiple of 8 (workgroups are dispatched
+// to the 8 XCDs round-robin by id), keeping a head's intermediates in one L2.
+// A bijection of [0, HV * per_head) in both branches.
+__device__ __forceinline__ void head_major_block(int b, int HV, int per_head, int& hv, int& rest) {
+  if ((HV & 7) == 0) {
+    const int x = b & 7, j = b >> 3;
+    const int hl = j / per_head;
+    rest = j - hl * per_head;
+    hv = x + 8 * hl;
+  } else {
+    hv = b / per_head;
+    rest = b - hv * per_head;
+  }
+}
+
 }  // namespace gdn

@@ -203,7 +203,8 @@ __global__ __launch_bounds__(256) void gdn_prologue_kernel(Geo geo, const float*
 // Outputs (fragment-major, dtype E):
 //   wf  [hv][slot][ct<4][kb<K/32][lane]   A operand of  w H        (rows c, k over K)
 //   ktf [hv][slot][mt<K/16][cb<2][lane]   A operand of  kd^T v_new (rows K, k over c)
-//   uf  [hv][slot][vt<V/16][ct<4][lane]   D tile (4 values) of u   (rows c, column v)
+//   uf  [hv][slot][vt<V/16][cp<2][lane][2] D tiles ct = 2cp, 2cp+1 of u (rows c, column v);
+//                                         a lane's pair is one fragment-sized block
 template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
@@ -217,18 +218,23 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   constexpr int KS = K + P;          // K natural row stride
   constexpr int CS = kChunk + P;     // K^T, V^T, T_w, T_u row stride
   constexpr int FS = kChunk + 4;     // A, T row stride (fp32)
-  constexpr int R0 = (kChunk * KS > 2 * kChunk * CS) ? kChunk * KS : 2 * kChunk * CS;
-  __shared__ __align__(16) E r0[R0];
+  // Region 0 holds, in turn: K natural (until A is formed), A (until T is
+  // complete), then T_w and T_u.
+  constexpr int R0A = kChunk * KS * (int)sizeof(E), R0B = 2 * kChunk * CS * (int)sizeof(E);
+  constexpr int R0C = kChunk * FS * 4;
+  constexpr int R0 = R0A > R0B ? (R0A > R0C ? R0A : R0C) : (R0B > R0C ? R0B : R0C);
+  __shared__ __align__(16) char r0[R0];
   __shared__ __align__(16) E Kt[K * CS];
   __shared__ __align__(16) E Vt[V * CS];
-  __shared__ __align__(16) float As[kChunk * FS];
   __shared__ __align__(16) float Ts[kChunk * FS];
   __shared__ float sg[kChunk], sb[kChunk];
-  E* const Ks = r0;
-  E* const Tw = r0;
-  E* const Tu = r0 + kChunk * CS;
+  E* const Ks = reinterpret_cast<E*>(r0);
+  float* const As = reinterpret_cast<float*>(r0);
+  E* const Tw = reinterpret_cast<E*>(r0);
+  E* const Tu = Tw + kChunk * CS;
 
-  const int slot = blockIdx.x, hv = blockIdx.y;
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
@@ -272,31 +278,51 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   }
   __syncthreads();
 
-  // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)); wave w owns row tile w.
-  for (int jt = 0; jt <= wave; ++jt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)); wave w owns row tile
+  // w.  The products finish before A overwrites K natural in region 0.
+  {
+    f32x4 acc[4];
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb)
-      mma_k32(acc, frag_from_row(Ks + (16 * wave + lc) * KS + 32 * kb),
-              frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb));
+    for (int jt = 0; jt < 4; ++jt) {
+      acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt <= wave) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * wave + 4 * g + r, col = 16 * jt + lc;
-      As[row * FS + col] = col < row ? sb[row] * acc[r] * fast_exp2(sg[row] - sg[col]) : 0.f;
+        for (int kb = 0; kb < K / 32; ++kb)
+          mma_k32(acc[jt], frag_from_row(Ks + (16 * wave + lc) * KS + 32 * kb),
+                  frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      if (jt <= wave) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * wave + 4 * g + r, col = 16 * jt + lc;
+          As[row * FS + col] = col < row ? sb[row] * acc[jt][r] * fast_exp2(sg[row] - sg[col]) : 0.f;
+        }
+      }
     }
   }
   __syncthreads();
 
-  // Diagonal blocks of T by forward substitution; zero the blocks above them.
+  // Diagonal blocks of T by forward substitution (the block's strictly lower
+  // part is read into registers first, so the dependent chain runs on
+  // registers); zero the blocks above them.
   {
     const int b = wave;
     if (lane < 16) {
+      float a[16][16];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+#pragma unroll
+        for (int m = 0; m < i; ++m) a[i][m] = As[(16 * b + i) * FS + 16 * b + m];
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float s = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s -= As[(16 * b + i) * FS + 16 * b + m] * x[m];
+        for (int m = 0; m < i; ++m) s -= a[i][m] * x[m];
         x[i] = s;
       }
 #pragma unroll
@@ -366,7 +392,7 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
       for (int cb = 0; cb < 2; ++cb)
         mma_k32(acc, frag_from_row(Tu + (16 * ct + lc) * CS + 32 * cb),
                 frag_from_row(Vt + (16 * vt + lc) * CS + 32 * cb));
-      dst[(vt * 4 + ct) * 64 + lane] = make_quad<E>(acc);
+      dst[((vt * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)] = make_quad<E>(acc);
     }
   }
   // kd^T = (diag(e^{G_last - G}) K)^T as A fragments over the chunk index.
@@ -391,44 +417,45 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 //   v_new = u - w H_c            (B operand: the state tiles, paired),
 //   store v_new,
 //   H <- e^{G_last} H + kd^T v_new (B operand: the v_new tiles, paired).
+// A chunk's operands (w and kd^T fragments, the u tiles, e^{G_last}) are
+// loaded in one batch, one chunk ahead of their use (two register buffers), so
+// the loads of chunk c+1 are in flight while chunk c computes.
 // Outputs (fragment-major, dtype E):
 //   hcf [hv][slot][vt][kb<K/32][lane]  A operand of H_c^T q^T (rows v, k over K)
 //   vnf [hv][slot][vt][cb<2][lane]     A operand of v_new^T P^T (rows v, k over c)
-template <typename E, int K, int V, bool VARLEN>
-__global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* __restrict__ wf,
-                                                       const Frag<E>* __restrict__ ktf,
-                                                       const Quad<E>* __restrict__ uf,
-                                                       const float* __restrict__ gam,
-                                                       const int* __restrict__ seq_slot,
-                                                       const float* __restrict__ h0,
-                                                       float* __restrict__ fin,
-                                                       Frag<E>* __restrict__ hcf,
-                                                       Frag<E>* __restrict__ vnf) {
-  constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
-  const int unit = blockIdx.x;
-  const int vt = unit % NV, nh = unit / NV;
-  const int hv = nh % geo.HV, n = nh / geo.HV;
-  if (n >= geo.N) return;
-  int s0, s1;
-  if constexpr (VARLEN) {
-    s0 = seq_slot[n];
-    s1 = seq_slot[n + 1];
-  } else {
-    s0 = n * geo.NT;
-    s1 = s0 + geo.NT;
+template <typename E, int K, int V>
+struct ChainStep {
+  static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
+  Frag<E> w[4][KB];
+  Frag<E> kt[KT][2];
+  Quad<E> u[4];
+  float gl;  // lane l: entry l of the chunk's (log2-scaled) cumulative gate row
+
+  __device__ __forceinline__ void load(const Frag<E>* __restrict__ wf,
+                                       const Frag<E>* __restrict__ ktf,
+                                       const Quad<E>* __restrict__ uf,
+                                       const float* __restrict__ gam, size_t hs, int vt,
+                                       int lane) {
+    // Every lane loads one entry of the chunk's gate row (a vector load, issued
+    // first so it is the oldest of the batch; a scalar load would make every
+    // later LDS or scalar wait a full drain).  Lane 63 holds the last value.
+    gl = gam[hs * kChunk + lane];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) w[ct][kb] = wf[((hs * 4 + ct) * KB + kb) * 64 + lane];
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) kt[mt][cb] = ktf[((hs * KT + mt) * 2 + cb) * 64 + lane];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) u[ct] = uf[(((hs * NV + vt) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
   }
-  const int lane = lane_id(), g = lane >> 4, lc = lane & 15;
-  const int v = 16 * vt + lc;
-  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
 
-  f32x4 Hs[KT];
-#pragma unroll
-  for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Hs[mt][r] = h0 ? h0[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] : 0.f;
-
-  for (int s = s0; s < s1; ++s) {
-    const size_t hs = (size_t)hv * geo.slots + s;
+  // One chunk: consumes this step's operands, updates Hs, writes H_c and v_new.
+  __device__ __forceinline__ void compute(f32x4 (&Hs)[KT], Frag<E>* __restrict__ hcf,
+                                          Frag<E>* __restrict__ vnf, size_t hs, int vt,
+                                          int lane) const {
     Frag<E> hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -440,8 +467,8 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
     for (int ct = 0; ct < 4; ++ct) {
       f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma_k32(p, wf[((hs * 4 + ct) * KB + kb) * 64 + lane], hb[kb]);
-      vn[ct] = quad_f32(uf[((hs * NV + vt) * 4 + ct) * 64 + lane]) - p;
+      for (int kb = 0; kb < KB; ++kb) mma_k32(p, w[ct][kb], hb[kb]);
+      vn[ct] = quad_f32(u[ct]) - p;
     }
     Frag<E> vb[2];
 #pragma unroll
@@ -449,12 +476,88 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
       vb[cb] = frag_from_tiles<E>(vn[2 * cb], vn[2 * cb + 1]);
       vnf[((hs * NV + vt) * 2 + cb) * 64 + lane] = vb[cb];
     }
-    const float dec = fast_exp2(gam[hs * kChunk + kChunk - 1]);
+    // gl holds the chunk's gate row, one entry per lane; the decay uses the last.
+    const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
       Hs[mt] *= dec;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mma_k32(Hs[mt], ktf[((hs * KT + mt) * 2 + cb) * 64 + lane], vb[cb]);
+      for (int cb = 0; cb < 2; ++cb) mma_k32(Hs[mt], kt[mt][cb], vb[cb]);
+    }
+  }
+};
+
+// Initial state tiles (rows 16*mt + 4g + r, column v) from h0, or zero.
+template <int K, int V>
+__device__ __forceinline__ void load_state(f32x4 (&Hs)[K / 16], const float* __restrict__ h0,
+                                           size_t sbase, int v, int g) {
+  if (h0) {
+#pragma unroll
+    for (int mt = 0; mt < K / 16; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Hs[mt][r] = h0[sbase + (size_t)(16 * mt + 4 * g + r) * V + v];
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < K / 16; ++mt) Hs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* __restrict__ wf,
+                                                       const Frag<E>* __restrict__ ktf,
+                                                       const Quad<E>* __restrict__ uf,
+                                                       const float* __restrict__ gam,
+                                                       const int* __restrict__ seq_slot,
+                                                       const float* __restrict__ h0,
+                                                       float* __restrict__ fin,
+                                                       Frag<E>* __restrict__ hcf,
+                                                       Frag<E>* __restrict__ vnf) {
+  using Step = ChainStep<E, K, V>;
+  constexpr int NV = V / 16, KT = K / 16;
+  // Two register buffers when a step's operands fit in ~150 VGPRs.
+  constexpr bool kDouble = sizeof(Step) <= 600;
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+  const int n = rest / NV, vt = rest - n * NV;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int lane = lane_id(), g = lane >> 4, lc = lane & 15;
+  const int v = 16 * vt + lc;
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+  const size_t hbase = (size_t)hv * geo.slots;
+
+  f32x4 Hs[KT];
+  load_state<K, V>(Hs, h0, sbase, v, g);
+
+  if constexpr (kDouble) {
+    // The next chunk's loads are issued unconditionally (the last chunk reloads
+    // itself, in bounds), so the compiler's wait counts stay exact across the
+    // loop instead of falling back to full drains at the join.
+    Step A, B;
+    const int last = s1 - 1;
+    // The empty asm statements keep the compiler from sinking a prefetch batch
+    // below the compute that should overlap it.
+    if (s0 < s1) A.load(wf, ktf, uf, gam, hbase + s0, vt, lane);
+    for (int s = s0; s < s1; s += 2) {
+      B.load(wf, ktf, uf, gam, hbase + min(s + 1, last), vt, lane);
+      asm volatile("" ::: "memory");
+      A.compute(Hs, hcf, vnf, hbase + s, vt, lane);
+      if (s + 1 >= s1) break;
+      A.load(wf, ktf, uf, gam, hbase + min(s + 2, last), vt, lane);
+      asm volatile("" ::: "memory");
+      B.compute(Hs, hcf, vnf, hbase + s + 1, vt, lane);
+    }
+  } else {
+    Step A;
+    for (int s = s0; s < s1; ++s) {
+      A.load(wf, ktf, uf, gam, hbase + s, vt, lane);
+      A.compute(Hs, hcf, vnf, hbase + s, vt, lane);
     }
   }
   if (fin) {
@@ -462,6 +565,203 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
     for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State pass, LDS-ring variant (used when every (sequence, head, 16 columns)
+// unit can have a CU of its own).  Same arithmetic as gdn_chain_kernel; only
+// the operand supply differs: a workgroup is one compute wave plus two loader
+// waves.  The loaders stream each chunk's operand fragments (w, kd^T, u pairs)
+// into a D-stage LDS ring with global_load_lds (16 bytes per lane, written to
+// LDS at lane*16 from the stage base), D-1 chunks ahead of the compute wave.
+// Each loader issues half of a chunk's loads, so its in-flight count stays
+// within the 6-bit vmcnt.  One workgroup barrier per chunk:
+//   loaders:  wait until their loads of chunk i have landed (vmcnt allows the
+//             later, still-streaming chunks), barrier, then refill the stage
+//             the compute wave finished at chunk i-1 with chunk i+D-1;
+//   compute:  barrier, read chunk i's fragments from stage i % D, compute.
+// The barrier is s_barrier between compiler-level memory fences only: the
+// loaders' explicit vmcnt waits are the only waits the protocol needs.
+template <typename E, int K, int V>
+struct RingCfg {
+  static constexpr int FB = (int)sizeof(Frag<E>);      // bytes per lane per fragment
+  static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
+  static constexpr int NFRAG = 4 * KB + 2 * KT + 2;    // w, kd^T, u-pair fragments per chunk
+  static constexpr int SUB = FB / 16;                  // 1 KB blocks per fragment
+  static constexpr int GOFF = NFRAG * 64 * FB;         // gate row (256 bytes) after the fragments
+  static constexpr int STEP = GOFF + 256;              // bytes per ring stage
+  static constexpr int D0 = (144 * 1024) / STEP;
+  static constexpr int D = D0 > 6 ? 6 : D0;            // ring stages
+  static constexpr int NLOAD = NFRAG * SUB;            // 1 KB loads per chunk
+  static constexpr int PER = NLOAD / 2;                // per loader wave; the first
+                                                       // loader also loads the gate row
+  static_assert(D >= 2, "ring needs two stages");
+  static_assert(NLOAD % 2 == 0, "loads split evenly over two loader waves");
+  static_assert((D - 1) * (PER + 1) <= 63, "in-flight loads exceed vmcnt");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most ahead * PER of this wave's loads are outstanding.
+template <int PER, int D>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if (ahead <= 0) wait_vmcnt<0>();
+  else if constexpr (D > 2) {
+    if (ahead == 1) wait_vmcnt<PER>();
+    else if constexpr (D > 3) {
+      if (ahead == 2) wait_vmcnt<2 * PER>();
+      else if constexpr (D > 4) {
+        if (ahead == 3) wait_vmcnt<3 * PER>();
+        else if constexpr (D > 5) {
+          wait_vmcnt<4 * PER>();
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// Fragment f of a ring stage (1 KB blocks, 16 bytes per lane).
+__device__ __forceinline__ Frag<bf16> ring_frag(const char* stage, int f, int lane, bf16*) {
+  return *reinterpret_cast<const Frag<bf16>*>(stage + f * 1024 + 16 * lane);
+}
+__device__ __forceinline__ Frag<float> ring_frag(const char* stage, int f, int lane, float*) {
+  const char* b = stage + f * 2048 + 16 * lane;
+  return {*reinterpret_cast<const f32x4*>(b), *reinterpret_cast<const f32x4*>(b + 1024)};
+}
+__device__ __forceinline__ void split_pair(const Frag<bf16>& f, Quad<bf16>& a, Quad<bf16>& b) {
+  a.x = __builtin_shufflevector(f.x, f.x, 0, 1, 2, 3);
+  b.x = __builtin_shufflevector(f.x, f.x, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void split_pair(const Frag<float>& f, Quad<float>& a, Quad<float>& b) {
+  a.x = f.lo;
+  b.x = f.hi;
+}
+
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(192) void gdn_chain_ring_kernel(Geo geo, const Frag<E>* __restrict__ wf,
+                                                             const Frag<E>* __restrict__ ktf,
+                                                             const Quad<E>* __restrict__ uf,
+                                                             const float* __restrict__ gam,
+                                                             const int* __restrict__ seq_slot,
+                                                             const float* __restrict__ h0,
+                                                             float* __restrict__ fin,
+                                                             Frag<E>* __restrict__ hcf,
+                                                             Frag<E>* __restrict__ vnf) {
+  using R = RingCfg<E, K, V>;
+  using Step = ChainStep<E, K, V>;
+  constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D;
+  __shared__ __align__(16) char ring[D * R::STEP];
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+  const int n = rest / NV, vt = rest - n * NV;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int nsteps = s1 - s0;
+  // wave index made provably uniform, so the loader branches and the LDS base
+  // of global_load_lds stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const size_t hbase = (size_t)hv * geo.slots + s0;
+
+  if (wave == 0) {
+    const int g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
+    const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+    f32x4 Hs[KT];
+    load_state<K, V>(Hs, h0, sbase, v, g);
+    for (int i = 0; i < nsteps; ++i) {
+      ring_barrier();
+      const char* stage = ring + (i % D) * R::STEP;
+      Step st;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) st.w[ct][kb] = ring_frag(stage, ct * KB + kb, lane, (E*)nullptr);
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          st.kt[mt][cb] = ring_frag(stage, 4 * KB + 2 * mt + cb, lane, (E*)nullptr);
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        split_pair(ring_frag(stage, 4 * KB + 2 * KT + cp, lane, (E*)nullptr), st.u[2 * cp],
+                   st.u[2 * cp + 1]);
+      st.gl = reinterpret_cast<const float*>(stage + R::GOFF)[lane];
+      st.compute(Hs, hcf, vnf, hbase + i, vt, lane);
+    }
+    if (fin) {
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
+    }
+  } else {
+    // Source of each of this wave's loads at chunk 0 (per lane); a chunk later
+    // every source has advanced by one slot of its array.
+    const int j0 = (wave - 1) * R::PER;
+    const char* src0[R::PER];
+    size_t adv[R::PER];
+#pragma unroll
+    for (int jj = 0; jj < R::PER; ++jj) {
+      const int j = j0 + jj;
+      const int f = j / R::SUB, h = j - f * R::SUB;
+      const char* base;
+      if (f < 4 * KB) {
+        const int ct = f / KB, kb = f - ct * KB;
+        base = reinterpret_cast<const char*>(wf + ((hbase * 4 + ct) * KB + kb) * 64);
+        adv[jj] = (size_t)4 * KB * 64 * R::FB;
+      } else if (f < 4 * KB + 2 * KT) {
+        const int f2 = f - 4 * KB, mt = f2 >> 1, cb = f2 & 1;
+        base = reinterpret_cast<const char*>(ktf + ((hbase * KT + mt) * 2 + cb) * 64);
+        adv[jj] = (size_t)KT * 2 * 64 * R::FB;
+      } else {
+        const int cp = f - 4 * KB - 2 * KT;
+        base = reinterpret_cast<const char*>(uf + ((hbase * NV + vt) * 2 + cp) * 64 * 2);
+        adv[jj] = (size_t)NV * 2 * 64 * R::FB;
+      }
+      src0[jj] = base + lane * R::FB + 16 * h;
+    }
+    const float* gsrc0 = gam + hbase * kChunk + lane;
+    auto issue = [&](int i) {
+      char* stage = ring + (i % D) * R::STEP;
+#pragma unroll
+      for (int jj = 0; jj < R::PER; ++jj) dma16(src0[jj] + (size_t)i * adv[jj], stage + (j0 + jj) * 1024);
+      if (wave == 1)
+        __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc0 + (size_t)i * kChunk),
+                                         (lds_void_t*)(stage + R::GOFF), 4, 0, 0);
+    };
+    for (int p = 0; p < D - 1 && p < nsteps; ++p) issue(p);
+    for (int i = 0; i < nsteps; ++i) {
+      const int later = nsteps - 1 - i;
+      const int ahead = later < D - 2 ? later : D - 2;
+      if (wave == 1) wait_ahead<R::PER + 1, D>(ahead);  // also loads the gate row
+      else wait_ahead<R::PER, D>(ahead);
+      ring_barrier();
+      if (i + D - 1 < nsteps) issue(i + D - 1);
+    }
   }
 }
 
@@ -485,7 +785,8 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
   __shared__ __align__(16) Frag<E> Pb[4][2][64];
   __shared__ float sg[kChunk];
 
-  const int slot = blockIdx.x, hv = blockIdx.y;
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;

@@ -55,13 +55,15 @@ def decode_kt(buf, HV, slots, K):
 
 
 def decode_u(buf, HV, slots, V):
-    """uf [hv][slot][vt][ct<4][lane][4] -> u[hv][slot][c][v]."""
-    f = buf.reshape(HV, slots, V // 16, 4, 64, 4)
+    """uf [hv][slot][vt][cp<2][lane][2][4] (tiles ct = 2cp + q) -> u[hv][slot][c][v]."""
+    f = buf.reshape(HV, slots, V // 16, 2, 64, 2, 4)
     out = np.zeros((HV, slots, 64, V))
     for vt in range(V // 16):
-        for ct in range(4):
-            for r in range(4):
-                out[:, :, 16 * ct + 4 * G_OF_LANE + r, 16 * vt + LC] = f[:, :, vt, ct, :, r]
+        for cp in range(2):
+            for q in range(2):
+                for r in range(4):
+                    ct = 2 * cp + q
+                    out[:, :, 16 * ct + 4 * G_OF_LANE + r, 16 * vt + LC] = f[:, :, vt, cp, :, q, r]
     return out
 
 
