@@ -4,6 +4,8 @@ Small cases are compared in full; the full-size workloads (run in the same
 launch configuration bench.py times) are compared on sampled (sequence,
 value head) units whose o rows and final state the oracle computes one by one.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -39,10 +41,17 @@ def test_ragged_gqa_h0(dtype, K, V):
     check_full(inp, "ragged_gqa_h0_%s_K%d_V%d" % (dtype, K, V))
 
 
+def _edge_lengths():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "block_edge_lengths.txt")
+    vals = [int(x) for line in open(path) if not line.startswith("#") for x in line.split()]
+    return [t for t in vals if t <= 2048]
+
+
 @pytest.mark.parametrize("dtype", [BF, F32])
-@pytest.mark.parametrize("T", [1, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 512])
+@pytest.mark.parametrize("T", _edge_lengths())
 def test_block_edge_lengths(dtype, T):
-    # the block-edge lengths of the KDA gate precision sweep (page 4)
+    # the block-edge lengths of the KDA gate precision sweep (tests/golden)
     inp = make_inputs(B=2, T=T, H=2, HV=2, K=128, V=128, dtype=dtype, seed=200 + T)
     check_full(inp, "edge_T%d_%s" % (T, dtype))
 
