@@ -67,8 +67,9 @@ def algorithmic(shape, esz, has_h0, used_slots):
     k_in = ntok * H * K * esz
     kern = {
         "chunk_map": dict(bytes=(N + 1) * 8 + used_slots * 16 + (N + 1) * 4, flops=0),
-        "prologue": dict(bytes=U * 16, flops=U * 4),
-        "wy": dict(bytes=k_in + ntok * HV * V * esz + U * 8 + U * (2 * K + V) * esz,
+        # WY includes the gate prologue: reads g_raw, beta (8 B) and writes the
+        # stride-1 cumulative gate and beta rows (8 B) per token-head.
+        "wy": dict(bytes=k_in + ntok * HV * V * esz + U * 16 + U * (2 * K + V) * esz,
                    flops=U * C * (2 * K + V)),
         "chain": dict(bytes=U * (2 * K + V) * esz + Ck * 4 + Ck * K * V * esz + U * V * esz
                       + (state if has_h0 else 0) + state,

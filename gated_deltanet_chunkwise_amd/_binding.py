@@ -15,8 +15,8 @@ GDN_BF16 = 1
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
            "gdn_fwd", "gdn_fwd_timed", "gdn_status_string")
-NUM_STAGES = 5
-STAGES = ("chunk_map", "prologue", "wy", "chain", "output")
+NUM_STAGES = 4
+STAGES = ("chunk_map", "wy", "chain", "output")
 
 
 class Params(ctypes.Structure):

@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall",
     # Keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (gfx950 allows either): no AGPR<->VGPR
+    # copies around the VALU work on accumulators (state decay, conversions).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

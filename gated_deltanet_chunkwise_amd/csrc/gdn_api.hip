@@ -154,13 +154,9 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               geo.slots, cmap, seq_slot));
   mark(1);
   if (work && geo.slots > 0)
-    ok(launch(gdn::gdn_prologue_kernel<VARLEN>, dim3(geo.slots), dim3(256), s, geo, g_raw, beta,
-              A_log, dt_bias, cmap, gam, bet));
-  mark(2);
-  if (work && geo.slots > 0)
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo, ke,
-              ve, cmap, gam, bet, wf, ktf, uf));
-  mark(3);
+              ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf));
+  mark(2);
   if (work) {
     // One CU per state-pass unit when they fit: the LDS-ring variant; otherwise
     // many units share a CU and the register-buffered variant is used.
@@ -172,11 +168,11 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
       ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo, wf, ktf,
                 uf, gam, seq_slot, h0, fin, hcf, vnf));
   }
-  mark(4);
+  mark(3);
   if (work && geo.slots > 0)
     ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo,
               qe, ke, cmap, gam, hcf, vnf, oe));
-  mark(5);
+  mark(4);
   return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

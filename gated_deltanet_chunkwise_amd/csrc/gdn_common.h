@@ -64,6 +64,16 @@ template <> __device__ __forceinline__ Frag<float> frag_from_tiles<float>(f32x4 
   return {d0, d1};
 }
 
+// k32 fragment from its two 4-element pieces (k offsets 4g.. and 16+4g..).
+__device__ __forceinline__ Frag<bf16> frag_from_pieces(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  return {__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)};
+}
+__device__ __forceinline__ Frag<float> frag_from_pieces(const float* p0, const float* p1) {
+  return {*reinterpret_cast<const f32x4*>(p0), *reinterpret_cast<const f32x4*>(p1)};
+}
+
 // k32 fragment from a row-major matrix row: `row` points at element 32*kb of
 // the lane's row (A operand) or column-as-row (B operand).  Works for LDS and
 // global pointers; both 4-element pieces must be 8-byte (bf16) / 16-byte

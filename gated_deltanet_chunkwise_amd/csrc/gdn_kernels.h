@@ -2,11 +2,12 @@
 //
 // Pipeline (one stream, no host sync):
 //   chunk map  (packed sequences only)  cu_seqlens -> chunk slot table
-//   prologue   g = -exp(A_log) softplus(g_raw + dt_bias); chunk-local cumsum
-//              G (times log2 e) and beta, both stored [HV][slot][64]: stride 1
-//              along T, the relayout the G_T_CONTIG page does with a host
-//              transpose, fused here into the producing kernel.
-//   WY         per (slot, hv): A = strictly_lower(beta_i k_i.k_j e^{G_i-G_j}),
+//   WY         per (slot, hv), gate prologue first: g = -exp(A_log)
+//              softplus(g_raw + dt_bias), chunk-local cumsum G (times log2 e),
+//              stored with beta as [HV][slot][64] rows: stride 1 along T, the
+//              relayout the G_T_CONTIG page does with a host transpose, here
+//              fused into the kernel that first needs the gates.  Then
+//              A = strictly_lower(beta_i k_i.k_j e^{G_i-G_j}),
 //              T = (I+A)^-1, w = T diag(beta e^G) K, u = T diag(beta) V and
 //              kd^T = (diag(e^{G_last-G}) K)^T.
 //   chain      per (sequence, hv, 16 value columns): sequential over chunks,
@@ -66,6 +67,13 @@ __device__ __forceinline__ Frag<bf16> frag_scale(const Frag<bf16>& f, const floa
 __device__ __forceinline__ Frag<float> frag_scale(const Frag<float>& f, const float (&s)[8]) {
   return {f.lo * f32x4{s[0], s[1], s[2], s[3]}, f.hi * f32x4{s[4], s[5], s[6], s[7]}};
 }
+
+// fp32 k32 fragment -> operand dtype (one rounding).
+template <typename E> __device__ __forceinline__ Frag<E> to_frag(const Frag<float>& f);
+template <> __device__ __forceinline__ Frag<bf16> to_frag<bf16>(const Frag<float>& f) {
+  return frag_from_tiles<bf16>(f.lo, f.hi);
+}
+template <> __device__ __forceinline__ Frag<float> to_frag<float>(const Frag<float>& f) { return f; }
 
 // k offset (0..31) of fragment element i for lane group g.
 __device__ __forceinline__ int kslot(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
@@ -135,70 +143,31 @@ __global__ __launch_bounds__(256) void gdn_chunk_map_kernel(const int64_t* __res
   if (tid == 0) seq_slot[N] = used;
 }
 
-// ---------------------------------------------------------------------------
-// Gate prologue.  One workgroup per chunk slot.  The 64 x HV tiles of g_raw and
-// beta are read coalesced (HV contiguous) into LDS, then one wave per head
-// evaluates the gate in fp32 (softplus threshold 20 as in the KDA gate guide,
-// "core computation logic"), scans along the 64 tokens and writes the
-// chunk's row for that head: stride 1 along T.
-// Padding past a chunk's end: g = 0 (so G stays at its last value) and beta = 0.
-template <bool VARLEN>
-__global__ __launch_bounds__(256) void gdn_prologue_kernel(Geo geo, const float* __restrict__ g_raw,
-                                                           const float* __restrict__ beta,
-                                                           const float* __restrict__ A_log,
-                                                           const float* __restrict__ dt_bias,
-                                                           const int4* __restrict__ cmap,
-                                                           float* __restrict__ gam,
-                                                           float* __restrict__ bet) {
-  constexpr int HG = 32;  // heads per LDS pass
-  __shared__ float sa[kChunk][HG + 1];
-  __shared__ float sb[kChunk][HG + 1];
-  const int slot = blockIdx.x;
-  int n, len;
-  int64_t t0;
-  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
-  const int HV = geo.HV, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int hb = 0; hb < HV; hb += HG) {
-    const int nh = min(HG, HV - hb);
-    __syncthreads();
-    for (int i = tid; i < len * nh; i += 256) {
-      const int t = i / nh, j = i - t * nh;
-      const int64_t src = (t0 + t) * HV + hb + j;
-      sa[t][j] = g_raw[src];
-      sb[t][j] = beta[src];
-    }
-    __syncthreads();
-    for (int j = wave; j < nh; j += 4) {
-      const int hv = hb + j;
-      float g = 0.f, b = 0.f;
-      if (lane < len) {
-        const float x = sa[lane][j] + (dt_bias ? dt_bias[hv] : 0.f);
-        const float sp = x > 20.f ? x : log1pf(expf(x));
-        g = -expf(A_log[hv]) * sp;
-        b = sb[lane][j];
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off, 64);
-        if (lane >= off) g += y;
-      }
-      const size_t o = ((size_t)hv * geo.slots + slot) * kChunk + lane;
-      gam[o] = g * kLog2e;
-      bet[o] = b;
-    }
-  }
+// Transposed K / V tiles in LDS ([K or V][64] rows, chunk index along a row)
+// are stored with their 4-element column groups XOR-swizzled by row / 8, which
+// makes the transposed 8-byte writes of a wave (rows 8 apart) bank-conflict
+// free.  Readers apply the same swizzle; groups stay 4 contiguous elements.
+__device__ __forceinline__ int tswz(int row) { return 4 * ((row >> 3) & 15); }
+
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int stride, int col0) {
+  const int g = lane_id() >> 4, sw = tswz(row);
+  const E* r = tile + row * stride;
+  return frag_from_pieces(r + ((col0 + 4 * g) ^ sw), r + ((col0 + 16 + 4 * g) ^ sw));
 }
 
 // ---------------------------------------------------------------------------
 // WY representation.  One workgroup (4 waves) per (chunk slot, value head).
 //
-// LDS: K natural [64][K] (later reused for T_w, T_u), K^T [K][64], V^T [V][64],
-// A and T (fp32 [64][64]).  Rows past the chunk end are zero.
+// LDS: K natural [64][K] (later reused for A), K^T [K][64], V^T [V][64], and
+// T (fp32 [64][64]).  Rows past the chunk end are zero.
 //
 // T = (I + A)^-1 is unit lower triangular.  Its 16x16 diagonal blocks are
-// found by forward substitution (one lane per column), the off-diagonal
-// blocks block-row by block-row:  T_rc = -T_rr sum_{m=c}^{r-1} A_rm T_mc,
-// on fp32 MFMAs.
+// found by forward substitution (one lane per column, the block held in
+// registers), the off-diagonal blocks block-row by block-row:
+// T_rc = -T_rr sum_{m=c}^{r-1} A_rm T_mc, on fp32 MFMAs.  The scaled factors
+// T diag(beta e^G) and T diag(beta) are never stored: each wave builds its
+// operand fragments for w and u from its own rows of T, scaled in registers.
 //
 // Outputs (fragment-major, dtype E):
 //   wf  [hv][slot][ct<4][kb<K/32][lane]   A operand of  w H        (rows c, k over K)
@@ -208,21 +177,23 @@ __global__ __launch_bounds__(256) void gdn_prologue_kernel(Geo geo, const float*
 template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
+                                                     const float* __restrict__ g_raw,
+                                                     const float* __restrict__ beta,
+                                                     const float* __restrict__ A_log,
+                                                     const float* __restrict__ dt_bias,
                                                      const int4* __restrict__ cmap,
-                                                     const float* __restrict__ gam,
-                                                     const float* __restrict__ bet,
+                                                     float* __restrict__ gam,
+                                                     float* __restrict__ bet,
                                                      Frag<E>* __restrict__ wf,
                                                      Frag<E>* __restrict__ ktf,
                                                      Quad<E>* __restrict__ uf) {
   constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
   constexpr int KS = K + P;          // K natural row stride
-  constexpr int CS = kChunk + P;     // K^T, V^T, T_w, T_u row stride
+  constexpr int CS = kChunk + P;     // K^T, V^T row stride
   constexpr int FS = kChunk + 4;     // A, T row stride (fp32)
-  // Region 0 holds, in turn: K natural (until A is formed), A (until T is
-  // complete), then T_w and T_u.
-  constexpr int R0A = kChunk * KS * (int)sizeof(E), R0B = 2 * kChunk * CS * (int)sizeof(E);
-  constexpr int R0C = kChunk * FS * 4;
-  constexpr int R0 = R0A > R0B ? (R0A > R0C ? R0A : R0C) : (R0B > R0C ? R0B : R0C);
+  // Region 0 holds K natural until the products of A are formed, then A.
+  constexpr int R0A = kChunk * KS * (int)sizeof(E), R0C = kChunk * FS * 4;
+  constexpr int R0 = R0A > R0C ? R0A : R0C;
   __shared__ __align__(16) char r0[R0];
   __shared__ __align__(16) E Kt[K * CS];
   __shared__ __align__(16) E Vt[V * CS];
@@ -230,8 +201,6 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   __shared__ float sg[kChunk], sb[kChunk];
   E* const Ks = reinterpret_cast<E*>(r0);
   float* const As = reinterpret_cast<float*>(r0);
-  E* const Tw = reinterpret_cast<E*>(r0);
-  E* const Tu = Tw + kChunk * CS;
 
   int hv, slot;
   head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
@@ -242,89 +211,129 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
   const size_t hs = (size_t)hv * geo.slots + slot;
 
-  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
-  else if (tid < 2 * kChunk) sb[tid - kChunk] = bet[hs * kChunk + tid - kChunk];
-
-  // K tile: 4x8 micro-tiles, stored natural and transposed.
-  for (int m = tid; m < 16 * (K / 8); m += 256) {
-    const int rb = 4 * (m / (K / 8)), c0 = 8 * (m % (K / 8));
-    float e[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (rb + r < len) ld8(kg + ((t0 + rb + r) * geo.H + h) * K + c0, e[r]);
-      else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
-      }
-      st8(Ks + (rb + r) * KS + c0, e[r]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st4(Kt + (c0 + j) * CS + rb, e[0][j], e[1][j], e[2][j], e[3][j]);
+  // All global loads first (one memory latency for K, V and the gate inputs):
+  // thread t owns the 4x8 micro-tile t of K and of V; wave 0 also reads this
+  // head's 64 raw gates and betas (stride HV along T).
+  float graw = 0.f, braw = 0.f;
+  if (wave == 0 && lane < len) {
+    graw = g_raw[(t0 + lane) * geo.HV + hv];
+    braw = beta[(t0 + lane) * geo.HV + hv];
   }
-  // V tile, transposed only.
-  for (int m = tid; m < 16 * (V / 8); m += 256) {
-    const int rb = 4 * (m / (V / 8)), c0 = 8 * (m % (V / 8));
-    float e[4][8];
+  constexpr int NKM = 16 * (K / 8), NVM = 16 * (V / 8);  // micro-tiles (<= 256 each)
+  float ek[4][8], ev[4][8];
+  const int krb = 4 * (tid / (K / 8)), kc0 = 8 * (tid % (K / 8));
+  const int vrb = 4 * (tid / (V / 8)), vc0 = 8 * (tid % (V / 8));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (rb + r < len) ld8(vg + ((t0 + rb + r) * geo.HV + hv) * V + c0, e[r]);
-      else {
+  for (int r = 0; r < 4; ++r) {
+    if (tid < NKM && krb + r < len) ld8(kg + ((t0 + krb + r) * geo.H + h) * K + kc0, ek[r]);
+    else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
-      }
+      for (int j = 0; j < 8; ++j) ek[r][j] = 0.f;
+    }
+    if (tid < NVM && vrb + r < len) ld8(vg + ((t0 + vrb + r) * geo.HV + hv) * V + vc0, ev[r]);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ev[r][j] = 0.f;
+    }
+  }
+  if (tid < NKM) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st8(Ks + (krb + r) * KS + kc0, ek[r]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      st4(Kt + (kc0 + j) * CS + (krb ^ tswz(kc0 + j)), ek[0][j], ek[1][j], ek[2][j], ek[3][j]);
+  }
+  if (tid < NVM) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      st4(Vt + (vc0 + j) * CS + (vrb ^ tswz(vc0 + j)), ev[0][j], ev[1][j], ev[2][j], ev[3][j]);
+  }
+  // Gate prologue (wave 0, lane = token): g in fp32 with the softplus
+  // threshold of the KDA gate guide ("core computation logic"), the chunk-local
+  // scan, and this head's stride-1 rows of the cumulative gate (times log2 e)
+  // and beta for the state pass and the output.  Past the chunk end g = 0 (the
+  // cumulative gate stays at its last value) and beta = 0.
+  if (wave == 0) {
+    float gv = 0.f;
+    if (lane < len) {
+      const float x = graw + (dt_bias ? dt_bias[hv] : 0.f);
+      const float sp = x > 20.f ? x : log1pf(expf(x));
+      gv = -expf(A_log[hv]) * sp;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st4(Vt + (c0 + j) * CS + rb, e[0][j], e[1][j], e[2][j], e[3][j]);
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(gv, off, 64);
+      if (lane >= off) gv += y;
+    }
+    gv *= kLog2e;
+    sg[lane] = gv;
+    sb[lane] = braw;
+    gam[hs * kChunk + lane] = gv;
+    bet[hs * kChunk + lane] = braw;
   }
   __syncthreads();
 
-  // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)); wave w owns row tile
-  // w.  The products finish before A overwrites K natural in region 0.
+  // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)).  The 10 tiles on or
+  // below the diagonal go 3/3/2/2 to the waves; the products finish before A
+  // overwrites K natural in region 0.
   {
-    f32x4 acc[4];
+    f32x4 acc[3];
+    int ti[3], tj[3];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (jt <= wave) {
+    for (int q = 0; q < 3; ++q) {
+      const int t = wave + 4 * q;  // tile index in (0,0),(1,0),(1,1),(2,0),...
+      const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      ti[q] = it;
+      tj[q] = t - it * (it + 1) / 2;
+      acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < 10) {
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb)
-          mma_k32(acc[jt], frag_from_row(Ks + (16 * wave + lc) * KS + 32 * kb),
-                  frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb));
+          mma_k32(acc[q], frag_from_row(Ks + (16 * ti[q] + lc) * KS + 32 * kb),
+                  frag_from_row(Ks + (16 * tj[q] + lc) * KS + 32 * kb));
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      if (jt <= wave) {
+    for (int q = 0; q < 3; ++q) {
+      if (wave + 4 * q < 10) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * wave + 4 * g + r, col = 16 * jt + lc;
-          As[row * FS + col] = col < row ? sb[row] * acc[jt][r] * fast_exp2(sg[row] - sg[col]) : 0.f;
+          const int row = 16 * ti[q] + 4 * g + r, col = 16 * tj[q] + lc;
+          As[row * FS + col] = col < row ? sb[row] * acc[q][r] * fast_exp2(sg[row] - sg[col]) : 0.f;
         }
       }
     }
   }
   __syncthreads();
 
-  // Diagonal blocks of T by forward substitution (the block's strictly lower
-  // part is read into registers first, so the dependent chain runs on
+  // Diagonal blocks of T by forward substitution (the block read into
+  // registers with 16-byte LDS loads, so the dependent chain runs on
   // registers); zero the blocks above them.
   {
     const int b = wave;
     if (lane < 16) {
       float a[16][16];
 #pragma unroll
-      for (int i = 1; i < 16; ++i)
+      for (int i = 1; i < 16; ++i) {
+        const f32x4* rowp = reinterpret_cast<const f32x4*>(As + (16 * b + i) * FS + 16 * b);
 #pragma unroll
-        for (int m = 0; m < i; ++m) a[i][m] = As[(16 * b + i) * FS + 16 * b + m];
+        for (int q = 0; q < 4; ++q) {
+          if (4 * q < i) {
+            const f32x4 x = rowp[q];
+            a[i][4 * q] = x[0]; a[i][4 * q + 1] = x[1]; a[i][4 * q + 2] = x[2]; a[i][4 * q + 3] = x[3];
+          }
+        }
+      }
+      // Column sweep: once x[m] is final, subtract its contribution from every
+      // later row, so the dependent chain is 15 FMAs long, not 120.
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == lane) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s -= a[i][m] * x[m];
-        x[i] = s;
-      }
+      for (int m = 0; m < 15; ++m)
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) x[i] -= a[i][m] * x[m];
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ts[(16 * b + i) * FS + 16 * b + lane] = x[i];
     }
@@ -355,43 +364,50 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     __syncthreads();
   }
 
-  // T_w = T diag(beta e^G), T_u = T diag(beta) in the operand dtype.
-  for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
-    const int i = idx >> 6, j = idx & 63;
-    const float t = Ts[i * FS + j] * sb[j];
-    Tw[i * CS + j] = (E)(t * fast_exp2(sg[j]));
-    Tu[i * CS + j] = (E)t;
+  // Wave w owns chunk rows 16w..16w+15.  Its k32 fragments of T diag(beta e^G)
+  // and T diag(beta) over the chunk index (row 16w + lane%16, columns
+  // 32cb + kslot(g, i)) are formed from T in registers.
+  const int ct = wave;
+  Frag<E> bw[2], bu[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float* trow = Ts + (16 * ct + lc) * FS + 32 * cb;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(trow + 4 * g);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(trow + 16 + 4 * g);
+    float sw[8], su[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 32 * cb + kslot(g, i);
+      su[i] = sb[j];
+      sw[i] = sb[j] * fast_exp2(sg[j]);
+    }
+    const Frag<float> tf = {lo, hi};
+    bw[cb] = to_frag<E>(frag_scale(tf, sw));
+    bu[cb] = to_frag<E>(frag_scale(tf, su));
   }
-  __syncthreads();
 
-  // w^T = K^T T_w^T: wave w owns chunk-row tile ct = w; D tile (mt) holds
-  // w[16ct + lane%16][16mt + 4g + r], so tile pairs are the chain's A fragments.
+  // w^T = K^T T_w^T: D tile (mt) holds w[16ct + lane%16][16mt + 4g + r], so
+  // tile pairs are the state pass's A fragments.
   {
-    const int ct = wave;
     f32x4 acc[K / 16];
 #pragma unroll
     for (int mt = 0; mt < K / 16; ++mt) {
       acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        mma_k32(acc[mt], frag_from_row(Kt + (16 * mt + lc) * CS + 32 * cb),
-                frag_from_row(Tw + (16 * ct + lc) * CS + 32 * cb));
+      for (int cb = 0; cb < 2; ++cb) mma_k32(acc[mt], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
     }
     Frag<E>* dst = wf + (hs * 4 + ct) * (K / 32) * 64;
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) dst[kb * 64 + lane] = frag_from_tiles<E>(acc[2 * kb], acc[2 * kb + 1]);
   }
-  // u = T_u V: wave w owns chunk-row tile ct = w.
+  // u = T_u V (A operand: this wave's rows of T_u).
   {
-    const int ct = wave;
     Quad<E>* dst = uf + hs * (V / 16) * 4 * 64;
 #pragma unroll
     for (int vt = 0; vt < V / 16; ++vt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        mma_k32(acc, frag_from_row(Tu + (16 * ct + lc) * CS + 32 * cb),
-                frag_from_row(Vt + (16 * vt + lc) * CS + 32 * cb));
+      for (int cb = 0; cb < 2; ++cb) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CS, 32 * cb));
       dst[((vt * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)] = make_quad<E>(acc);
     }
   }
@@ -401,10 +417,10 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     const float gl = sg[kChunk - 1];
     for (int f = wave; f < (K / 16) * 2; f += 4) {
       const int mt = f >> 1, cb = f & 1;
-      float s[8];
+      float sc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = fast_exp2(gl - sg[32 * cb + kslot(g, i)]);
-      dst[f * 64 + lane] = frag_scale(frag_from_row(Kt + (16 * mt + lc) * CS + 32 * cb), s);
+      for (int i = 0; i < 8; ++i) sc[i] = fast_exp2(gl - sg[32 * cb + kslot(g, i)]);
+      dst[f * 64 + lane] = frag_scale(frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), sc);
     }
   }
 }
@@ -794,19 +810,39 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
   const size_t hs = (size_t)hv * geo.slots + slot;
 
+  // All global loads first: this wave's H_c and v_new fragments (value tiles
+  // wave, wave+4, ...), the gate row, and the Q and K rows of the chunk.
+  constexpr int NVW = (NV + 3) / 4;  // value tiles per wave
+  Frag<E> hc[NVW][KB], vn[NVW][2];
+#pragma unroll
+  for (int a = 0; a < NVW; ++a) {
+    const int vt = wave + 4 * a;
+    if (vt < NV) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) hc[a][kb] = hcf[((hs * NV + vt) * KB + kb) * 64 + lane];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) vn[a][jb] = vnf[((hs * NV + vt) * 2 + jb) * 64 + lane];
+    }
+  }
   if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
-  for (int m = tid; m < kChunk * (K / 8); m += 256) {
-    const int row = m / (K / 8), c0 = 8 * (m % (K / 8));
-    float eq[8], ek[8];
+  constexpr int NIT = kChunk * (K / 8) / 256;  // 8-element pieces per thread
+  float eq[NIT][8], ek[NIT][8];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int m = tid + 256 * it, row = m / (K / 8), c0 = 8 * (m % (K / 8));
     if (row < len) {
-      ld8(qg + ((t0 + row) * geo.H + h) * K + c0, eq);
-      ld8(kg + ((t0 + row) * geo.H + h) * K + c0, ek);
+      ld8(qg + ((t0 + row) * geo.H + h) * K + c0, eq[it]);
+      ld8(kg + ((t0 + row) * geo.H + h) * K + c0, ek[it]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) eq[j] = ek[j] = 0.f;
+      for (int j = 0; j < 8; ++j) eq[it][j] = ek[it][j] = 0.f;
     }
-    st8(Qs + row * KS + c0, eq);
-    st8(Ks + row * KS + c0, ek);
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int m = tid + 256 * it, row = m / (K / 8), c0 = 8 * (m % (K / 8));
+    st8(Qs + row * KS + c0, eq[it]);
+    st8(Ks + row * KS + c0, ek[it]);
   }
   __syncthreads();
 
@@ -834,20 +870,18 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
   }
   __syncthreads();
 
-  for (int vt = wave; vt < NV; vt += 4) {
-    Frag<E> hc[KB], vn[2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hc[kb] = hcf[((hs * NV + vt) * KB + kb) * 64 + lane];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) vn[jb] = vnf[((hs * NV + vt) * 2 + jb) * 64 + lane];
+  for (int a = 0; a < NVW; ++a) {
+    const int vt = wave + 4 * a;
+    if (vt >= NV) break;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[kb], frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
+      for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[a][kb], frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
       acc *= fast_exp2(sg[16 * it + lc]);
 #pragma unroll
-      for (int jb = 0; jb <= (it >> 1); ++jb) mma_k32(acc, vn[jb], Pb[it][jb][lane]);
+      for (int jb = 0; jb <= (it >> 1); ++jb) mma_k32(acc, vn[a][jb], Pb[it][jb][lane]);
       acc *= geo.scale;
       const int i = 16 * it + lc;
       if (i < len) {

@@ -20,12 +20,13 @@
  * element [n][hv][i][j] = S[j][i].
  *
  * It is computed chunkwise (chunks of 64 tokens, aligned to every sequence
- * start, last chunk of a sequence possibly shorter) by four gfx950 kernels
- * on the caller's stream: gate prologue + chunk-local cumsum (stride-1 along T,
- * the layout fix of the G_T_CONTIG page, "fix: host transpose + stride-1
- * pointer", done inside the kernel instead of on the host), the per-chunk WY
- * representation, the sequential inter-chunk state pass, and the chunk
- * output.  A fifth kernel builds the chunk map when cu_seqlens is given.
+ * start, last chunk of a sequence possibly shorter) by three gfx950 kernels
+ * on the caller's stream: the per-chunk WY representation, which first runs
+ * the gate prologue and chunk-local cumsum and writes them stride-1 along T
+ * (the layout fix of the G_T_CONTIG page, "fix: host transpose + stride-1
+ * pointer", done inside the kernel instead of on the host), the sequential
+ * inter-chunk state pass, and the chunk output.  A fourth kernel builds the
+ * chunk map when cu_seqlens is given.
  *
  * Layouts (all contiguous, row-major, device memory):
  *   q, k           [B][T][H][K]   dtype (GDN_BF16 or GDN_F32)
@@ -136,9 +137,9 @@ gdn_status_t gdn_fwd(const gdn_params_t *p, const void *q, const void *k, const 
                      const float *initial_state, void *o, float *final_state,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Number of stages gdn_fwd_timed brackets with events: chunk map, gate
- * prologue, WY, state pass, output. */
-#define GDN_NUM_STAGES 5
+/* Number of stages gdn_fwd_timed brackets with events: chunk map, WY (with
+ * the gate prologue), state pass, output. */
+#define GDN_NUM_STAGES 4
 
 /* gdn_fwd that also records timing events on `stream`, for profiling:
  * events[0] before the first kernel and events[i] right after stage i
