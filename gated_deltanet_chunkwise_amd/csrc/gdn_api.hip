@@ -158,13 +158,27 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf));
   mark(2);
   if (work) {
-    // One CU per state-pass unit when they fit: the LDS-ring variant; otherwise
-    // many units share a CU and the register-buffered variant is used.
+    // LDS-ring variant when its workgroups fit one per CU: one compute wave
+    // (16 columns) per workgroup when the units fit, two sharing the ring
+    // otherwise; beyond that many units share a CU and the register-buffered
+    // variant is used (also for fp32 at K = 128, whose pipelined operands do
+    // not fit the ring variant's registers).
     const int units = geo.N * geo.HV * (V / 16);
-    if (units <= device_cus())
-      ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN>, dim3(units), dim3(192), s, geo, wf,
-                ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
-    else
+    const int cus = device_cus();
+    bool done = false;
+    if constexpr (gdn::RingCfg<E, K, V, 1>::FITS) {
+      if (units <= cus) {
+        ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1>, dim3(units),
+                  dim3(64 * gdn::RingCfg<E, K, V, 1>::WAVES), s, geo,
+                  wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+        done = true;
+      } else if (units <= 2 * cus) {
+        ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 2>, dim3(units / 2),
+                  dim3(64 * gdn::RingCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
+        done = true;
+      }
+    }
+    if (!done)
       ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo, wf, ktf,
                 uf, gam, seq_slot, h0, fin, hcf, vnf));
   }

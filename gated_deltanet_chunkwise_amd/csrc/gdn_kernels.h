@@ -468,38 +468,63 @@ struct ChainStep {
     for (int ct = 0; ct < 4; ++ct) u[ct] = uf[(((hs * NV + vt) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
   }
 
-  // One chunk: consumes this step's operands, updates Hs, writes H_c and v_new.
-  __device__ __forceinline__ void compute(f32x4 (&Hs)[KT], Frag<E>* __restrict__ hcf,
-                                          Frag<E>* __restrict__ vnf, size_t hs, int vt,
-                                          int lane) const {
+  // First half of a chunk: emits H_c (the state on entry) and v_new = u - w H_c
+  // through the sinks put_hc(kb, fragment) / put_vn(cb, fragment), and returns
+  // v_new as the two B fragments of the state update.  Uses w and u.
+  template <typename PutH, typename PutV>
+  __device__ __forceinline__ void vnew(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2], PutH&& put_hc,
+                                       PutV&& put_vn) const {
     Frag<E> hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       hb[kb] = frag_from_tiles<E>(Hs[2 * kb], Hs[2 * kb + 1]);
-      hcf[((hs * NV + vt) * KB + kb) * 64 + lane] = hb[kb];
+      put_hc(kb, hb[kb]);
     }
-    f32x4 vn[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma_k32(p, w[ct][kb], hb[kb]);
-      vn[ct] = quad_f32(u[ct]) - p;
-    }
-    Frag<E> vb[2];
+    // by pairs of row tiles, so the first pair's conversion can overlap the
+    // second pair's products
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      vb[cb] = frag_from_tiles<E>(vn[2 * cb], vn[2 * cb + 1]);
-      vnf[((hs * NV + vt) * 2 + cb) * 64 + lane] = vb[cb];
+      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        mma_k32(p0, w[2 * cb][kb], hb[kb]);
+        mma_k32(p1, w[2 * cb + 1][kb], hb[kb]);
+      }
+      vb[cb] = frag_from_tiles<E>(quad_f32(u[2 * cb]) - p0, quad_f32(u[2 * cb + 1]) - p1);
+      put_vn(cb, vb[cb]);
     }
+  }
+
+  // vnew with H_c and v_new stored straight to their fragment-major arrays.
+  __device__ __forceinline__ void vnew_global(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2],
+                                              Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf,
+                                              size_t hs, int vt, int lane) const {
+    Frag<E>* hc = hcf + (hs * NV + vt) * KB * 64 + lane;
+    Frag<E>* vn = vnf + (hs * NV + vt) * 2 * 64 + lane;
+    vnew(Hs, vb, [&](int kb, const Frag<E>& f) { hc[kb * 64] = f; },
+         [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; });
+  }
+
+  // Second half: H += kd^T v_new, on a state already multiplied by e^{G_last}.
+  // Uses kt.
+  __device__ __forceinline__ void update(f32x4 (&Hs)[KT], const Frag<E> (&vb)[2]) const {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) mma_k32(Hs[mt], kt[mt][cb], vb[cb]);
+  }
+
+  // One chunk: consumes this step's operands, updates Hs, writes H_c and v_new.
+  __device__ __forceinline__ void compute(f32x4 (&Hs)[KT], Frag<E>* __restrict__ hcf,
+                                          Frag<E>* __restrict__ vnf, size_t hs, int vt,
+                                          int lane) const {
+    Frag<E> vb[2];
+    vnew_global(Hs, vb, hcf, vnf, hs, vt, lane);
     // gl holds the chunk's gate row, one entry per lane; the decay uses the last.
     const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt) {
-      Hs[mt] *= dec;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mma_k32(Hs[mt], kt[mt][cb], vb[cb]);
-    }
+    for (int mt = 0; mt < KT; ++mt) Hs[mt] *= dec;
+    update(Hs, vb);
   }
 };
 
@@ -585,35 +610,58 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
 }
 
 // ---------------------------------------------------------------------------
-// State pass, LDS-ring variant (used when every (sequence, head, 16 columns)
-// unit can have a CU of its own).  Same arithmetic as gdn_chain_kernel; only
-// the operand supply differs: a workgroup is one compute wave plus two loader
-// waves.  The loaders stream each chunk's operand fragments (w, kd^T, u pairs)
-// into a D-stage LDS ring with global_load_lds (16 bytes per lane, written to
-// LDS at lane*16 from the stage base), D-1 chunks ahead of the compute wave.
-// Each loader issues half of a chunk's loads, so its in-flight count stays
-// within the 6-bit vmcnt.  One workgroup barrier per chunk:
-//   loaders:  wait until their loads of chunk i have landed (vmcnt allows the
-//             later, still-streaming chunks), barrier, then refill the stage
-//             the compute wave finished at chunk i-1 with chunk i+D-1;
-//   compute:  barrier, read chunk i's fragments from stage i % D, compute.
-// The barrier is s_barrier between compiler-level memory fences only: the
-// loaders' explicit vmcnt waits are the only waits the protocol needs.
-template <typename E, int K, int V>
+// State pass, LDS-ring variant (used when its workgroups fit one per CU).
+// Same arithmetic as gdn_chain_kernel; only the operand supply differs.  A
+// workgroup is:
+//   NC compute waves  -- NC 16-column tiles of one (sequence, value head); each
+//                        stores its H_c and v_new fragments itself (staging
+//                        them through LDS for another wave to store measured
+//                        slower: the LDS traffic costs more than the stores);
+//   two loader waves  -- stream each chunk's operands (w and kd^T fragments,
+//                        shared by the compute waves, the tiles' u pairs and
+//                        the gate row) into a D-stage LDS ring with
+//                        global_load_lds (16 bytes per lane, written to LDS at
+//                        lane*16 from the stage base), each issuing half of a
+//                        chunk's loads and waiting for them by vmcnt alone.
+// A compute wave takes in about 1 KB of operands per ~40 cycles whether from
+// LDS or from memory, so its 34 KB of fragments per chunk, not the MFMAs,
+// bound a chunk's time; the ring keeps that intake off memory latency and
+// overlaps it with the products (below).
+//
+// The compute waves are software-pipelined across chunks: chunk i's w
+// fragments are read into registers during chunk i-1's state update, and its
+// kd^T, u and gate reads overlap its own v_new products.  One workgroup
+// barrier per chunk, B_i, between the two halves of chunk i:
+//   compute:  [reads of chunk i's kd^T, u, gate; v_new; all reads of stage
+//             i % D complete]  B_i  [reads of chunk i+1's w; state update]
+//   loaders:  [wait until chunk i+1 has landed]  B_i  [refill stage i % D,
+//             which no compute wave reads again, with chunk i+D]
+// B_{-1} (before the loop) certifies chunk 0.  The barrier is s_barrier
+// between compiler-level memory fences; the explicit waits named above are
+// the only ones it relies on.
+template <typename E, int K, int V, int NC_>
 struct RingCfg {
   static constexpr int FB = (int)sizeof(Frag<E>);      // bytes per lane per fragment
   static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
-  static constexpr int NFRAG = 4 * KB + 2 * KT + 2;    // w, kd^T, u-pair fragments per chunk
+  static constexpr int NC = NC_;                       // compute waves (16-column tiles)
+  static constexpr int WAVES = NC + 2;                 // compute waves, then two loaders
+  static constexpr int FU = 4 * KB + 2 * KT;           // first u-pair fragment
+  static constexpr int NFRAG = FU + 2 * NC;            // w, kd^T, u-pair fragments per chunk
   static constexpr int SUB = FB / 16;                  // 1 KB blocks per fragment
   static constexpr int GOFF = NFRAG * 64 * FB;         // gate row (256 bytes) after the fragments
   static constexpr int STEP = GOFF + 256;              // bytes per ring stage
-  static constexpr int D0 = (144 * 1024) / STEP;
-  static constexpr int D = D0 > 6 ? 6 : D0;            // ring stages
   static constexpr int NLOAD = NFRAG * SUB;            // 1 KB loads per chunk
   static constexpr int PER = NLOAD / 2;                // per loader wave; the first
                                                        // loader also loads the gate row
+  static constexpr int D0 = (160 * 1024) / STEP;
+  static constexpr int D = D0 > 6 ? 6 : D0;            // ring stages
+  static constexpr int LDS = D * STEP;
+  // fp32 fragments at K = 128 do not fit the pipelined registers in 256 VGPRs
+  static constexpr bool FITS = FB == 16 || K <= 64;
+  static_assert(NC == 1 || NC == 2, "one or two compute waves");
+  static_assert(NV % NC == 0, "value tiles group evenly");
+  static_assert(NLOAD % 2 == 0, "loads split evenly over the two loader waves");
   static_assert(D >= 2, "ring needs two stages");
-  static_assert(NLOAD % 2 == 0, "loads split evenly over two loader waves");
   static_assert((D - 1) * (PER + 1) <= 63, "in-flight loads exceed vmcnt");
 };
 
@@ -672,23 +720,24 @@ __device__ __forceinline__ void split_pair(const Frag<float>& f, Quad<float>& a,
   b.x = f.hi;
 }
 
-template <typename E, int K, int V, bool VARLEN>
-__global__ __launch_bounds__(192) void gdn_chain_ring_kernel(Geo geo, const Frag<E>* __restrict__ wf,
-                                                             const Frag<E>* __restrict__ ktf,
-                                                             const Quad<E>* __restrict__ uf,
-                                                             const float* __restrict__ gam,
-                                                             const int* __restrict__ seq_slot,
-                                                             const float* __restrict__ h0,
-                                                             float* __restrict__ fin,
-                                                             Frag<E>* __restrict__ hcf,
-                                                             Frag<E>* __restrict__ vnf) {
-  using R = RingCfg<E, K, V>;
+__device__ __forceinline__ void wait_lgkm0() {
+  // gfx9 s_waitcnt with lgkmcnt = 0 and vmcnt / expcnt at their maxima
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+template <typename E, int K, int V, bool VARLEN, int NC>
+__global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_ring_kernel(
+    Geo geo, const Frag<E>* __restrict__ wf, const Frag<E>* __restrict__ ktf,
+    const Quad<E>* __restrict__ uf, const float* __restrict__ gam,
+    const int* __restrict__ seq_slot, const float* __restrict__ h0, float* __restrict__ fin,
+    Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf) {
+  using R = RingCfg<E, K, V, NC>;
   using Step = ChainStep<E, K, V>;
   constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D;
-  __shared__ __align__(16) char ring[D * R::STEP];
+  __shared__ __align__(16) char ring[R::LDS];
   int hv, rest;
-  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
-  const int n = rest / NV, vt = rest - n * NV;
+  head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
+  const int n = rest / (NV / NC), vp = rest - n * (NV / NC);
   int s0, s1;
   if constexpr (VARLEN) {
     s0 = seq_slot[n];
@@ -698,35 +747,52 @@ __global__ __launch_bounds__(192) void gdn_chain_ring_kernel(Geo geo, const Frag
     s1 = s0 + geo.NT;
   }
   const int nsteps = s1 - s0;
-  // wave index made provably uniform, so the loader branches and the LDS base
+  // wave index made provably uniform, so the role branches and the LDS base
   // of global_load_lds stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const size_t hbase = (size_t)hv * geo.slots + s0;
 
-  if (wave == 0) {
+  if (wave < NC) {
+    const int vt = NC * vp + wave;
     const int g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
     const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
     f32x4 Hs[KT];
     load_state<K, V>(Hs, h0, sbase, v, g);
-    for (int i = 0; i < nsteps; ++i) {
-      ring_barrier();
-      const char* stage = ring + (i % D) * R::STEP;
-      Step st;
+    Step st;
+    auto read_w = [&](const char* stage) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) st.w[ct][kb] = ring_frag(stage, ct * KB + kb, lane, (E*)nullptr);
+    };
+    ring_barrier();  // B_{-1}
+    if (nsteps > 0) read_w(ring);
+    for (int i = 0; i < nsteps; ++i) {
+      const char* stage = ring + (i % D) * R::STEP;
+      // the chunk's last cumulative gate value, read by every lane (broadcast)
+      const float glast = reinterpret_cast<const float*>(stage + R::GOFF)[kChunk - 1];
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        split_pair(ring_frag(stage, R::FU + 2 * wave + cp, lane, (E*)nullptr), st.u[2 * cp],
+                   st.u[2 * cp + 1]);
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           st.kt[mt][cb] = ring_frag(stage, 4 * KB + 2 * mt + cb, lane, (E*)nullptr);
+      Frag<E> vb[2];
+      st.vnew_global(Hs, vb, hcf, vnf, hbase + i, vt, lane);
+      const float dec = fast_exp2(glast);
 #pragma unroll
-      for (int cp = 0; cp < 2; ++cp)
-        split_pair(ring_frag(stage, 4 * KB + 2 * KT + cp, lane, (E*)nullptr), st.u[2 * cp],
-                   st.u[2 * cp + 1]);
-      st.gl = reinterpret_cast<const float*>(stage + R::GOFF)[lane];
-      st.compute(Hs, hcf, vnf, hbase + i, vt, lane);
+      for (int mt = 0; mt < KT; ++mt) {
+        Hs[mt] *= dec;
+        // keep the decay ahead of the barrier, overlapping the products above
+        asm volatile("" : "+v"(Hs[mt]));
+      }
+      wait_lgkm0();    // every read of stage i % D has completed
+      ring_barrier();  // B_i
+      if (i + 1 < nsteps) read_w(ring + ((i + 1) % D) * R::STEP);
+      st.update(Hs, vb);
     }
     if (fin) {
 #pragma unroll
@@ -735,9 +801,12 @@ __global__ __launch_bounds__(192) void gdn_chain_ring_kernel(Geo geo, const Frag
         for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
     }
   } else {
-    // Source of each of this wave's loads at chunk 0 (per lane); a chunk later
-    // every source has advanced by one slot of its array.
-    const int j0 = (wave - 1) * R::PER;
+    // Loader l issues loads l*PER .. l*PER + PER-1 of each chunk (1 KB blocks
+    // of the fragments); loader 0 also loads the gate row.  Sources at chunk 0
+    // (per lane); a chunk later every source has advanced by one slot of its
+    // array.
+    const int lw = wave - NC;  // loader index 0 / 1
+    const int j0 = lw * R::PER;
     const char* src0[R::PER];
     size_t adv[R::PER];
 #pragma unroll
@@ -749,34 +818,37 @@ __global__ __launch_bounds__(192) void gdn_chain_ring_kernel(Geo geo, const Frag
         const int ct = f / KB, kb = f - ct * KB;
         base = reinterpret_cast<const char*>(wf + ((hbase * 4 + ct) * KB + kb) * 64);
         adv[jj] = (size_t)4 * KB * 64 * R::FB;
-      } else if (f < 4 * KB + 2 * KT) {
+      } else if (f < R::FU) {
         const int f2 = f - 4 * KB, mt = f2 >> 1, cb = f2 & 1;
         base = reinterpret_cast<const char*>(ktf + ((hbase * KT + mt) * 2 + cb) * 64);
         adv[jj] = (size_t)KT * 2 * 64 * R::FB;
       } else {
-        const int cp = f - 4 * KB - 2 * KT;
+        const int q = f - R::FU, vt = NC * vp + (q >> 1), cp = q & 1;
         base = reinterpret_cast<const char*>(uf + ((hbase * NV + vt) * 2 + cp) * 64 * 2);
         adv[jj] = (size_t)NV * 2 * 64 * R::FB;
       }
       src0[jj] = base + lane * R::FB + 16 * h;
     }
     const float* gsrc0 = gam + hbase * kChunk + lane;
-    auto issue = [&](int i) {
-      char* stage = ring + (i % D) * R::STEP;
+    auto issue = [&](int c) {
+      char* stage = ring + (c % D) * R::STEP;
 #pragma unroll
-      for (int jj = 0; jj < R::PER; ++jj) dma16(src0[jj] + (size_t)i * adv[jj], stage + (j0 + jj) * 1024);
-      if (wave == 1)
-        __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc0 + (size_t)i * kChunk),
+      for (int jj = 0; jj < R::PER; ++jj) dma16(src0[jj] + (size_t)c * adv[jj], stage + (j0 + jj) * 1024);
+      if (lw == 0)
+        __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc0 + (size_t)c * kChunk),
                                          (lds_void_t*)(stage + R::GOFF), 4, 0, 0);
     };
-    for (int p = 0; p < D - 1 && p < nsteps; ++p) issue(p);
-    for (int i = 0; i < nsteps; ++i) {
-      const int later = nsteps - 1 - i;
-      const int ahead = later < D - 2 ? later : D - 2;
-      if (wave == 1) wait_ahead<R::PER + 1, D>(ahead);  // also loads the gate row
-      else wait_ahead<R::PER, D>(ahead);
-      ring_barrier();
-      if (i + D - 1 < nsteps) issue(i + D - 1);
+    for (int c = 0; c < D - 1 && c < nsteps; ++c) issue(c);
+    for (int i = -1; i < nsteps; ++i) {
+      if (i + 1 < nsteps) {
+        // chunk i+1 must have landed; chunks i+2 .. min(nsteps, i+D) - 1 may be in flight
+        const int later = nsteps - 2 - i;
+        const int ahead = later < D - 2 ? later : D - 2;
+        if (lw == 0) wait_ahead<R::PER + 1, D>(ahead);  // also loads the gate row
+        else wait_ahead<R::PER, D>(ahead);
+      }
+      ring_barrier();  // B_i
+      if (i + D < nsteps) issue(i + D);
     }
   }
 }
