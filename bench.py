@@ -11,7 +11,6 @@ kernel (per-kernel durations measured live with HIP events on the launch
 stream), and the fp64 CPU oracle timed on this host as a baseline.
 """
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -39,6 +38,10 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="no GPU: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE passes under DIR "
+                         "(fetch/, write/, copy_fetch/, copy_write/) into profiles/traffic.json "
+                         "for --workload")
     return ap.parse_args()
 
 
@@ -83,14 +86,64 @@ def algorithmic(shape, esz, has_h0, used_slots):
     return kern, path, ntok
 
 
-def hip_runtime():
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                        ctypes.c_void_p]
-    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    return hip
+KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
+                ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
+                ("gdn_output_kernel", "output"))
+
+
+def counter_means(path):
+    """Mean counter value (KiB) per dispatch of each stage's kernel, and of the
+    largest plain copy, from one rocprofv3 counter_collection.csv."""
+    import csv
+    vals, copies = {}, []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            for key, stage in KERNEL_STAGE:
+                if key in name:
+                    vals.setdefault(stage, []).append(v)
+                    break
+            else:
+                if "copyBuffer" in name:
+                    copies.append(v)
+    return {k: sum(v) / len(v) for k, v in vals.items()}, (max(copies) if copies else None)
+
+
+def write_traffic(d, workload, copy_bytes):
+    """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by copy_bytes / (the same counter for a plain copy of
+    copy_bytes bytes read and copy_bytes written)."""
+    import glob
+
+    def one(sub):
+        f = glob.glob(os.path.join(d, sub, "*_counter_collection.csv"))
+        if len(f) != 1:
+            raise SystemExit("expected one counter_collection.csv under %s/%s" % (d, sub))
+        return counter_means(f[0])
+    fetch, _ = one("fetch")
+    write, _ = one("write")
+    _, copy_fetch = one("copy_fetch")
+    _, copy_write = one("copy_write")
+    kf = copy_bytes / (copy_fetch * 1024.0)
+    kw = copy_bytes / (copy_write * 1024.0)
+    src = source_hash()
+    tr = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+    ent = {}
+    for stage in fetch:
+        fb, wb = fetch[stage] * 1024.0 * kf, write.get(stage, 0.0) * 1024.0 * kw
+        ent[stage] = {"bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+                      "write_bytes": int(round(wb)), "fetch_kib_raw": round(fetch[stage], 2),
+                      "write_kib_raw": round(write.get(stage, 0.0), 2),
+                      "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
+                      "source_hash": src}
+    tr[workload] = ent
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(tr, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(tr[workload]), flush=True)
 
 
 def copy_calibration(mib):
@@ -133,6 +186,9 @@ def cpu_baseline(inp, target_s):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.workload, args.copy_mib << 20)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr, flush=True)
@@ -152,8 +208,6 @@ def main():
     packed = inp.cu_seqlens is not None
     plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], inp.q.dtype, "cuda",
                           num_seqs=s["N"] if packed else None, scale=inp.scale)
-    call = lambda ev=None: plan(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log,  # noqa
-                                inp.dt_bias, inp.cu_seqlens, inp.h0, events=ev)
     stream = torch.cuda.current_stream()
 
     step = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias,
@@ -196,30 +250,19 @@ def main():
     except Exception as exc:  # graph capture is an extra view, not the headline
         print("graph timing skipped: %s" % exc, file=sys.stderr, flush=True)
 
-    # per-kernel durations: the same K steps with events between the stages
-    hip = hip_runtime()
-    nev = gdn.NUM_STAGES + 1
-    handles = []
-    for _ in range(nev * args.steps):
-        e = ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        handles.append(e.value)
-    per_step = [(ctypes.c_void_p * nev)(*handles[i * nev:(i + 1) * nev])
-                for i in range(args.steps)]
-    torch.cuda.synchronize()
-    for arr in per_step:
-        call(arr)
-    torch.cuda.synchronize()
-    stage_ms = [0.0] * gdn.NUM_STAGES
-    f = ctypes.c_float()
-    for arr in per_step:
-        for i in range(gdn.NUM_STAGES):
-            if hip.hipEventElapsedTime(ctypes.byref(f), arr[i], arr[i + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            stage_ms[i] += f.value / args.steps
-    for h in handles:
-        hip.hipEventDestroy(h)
+    # per-kernel durations: each kernel alone, K back-to-back launches between two
+    # events on the launch stream (gdn_fwd_stages re-runs one stage on the
+    # workspace the full steps above left; results are unchanged by it)
+    stage_ms = []
+    for name in gdn.STAGES:
+        if name == "chunk_map" and not packed:
+            stage_ms.append(0.0)
+            continue
+        one = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias,
+                        inp.cu_seqlens, inp.h0, stream=stream, stage_mask=gdn.STAGE_BITS[name])
+        for _ in range(max(1, args.warmup)):
+            one()
+        stage_ms.append(timed(one, args.steps))
 
     dtype = cfg["dtype"]
     esz = 2 if dtype == "bf16" else 4

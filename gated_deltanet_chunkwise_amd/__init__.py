@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     NUM_STAGES,
     Params,
     STAGES,
+    STAGE_ALL,
+    STAGE_BITS,
     WorkspaceLayout,
     check,
     fwd,
@@ -26,7 +28,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "WorkspaceLayout",
+    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
     "check", "fwd", "lib_path", "load_library", "make_params", "status_string",
     "workspace_layout", "workspace_size",
 ]

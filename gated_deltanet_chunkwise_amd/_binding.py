@@ -14,9 +14,12 @@ GDN_F32 = 0
 GDN_BF16 = 1
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
-           "gdn_fwd", "gdn_fwd_timed", "gdn_status_string")
+           "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_status_string")
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
+# gdn_fwd_stages bits, one per entry of STAGES
+STAGE_BITS = {name: 1 << i for i, name in enumerate(STAGES)}
+STAGE_ALL = (1 << len(STAGES)) - 1
 
 
 class Params(ctypes.Structure):
@@ -70,6 +73,8 @@ def _declare(lib):
     lib.gdn_fwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp]
     lib.gdn_fwd_timed.restype = ctypes.c_int
     lib.gdn_fwd_timed.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp, ctypes.c_void_p]
+    lib.gdn_fwd_stages.restype = ctypes.c_int
+    lib.gdn_fwd_stages.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, ctypes.c_uint, fp]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -148,10 +153,8 @@ class GdnForward:
         self.final_state = (torch.empty((self.N, HV, K, V), dtype=torch.float32, device=device)
                             if final_state else None)
 
-    def __call__(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
-                 initial_state=None, stream=None, events=None):
-        """Launch on `stream` (default: torch's current stream).  `events`: optional
-        ctypes array of NUM_STAGES + 1 hipEvent_t recorded around the stages."""
+    def _args(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream):
+        """Checked ctypes argument tuple of gdn_fwd (host-side checks only)."""
         torch = _torch()
         if (cu_seqlens is not None) != self.packed:
             raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
@@ -166,6 +169,16 @@ class GdnForward:
                 _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
                 _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
                 ctypes.c_void_p(stream.cuda_stream))
+        st = self.lib.gdn_fwd_check(*args[:-1])
+        if st:
+            raise GdnError(st, "gdn_fwd_check")
+        return args
+
+    def __call__(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
+                 initial_state=None, stream=None, events=None):
+        """Launch on `stream` (default: torch's current stream).  `events`: optional
+        ctypes array of NUM_STAGES + 1 hipEvent_t recorded around the stages."""
+        args = self._args(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream)
         if events is None:
             st = self.lib.gdn_fwd(*args)
         else:
@@ -175,19 +188,21 @@ class GdnForward:
         return self.o, self.final_state
 
     def bind(self, q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
-             initial_state=None, stream=None):
-        """Marshal the arguments once; returns a zero-argument callable that
-        launches the pass (for hot loops: no per-call Python checks)."""
-        torch = _torch()
-        self(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream)  # validate
-        if stream is None:
-            stream = torch.cuda.current_stream(q.device)
-        args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
-                _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(self.o),
-                _ptr(self.final_state), _ptr(self.workspace), self.ws_bytes,
-                ctypes.c_void_p(stream.cuda_stream))
+             initial_state=None, stream=None, stage_mask=None):
+        """Marshal and check the arguments once (nothing is launched); returns a
+        zero-argument callable that launches the pass (for hot loops: no
+        per-call Python checks).  `stage_mask` (STAGE_BITS values) restricts it
+        to those stages, through gdn_fwd_stages: meaningful once a full call
+        has filled the workspace."""
+        args = self._args(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream)
         keep = (q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state)
-        fn = self.lib.gdn_fwd
+        if stage_mask is None:
+            fn = self.lib.gdn_fwd
+        else:
+            st_fn = self.lib.gdn_fwd_stages
+            mask = ctypes.c_uint(stage_mask)
+            args, stream_arg = args[:-1], args[-1]
+            fn = lambda *a: st_fn(*a, mask, stream_arg)  # noqa: E731
 
         def launch():
             keep  # the tensors stay alive as long as the callable

@@ -120,7 +120,7 @@ template <typename E, int K, int V, bool VARLEN>
 gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                  const float* beta, const float* A_log, const float* dt_bias,
                  const int64_t* cu_seqlens, const float* h0, void* o, float* fin, void* ws,
-                 hipStream_t s, void* const* events) {
+                 hipStream_t s, void* const* events, unsigned mask) {
   using gdn::Frag;
   using gdn::Quad;
   const gdn::Geo& geo = pl.geo;
@@ -149,15 +149,15 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   };
   mark(0);
   const bool work = geo.N > 0;
-  if (VARLEN && work)
+  if (VARLEN && work && (mask & GDN_STAGE_CHUNK_MAP))
     ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
               geo.slots, cmap, seq_slot));
   mark(1);
-  if (work && geo.slots > 0)
+  if (work && geo.slots > 0 && (mask & GDN_STAGE_WY))
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo, ke,
               ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf));
   mark(2);
-  if (work) {
+  if (work && (mask & GDN_STAGE_STATE)) {
     // LDS-ring variant when its workgroups fit one per CU: one compute wave
     // (16 columns) per workgroup when the units fit, two sharing the ring
     // otherwise; beyond that many units share a CU and the register-buffered
@@ -183,7 +183,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
                 uf, gam, seq_slot, h0, fin, hcf, vnf));
   }
   mark(3);
-  if (work && geo.slots > 0)
+  if (work && geo.slots > 0 && (mask & GDN_STAGE_OUTPUT))
     ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo,
               qe, ke, cmap, gam, hcf, vnf, oe));
   mark(4);
@@ -194,21 +194,21 @@ template <typename E, int K, int V>
 gdn_status_t run_v(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                    const float* beta, const float* A_log, const float* dt_bias,
                    const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s,
-                   void* const* ev) {
-  return pl.varlen ? run<E, K, V, true>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev)
-                   : run<E, K, V, false>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
+                   void* const* ev, unsigned m) {
+  return pl.varlen ? run<E, K, V, true>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m)
+                   : run<E, K, V, false>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
 }
 
 template <typename E>
 gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                    const float* beta, const float* A_log, const float* dt_bias,
                    const int64_t* cu, const float* h0, void* o, float* fin, void* ws, hipStream_t s,
-                   void* const* ev) {
+                   void* const* ev, unsigned m) {
   const int K = pl.geo.K, V = pl.geo.V;
-  if (K == 128 && V == 128) return run_v<E, 128, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
-  if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
-  if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
-  return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev);
+  if (K == 128 && V == 128) return run_v<E, 128, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
+  if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
+  if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
+  return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
 }
 
 }  // namespace
@@ -240,22 +240,44 @@ gdn_status_t gdn_fwd_check(const gdn_params_t* p, const void* q, const void* k, 
                    final_state, workspace, workspace_bytes, &pl);
 }
 
+namespace {
+gdn_status_t fwd_entry(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                       const float* g_raw, const float* beta, const float* A_log,
+                       const float* dt_bias, const int64_t* cu_seqlens, const float* initial_state,
+                       void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* events, unsigned mask) {
+  Plan pl;
+  gdn_status_t st = check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
+                              o, final_state, workspace, workspace_bytes, &pl);
+  if (st != GDN_OK) return st;
+  if (mask & ~GDN_STAGE_ALL) return GDN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == GDN_BF16)
+    return run_e<gdn::bf16>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                            final_state, workspace, s, events, mask);
+  return run_e<float>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                      final_state, workspace, s, events, mask);
+}
+}  // namespace
+
 gdn_status_t gdn_fwd_timed(const gdn_params_t* p, const void* q, const void* k, const void* v,
                            const float* g_raw, const float* beta, const float* A_log,
                            const float* dt_bias, const int64_t* cu_seqlens,
                            const float* initial_state, void* o, float* final_state,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* events) {
-  Plan pl;
-  gdn_status_t st = check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
-                              o, final_state, workspace, workspace_bytes, &pl);
-  if (st != GDN_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->dtype == GDN_BF16)
-    return run_e<gdn::bf16>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
-                            final_state, workspace, s, events);
-  return run_e<float>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
-                      final_state, workspace, s, events);
+  return fwd_entry(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                   final_state, workspace, workspace_bytes, stream, events, GDN_STAGE_ALL);
+}
+
+gdn_status_t gdn_fwd_stages(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                            const float* g_raw, const float* beta, const float* A_log,
+                            const float* dt_bias, const int64_t* cu_seqlens,
+                            const float* initial_state, void* o, float* final_state,
+                            void* workspace, size_t workspace_bytes, unsigned stage_mask,
+                            void* stream) {
+  return fwd_entry(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                   final_state, workspace, workspace_bytes, stream, nullptr, stage_mask);
 }
 
 gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const void* v,

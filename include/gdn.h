@@ -156,6 +156,28 @@ gdn_status_t gdn_fwd_timed(const gdn_params_t *p, const void *q, const void *k,
                            float *final_state, void *workspace, size_t workspace_bytes,
                            void *stream, void *const *events);
 
+/* Stage bits for gdn_fwd_stages, in the order the pass runs them. */
+#define GDN_STAGE_CHUNK_MAP 1u /* packed sequences only */
+#define GDN_STAGE_WY 2u        /* with the gate prologue */
+#define GDN_STAGE_STATE 4u
+#define GDN_STAGE_OUTPUT 8u
+#define GDN_STAGE_ALL 15u
+
+/* gdn_fwd restricted to the stages whose bits are set in `stage_mask`, for
+ * timing or profiling one kernel on its own.  Each stage reads what the
+ * earlier ones left in the workspace, so a partial mask reproduces gdn_fwd's
+ * results only on a workspace that already holds a full call with the same
+ * arguments; the stages are deterministic, so re-running any subset on such a
+ * workspace leaves o, final_state and the workspace as they were.
+ * GDN_STAGE_ALL is gdn_fwd.  Same validation and errors as gdn_fwd, plus
+ * GDN_ERR_UNSUPPORTED for bits outside GDN_STAGE_ALL. */
+gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
+                            const void *v, const float *g_raw, const float *beta,
+                            const float *A_log, const float *dt_bias,
+                            const int64_t *cu_seqlens, const float *initial_state, void *o,
+                            float *final_state, void *workspace, size_t workspace_bytes,
+                            unsigned stage_mask, void *stream);
+
 /* Static description of a status code. */
 const char *gdn_status_string(gdn_status_t s);
 

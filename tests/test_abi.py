@@ -110,6 +110,21 @@ def test_packed_rules():
     assert gdn.check(p, ptrs(cu_seqlens=0x90000), ws - 256) == EWS
 
 
+def test_stage_mask_outside_the_stages_is_rejected():
+    """gdn_fwd_stages validates like gdn_fwd, then refuses unknown stage bits
+    before anything is enqueued (the fake pointers are never used)."""
+    lib = gdn.load_library()
+    p = P()
+    ws = gdn.workspace_size(p)
+    vp = [ctypes.c_void_p(a) for a in ptrs()]
+    for mask in (gdn.STAGE_ALL + 1, 1 << 31):
+        assert lib.gdn_fwd_stages(ctypes.byref(p), *vp, ws, mask, None) == EUNSUP
+    # argument errors come first, as in gdn_fwd
+    vp_null = [ctypes.c_void_p(a) if a else None for a in ptrs(q=None)]
+    assert lib.gdn_fwd_stages(ctypes.byref(p), *vp_null, ws, 1, None) == ENULL
+    assert gdn.STAGE_ALL == 15 and gdn.STAGE_BITS["chain"] == 4
+
+
 def test_empty_token_batch_needs_no_token_pointers():
     p = P(T=0)
     null = dict(q=None, k=None, v=None, g_raw=None, beta=None, A_log=None, o=None)
