@@ -30,6 +30,9 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 def _declare(lib):
     lib.gdn_oracle_gate.restype = None
     lib.gdn_oracle_gate.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int, _dp]
+    lib.gdn_oracle_kda_gate.restype = None
+    lib.gdn_oracle_kda_gate.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, _dp]
     common = [ctypes.c_int] * 6 + [_i64p, ctypes.c_int, _dp, _dp, _dp]
     tail = [ctypes.c_double, _i32p, ctypes.c_int, _dp, _dp, ctypes.c_int]
     lib.gdn_oracle_recurrence.restype = ctypes.c_int
@@ -80,6 +83,26 @@ def gate(g_raw, A_log, dt_bias=None, lib=None):
     out = np.empty_like(flat)
     lib.gdn_oracle_gate(_ptr(flat), _ptr(A_log), _ptr(dt_bias), flat.shape[0], HV, _ptr(out))
     return out.reshape(g_raw.shape)
+
+
+def kda_gate(g, A_log, dt_bias=None, lib=None):
+    """KDA per-channel gate in fp64: g [..., H, D] -> yg of the same shape,
+    yg = -exp(A_log[h]) * softplus(g + dt_bias.reshape(H, D))."""
+    lib = lib or load()
+    g = _f64(g)
+    A_log = _f64(A_log)
+    H, D = g.shape[-2:]
+    if A_log.shape != (H,):
+        raise ValueError("A_log must be [H]")
+    if dt_bias is not None:
+        dt_bias = _f64(dt_bias).reshape(-1)
+        if dt_bias.shape != (H * D,):
+            raise ValueError("dt_bias must hold H*D values")
+    flat = g.reshape(-1, H, D)
+    out = np.empty_like(flat)
+    lib.gdn_oracle_kda_gate(_ptr(flat), _ptr(A_log), _ptr(dt_bias), flat.shape[0], H, D,
+                            _ptr(out))
+    return out.reshape(g.shape)
 
 
 def _shapes(q, v, cu_seqlens):

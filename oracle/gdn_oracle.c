@@ -71,6 +71,24 @@ void gdn_oracle_gate(const double *g_raw, const double *A_log, const double *dt_
     }
 }
 
+/* KDA gate, per channel (the KDA gate guide, "core computation logic": the
+ * formula, the stable softplus, fp32 inside the operator -- here fp64):
+ *   yg[t,h,d] = -exp(A_log[h]) * softplus(g[t,h,d] + dt_bias[h*D + d]).
+ * Layouts: g, yg [T][H][D] contiguous; A_log [H]; dt_bias [H*D] or NULL (no
+ * bias).  T is the number of rows after flattening the leading dimensions. */
+void gdn_oracle_kda_gate(const double *g, const double *A_log, const double *dt_bias,
+                         int64_t T, int H, int D, double *yg) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      const double head_scale = -exp(A_log[h]);
+      const int64_t row = (t * H + h) * (int64_t)D;
+      for (int d = 0; d < D; ++d) {
+        const double biased = g[row + d] + (dt_bias ? dt_bias[(int64_t)h * D + d] : 0.0);
+        yg[row + d] = head_scale * oracle_softplus(biased);
+      }
+    }
+}
+
 typedef struct {
   int HV, H, K, V, N;
   const int64_t *bos; /* [N+1] sequence offsets */

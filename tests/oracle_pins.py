@@ -86,6 +86,51 @@ def pin_gate(lib):
     assert oracle.gate(np.array([[1.0]]), np.array([-np.inf]), z[:1], lib=lib)[0, 0] == 0.0
 
 
+def pin_kda_gate(lib):
+    """KDA per-channel gate: yg[t,h,d] = -exp(A_log[h]) softplus(g[t,h,d] + dt_bias[h,d])."""
+    rng = np.random.default_rng(17)
+    T, H, D = 7, 3, 5
+    g = rng.standard_normal((T, H, D)) * 4.0
+    A = rng.standard_normal(H)
+    b = rng.standard_normal(H * D)
+    y = oracle.kda_gate(g, A, b, lib=lib)
+    # a library routine: softplus(x) = logaddexp(0, x) = log(e^0 + e^x) (below 20)
+    ref = -np.exp(A)[None, :, None] * np.logaddexp(0.0, g + b.reshape(H, D)[None])
+    _close(y, ref, 1e-14, "kda gate vs logaddexp")
+    # indexing by hand on a tiny case: bias per (head, channel), scale per head
+    for t in range(T):
+        for h in range(H):
+            for d in range(D):
+                x = g[t, h, d] + b[h * D + d]
+                want = -math.exp(A[h]) * math.log1p(math.exp(x))
+                assert abs(y[t, h, d] - want) <= 1e-14 * abs(want), (t, h, d)
+    # no bias = zero bias
+    _close(oracle.kda_gate(g, A, None, lib=lib), oracle.kda_gate(g, A, np.zeros(H * D), lib=lib),
+           0.0, "no bias")
+    # shifting g by c[h,d] and the bias by -c leaves yg unchanged
+    c = rng.standard_normal((H, D))
+    _close(oracle.kda_gate(g + c[None], A, b - c.reshape(-1), lib=lib), y, 1e-14,
+           "bias shift")
+    # exp(A_log[h]) scales head h only
+    A2 = A.copy()
+    A2[1] += math.log(5.0)
+    y2 = oracle.kda_gate(g, A2, b, lib=lib)
+    _close(y2[:, 1], 5.0 * y[:, 1], 1e-14, "head scale")
+    _close(np.delete(y2, 1, axis=1), np.delete(y, 1, axis=1), 0.0, "other heads")
+    # identity branch above 20, exactly; D = 1 is the per-head gate of the GDN path
+    big = np.full((2, H, 1), 25.0)
+    _close(oracle.kda_gate(big, A, None, lib=lib)[..., 0], np.tile(-np.exp(A) * 25.0, (2, 1)), 0.0,
+           "identity branch")
+    g1 = rng.standard_normal((T, H, 1))
+    b1 = rng.standard_normal(H)
+    _close(oracle.kda_gate(g1, A, b1, lib=lib)[..., 0], oracle.gate(g1[..., 0], A, b1, lib=lib),
+           0.0, "D = 1 is the per-head gate")
+    # leading dimensions flatten into T
+    g4 = rng.standard_normal((2, 3, H, D))
+    _close(oracle.kda_gate(g4, A, b, lib=lib).reshape(-1, H, D),
+           oracle.kda_gate(g4.reshape(-1, H, D), A, b, lib=lib), 0.0, "flattening")
+
+
 # ---------------------------------------------------------------------------
 # brute force: the literal matrix form S_t = e^g S (I - b k k^T) + b v k^T
 
@@ -303,5 +348,5 @@ def pin_full_forward(lib):
     _close(o3, o1, 1e-15, "dt_bias None")
 
 
-ALL_PINS = [pin_gate, pin_brute_force, pin_transition_product, pin_identities, pin_chunkwise,
-            pin_invariants, pin_full_forward]
+ALL_PINS = [pin_gate, pin_kda_gate, pin_brute_force, pin_transition_product, pin_identities,
+            pin_chunkwise, pin_invariants, pin_full_forward]

@@ -30,6 +30,12 @@ MUTANTS = {
     "scale_ignored": ("ot[j] *= J->scale;", "ot[j] *= 1.0;"),
     "h0_ignored": ("  if (J->h0)\n    memcpy", "  if (0)\n    memcpy"),
     "no_reset_between_sequences": ("for (int64_t t = J->bos[n];", "for (int64_t t = J->bos[0];"),
+    "kda_bias_per_channel_only": ("dt_bias[(int64_t)h * D + d]", "dt_bias[d]"),
+    "kda_bias_per_head_only": ("dt_bias[(int64_t)h * D + d]", "dt_bias[h]"),
+    "kda_scale_not_exponentiated": ("const double head_scale = -exp(A_log[h]);",
+                                    "const double head_scale = -A_log[h];"),
+    "kda_rows_strided_by_D": ("const int64_t row = (t * H + h) * (int64_t)D;",
+                              "const int64_t row = (h * T + t) * (int64_t)D;"),
     "decay_is_exp_of_negative": ("const double a = exp(J->g[t * HV + hv]);",
                                  "const double a = exp(-J->g[t * HV + hv]);"),
 }
