@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pages_bf16")
+    ap.add_argument("--op", default="gdn_fwd", choices=["gdn_fwd", "kda_gate"],
+                    help="gdn_fwd: the forward pass (headline); kda_gate: the KDA per-channel "
+                         "gate on the guide's timing shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -88,7 +91,8 @@ def algorithmic(shape, esz, has_h0, used_slots):
 
 KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
                 ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
-                ("gdn_output_kernel", "output"))
+                ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
+                ("gdn_kda_gate_scalar_kernel", "kda_gate"))
 
 
 def counter_means(path):
@@ -184,6 +188,97 @@ def cpu_baseline(inp, target_s):
                       "%.1f s; threads=%d" % (ntok, s["HV"], units, reps, total, threads)}
 
 
+# The KDA gate guide's timing configuration ("performance tests"): T=2048,
+# H=16, D=128, bf16, with a bias; its inputs as in its tests (N(0,1)).
+KDA_SHAPE = dict(T=2048, H=16, D=128)
+
+
+def bench_kda(args):
+    """One JSON line for the KDA per-channel gate: elements/s, its HBM roofline and
+    the fp64 oracle on the host."""
+    import numpy as np
+    import torch
+    import gated_deltanet_chunkwise_amd as gdn
+    T, H, D = KDA_SHAPE["T"], KDA_SHAPE["H"], KDA_SHAPE["D"]
+    gen = torch.Generator().manual_seed(20270)
+    g = torch.randn((T, H, D), generator=gen).to(torch.bfloat16)
+    A = torch.randn(H, generator=gen)
+    b = torch.randn(H * D, generator=gen)
+    gd, Ad, bd = g.cuda(), A.cuda(), b.cuda()
+    out = torch.empty_like(gd)
+    # one launch takes a few microseconds, less than the host needs to issue one,
+    # so the timed region replays a HIP graph of PER back-to-back launches
+    PER = 20
+    cap = torch.cuda.Stream()
+    launch, _ = gdn.kda_gate_launcher(gd, Ad, bd, out=out, stream=cap)
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for _ in range(3):
+            launch()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(PER):
+            launch()
+    stream = torch.cuda.current_stream()
+    reps = max(1, args.steps // PER)
+    for _ in range(max(1, args.warmup // PER)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * PER)
+    # the graph's result equals one eager call's (the gate is deterministic)
+    ref_launch, ref = gdn.kda_gate_launcher(gd, Ad, bd)
+    ref_launch()
+    torch.cuda.synchronize()
+    if not torch.equal(ref, out):
+        raise RuntimeError("graph replay of the KDA gate differs from an eager call")
+    n = T * H * D
+    nbytes = n * (2 + 2) + H * 4 + H * D * 4     # g in, yg out (bf16), A_log, dt_bias
+    sec = ms / 1e3
+    line = {
+        "metric": "KDA gate elements/s (T=2048,H=16,D=128 bf16, bias)",
+        "value": round(n / sec, 1), "unit": "elements/s", "n_gpus": 1,
+        "steps": reps * PER, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_gate", "T": T, "H": H, "D": D, "bias": True,
+                   "out_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(nbytes / sec / HBM_PEAK, 4), "kernel": "kda_gate",
+                     "traffic": None},
+        "kernel_source_hash": source_hash(),
+    }
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            ent = json.load(fh).get("kda_gate", {}).get("kda_gate")
+        if ent and ent.get("source_hash") == line["kernel_source_hash"]:
+            line["roofline"]["traffic"] = ent["bytes_per_launch"]
+    if not args.no_cpu_baseline:
+        import oracle
+        g64 = g.float().numpy().astype(np.float64)
+        A64, b64 = A.numpy().astype(np.float64), b.numpy().astype(np.float64)
+        oracle.load()
+        reps, total = 0, 0.0
+        while total < args.cpu_seconds:
+            t0 = time.perf_counter()
+            oracle.kda_gate(g64, A64, b64)
+            total += time.perf_counter() - t0
+            reps += 1
+        line["cpu_baseline"] = {"value": reps * n / total, "unit": "elements/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": "the whole shape (%d elements), %d run(s), %.1f s, "
+                                          "one thread" % (n, reps, total)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -196,6 +291,9 @@ def main():
     import torch
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.op == "kda_gate":
+        bench_kda(args)
         return
     import gated_deltanet_chunkwise_amd as gdn
     from gated_deltanet_chunkwise_amd.inputs import WORKLOADS, workload_inputs

@@ -8,6 +8,7 @@ load the library; the first call does, and raises if it was not built
 """
 from ._binding import (  # noqa: F401
     GDN_BF16,
+    GDN_F16,
     GDN_F32,
     GdnError,
     GdnForward,
@@ -19,6 +20,8 @@ from ._binding import (  # noqa: F401
     WorkspaceLayout,
     check,
     fwd,
+    kda_gate,
+    kda_gate_launcher,
     lib_path,
     load_library,
     make_params,
@@ -28,7 +31,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "GDN_BF16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
-    "check", "fwd", "lib_path", "load_library", "make_params", "status_string",
+    "GDN_BF16", "GDN_F16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
+    "check", "fwd", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
     "workspace_layout", "workspace_size",
 ]

@@ -12,9 +12,10 @@ _LIB = None
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_F16 = 2  # KDA gate only
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
-           "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_status_string")
+           "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_kda_gate", "gdn_status_string")
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
 # gdn_fwd_stages bits, one per entry of STAGES
@@ -73,6 +74,9 @@ def _declare(lib):
     lib.gdn_fwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp]
     lib.gdn_fwd_timed.restype = ctypes.c_int
     lib.gdn_fwd_timed.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp, ctypes.c_void_p]
+    lib.gdn_kda_gate.restype = ctypes.c_int
+    lib.gdn_kda_gate.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_int32, ctypes.c_int32, fp]
     lib.gdn_fwd_stages.restype = ctypes.c_int
     lib.gdn_fwd_stages.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, ctypes.c_uint, fp]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -210,6 +214,58 @@ class GdnForward:
             if st:
                 raise GdnError(st)
         return launch
+
+
+def _any_dtype_code(dt):
+    torch = _torch()
+    codes = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
+    if dt not in codes:
+        raise TypeError("dtype must be float32, bfloat16 or float16, got %s" % dt)
+    return codes[dt]
+
+
+def kda_gate(g, A_log, dt_bias=None, output_dtype=None, out=None, stream=None):
+    """KDA per-channel gate through gdn_kda_gate: g [..., H, D] (fp32 / bf16 / fp16),
+    A_log [H] fp32, dt_bias [H*D] (or [H, D]) fp32 or None.  Returns yg, shaped
+    like g, in output_dtype (default: g's dtype), or written into `out`.
+    `out` may be g itself (in place) when the dtypes match."""
+    launch, out = kda_gate_launcher(g, A_log, dt_bias, output_dtype, out, stream)
+    launch()
+    return out
+
+
+def kda_gate_launcher(g, A_log, dt_bias=None, output_dtype=None, out=None, stream=None):
+    """Check and marshal kda_gate's arguments once; returns (launch, out), where
+    launch() enqueues gdn_kda_gate with them (for timing loops and graph capture)."""
+    torch = _torch()
+    if g.dim() < 2:
+        raise ValueError("g must be [..., H, D]")
+    H, D = g.shape[-2:]
+    T = g.numel() // (H * D) if H * D else 0
+    if A_log.shape != (H,) or A_log.dtype != torch.float32:
+        raise ValueError("A_log must be float32 [H]")
+    if dt_bias is not None and (dt_bias.numel() != H * D or dt_bias.dtype != torch.float32):
+        raise ValueError("dt_bias must be float32 with H*D elements")
+    if out is None:
+        out = torch.empty(g.shape, dtype=output_dtype or g.dtype, device=g.device)
+    elif out.shape != g.shape:
+        raise ValueError("out must have g's shape")
+    for name, t in (("g", g), ("A_log", A_log), ("dt_bias", dt_bias), ("out", out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if stream is None:
+        stream = torch.cuda.current_stream(g.device)
+    fn = load_library().gdn_kda_gate
+    args = (_ptr(g), _any_dtype_code(g.dtype), _ptr(A_log), _ptr(dt_bias), _ptr(out),
+            _any_dtype_code(out.dtype), T, H, D, ctypes.c_void_p(stream.cuda_stream))
+    keep = (g, A_log, dt_bias, out)
+
+    def launch():
+        keep  # the tensors stay alive as long as the callable
+        st = fn(*args)
+        if st:
+            raise GdnError(st, "gdn_kda_gate")
+    return launch, out
 
 
 def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_state=None,

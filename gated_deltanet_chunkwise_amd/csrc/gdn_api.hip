@@ -2,12 +2,14 @@
 // and the launch sequence.  See include/gdn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <tuple>
 #include <utility>
 
 #include "gdn.h"
+#include "gdn_kda.h"
 #include "gdn_kernels.h"
 
 namespace {
@@ -213,6 +215,42 @@ gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, 
 
 }  // namespace
 
+namespace {
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t elem_size(gdn_dtype_t t) { return t == GDN_F32 ? 4 : 2; }
+
+template <typename TI, typename TO>
+gdn_status_t kda_launch(const void* g, const float* A_log, const float* dt_bias, void* yg,
+                        int64_t T, int H, int D, hipStream_t s) {
+  const TI* gi = static_cast<const TI*>(g);
+  TO* yo = static_cast<TO*>(yg);
+  const int64_t rows = T * H;
+  const int64_t cap = (int64_t)device_cus() * 32;  // grid-stride beyond ~32 workgroups per CU
+  hipError_t e;
+  if (D % 8 == 0 && D <= 8 * 256 && aligned_to(g, 16) && aligned_to(yg, 16) &&
+      (!dt_bias || aligned_to(dt_bias, 16))) {
+    const int rows_per_wg = 256 / (D / 8);
+    const int64_t blocks = std::min<int64_t>((rows + rows_per_wg - 1) / rows_per_wg, cap);
+    e = launch(gdn::gdn_kda_gate_vec_kernel<TI, TO>, dim3((unsigned)blocks), dim3(256), s, gi,
+               A_log, dt_bias, yo, rows, H, D);
+  } else {
+    const int64_t n = rows * D;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, cap);
+    e = launch(gdn::gdn_kda_gate_scalar_kernel<TI, TO>, dim3((unsigned)blocks), dim3(256), s, gi,
+               A_log, dt_bias, yo, n, H, D);
+  }
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename TI>
+gdn_status_t kda_out(const void* g, const float* A_log, const float* dt_bias, void* yg,
+                     gdn_dtype_t yt, int64_t T, int H, int D, hipStream_t s) {
+  if (yt == GDN_F32) return kda_launch<TI, float>(g, A_log, dt_bias, yg, T, H, D, s);
+  if (yt == GDN_BF16) return kda_launch<TI, gdn::bf16>(g, A_log, dt_bias, yg, T, H, D, s);
+  return kda_launch<TI, gdn::f16>(g, A_log, dt_bias, yg, T, H, D, s);
+}
+}  // namespace
+
 extern "C" {
 
 size_t gdn_fwd_workspace_size(const gdn_params_t* p, int packed) {
@@ -287,6 +325,24 @@ gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const 
                      void* stream) {
   return gdn_fwd_timed(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
                        final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status_t gdn_kda_gate(const void* g, gdn_dtype_t g_dtype, const float* A_log,
+                          const float* dt_bias, void* yg, gdn_dtype_t yg_dtype, int64_t T,
+                          int32_t H, int32_t D, void* stream) {
+  if (T < 0 || H < 1 || D < 1) return GDN_ERR_SHAPE;
+  if ((int64_t)H * D > INT64_MAX / (T > 0 ? T : 1)) return GDN_ERR_SHAPE;
+  auto known = [](gdn_dtype_t t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; };
+  if (!known(g_dtype) || !known(yg_dtype)) return GDN_ERR_DTYPE;
+  if (T == 0) return GDN_OK;
+  if (!g || !A_log || !yg) return GDN_ERR_NULL;
+  if (!aligned_to(g, elem_size(g_dtype)) || !aligned_to(yg, elem_size(yg_dtype)) ||
+      !aligned_to(A_log, 4) || (dt_bias && !aligned_to(dt_bias, 4)))
+    return GDN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_dtype == GDN_F32) return kda_out<float>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
+  if (g_dtype == GDN_BF16) return kda_out<gdn::bf16>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
+  return kda_out<gdn::f16>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
 }
 
 const char* gdn_status_string(gdn_status_t s) {

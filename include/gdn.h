@@ -74,14 +74,15 @@ typedef enum {
   GDN_OK = 0,
   GDN_ERR_NULL = 1,        /* a required pointer is NULL */
   GDN_ERR_SHAPE = 2,       /* negative size, HV % H != 0, cu_seqlens with B != 1, ... */
-  GDN_ERR_DTYPE = 3,       /* dtype is not GDN_F32 or GDN_BF16 */
+  GDN_ERR_DTYPE = 3,       /* dtype not supported by the entry point */
   GDN_ERR_UNSUPPORTED = 4, /* K or V not in {64, 128}, or a size beyond the int32 index range */
   GDN_ERR_ALIGN = 5,       /* a pointer is not aligned as required below */
   GDN_ERR_WORKSPACE = 6,   /* workspace smaller than gdn_fwd_workspace_size() */
   GDN_ERR_LAUNCH = 7       /* a kernel launch failed */
 } gdn_status_t;
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+/* Element types.  gdn_fwd takes GDN_F32 or GDN_BF16; the KDA gate takes all three. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype_t;
 
 typedef struct {
   int32_t B;        /* sequences (fixed length), or 1 with cu_seqlens */
@@ -177,6 +178,29 @@ gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
                             const int64_t *cu_seqlens, const float *initial_state, void *o,
                             float *final_state, void *workspace, size_t workspace_bytes,
                             unsigned stage_mask, void *stream);
+
+/* ---- KDA per-channel gate --------------------------------------------------
+ * The KDA gate guide (MindSpeed-Ops issue page, "core computation logic"):
+ *     yg[t,h,d] = -exp(A_log[h]) * softplus(g[t,h,d] + dt_bias[h*D + d]),
+ *     softplus(x) = x for x > 20, else log(1 + e^x),
+ * evaluated in fp32 (log(1 + e^x) as log1p(exp(x))) and rounded to yg_dtype
+ * with round-to-nearest-even.
+ *   g       [T][H][D] contiguous, g_dtype (leading dimensions flattened into T)
+ *   A_log   [H] fp32
+ *   dt_bias [H*D] fp32 (the guide's [H, D] bias), or NULL for no bias
+ *   yg      [T][H][D] contiguous, yg_dtype; written, never read.  yg may be
+ *           the same buffer as g when the dtypes are equal (in place); any
+ *           other overlap is undefined.
+ * dtypes: GDN_F32, GDN_BF16 or GDN_F16, independently for g and yg.
+ * Alignment: g and yg to their element size, A_log and dt_bias to 4 bytes.
+ * Errors (checked before anything is enqueued): GDN_ERR_SHAPE for T < 0, H < 1,
+ * D < 1 or T*H*D beyond int64; GDN_ERR_DTYPE; GDN_ERR_NULL for g, A_log or yg
+ * NULL with T > 0; GDN_ERR_ALIGN; GDN_ERR_LAUNCH.  T = 0 enqueues nothing.
+ * Enqueued on `stream` (hipStream_t); returns without waiting.  The caller
+ * owns every buffer; nothing is allocated. */
+gdn_status_t gdn_kda_gate(const void *g, gdn_dtype_t g_dtype, const float *A_log,
+                          const float *dt_bias, void *yg, gdn_dtype_t yg_dtype, int64_t T,
+                          int32_t H, int32_t D, void *stream);
 
 /* Static description of a status code. */
 const char *gdn_status_string(gdn_status_t s);

@@ -162,3 +162,28 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_binding, "_LIB_PATH", "/nonexistent/libgdn.so")
     with pytest.raises(OSError):
         _binding.load_library()
+
+
+def test_kda_gate_validation():
+    """gdn_kda_gate rejects bad arguments before enqueuing anything."""
+    lib = gdn.load_library()
+    F32, BF16, F16 = gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_F16
+    g, A, b, y = (ctypes.c_void_p(0x10000 * i) for i in (1, 2, 3, 4))
+
+    def call(g=g, gt=BF16, A=A, b=b, y=y, yt=F32, T=8, H=4, D=64):
+        return lib.gdn_kda_gate(g, gt, A, b, y, yt, T, H, D, None)
+    assert call(T=-1) == ESHAPE
+    assert call(H=0) == ESHAPE
+    assert call(D=0) == ESHAPE
+    assert call(T=1 << 62, H=4, D=64) == ESHAPE            # T*H*D beyond int64
+    assert call(gt=7) == EDTYPE
+    assert call(yt=-1) == EDTYPE
+    assert call(g=None) == ENULL
+    assert call(A=None) == ENULL
+    assert call(y=None) == ENULL
+    assert call(g=ctypes.c_void_p(0x10001)) == EALIGN       # bf16 needs 2 bytes
+    assert call(y=ctypes.c_void_p(0x10002)) == EALIGN       # fp32 needs 4
+    assert call(b=ctypes.c_void_p(0x30002)) == EALIGN
+    # nothing to do: no pointer is needed and nothing is enqueued
+    assert call(g=None, A=None, b=None, y=None, T=0) == OK
+    assert F16 == 2
