@@ -33,9 +33,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pages_bf16")
-    ap.add_argument("--op", default="gdn_fwd", choices=["gdn_fwd", "kda_gate"],
+    ap.add_argument("--op", default="gdn_fwd", choices=["gdn_fwd", "kda_gate", "decode"],
                     help="gdn_fwd: the forward pass (headline); kda_gate: the KDA per-channel "
-                         "gate on the guide's timing shape")
+                         "gate on the guide's timing shape; decode: one recurrent step for a "
+                         "batch of sequences")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -92,7 +93,7 @@ def algorithmic(shape, esz, has_h0, used_slots):
 KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
                 ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
                 ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
-                ("gdn_kda_gate_scalar_kernel", "kda_gate"))
+                ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"))
 
 
 def counter_means(path):
@@ -207,32 +208,11 @@ def bench_kda(args):
     gd, Ad, bd = g.cuda(), A.cuda(), b.cuda()
     out = torch.empty_like(gd)
     # one launch takes a few microseconds, less than the host needs to issue one,
-    # so the timed region replays a HIP graph of PER back-to-back launches
-    PER = 20
-    cap = torch.cuda.Stream()
-    launch, _ = gdn.kda_gate_launcher(gd, Ad, bd, out=out, stream=cap)
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        for _ in range(3):
-            launch()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        for _ in range(PER):
-            launch()
-    stream = torch.cuda.current_stream()
-    reps = max(1, args.steps // PER)
-    for _ in range(max(1, args.warmup // PER)):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * PER)
+    # so the timed region replays a HIP graph of back-to-back launches
+    out.fill_(float("nan"))
+    ms, steps = graph_time(
+        lambda st: gdn.kda_gate_launcher(gd, Ad, bd, out=out, stream=st)[0], args.steps,
+        args.warmup)
     # the graph's result equals one eager call's (the gate is deterministic)
     ref_launch, ref = gdn.kda_gate_launcher(gd, Ad, bd)
     ref_launch()
@@ -245,7 +225,7 @@ def bench_kda(args):
     line = {
         "metric": "KDA gate elements/s (T=2048,H=16,D=128 bf16, bias)",
         "value": round(n / sec, 1), "unit": "elements/s", "n_gpus": 1,
-        "steps": reps * PER, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "kda_gate", "T": T, "H": H, "D": D, "bias": True,
@@ -279,6 +259,106 @@ def bench_kda(args):
     print(json.dumps(line), flush=True)
 
 
+def graph_time(make_launch, steps, warmup, per=20):
+    """Milliseconds per launch, from a HIP graph of `per` back-to-back launches
+    replayed between two events (for kernels shorter than one host launch).
+    make_launch(stream) returns a zero-argument callable that enqueues one
+    launch on `stream` (the capture stream)."""
+    import torch
+    cap = torch.cuda.Stream()
+    launch = make_launch(cap)
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for _ in range(3):
+            launch()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(per):
+            launch()
+    stream = torch.cuda.current_stream()
+    reps = max(1, steps // per)
+    for _ in range(max(1, warmup // per)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * per), reps * per
+
+
+# A batch-decode shape: 64 sequences, one new token each, with the pages' heads
+# (H = HV = 8, K = V = 128, bf16); the pages give no decode configuration.
+DECODE_SHAPE = dict(B=64, T=1, H=8, HV=8, K=128, V=128)
+
+
+def bench_decode(args):
+    """One JSON line for the recurrent step: tokens/s, HBM roofline (the state is
+    read and written once per call), and the fp64 oracle on the host."""
+    import numpy as np
+    import torch
+    import gated_deltanet_chunkwise_amd as gdn
+    from gated_deltanet_chunkwise_amd.inputs import make_inputs
+    c = DECODE_SHAPE
+    inp = make_inputs(dtype="bf16", seed=20280, h0=True, **c)
+    d = inp.to("cuda")
+    state = d.h0.clone()
+    out = torch.empty((c["B"], c["T"], c["HV"], c["V"]), dtype=d.q.dtype, device="cuda")
+    out.fill_(float("nan"))
+    ms, steps = graph_time(
+        lambda st: gdn.decode_launcher(d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, state,
+                                       dt_bias=d.dt_bias, out=out, stream=st)[0],
+        args.steps, args.warmup)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all() or torch.equal(state, d.h0):
+        raise RuntimeError("the timed decode launches did not run")
+    B, T, H, HV, K, V = (c[x] for x in ("B", "T", "H", "HV", "K", "V"))
+    nbytes = (2 * B * HV * K * V * 4 + 2 * B * T * H * K * 2 + 2 * B * T * HV * V * 2
+              + B * T * HV * 8 + HV * 8)
+    sec = ms / 1e3
+    line = {
+        "metric": "GDN decode tokens/s (B=64 sequences x 1 token, H=HV=8, K=V=128 bf16)",
+        "value": round(B * T / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict(c, workload="decode"),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(nbytes / sec / HBM_PEAK, 4), "kernel": "decode",
+                     "traffic": None},
+        "kernel_source_hash": source_hash(),
+    }
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            ent = json.load(fh).get("decode", {}).get("decode")
+        if ent and ent.get("source_hash") == line["kernel_source_hash"]:
+            line["roofline"]["traffic"] = ent["bytes_per_launch"]
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+        a = [f(inp.q), f(inp.k), f(inp.v), f(inp.g_raw), f(inp.beta), f(inp.A_log),
+             f(inp.dt_bias)]
+        h0 = f(inp.h0)
+        threads = oracle.default_threads()
+        oracle.load()
+        reps, total = 0, 0.0
+        while total < args.cpu_seconds:
+            t0 = time.perf_counter()
+            oracle.fwd(*a, h0=h0, nthreads=threads)
+            total += time.perf_counter() - t0
+            reps += 1
+        line["cpu_baseline"] = {"value": reps * B * T / total, "unit": "tokens/s",
+                                "cores": min(threads, B * HV), "kind": "oracle",
+                                "sample": "the whole shape (%d sequences x %d value heads), %d "
+                                          "run(s), %.1f s; threads=%d"
+                                          % (B, HV, reps, total, threads)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -294,6 +374,9 @@ def main():
         return
     if args.op == "kda_gate":
         bench_kda(args)
+        return
+    if args.op == "decode":
+        bench_decode(args)
         return
     import gated_deltanet_chunkwise_amd as gdn
     from gated_deltanet_chunkwise_amd.inputs import WORKLOADS, workload_inputs

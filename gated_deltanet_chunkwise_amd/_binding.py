@@ -15,7 +15,8 @@ GDN_BF16 = 1
 GDN_F16 = 2  # KDA gate only
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
-           "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_kda_gate", "gdn_status_string")
+           "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_decode", "gdn_kda_gate",
+           "gdn_status_string")
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
 # gdn_fwd_stages bits, one per entry of STAGES
@@ -74,6 +75,8 @@ def _declare(lib):
     lib.gdn_fwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp]
     lib.gdn_fwd_timed.restype = ctypes.c_int
     lib.gdn_fwd_timed.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, fp, ctypes.c_void_p]
+    lib.gdn_decode.restype = ctypes.c_int
+    lib.gdn_decode.argtypes = [P] + [vp] * 9 + [fp]
     lib.gdn_kda_gate.restype = ctypes.c_int
     lib.gdn_kda_gate.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_int32, fp]
@@ -222,6 +225,53 @@ def _any_dtype_code(dt):
     if dt not in codes:
         raise TypeError("dtype must be float32, bfloat16 or float16, got %s" % dt)
     return codes[dt]
+
+
+def decode_launcher(q, k, v, g_raw, beta, A_log, state, dt_bias=None, scale=1.0, out=None,
+                    stream=None):
+    """Check and marshal gdn_decode's arguments once; returns (launch, o), where
+    launch() enqueues the recurrent step over q's T tokens, updating `state` in
+    place.  q, k [B,T,H,K] and v [B,T,HV,V] in bf16 or fp32; g_raw, beta
+    [B,T,HV], A_log [HV], dt_bias [HV] or None, state [B,HV,K,V], all fp32."""
+    torch = _torch()
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    if g_raw.shape != (B, T, HV) or beta.shape != (B, T, HV) or state.shape != (B, HV, K, V):
+        raise ValueError("g_raw, beta must be [B,T,HV] and state [B,HV,K,V]")
+    for name, t in (("g_raw", g_raw), ("beta", beta), ("A_log", A_log), ("dt_bias", dt_bias),
+                    ("state", state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % name)
+    if out is None:
+        out = torch.empty((B, T, HV, V), dtype=q.dtype, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta),
+                    ("A_log", A_log), ("dt_bias", dt_bias), ("state", state), ("out", out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    params = make_params(B, T, H, HV, K, V, _dtype_code(q.dtype), 0, scale)
+    fn = load_library().gdn_decode
+    args = (ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log),
+            _ptr(dt_bias), _ptr(state), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+    keep = (params, q, k, v, g_raw, beta, A_log, dt_bias, state, out)
+
+    def launch():
+        keep  # the tensors stay alive as long as the callable
+        st = fn(*args)
+        if st:
+            raise GdnError(st, "gdn_decode")
+    return launch, out
+
+
+def decode(q, k, v, g_raw, beta, A_log, state, dt_bias=None, scale=1.0, out=None, stream=None):
+    """Recurrent GDN step(s) through gdn_decode: returns o [B,T,HV,V] and leaves the
+    state after the T tokens in `state` (updated in place)."""
+    launch, out = decode_launcher(q, k, v, g_raw, beta, A_log, state, dt_bias, scale, out, stream)
+    launch()
+    return out
 
 
 def kda_gate(g, A_log, dt_bias=None, output_dtype=None, out=None, stream=None):

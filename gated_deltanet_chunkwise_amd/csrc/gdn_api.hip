@@ -6,9 +6,11 @@
 #include <atomic>
 #include <cstdint>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "gdn.h"
+#include "gdn_decode.h"
 #include "gdn_kda.h"
 #include "gdn_kernels.h"
 
@@ -325,6 +327,49 @@ gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const 
                      void* stream) {
   return gdn_fwd_timed(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
                        final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status_t gdn_decode(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                        const float* g_raw, const float* beta, const float* A_log,
+                        const float* dt_bias, float* state, void* o, void* stream) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->num_seqs != 0) return GDN_ERR_SHAPE;
+  Plan pl;
+  gdn_status_t st = make_plan(p, false, &pl);
+  if (st != GDN_OK) return st;
+  if (!state) return GDN_ERR_NULL;
+  const bool tokens = (int64_t)p->B * p->T > 0;
+  if (tokens && (!q || !k || !v || !g_raw || !beta || !A_log || !o)) return GDN_ERR_NULL;
+  if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 16) ||
+      !aligned_to(g_raw, 4) || !aligned_to(beta, 4) || !aligned_to(A_log, 4) ||
+      !aligned_to(dt_bias, 4) || !aligned_to(state, 4))
+    return GDN_ERR_ALIGN;
+  if (!tokens) return GDN_OK;
+  const gdn::Geo& geo = pl.geo;
+  const dim3 grid((unsigned)((int64_t)p->B * p->HV * (p->V / 64)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  auto go = [&](auto kern, auto* tag) {
+    using E = std::remove_pointer_t<decltype(tag)>;
+    return launch(kern, grid, dim3(256), s, geo, static_cast<const E*>(q),
+                  static_cast<const E*>(k), static_cast<const E*>(v), g_raw, beta, A_log, dt_bias,
+                  state, static_cast<E*>(o));
+  };
+  const int kv = p->K * 1000 + p->V;
+  if (p->dtype == GDN_BF16) {
+    gdn::bf16* tag = nullptr;
+    e = kv == 128128 ? go(gdn::gdn_decode_kernel<gdn::bf16, 128, 128>, tag)
+      : kv == 128064 ? go(gdn::gdn_decode_kernel<gdn::bf16, 128, 64>, tag)
+      : kv == 64128  ? go(gdn::gdn_decode_kernel<gdn::bf16, 64, 128>, tag)
+                     : go(gdn::gdn_decode_kernel<gdn::bf16, 64, 64>, tag);
+  } else {
+    float* tag = nullptr;
+    e = kv == 128128 ? go(gdn::gdn_decode_kernel<float, 128, 128>, tag)
+      : kv == 128064 ? go(gdn::gdn_decode_kernel<float, 128, 64>, tag)
+      : kv == 64128  ? go(gdn::gdn_decode_kernel<float, 64, 128>, tag)
+                     : go(gdn::gdn_decode_kernel<float, 64, 64>, tag);
+  }
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 gdn_status_t gdn_kda_gate(const void* g, gdn_dtype_t g_dtype, const float* A_log,

@@ -179,6 +179,31 @@ gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
                             float *final_state, void *workspace, size_t workspace_bytes,
                             unsigned stage_mask, void *stream);
 
+/* ---- Recurrent step (decode) ---------------------------------------------------
+ * The state updated token by token, as the Ascend GDN blog describes the
+ * recurrence ("GDN sequence structure and Triton introduction": one state per
+ * head, updated as each token arrives).  For each of p->B sequences and each of
+ * its p->T new tokens, in order (T = 1: one decode step):
+ *     g = -exp(A_log[hv]) * softplus(g_raw + dt_bias[hv]),   a = e^g,
+ *     p = H^T k;   H <- a H + beta k (v - a p)^T;   o = scale * H^T q,
+ * with H = S^T the [K][V] fp32 state of each (sequence, value head), exactly
+ * the recurrence gdn_fwd computes chunkwise.
+ *   p        B, T, H, HV, K, V, dtype and scale as for gdn_fwd; num_seqs = 0
+ *            (fixed-length sequences only)
+ *   q, k     [B][T][H][K]; v [B][T][HV][V] (dtype); g_raw, beta [B][T][HV] fp32
+ *   A_log    [HV] fp32; dt_bias [HV] fp32 or NULL
+ *   state    [B][HV][K][V] fp32, required: read as the state before the tokens
+ *            and overwritten with the state after them (gdn_fwd's
+ *            initial_state / final_state layout, so a prefill's final state
+ *            continues here)
+ *   o        [B][T][HV][V] (dtype)
+ * Same sizes, dtypes, alignment and status codes as gdn_fwd (GDN_ERR_SHAPE for
+ * num_seqs != 0); no workspace.  B = 0 or T = 0 enqueues nothing.  Enqueued on
+ * `stream` (hipStream_t); returns without waiting. */
+gdn_status_t gdn_decode(const gdn_params_t *p, const void *q, const void *k, const void *v,
+                        const float *g_raw, const float *beta, const float *A_log,
+                        const float *dt_bias, float *state, void *o, void *stream);
+
 /* ---- KDA per-channel gate --------------------------------------------------
  * The KDA gate guide (MindSpeed-Ops issue page, "core computation logic"):
  *     yg[t,h,d] = -exp(A_log[h]) * softplus(g[t,h,d] + dt_bias[h*D + d]),

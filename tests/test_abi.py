@@ -187,3 +187,24 @@ def test_kda_gate_validation():
     # nothing to do: no pointer is needed and nothing is enqueued
     assert call(g=None, A=None, b=None, y=None, T=0) == OK
     assert F16 == 2
+
+
+def test_decode_validation():
+    """gdn_decode: gdn_fwd's size rules, fixed-length sequences only, a state is
+    required, and nothing is enqueued when there are no tokens."""
+    lib = gdn.load_library()
+    vp = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(9)]   # q k v g beta A dt state o
+
+    def call(p, ptrs=vp):
+        return lib.gdn_decode(ctypes.byref(p), *ptrs, None)
+    assert call(P(num_seqs=2, B=1)) == ESHAPE
+    assert call(P(K=96)) == EUNSUP
+    assert call(P(dtype=gdn.GDN_F16)) == EDTYPE
+    assert call(P(HV=6)) == ESHAPE
+    assert call(P(), vp[:7] + [None] + vp[8:]) == ENULL               # state
+    assert call(P(), [None] + vp[1:]) == ENULL                         # q
+    assert call(P(), vp[:3] + [ctypes.c_void_p(0x40002)] + vp[4:]) == EALIGN
+    # no tokens: only the state is needed, and nothing is launched
+    none = [None] * 7 + [vp[7], None]
+    assert call(P(T=0), none) == OK
+    assert call(P(B=0), none) == OK
