@@ -104,3 +104,69 @@ def fwd(q, k, v, g, beta, cu_seqlens=None, h0=None, chunk=64, scale=1.0,
             kept[(n, hv)] = steps
     o = o.reshape(B, T, HV, V)
     return (o, fin, kept) if keep else (o, fin)
+
+
+def chunk_transition(Kc, gc, bc):
+    """The chunk's state map H_next = M H + B, linear part only:
+    M = exp(G_last) I - (diag(exp(G_last - G)) K)^T w, from chunk_step's own
+    w and decayed keys (so M H equals chunk_step's H_next with V = 0)."""
+    K = Kc.shape[1]
+    _, _, inter = chunk_step(np.zeros_like(Kc), Kc, np.zeros((Kc.shape[0], 1)), gc, bc,
+                             np.zeros((K, 1)))
+    Gl = inter["G"][-1]
+    return np.exp(Gl) * np.eye(K) - inter["kdecay"].T @ inter["w"]
+
+
+def segment_scan(q, k, v, g, beta, cu_seqlens=None, h0=None, chunk=64, seg_chunks=4,
+                 scale=1.0):
+    """Two-level (segment-parallel) form of fwd, in fp64.
+
+    Each sequence's chunks are cut into segments of seg_chunks chunks.  The
+    chunk update is affine in the state, H_next = M_c H + B_c, so a segment
+    composes to H_end = M_s H_start + E_s with M_s the ordered product of its
+    chunks' M_c and E_s its end state from a zero start.  Level 1 forms
+    (M_s, E_s) for every segment independently; level 2 walks the segments of
+    a sequence in order, H_start(s+1) = M_s H_start(s) + E_s; level 3 reruns
+    each segment from its true start state for the outputs.  Same results as
+    fwd up to rounding.  Returns (o, fin)."""
+    q, k, v, g, beta = (np.asarray(x, np.float64) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    G = HV // H
+    qf, kf = q.reshape(B * T, H, K), k.reshape(B * T, H, K)
+    vf, gf, bf = v.reshape(B * T, HV, V), g.reshape(B * T, HV), beta.reshape(B * T, HV)
+    bounds = _seq_bounds(B, T, cu_seqlens)
+    o = np.zeros((B * T, HV, V))
+    fin = np.zeros((len(bounds), HV, K, V))
+    for n, (bos, eos) in enumerate(bounds):
+        starts = list(range(bos, eos, chunk))
+        segs = [starts[i:i + seg_chunks] for i in range(0, len(starts), seg_chunks)]
+        for hv in range(HV):
+            h = hv // G
+            # level 1: per segment, from a zero state and as a linear map
+            ME = []
+            for seg in segs:
+                M, E = np.eye(K), np.zeros((K, V))
+                for s in seg:
+                    e = min(s + chunk, eos)
+                    Mc = chunk_transition(kf[s:e, h], gf[s:e, hv], bf[s:e, hv])
+                    _, E, _ = chunk_step(qf[s:e, h], kf[s:e, h], vf[s:e, hv], gf[s:e, hv],
+                                         bf[s:e, hv], E, scale)
+                    M = Mc @ M
+                ME.append((M, E))
+            # level 2: start states in order
+            Hs = np.zeros((K, V)) if h0 is None else np.array(h0[n, hv], np.float64)
+            starts_state = []
+            for M, E in ME:
+                starts_state.append(Hs)
+                Hs = M @ Hs + E
+            fin[n, hv] = Hs
+            # level 3: outputs from the true start states
+            for seg, Hstart in zip(segs, starts_state):
+                Hc = Hstart
+                for s in seg:
+                    e = min(s + chunk, eos)
+                    o_c, Hc, _ = chunk_step(qf[s:e, h], kf[s:e, h], vf[s:e, hv], gf[s:e, hv],
+                                            bf[s:e, hv], Hc, scale)
+                    o[s:e, hv] = o_c
+    return o.reshape(B, T, HV, V), fin

@@ -348,5 +348,38 @@ def pin_full_forward(lib):
     _close(o3, o1, 1e-15, "dt_bias None")
 
 
+def pin_segment_scan(lib):
+    """The two-level form equals the flat chunkwise form (and so the token
+    oracle), for several segment lengths, packed ragged sequences and h0; and a
+    chunk's linear map M_c is the chunk step run with V = 0."""
+    rng = np.random.default_rng(19)
+    B, T, H, HV, K, V = 1, 300, 1, 2, 8, 5
+    lengths = [130, 0, 65, 105]
+    cu = np.cumsum([0] + lengths)
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, HV, V))
+    g = -rng.uniform(0.0, 0.3, (B, T, HV))
+    beta = rng.uniform(0.2, 1.0, (B, T, HV))
+    h0 = rng.standard_normal((len(lengths), HV, K, V))
+    o_ref, f_ref = chunkwise.fwd(q, k, v, g, beta, cu_seqlens=cu, h0=h0, chunk=16, scale=0.5)
+    for L in (1, 2, 3, 100):
+        o_s, f_s = chunkwise.segment_scan(q, k, v, g, beta, cu_seqlens=cu, h0=h0, chunk=16,
+                                          seg_chunks=L, scale=0.5)
+        _close(o_s, o_ref, 1e-11, "segment scan o (L=%d)" % L)
+        _close(f_s, f_ref, 1e-11, "segment scan final (L=%d)" % L)
+    # the linear part: chunk_step with zero values from X equals M_c X
+    Kc, gc, bc = k[0, :16, 0], g[0, :16, 1], beta[0, :16, 1]
+    X = rng.standard_normal((K, 3))
+    _, HX, _ = chunkwise.chunk_step(np.zeros_like(Kc), Kc, np.zeros((16, 3)), gc, bc, X)
+    _close(chunkwise.chunk_transition(Kc, gc, bc) @ X, HX, 1e-13, "chunk transition")
+    # and M_c is the product of the per-token maps e^g (I - b k k^T) (transposed form)
+    M = np.eye(K)
+    for t in range(16):
+        M = (math.exp(gc[t]) * (np.eye(K) - bc[t] * np.outer(Kc[t], Kc[t]))) @ M
+    _close(chunkwise.chunk_transition(Kc, gc, bc), M, 1e-13, "transition = token product")
+
+
 ALL_PINS = [pin_gate, pin_kda_gate, pin_brute_force, pin_transition_product, pin_identities,
-            pin_chunkwise, pin_invariants, pin_full_forward]
+            pin_chunkwise, pin_invariants, pin_full_forward, pin_segment_scan]
