@@ -38,6 +38,8 @@ def parse():
                          "gate on the guide's timing shape; decode: one recurrent step for a "
                          "batch of sequences")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seg-chunks", type=int, default=0,
+                    help="segment-parallel state pass with segments of this many chunks (0: off)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -388,7 +390,8 @@ def main():
     s = inp.shape
     packed = inp.cu_seqlens is not None
     plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], inp.q.dtype, "cuda",
-                          num_seqs=s["N"] if packed else None, scale=inp.scale)
+                          num_seqs=s["N"] if packed else None, scale=inp.scale,
+                          seg_chunks=args.seg_chunks)
     stream = torch.cuda.current_stream()
 
     step = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias,
@@ -501,7 +504,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl, "B": s["B"], "T": s["T"], "H": s["H"], "HV": s["HV"],
                    "K": s["K"], "V": s["V"], "chunk": CHUNK, "packed_seqs": s["N"] if packed
-                   else None, "initial_state": inp.h0 is not None},
+                   else None, "initial_state": inp.h0 is not None,
+                   "seg_chunks": args.seg_chunks},
         "roofline": roof,
         "path_roofline": {"bytes": path["bytes"], "flops": path["flops"],
                           "hbm_frac": round(path["bytes"] / sec / HBM_PEAK, 4),

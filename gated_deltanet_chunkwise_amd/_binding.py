@@ -29,14 +29,16 @@ class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("seg_chunks", ctypes.c_int32)]
 
 
 class WorkspaceLayout(ctypes.Structure):
     """gdn_workspace_layout_t."""
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gamma", "beta", "w", "kt", "u", "hc", "vn", "chunk_map", "seq_slot", "total")] + [
-                    ("num_slots", ctypes.c_int32), ("num_seqs", ctypes.c_int32)]
+                ("gamma", "beta", "w", "kt", "u", "hc", "vn", "chunk_map", "seq_slot",
+                 "seg_slot", "seq_seg", "seg_e", "seg_m", "seg_h", "total")] + [
+                    ("num_slots", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                    ("num_segs", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -91,9 +93,9 @@ def status_string(status):
     return load_library().gdn_status_string(int(status)).decode()
 
 
-def make_params(B, T, H, HV, K, V, dtype, num_seqs=0, scale=1.0):
+def make_params(B, T, H, HV, K, V, dtype, num_seqs=0, scale=1.0, seg_chunks=0):
     return Params(int(B), int(T), int(H), int(HV), int(K), int(V), int(num_seqs), int(dtype),
-                  float(scale))
+                  float(scale), int(seg_chunks))
 
 
 def workspace_size(params, packed=False):
@@ -145,12 +147,12 @@ class GdnForward:
     """
 
     def __init__(self, B, T, H, HV, K, V, dtype, device, num_seqs=None, scale=1.0,
-                 final_state=True):
+                 final_state=True, seg_chunks=0):
         torch = _torch()
         self.packed = num_seqs is not None
         self.N = num_seqs if self.packed else B
         self.params = make_params(B, T, H, HV, K, V, _dtype_code(dtype),
-                                  num_seqs if self.packed else 0, scale)
+                                  num_seqs if self.packed else 0, scale, seg_chunks)
         self.lib = load_library()
         self.layout = workspace_layout(self.params, self.packed)  # raises on bad sizes
         self.ws_bytes = int(self.layout.total)

@@ -23,7 +23,8 @@ struct Plan {
   gdn::Geo geo;
   gdn_workspace_layout_t lay;
   bool varlen;
-  int64_t ntok;  // tokens in q/k/v/o
+  int64_t ntok;    // tokens in q/k/v/o
+  int seg_chunks;  // chunks per segment of the segment-parallel state pass (0: off)
 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -52,6 +53,7 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   if (p->HV % p->H) return GDN_ERR_SHAPE;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDN_ERR_UNSUPPORTED;
   if (varlen && (p->B != 1 || p->num_seqs < 0)) return GDN_ERR_SHAPE;
+  if (p->seg_chunks < 0) return GDN_ERR_SHAPE;
   const int64_t N = varlen ? p->num_seqs : p->B;
   const int64_t NT = ((int64_t)p->T + gdn::kChunk - 1) / gdn::kChunk;
   const int64_t slots = varlen ? (int64_t)p->T / gdn::kChunk + N : (int64_t)p->B * NT;
@@ -64,6 +66,7 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   Plan pl{};
   pl.varlen = varlen;
   pl.ntok = ntok;
+  pl.seg_chunks = p->seg_chunks;
   gdn::Geo& g = pl.geo;
   g.B = p->B; g.T = p->T; g.H = p->H; g.HV = p->HV; g.K = p->K; g.V = p->V;
   g.N = (int)N; g.G = p->HV / p->H; g.NT = (int)NT; g.slots = (int)slots; g.scale = p->scale;
@@ -81,9 +84,22 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   L.vn = off;    off = align_up(off + hsl * gdn::kChunk * p->V * esz);
   L.chunk_map = off; off = align_up(off + (varlen ? (size_t)slots * 16 : 0));
   L.seq_slot = off;  off = align_up(off + (varlen ? (size_t)(N + 1) * 4 : 0));
+  // segments: at most ceil(c_n / L) per sequence, summing to <= slots / L + N
+  int64_t nseg = 0;
+  if (p->seg_chunks > 0) {
+    nseg = varlen ? slots / p->seg_chunks + N : N * ((NT + p->seg_chunks - 1) / p->seg_chunks);
+    if (nseg * p->HV * (p->V / 16) > INT32_MAX || nseg + 1 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    const size_t per = (size_t)nseg * p->HV * p->K;
+    L.seg_slot = off; off = align_up(off + (size_t)(nseg + 1) * 4);
+    L.seq_seg = off;  off = align_up(off + (size_t)(N + 1) * 4);
+    L.seg_e = off;    off = align_up(off + per * p->V * 4);
+    L.seg_m = off;    off = align_up(off + per * p->K * 4);
+    L.seg_h = off;    off = align_up(off + per * p->V * 4);
+  }
   L.total = off;
   L.num_slots = (int32_t)slots;
   L.num_seqs = (int32_t)N;
+  L.num_segs = (int32_t)nseg;
   *out = pl;
   return GDN_OK;
 }
@@ -118,6 +134,35 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, 
         return hipLaunchKernel((const void*)kern, grid, block, argv, 0, s);
       },
       t);
+}
+
+// The state pass in one mode, over geo.N pseudo-sequences whose slot ranges
+// are seq_slot[n] .. seq_slot[n+1]-1 (VARLEN) or n*NT .. (n+1)*NT-1.  The
+// LDS-ring variant when its workgroups fit one per CU: one compute wave (16
+// columns) per workgroup when the units fit, two sharing the ring otherwise;
+// beyond that many units share a CU and the register-buffered variant is used
+// (also for fp32 at K = 128, whose pipelined operands do not fit the ring
+// variant's registers).
+template <typename E, int K, int V, bool VARLEN, int MODE>
+hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* wf,
+                        const gdn::Frag<E>* ktf, const gdn::Quad<E>* uf, const float* gam,
+                        const int* seq_slot, const float* h0, float* fin, gdn::Frag<E>* hcf,
+                        gdn::Frag<E>* vnf) {
+  const int units = geo.N * geo.HV * (V / 16);
+  if (units == 0) return hipSuccess;
+  const int cus = device_cus();
+  if constexpr (gdn::RingCfg<E, K, V, 1>::FITS) {
+    if (units <= cus)
+      return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1, MODE>, dim3(units),
+                    dim3(64 * gdn::RingCfg<E, K, V, 1>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
+                    h0, fin, hcf, vnf);
+    if (units <= 2 * cus)
+      return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 2, MODE>, dim3(units / 2),
+                    dim3(64 * gdn::RingCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
+                    h0, fin, hcf, vnf);
+  }
+  return launch(gdn::gdn_chain_kernel<E, K, V, VARLEN, MODE>, dim3(units), dim3(64), s, geo, wf,
+                ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
 }
 
 template <typename E, int K, int V, bool VARLEN>
@@ -162,29 +207,30 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf));
   mark(2);
   if (work && (mask & GDN_STAGE_STATE)) {
-    // LDS-ring variant when its workgroups fit one per CU: one compute wave
-    // (16 columns) per workgroup when the units fit, two sharing the ring
-    // otherwise; beyond that many units share a CU and the register-buffered
-    // variant is used (also for fp32 at K = 128, whose pipelined operands do
-    // not fit the ring variant's registers).
-    const int units = geo.N * geo.HV * (V / 16);
-    const int cus = device_cus();
-    bool done = false;
-    if constexpr (gdn::RingCfg<E, K, V, 1>::FITS) {
-      if (units <= cus) {
-        ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1>, dim3(units),
-                  dim3(64 * gdn::RingCfg<E, K, V, 1>::WAVES), s, geo,
-                  wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
-        done = true;
-      } else if (units <= 2 * cus) {
-        ok(launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 2>, dim3(units / 2),
-                  dim3(64 * gdn::RingCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf));
-        done = true;
-      }
+    if (L.num_segs > 0) {
+      // segment-parallel: E_s and M_s per segment, start states in order, then
+      // the full pass per segment from its start state
+      int* seg_slot = reinterpret_cast<int*>(w + L.seg_slot);
+      int* seq_seg = reinterpret_cast<int*>(w + L.seq_seg);
+      float* seg_e = reinterpret_cast<float*>(w + L.seg_e);
+      float* seg_m = reinterpret_cast<float*>(w + L.seg_m);
+      float* seg_h = reinterpret_cast<float*>(w + L.seg_h);
+      ok(launch(gdn::gdn_segment_map_kernel<VARLEN>, dim3(1), dim3(256), s, seq_slot, geo.N,
+                geo.NT, pl.seg_chunks, L.num_segs, seg_slot, seq_seg));
+      gdn::Geo gs = geo;
+      gs.N = L.num_segs;
+      ok(launch_chain<E, K, V, true, gdn::CHAIN_END>(gs, s, wf, ktf, uf, gam, seg_slot, nullptr,
+                                                     seg_e, hcf, vnf));
+      ok(launch_chain<E, K, K, true, gdn::CHAIN_MAP>(gs, s, wf, ktf, uf, gam, seg_slot, nullptr,
+                                                     seg_m, hcf, vnf));
+      ok(launch(gdn::gdn_segment_combine_kernel<E, K, V>, dim3(geo.N * geo.HV * (V / 16)),
+                dim3(64), s, geo, seq_seg, seg_m, seg_e, h0, fin, seg_h));
+      ok(launch_chain<E, K, V, true, gdn::CHAIN_FULL>(gs, s, wf, ktf, uf, gam, seg_slot, seg_h,
+                                                      nullptr, hcf, vnf));
+    } else {
+      ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_FULL>(geo, s, wf, ktf, uf, gam, seq_slot, h0,
+                                                        fin, hcf, vnf));
     }
-    if (!done)
-      ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo, wf, ktf,
-                uf, gam, seq_slot, h0, fin, hcf, vnf));
   }
   mark(3);
   if (work && geo.slots > 0 && (mask & GDN_STAGE_OUTPUT))

@@ -439,7 +439,13 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 // Outputs (fragment-major, dtype E):
 //   hcf [hv][slot][vt][kb<K/32][lane]  A operand of H_c^T q^T (rows v, k over K)
 //   vnf [hv][slot][vt][cb<2][lane]     A operand of v_new^T P^T (rows v, k over c)
-template <typename E, int K, int V>
+// State-pass modes.  CHAIN_FULL: the pass as described, storing H_c and v_new.
+// CHAIN_END: the same arithmetic without those stores (only the end state is
+// kept).  CHAIN_MAP: u taken as 0 and no stores; started from the identity
+// (with V = K), the end state is the chunks' composed linear map M.
+enum { CHAIN_FULL = 0, CHAIN_END = 1, CHAIN_MAP = 2 };
+
+template <typename E, int K, int V, int MODE = CHAIN_FULL>
 struct ChainStep {
   static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
   Frag<E> w[4][KB];
@@ -464,8 +470,13 @@ struct ChainStep {
     for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) kt[mt][cb] = ktf[((hs * KT + mt) * 2 + cb) * 64 + lane];
+    if constexpr (MODE == CHAIN_MAP) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) u[ct] = uf[(((hs * NV + vt) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
+      for (int ct = 0; ct < 4; ++ct) u[ct] = make_quad<E>(f32x4{0.f, 0.f, 0.f, 0.f});
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) u[ct] = uf[(((hs * NV + vt) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
+    }
   }
 
   // First half of a chunk: emits H_c (the state on entry) and v_new = u - w H_c
@@ -495,14 +506,19 @@ struct ChainStep {
     }
   }
 
-  // vnew with H_c and v_new stored straight to their fragment-major arrays.
+  // vnew with H_c and v_new stored straight to their fragment-major arrays
+  // (CHAIN_FULL), or not stored at all (the other modes).
   __device__ __forceinline__ void vnew_global(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2],
                                               Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf,
                                               size_t hs, int vt, int lane) const {
-    Frag<E>* hc = hcf + (hs * NV + vt) * KB * 64 + lane;
-    Frag<E>* vn = vnf + (hs * NV + vt) * 2 * 64 + lane;
-    vnew(Hs, vb, [&](int kb, const Frag<E>& f) { hc[kb * 64] = f; },
-         [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; });
+    if constexpr (MODE == CHAIN_FULL) {
+      Frag<E>* hc = hcf + (hs * NV + vt) * KB * 64 + lane;
+      Frag<E>* vn = vnf + (hs * NV + vt) * 2 * 64 + lane;
+      vnew(Hs, vb, [&](int kb, const Frag<E>& f) { hc[kb * 64] = f; },
+           [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; });
+    } else {
+      vnew(Hs, vb, [](int, const Frag<E>&) {}, [](int, const Frag<E>&) {});
+    }
   }
 
   // Second half: H += kd^T v_new, on a state already multiplied by e^{G_last}.
@@ -543,7 +559,23 @@ __device__ __forceinline__ void load_state(f32x4 (&Hs)[K / 16], const float* __r
   }
 }
 
-template <typename E, int K, int V, bool VARLEN>
+// Initial state tiles (rows 16*mt + 4g + r, column v): the identity for
+// CHAIN_MAP (V = K), else from h0, or zero.
+template <int K, int V, int MODE>
+__device__ __forceinline__ void init_state(f32x4 (&Hs)[K / 16], const float* __restrict__ h0,
+                                           size_t sbase, int v, int g) {
+  if constexpr (MODE == CHAIN_MAP) {
+    static_assert(K == V, "the map is K x K");
+#pragma unroll
+    for (int mt = 0; mt < K / 16; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Hs[mt][r] = (16 * mt + 4 * g + r == v) ? 1.f : 0.f;
+  } else {
+    load_state<K, V>(Hs, h0, sbase, v, g);
+  }
+}
+
+template <typename E, int K, int V, bool VARLEN, int MODE = CHAIN_FULL>
 __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* __restrict__ wf,
                                                        const Frag<E>* __restrict__ ktf,
                                                        const Quad<E>* __restrict__ uf,
@@ -553,7 +585,7 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
                                                        float* __restrict__ fin,
                                                        Frag<E>* __restrict__ hcf,
                                                        Frag<E>* __restrict__ vnf) {
-  using Step = ChainStep<E, K, V>;
+  using Step = ChainStep<E, K, V, MODE>;
   constexpr int NV = V / 16, KT = K / 16;
   // Two register buffers when a step's operands fit in ~150 VGPRs.
   constexpr bool kDouble = sizeof(Step) <= 600;
@@ -574,7 +606,7 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
   const size_t hbase = (size_t)hv * geo.slots;
 
   f32x4 Hs[KT];
-  load_state<K, V>(Hs, h0, sbase, v, g);
+  init_state<K, V, MODE>(Hs, h0, sbase, v, g);
 
   if constexpr (kDouble) {
     // The next chunk's loads are issued unconditionally (the last chunk reloads
@@ -639,14 +671,14 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
 // B_{-1} (before the loop) certifies chunk 0.  The barrier is s_barrier
 // between compiler-level memory fences; the explicit waits named above are
 // the only ones it relies on.
-template <typename E, int K, int V, int NC_>
+template <typename E, int K, int V, int NC_, bool HAS_U = true>
 struct RingCfg {
   static constexpr int FB = (int)sizeof(Frag<E>);      // bytes per lane per fragment
   static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
   static constexpr int NC = NC_;                       // compute waves (16-column tiles)
   static constexpr int WAVES = NC + 2;                 // compute waves, then two loaders
   static constexpr int FU = 4 * KB + 2 * KT;           // first u-pair fragment
-  static constexpr int NFRAG = FU + 2 * NC;            // w, kd^T, u-pair fragments per chunk
+  static constexpr int NFRAG = FU + (HAS_U ? 2 * NC : 0);  // w, kd^T, u-pair fragments per chunk
   static constexpr int SUB = FB / 16;                  // 1 KB blocks per fragment
   static constexpr int GOFF = NFRAG * 64 * FB;         // gate row (256 bytes) after the fragments
   static constexpr int STEP = GOFF + 256;              // bytes per ring stage
@@ -725,14 +757,14 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-template <typename E, int K, int V, bool VARLEN, int NC>
+template <typename E, int K, int V, bool VARLEN, int NC, int MODE = CHAIN_FULL>
 __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_ring_kernel(
     Geo geo, const Frag<E>* __restrict__ wf, const Frag<E>* __restrict__ ktf,
     const Quad<E>* __restrict__ uf, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const float* __restrict__ h0, float* __restrict__ fin,
     Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf) {
-  using R = RingCfg<E, K, V, NC>;
-  using Step = ChainStep<E, K, V>;
+  using R = RingCfg<E, K, V, NC, MODE != CHAIN_MAP>;
+  using Step = ChainStep<E, K, V, MODE>;
   constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D;
   __shared__ __align__(16) char ring[R::LDS];
   int hv, rest;
@@ -757,7 +789,7 @@ __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_
     const int g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
     const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
     f32x4 Hs[KT];
-    load_state<K, V>(Hs, h0, sbase, v, g);
+    init_state<K, V, MODE>(Hs, h0, sbase, v, g);
     Step st;
     auto read_w = [&](const char* stage) {
 #pragma unroll
@@ -771,10 +803,15 @@ __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_
       const char* stage = ring + (i % D) * R::STEP;
       // the chunk's last cumulative gate value, read by every lane (broadcast)
       const float glast = reinterpret_cast<const float*>(stage + R::GOFF)[kChunk - 1];
+      if constexpr (MODE == CHAIN_MAP) {
 #pragma unroll
-      for (int cp = 0; cp < 2; ++cp)
-        split_pair(ring_frag(stage, R::FU + 2 * wave + cp, lane, (E*)nullptr), st.u[2 * cp],
-                   st.u[2 * cp + 1]);
+        for (int ct = 0; ct < 4; ++ct) st.u[ct] = make_quad<E>(f32x4{0.f, 0.f, 0.f, 0.f});
+      } else {
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp)
+          split_pair(ring_frag(stage, R::FU + 2 * wave + cp, lane, (E*)nullptr), st.u[2 * cp],
+                     st.u[2 * cp + 1]);
+      }
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
@@ -850,6 +887,122 @@ __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_
       ring_barrier();  // B_i
       if (i + D < nsteps) issue(i + D);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segment table for the segment-parallel state pass.  Sequence n's chunks
+// (slots s0 .. s1-1: seq_slot for packed input, n*NT .. (n+1)*NT-1 otherwise)
+// are cut into ceil((s1 - s0) / L) segments of L chunks, numbered in sequence
+// order.  seg_slot[j] = first slot of segment j; entries from the number of
+// segments used up to nseg_max hold the end of the last sequence, so every
+// segment j covers seg_slot[j] .. seg_slot[j+1]-1 (empty for unused j).
+// seq_seg[n] = first segment of sequence n, seq_seg[N] = segments used.
+// One workgroup (prefix sums over the sequences, 256 at a time).
+template <bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_segment_map_kernel(const int* __restrict__ seq_slot,
+                                                              int N, int NT, int L, int nseg_max,
+                                                              int* __restrict__ seg_slot,
+                                                              int* __restrict__ seq_seg) {
+  __shared__ int ssum[256];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 256) {
+    const int n = base + tid;
+    int s0 = 0, s1 = 0;
+    if (n < N) {
+      s0 = VARLEN ? seq_slot[n] : n * NT;
+      s1 = VARLEN ? seq_slot[n + 1] : (n + 1) * NT;
+    }
+    const int ns = (s1 - s0 + L - 1) / L;
+    ssum[tid] = ns;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int y = tid >= off ? ssum[tid - off] : 0;
+      __syncthreads();
+      ssum[tid] += y;
+      __syncthreads();
+    }
+    const int j0 = carry + ssum[tid] - ns;
+    if (n < N) {
+      seq_seg[n] = min(j0, nseg_max);
+      for (int c = 0; c < ns; ++c)
+        if (j0 + c < nseg_max) seg_slot[j0 + c] = s0 + c * L;
+    }
+    __syncthreads();
+    if (tid == 255) carry += ssum[255];
+    __syncthreads();
+  }
+  const int used = min(carry, nseg_max);
+  const int end = N > 0 ? (VARLEN ? seq_slot[N] : N * NT) : 0;
+  if (tid == 0) seq_seg[N] = used;
+  for (int j = used + tid; j <= nseg_max; j += 256) seg_slot[j] = end;
+}
+
+// Level 2 of the segment-parallel state pass.  One wave per (sequence, value
+// head, 16 value columns) walks its sequence's segments in order:
+//     seg_h[s] = H;   H <- M_s H + E_s,
+// starting from h0 (or zero); the last H is the final state.  M_s H runs on
+// the MFMA with operands in E: M_s's rows as A fragments (converted from
+// fp32), H's columns as B fragments, accumulating onto E_s's tile in fp32.
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_from_f32_row(const float* row);
+template <>
+__device__ __forceinline__ Frag<bf16> frag_from_f32_row<bf16>(const float* row) {
+  const int g = lane_id() >> 4;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * g);
+  return frag_from_tiles<bf16>(a, b);
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_from_f32_row<float>(const float* row) {
+  return frag_from_row(row);
+}
+
+template <typename E, int K, int V>
+__global__ __launch_bounds__(64) void gdn_segment_combine_kernel(Geo geo,
+                                                                 const int* __restrict__ seq_seg,
+                                                                 const float* __restrict__ seg_m,
+                                                                 const float* __restrict__ seg_e,
+                                                                 const float* __restrict__ h0,
+                                                                 float* __restrict__ fin,
+                                                                 float* __restrict__ seg_h) {
+  constexpr int NV = V / 16, KB = K / 32, KT = K / 16;
+  const int b = blockIdx.x;
+  const int vt = b % NV, hv = (b / NV) % geo.HV, n = b / (NV * geo.HV);
+  const int lane = lane_id(), g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
+  f32x4 Hs[KT];
+  load_state<K, V>(Hs, h0, ((size_t)n * geo.HV + hv) * K * V, v, g);
+  const int j0 = seq_seg[n], j1 = seq_seg[n + 1];
+  for (int j = j0; j < j1; ++j) {
+    const size_t sb = ((size_t)j * geo.HV + hv) * K * V;
+    const float* M = seg_m + ((size_t)j * geo.HV + hv) * K * K;
+    Frag<E> hb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[kb] = frag_from_tiles<E>(Hs[2 * kb], Hs[2 * kb + 1]);
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t at = sb + (size_t)(16 * mt + 4 * g + r) * V + v;
+        seg_h[at] = Hs[mt][r];
+        acc[r] = seg_e[at];
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma_k32(acc, frag_from_f32_row<E>(M + (size_t)(16 * mt + lc) * K + 32 * kb), hb[kb]);
+      Hs[mt] = acc;
+    }
+  }
+  if (fin) {
+    const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
   }
 }
 

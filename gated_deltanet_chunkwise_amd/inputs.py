@@ -31,6 +31,9 @@ WORKLOADS = {
                         num_seqs=12, len_range=(64, 6000)),
     # one long sequence, 16 q/k heads each shared by 2 of 32 value heads
     "long_gqa_bf16": dict(B=1, T=65536, H=16, HV=32, K=128, V=128, dtype="bf16"),
+    # one long sequence with few heads: 32 (sequence, head, 16-column) units, so
+    # the plain state pass leaves most CUs idle (the segment-parallel case)
+    "long_single_bf16": dict(B=1, T=65536, H=4, HV=4, K=128, V=128, dtype="bf16"),
 }
 # Seeds per workload (20260 + index in the order above).
 SEEDS = {name: 20260 + i for i, name in enumerate(WORKLOADS)}

@@ -28,6 +28,25 @@
  * inter-chunk state pass, and the chunk output.  A fourth kernel builds the
  * chunk map when cu_seqlens is given.
  *
+ * Segment-parallel state pass (seg_chunks > 0).  The chunk update is affine in
+ * the state, H_next = M_c H + B_c (M_c = e^{G_last} I - kd^T w), so a run of
+ * L = seg_chunks chunks composes to H_end = M_s H_start + E_s.  With segments,
+ * the state pass runs in three levels:
+ *   1. for every segment of every sequence, in parallel, E_s (its end state
+ *      from a zero start) and M_s (its K x K linear map, the same pass run
+ *      with u = 0 from the identity);
+ *   2. per sequence, in segment order, H_start(s+1) = M_s H_start(s) + E_s,
+ *      from the initial state; the last one is the final state;
+ *   3. every segment again from its true start state, writing the chunk
+ *      states the output kernel reads.
+ * It does about three times the state-pass work, in sequential runs L chunks
+ * long instead of a whole sequence: worth it only when a few long sequences
+ * leave most CUs idle.  Measured on MI355X at B=1, T=65536, HV=4 (32 units of
+ * 16 value columns): L = 64 takes the state pass from 726 to 438 us.  At 256
+ * units (T=65536, HV=32) and at B=2, T=2048, HV=8 it is slower than the plain
+ * pass.  Same results as the plain pass up to rounding; M_s H is evaluated
+ * with operands in the call's dtype (bf16 for bf16 calls).
+ *
  * Layouts (all contiguous, row-major, device memory):
  *   q, k           [B][T][H][K]   dtype (GDN_BF16 or GDN_F32)
  *   v              [B][T][HV][V]  dtype
@@ -73,7 +92,7 @@ extern "C" {
 typedef enum {
   GDN_OK = 0,
   GDN_ERR_NULL = 1,        /* a required pointer is NULL */
-  GDN_ERR_SHAPE = 2,       /* negative size, HV % H != 0, cu_seqlens with B != 1, ... */
+  GDN_ERR_SHAPE = 2,       /* negative size, HV % H != 0, cu_seqlens with B != 1, seg_chunks < 0, ... */
   GDN_ERR_DTYPE = 3,       /* dtype not supported by the entry point */
   GDN_ERR_UNSUPPORTED = 4, /* K or V not in {64, 128}, or a size beyond the int32 index range */
   GDN_ERR_ALIGN = 5,       /* a pointer is not aligned as required below */
@@ -94,6 +113,7 @@ typedef struct {
   int32_t num_seqs; /* N with cu_seqlens; ignored (N = B) without */
   int32_t dtype;    /* gdn_dtype_t of q, k, v and o */
   float scale;      /* multiplies every o_t; 1.0 gives o_t = S_t q_t */
+  int32_t seg_chunks; /* 0: plain state pass; L > 0: segments of L chunks (see above) */
 } gdn_params_t;
 
 /* Byte offsets of the intermediates inside the workspace, for inspection.
@@ -104,11 +124,19 @@ typedef struct {
  *   beta  [HV][num_slots][64] fp32  beta in the same layout (0 past a chunk's end)
  *   w, kt, u, hc, vn                 MFMA-fragment-ordered dtype tensors (see
  *                                    the kernel sources for the lane order)
- *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32 (cu_seqlens only) */
+ *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32 (cu_seqlens only)
+ * With seg_chunks > 0 (num_segs = an upper bound on the segment count):
+ *   seg_slot [num_segs+1] int32    first slot of each segment, sequence order
+ *   seq_seg  [N+1] int32           first segment of each sequence
+ *   seg_e, seg_h [num_segs][HV][K][V] fp32   E_s, and the start states
+ *   seg_m    [num_segs][HV][K][K] fp32        M_s
+ * (their offsets are 0 and num_segs is 0 without segments). */
 typedef struct {
-  size_t gamma, beta, w, kt, u, hc, vn, chunk_map, seq_slot, total;
+  size_t gamma, beta, w, kt, u, hc, vn, chunk_map, seq_slot;
+  size_t seg_slot, seq_seg, seg_e, seg_m, seg_h, total;
   int32_t num_slots;
   int32_t num_seqs;
+  int32_t num_segs;
 } gdn_workspace_layout_t;
 
 /* Workspace bytes gdn_fwd needs for these parameters (0 if they are invalid).

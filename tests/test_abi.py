@@ -208,3 +208,22 @@ def test_decode_validation():
     none = [None] * 7 + [vp[7], None]
     assert call(P(T=0), none) == OK
     assert call(P(B=0), none) == OK
+
+
+def test_segment_layout():
+    """seg_chunks > 0 adds the segment tables and buffers; negative is an error."""
+    p0 = P(B=2, T=700, H=2, HV=4, K=128, V=64)
+    p2 = P(B=2, T=700, H=2, HV=4, K=128, V=64, seg_chunks=3)
+    l0, l2 = gdn.workspace_layout(p0), gdn.workspace_layout(p2)
+    assert l0.num_segs == 0 and l0.seg_m == 0
+    assert l2.num_segs == 2 * 4                      # 11 chunks per sequence -> 4 segments
+    per = l2.num_segs * 4 * 128
+    assert l2.seg_e - l2.seq_seg >= (2 + 1) * 4
+    assert l2.seg_m - l2.seg_e >= per * 64 * 4
+    assert l2.seg_h - l2.seg_m >= per * 128 * 4
+    assert l2.total - l2.seg_h >= per * 64 * 4
+    assert gdn.workspace_size(p2) == l2.total > gdn.workspace_size(p0)
+    # packed: an upper bound of slots / L + N segments
+    lp = gdn.workspace_layout(P(B=1, T=1000, num_seqs=3, seg_chunks=2), packed=True)
+    assert lp.num_segs == (1000 // 64 + 3) // 2 + 3
+    assert gdn.check(P(seg_chunks=-1), ptrs(), 1 << 40) == ESHAPE
