@@ -108,6 +108,30 @@ __device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 acc) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// softplus(x) = log(1 + e^x), taken as x above 20 (the threshold of the KDA
+// gate guide, "core computation logic"), in fp32.  log(1 + e^x) uses the
+// hardware base-2 exp and log (v_exp_f32, v_log_f32; measured on gfx950 against
+// fp64: at most 0.77 and 1.0 ulp for normal results, the log also just above 1)
+// and Kahan's log1p correction (D. Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", 1991, Theorem 4): with y = e^x
+// and u = fl(1 + y),
+//     log1p(y) = log(u) * y / (u - 1)    (u != 1),   = y   (u == 1),
+// which cancels the rounding of 1 + y.  v_exp_f32 flushes results below 2^-126,
+// so for x log2(e) < -64 the exponent is shifted by 64 and the result scaled by
+// 2^-64 (exact, one rounding into the subnormal range).  The error is a few ulp
+// plus the |x| * 2^-24 that rounding x itself costs, in ~15 instructions where
+// the device library's log1pf(expf(x)) takes ~140.
+__device__ __forceinline__ float gate_softplus(float x) {
+  if (x > 20.f) return x;
+  const float t = x * kLog2e;
+  const bool deep = t < -64.f;
+  float y = __builtin_amdgcn_exp2f(deep ? t + 64.f : t);
+  if (deep) y *= 0x1p-64f;
+  const float u = 1.f + y;
+  if (u == 1.f) return y;
+  return __builtin_amdgcn_logf(u) * 0.693147180559945309f * (y * __builtin_amdgcn_rcpf(u - 1.f));
+}
+
 // Chunk geometry shared by all kernels (passed by value).
 struct Geo {
   int B, T, H, HV, K, V, N;  // N = number of sequences

@@ -22,8 +22,6 @@
 
 namespace gdn {
 
-__device__ __forceinline__ float decode_softplus(float x) { return x > 20.f ? x : log1pf(expf(x)); }
-
 template <typename E, int K, int V>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(Geo geo, const E* __restrict__ q,
                                                          const E* __restrict__ k,
@@ -54,7 +52,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(Geo geo, const E* __res
     const size_t tok = (size_t)n * geo.T + t;
     if (threadIdx.x < K) sk[threadIdx.x] = (float)k[(tok * geo.H + h) * K + threadIdx.x];
     else if (threadIdx.x < 2 * K) sq[threadIdx.x - K] = (float)q[(tok * geo.H + h) * K + threadIdx.x - K];
-    const float a = expf(decay_scale * decode_softplus(g_raw[tok * geo.HV + hv] + bias));
+    const float a = expf(decay_scale * gate_softplus(g_raw[tok * geo.HV + hv] + bias));
     const float bt = beta[tok * geo.HV + hv];
     const float vj = (float)v[(tok * geo.HV + hv) * V + j];
     __syncthreads();

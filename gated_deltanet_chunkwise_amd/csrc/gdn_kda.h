@@ -6,17 +6,7 @@
 //     softplus(x) = x for x > 20, else log(1 + e^x),
 // evaluated in fp32 and rounded to the output dtype.
 //
-// log(1 + e^x) is computed with the hardware base-2 exp and log (v_exp_f32,
-// v_log_f32; measured on gfx950 against fp64: at most 0.77 and 1.0 ulp for
-// normal results, the log also just above 1) and Kahan's log1p correction
-// (D. Goldberg, "What every computer scientist should know about
-// floating-point arithmetic", 1991, Theorem 4): with y = e^x and u = fl(1 + y),
-//     log1p(y) = log(u) * y / (u - 1)    (u != 1),   = y   (u == 1),
-// which cancels the rounding of 1 + y.  v_exp_f32 flushes results below 2^-126,
-// so for x log2(e) < -64 the exponent is shifted by 64 and the result scaled by
-// 2^-64 (exact, one rounding into the subnormal range).  The total is a few ulp
-// plus the |x| * 2^-24 that rounding x itself costs; the device library's
-// log1pf(expf(x)) costs ~140 instructions per element here, this ~15.
+// softplus is gate_softplus (hardware exp2/log2 with Kahan's log1p correction).
 //
 // Purely elementwise and HBM-bound (2-4 bytes in and out per element, a few
 // flops).  The vector kernel gives each thread 8 consecutive channels of one
@@ -34,17 +24,6 @@ typedef _Float16 f16;
 
 template <typename T> __device__ __forceinline__ float kda_in(T x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T kda_out(float x) { return (T)x; }  // RNE
-
-__device__ __forceinline__ float kda_softplus(float x) {
-  if (x > 20.f) return x;
-  const float t = x * kLog2e;
-  const bool deep = t < -64.f;
-  float y = __builtin_amdgcn_exp2f(deep ? t + 64.f : t);
-  if (deep) y *= 0x1p-64f;
-  const float u = 1.f + y;
-  if (u == 1.f) return y;
-  return __builtin_amdgcn_logf(u) * 0.693147180559945309f * (y * __builtin_amdgcn_rcpf(u - 1.f));
-}
 
 template <typename T> struct Vec8;
 template <> struct Vec8<float> { f32x4 a, b; };
@@ -117,7 +96,7 @@ __global__ __launch_bounds__(256) void gdn_kda_gate_vec_kernel(const TI* g,
     }
     const float s = -expf(A_log[h]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = s * kda_softplus(x[j] + b[j]);
+    for (int j = 0; j < 8; ++j) x[j] = s * gate_softplus(x[j] + b[j]);
     *reinterpret_cast<Vec8<TO>*>(yg + r * D + d0) = vec8_pack<TO>(x);
   }
 }
@@ -134,7 +113,7 @@ __global__ __launch_bounds__(256) void gdn_kda_gate_scalar_kernel(const TI* g,
     const int d = (int)(e - row * D);
     const int h = (int)(row % H);
     const float x = kda_in(g[e]) + (dt_bias ? dt_bias[(int64_t)h * D + d] : 0.f);
-    yg[e] = kda_out<TO>(-expf(A_log[h]) * kda_softplus(x));
+    yg[e] = kda_out<TO>(-expf(A_log[h]) * gate_softplus(x));
   }
 }
 

@@ -257,8 +257,7 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     float gv = 0.f;
     if (lane < len) {
       const float x = graw + (dt_bias ? dt_bias[hv] : 0.f);
-      const float sp = x > 20.f ? x : log1pf(expf(x));
-      gv = -expf(A_log[hv]) * sp;
+      gv = -expf(A_log[hv]) * gate_softplus(x);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -309,7 +308,8 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 
   // Diagonal blocks of T by forward substitution (the block read into
   // registers with 16-byte LDS loads, so the dependent chain runs on
-  // registers); zero the blocks above them.
+  // registers).  The blocks above them are never written: T is lower
+  // triangular, and the reads below take those blocks as zero.
   {
     const int b = wave;
     if (lane < 16) {
@@ -337,9 +337,6 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ts[(16 * b + i) * FS + 16 * b + lane] = x[i];
     }
-    const int wcols = 16 * (3 - b);
-    for (int idx = lane; idx < 16 * wcols; idx += 64)
-      Ts[(16 * b + idx / wcols) * FS + 16 * (b + 1) + idx % wcols] = 0.f;
   }
   __syncthreads();
 
@@ -371,9 +368,12 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   Frag<E> bw[2], bu[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
+    // Columns 32cb..32cb+15 (lo) and 32cb+16..32cb+31 (hi) lie in the 16-wide
+    // column blocks 2cb and 2cb+1; a block right of the diagonal block ct is 0.
     const float* trow = Ts + (16 * ct + lc) * FS + 32 * cb;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(trow + 4 * g);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(trow + 16 + 4 * g);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 lo = 2 * cb <= ct ? *reinterpret_cast<const f32x4*>(trow + 4 * g) : zero;
+    const f32x4 hi = 2 * cb + 1 <= ct ? *reinterpret_cast<const f32x4*>(trow + 16 + 4 * g) : zero;
     float sw[8], su[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
