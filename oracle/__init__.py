@@ -8,6 +8,8 @@ from gated_deltanet_chunkwise_amd).
 * ``fwd``        -- token-by-token recurrence (C, fp64, pthreads), the oracle.
 * ``gate``       -- the gate activation alone (C, fp64).
 * ``recurrence`` -- the recurrence from a given log-decay g (C, fp64).
+* ``bwd``        -- reverse-mode derivative of ``fwd`` (C, fp64, pthreads) for
+                    L = sum <do, o> + <dht, final state>.
 * ``chunkwise``  -- numpy fp64 chunkwise (WY) reformulation with per-chunk
                     intermediates; a second, independent derivation used to
                     pin the token oracle and to expose intermediates.
@@ -39,6 +41,9 @@ def _declare(lib):
     lib.gdn_oracle_recurrence.argtypes = common + [_dp, _dp, _dp] + tail
     lib.gdn_oracle_fwd.restype = ctypes.c_int
     lib.gdn_oracle_fwd.argtypes = common + [_dp, _dp, _dp, _dp, _dp] + tail
+    lib.gdn_oracle_bwd.restype = ctypes.c_int
+    lib.gdn_oracle_bwd.argtypes = (common + [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp,
+                                             _i32p, ctypes.c_int] + [_dp] * 8 + [ctypes.c_int])
     return lib
 
 
@@ -166,3 +171,37 @@ def recurrence(q, k, v, g, beta, cu_seqlens=None, h0=None, scale=1.0,
     """Token recurrence from a given log-decay g [B,T,HV] (fp64)."""
     return _run("gdn_oracle_recurrence", q, k, v, [g], beta, cu_seqlens, h0,
                 scale, units, nthreads, lib)
+
+
+def bwd(q, k, v, g_raw, beta, A_log, dt_bias, do, dht=None, cu_seqlens=None, h0=None,
+        scale=1.0, units=None, nthreads=None, lib=None):
+    """Oracle backward pass in fp64: gradients of L = sum <do, o> + <dht, final
+    state> for the forward pass ``fwd`` with the same arguments.
+
+    do: [B,T,HV,V]; dht: None (zero) or [N,HV,K,V].  units: optional list of
+    n*HV+hv ids; only they contribute (dv, dg_raw, dbeta, dh0 of others stay 0).
+    Returns a dict of float64 arrays: dq, dk [B,T,H,K]; dv [B,T,HV,V];
+    dg_raw, dbeta [B,T,HV]; dA_log, ddt_bias [HV] (ddt_bias None without a
+    bias); dh0 [N,HV,K,V].
+    """
+    lib = lib or load()
+    B, T, H, HV, K, V, N = _shapes(q, v, cu_seqlens)
+    q, k, v, beta, h0, g_raw, A_log, dt_bias, do, dht = (
+        _f64(x) for x in (q, k, v, beta, h0, g_raw, A_log, dt_bias, do, dht))
+    cu = None if cu_seqlens is None else np.ascontiguousarray(np.asarray(cu_seqlens, np.int64))
+    un = None if units is None else np.ascontiguousarray(np.asarray(units, np.int32))
+    out = dict(dq=np.zeros((B, T, H, K)), dk=np.zeros((B, T, H, K)),
+               dv=np.zeros((B, T, HV, V)), dg_raw=np.zeros((B, T, HV)),
+               dbeta=np.zeros((B, T, HV)), dA_log=np.zeros(HV),
+               ddt_bias=None if dt_bias is None else np.zeros(HV),
+               dh0=np.zeros((N, HV, K, V)))
+    rc = lib.gdn_oracle_bwd(
+        B, T, H, HV, K, V, _ptr(cu, _i64p), N, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(g_raw), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(h0), float(scale),
+        _ptr(do), _ptr(dht), _ptr(un, _i32p), 0 if un is None else len(un),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg_raw"]),
+        _ptr(out["dbeta"]), _ptr(out["dA_log"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle returned error code %d" % rc)
+    return out

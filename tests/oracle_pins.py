@@ -15,7 +15,10 @@ planted mistake) and raises AssertionError when the oracle disagrees with:
   * the independent chunkwise (WY) reformulation at several chunk sizes with
     ragged tails;
   * invariants: packed = separate sequences, state passing, grouped heads =
-    repeated heads, causality, joint linearity in (v, h0), scale.
+    repeated heads, causality, joint linearity in (v, h0), scale;
+  * for the backward: central finite differences of the forward oracle's
+    L = sum <do, o> + <dht, final state> in every input, and the closed form
+    of the gradients when all keys are zero (the state then only decays).
 """
 import math
 
@@ -381,5 +384,104 @@ def pin_segment_scan(lib):
     _close(chunkwise.chunk_transition(Kc, gc, bc), M, 1e-13, "transition = token product")
 
 
+# ---------------------------------------------------------------------------
+# backward
+
+def _bwd_case(rng, B, T, H, HV, K, V, N):
+    """Small random inputs for the backward pins (keys not normalised, so the
+    rank-one updates are not special; one raw gate above the softplus identity
+    threshold of 20)."""
+    q = 0.7 * rng.standard_normal((B, T, H, K))
+    k = 0.6 * rng.standard_normal((B, T, H, K))
+    v = rng.standard_normal((B, T, HV, V))
+    g_raw = rng.standard_normal((B, T, HV))
+    g_raw[0, min(2, T - 1), 0] = 25.0
+    beta = rng.uniform(0.1, 0.9, (B, T, HV))
+    A_log = rng.uniform(-1.0, 0.5, HV)
+    dt_bias = 0.3 * rng.standard_normal(HV)
+    h0 = rng.standard_normal((N, HV, K, V))
+    do = rng.standard_normal((B, T, HV, V))
+    dht = rng.standard_normal((N, HV, K, V))
+    return dict(q=q, k=k, v=v, g_raw=g_raw, beta=beta, A_log=A_log, dt_bias=dt_bias, h0=h0), do, dht
+
+
+def pin_bwd_finite_differences(lib):
+    """Every gradient of the backward oracle equals the central finite
+    difference (step 1e-6, fp64) of L = sum <do, o> + <dht, final state>
+    computed by the forward oracle; fixed-length and packed sequences (one of
+    them empty), grouped value heads, h0, dt_bias and scale."""
+    rng = np.random.default_rng(31)
+    cases = [dict(B=2, T=5, H=1, HV=2, K=3, V=2, cu=None),
+             dict(B=1, T=7, H=2, HV=4, K=2, V=3, cu=np.array([0, 3, 3, 7]))]
+    eps = 1e-6
+    for c in cases:
+        N = c["B"] if c["cu"] is None else len(c["cu"]) - 1
+        x, do, dht = _bwd_case(rng, c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], N)
+        scale = 0.7
+
+        def loss(xx):
+            o, fin = oracle.fwd(xx["q"], xx["k"], xx["v"], xx["g_raw"], xx["beta"], xx["A_log"],
+                                xx["dt_bias"], cu_seqlens=c["cu"], h0=xx["h0"], scale=scale,
+                                lib=lib)
+            return float(np.sum(do * o) + np.sum(dht * fin))
+
+        gr = oracle.bwd(x["q"], x["k"], x["v"], x["g_raw"], x["beta"], x["A_log"], x["dt_bias"],
+                        do, dht, cu_seqlens=c["cu"], h0=x["h0"], scale=scale, lib=lib)
+        names = dict(q="dq", k="dk", v="dv", g_raw="dg_raw", beta="dbeta", A_log="dA_log",
+                     dt_bias="ddt_bias", h0="dh0")
+        for name, gname in names.items():
+            fd = np.zeros_like(x[name])
+            for idx in np.ndindex(x[name].shape):
+                xp = {kk: vv.copy() for kk, vv in x.items()}
+                xm = {kk: vv.copy() for kk, vv in x.items()}
+                xp[name][idx] += eps
+                xm[name][idx] -= eps
+                fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+            _close(gr[gname], fd, 2e-7, "finite differences %s (%s)" % (gname, c))
+
+
+def pin_bwd_no_keys(lib):
+    """With every key zero the state only decays, H_t = P_t h0 with
+    P_t = prod_{s<=t} exp(g_s), and the gradients have closed forms:
+    dH_t = sum_{s>=t} scale (P_s/P_t) q_s do_s^T + (P_T/P_t) dht, dh0 = dH_0,
+    dq_t = scale P_t h0 do_t, dk_t = beta_t dH_t v_t, dv = dbeta = 0,
+    dg_t = sum_{s>=t} scale P_s q_s^T h0 do_s + P_T <h0, dht>."""
+    rng = np.random.default_rng(32)
+    B, T, H, HV, K, V = 1, 6, 1, 1, 3, 2
+    x, do, dht = _bwd_case(rng, B, T, H, HV, K, V, 1)
+    x["k"][:] = 0.0
+    x["g_raw"][0, 2, 0] = 0.4
+    scale = 1.3
+    gr = oracle.bwd(x["q"], x["k"], x["v"], x["g_raw"], x["beta"], x["A_log"], x["dt_bias"],
+                    do, dht, h0=x["h0"], scale=scale, lib=lib)
+    xg = x["g_raw"][0, :, 0] + x["dt_bias"][0]
+    sp = np.log1p(np.exp(xg))
+    g = -math.exp(x["A_log"][0]) * sp
+    P = np.exp(np.cumsum(g))
+    h0, q, v, dO, beta = x["h0"][0, 0], x["q"][0, :, 0], x["v"][0, :, 0], do[0, :, 0], x["beta"][0, :, 0]
+    dH = [None] * T
+    for t in range(T):
+        acc = (P[-1] / P[t]) * dht[0, 0]
+        for s in range(t, T):
+            acc = acc + scale * (P[s] / P[t]) * np.outer(q[s], dO[s])
+        dH[t] = acc
+    dh0 = scale * sum(P[s] * np.outer(q[s], dO[s]) for s in range(T)) + P[-1] * dht[0, 0]
+    _close(gr["dh0"][0, 0], dh0, 1e-12, "no keys: dh0")
+    _close(gr["dq"][0, :, 0], np.stack([scale * P[t] * h0 @ dO[t] for t in range(T)]), 1e-12,
+           "no keys: dq")
+    _close(gr["dk"][0, :, 0], np.stack([beta[t] * dH[t] @ v[t] for t in range(T)]), 1e-12,
+           "no keys: dk")
+    _close(gr["dv"], np.zeros_like(gr["dv"]), 0.0, "no keys: dv")
+    _close(gr["dbeta"], np.zeros_like(gr["dbeta"]), 0.0, "no keys: dbeta")
+    dg = np.array([sum(scale * P[s] * (q[s] @ h0 @ dO[s]) for s in range(t, T))
+                   + P[-1] * np.sum(h0 * dht[0, 0]) for t in range(T)])
+    slope = 1.0 / (1.0 + np.exp(-xg))
+    _close(gr["dg_raw"][0, :, 0], dg * (-math.exp(x["A_log"][0])) * slope, 1e-12, "no keys: dg_raw")
+    _close(gr["dA_log"], [np.sum(dg * g)], 1e-12, "no keys: dA_log")
+    _close(gr["ddt_bias"], [np.sum(dg * (-math.exp(x["A_log"][0])) * slope)], 1e-12,
+           "no keys: ddt_bias")
+
+
 ALL_PINS = [pin_gate, pin_kda_gate, pin_brute_force, pin_transition_product, pin_identities,
-            pin_chunkwise, pin_invariants, pin_full_forward, pin_segment_scan]
+            pin_chunkwise, pin_invariants, pin_full_forward, pin_segment_scan,
+            pin_bwd_finite_differences, pin_bwd_no_keys]

@@ -36,6 +36,21 @@ MUTANTS = {
                                     "const double head_scale = -A_log[h];"),
     "kda_rows_strided_by_D": ("const int64_t row = (t * H + h) * (int64_t)D;",
                               "const int64_t row = (h * T + t) * (int64_t)D;"),
+    "bwd_dk_misses_prediction_path": ("dk[i] = b * acc_u + acc_p;", "dk[i] = b * acc_u;"),
+    "bwd_dp_sign": ("acc_p += Hp[i * V + j] * (-a * du[j]);", "acc_p += Hp[i * V + j] * (a * du[j]);"),
+    "bwd_state_grad_not_decayed": ("dH[i * V + j] = a * dH[i * V + j] + kt[i]",
+                                   "dH[i * V + j] = dH[i * V + j] + kt[i]"),
+    "bwd_da_misses_prediction": ("for (int j = 0; j < V; ++j) da -= p[j] * du[j];", ""),
+    "bwd_dg_not_times_a": ("const double dg = a * da;", "const double dg = da;"),
+    "bwd_softplus_slope_sign": ("1.0 / (1.0 + exp(-x))", "1.0 / (1.0 + exp(x))"),
+    "bwd_dq_uses_previous_state": ("acc += Hs[i * V + j] * dot[j];", "acc += Hp[i * V + j] * dot[j];"),
+    "bwd_gqa_first_head_only": ("for (int r = 0; r < G; ++r) {", "for (int r = 0; r < 1; ++r) {"),
+    "bwd_dA_log_uses_dg_raw": ("dA_sum += dg * gl[s];", "dA_sum += dgr * gl[s];"),
+    "bwd_dbeta_uses_v": ("dbeta += dH[i * V + j] * kt[i] * u[j];",
+                         "dbeta += dH[i * V + j] * kt[i] * vt[j];"),
+    "bwd_dht_ignored": ("  if (J->dht)\n    memcpy", "  if (0)\n    memcpy"),
+    "bwd_output_scale_dropped": ("dH[i * V + j] += J->scale * qt[i] * dot[j];",
+                                 "dH[i * V + j] += qt[i] * dot[j];"),
     "decay_is_exp_of_negative": ("const double a = exp(J->g[t * HV + hv]);",
                                  "const double a = exp(-J->g[t * HV + hv]);"),
 }

@@ -40,3 +40,20 @@ def test_invalid_arguments_rejected():
         oracle.recurrence(q, k, v, g, beta, cu_seqlens=[0, 4, 9])  # does not end at T
     with pytest.raises(ValueError):
         oracle.recurrence(q, k, v, g, beta, units=[5])
+
+
+def test_bwd_threads_and_units_do_not_change_results():
+    rng = np.random.default_rng(5)
+    x, do, dht = oracle_pins._bwd_case(rng, 2, 20, 1, 3, 4, 5, 2)
+    args = (x["q"], x["k"], x["v"], x["g_raw"], x["beta"], x["A_log"], x["dt_bias"], do, dht)
+    r1 = oracle.bwd(*args, h0=x["h0"], nthreads=1)
+    r8 = oracle.bwd(*args, h0=x["h0"], nthreads=8)
+    for name in r1:
+        assert np.array_equal(r1[name], r8[name]), name
+    # one key head read by all three value heads: the units of sequence 1 give
+    # that sequence's rows in full and nothing for sequence 0
+    ru = oracle.bwd(*args, h0=x["h0"], units=[3, 4, 5])
+    for name in ("dq", "dk", "dv", "dg_raw", "dbeta"):
+        assert np.array_equal(ru[name][1], r1[name][1]), name
+        assert not ru[name][0].any(), name
+    assert np.array_equal(ru["dh0"][1], r1["dh0"][1]) and not ru["dh0"][0].any()
