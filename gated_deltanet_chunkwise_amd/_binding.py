@@ -16,12 +16,14 @@ GDN_F16 = 2  # KDA gate only
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
            "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_decode", "gdn_kda_gate",
-           "gdn_status_string")
+           "gdn_bwd_workspace_size", "gdn_bwd", "gdn_bwd_timed", "gdn_status_string")
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
 # gdn_fwd_stages bits, one per entry of STAGES
 STAGE_BITS = {name: 1 << i for i, name in enumerate(STAGES)}
 STAGE_ALL = (1 << len(STAGES)) - 1
+BWD_NUM_STAGES = 6
+BWD_STAGES = ("recompute", "prep", "bwd_chain", "dqk", "bwd_wy", "sums")
 
 
 class Params(ctypes.Structure):
@@ -84,6 +86,12 @@ def _declare(lib):
                                  ctypes.c_int32, ctypes.c_int32, fp]
     lib.gdn_fwd_stages.restype = ctypes.c_int
     lib.gdn_fwd_stages.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, ctypes.c_uint, fp]
+    lib.gdn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_bwd_workspace_size.argtypes = [P, ctypes.c_int]
+    lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_bwd.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp]
+    lib.gdn_bwd_timed.restype = ctypes.c_int
+    lib.gdn_bwd_timed.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp, ctypes.c_void_p]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -343,3 +351,103 @@ def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_stat
     plan = GdnForward(B, T, H, HV, K, V, q.dtype, q.device, num_seqs=num_seqs, scale=scale,
                       final_state=output_final_state)
     return plan(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state)
+
+
+class GdnBackward:
+    """A planned backward pass (gdn_bwd): gradient outputs and workspace
+    allocated once, so that calling it launches the kernels and allocates
+    nothing.  Inputs as for GdnForward, plus d_o [B,T,HV,V] (q's dtype) and
+    d_final_state [N,HV,K,V] fp32 or None.  Outputs (attributes, overwritten
+    by each call): dq, dk [B,T,H,K] and dv [B,T,HV,V] in q's dtype; dg_raw,
+    dbeta [B,T,HV], dA_log [HV], ddt_bias [HV] and d_initial_state
+    [N,HV,K,V] in fp32.
+    """
+
+    def __init__(self, B, T, H, HV, K, V, dtype, device, num_seqs=None, scale=1.0):
+        torch = _torch()
+        self.packed = num_seqs is not None
+        self.N = num_seqs if self.packed else B
+        self.params = make_params(B, T, H, HV, K, V, _dtype_code(dtype),
+                                  num_seqs if self.packed else 0, scale)
+        self.lib = load_library()
+        workspace_layout(self.params, self.packed)  # raises on bad sizes
+        self.ws_bytes = int(self.lib.gdn_bwd_workspace_size(ctypes.byref(self.params),
+                                                            int(self.packed)))
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        f32 = torch.float32
+        self.dq = torch.empty((B, T, H, K), dtype=dtype, device=device)
+        self.dk = torch.empty((B, T, H, K), dtype=dtype, device=device)
+        self.dv = torch.empty((B, T, HV, V), dtype=dtype, device=device)
+        self.dg_raw = torch.empty((B, T, HV), dtype=f32, device=device)
+        self.dbeta = torch.empty((B, T, HV), dtype=f32, device=device)
+        self.dA_log = torch.empty((HV,), dtype=f32, device=device)
+        self.ddt_bias = torch.empty((HV,), dtype=f32, device=device)
+        self.d_initial_state = torch.empty((self.N, HV, K, V), dtype=f32, device=device)
+
+    def grads(self):
+        return dict(dq=self.dq, dk=self.dk, dv=self.dv, dg_raw=self.dg_raw, dbeta=self.dbeta,
+                    dA_log=self.dA_log, ddt_bias=self.ddt_bias, dh0=self.d_initial_state)
+
+    def _args(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+              d_final_state, stream):
+        torch = _torch()
+        if (cu_seqlens is not None) != self.packed:
+            raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
+        for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta),
+                        ("A_log", A_log), ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
+                        ("initial_state", initial_state), ("d_o", d_o),
+                        ("d_final_state", d_final_state)):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if d_o.shape != self.dv.shape or d_o.dtype != self.dv.dtype:
+            raise ValueError("d_o must match o's shape and dtype")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        return (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
+                _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(d_o),
+                _ptr(d_final_state), _ptr(self.dq), _ptr(self.dk), _ptr(self.dv),
+                _ptr(self.dg_raw), _ptr(self.dbeta), _ptr(self.dA_log), _ptr(self.ddt_bias),
+                _ptr(self.d_initial_state), _ptr(self.workspace), self.ws_bytes,
+                ctypes.c_void_p(stream.cuda_stream))
+
+    def __call__(self, q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_final_state=None,
+                 cu_seqlens=None, initial_state=None, stream=None, events=None):
+        """Launch on `stream` (default: torch's current stream); returns grads().
+        `events`: optional ctypes array of BWD_NUM_STAGES + 1 hipEvent_t."""
+        args = self._args(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+                          d_final_state, stream)
+        if events is None:
+            st = self.lib.gdn_bwd(*args)
+        else:
+            st = self.lib.gdn_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p))
+        if st:
+            raise GdnError(st, "gdn_bwd")
+        return self.grads()
+
+    def bind(self, q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_final_state=None,
+             cu_seqlens=None, initial_state=None, stream=None):
+        """Marshal the arguments once; returns a zero-argument launcher."""
+        args = self._args(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+                          d_final_state, stream)
+        keep = (q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+                d_final_state)
+        fn = self.lib.gdn_bwd
+
+        def launch():
+            keep  # the tensors stay alive as long as the callable
+            st = fn(*args)
+            if st:
+                raise GdnError(st, "gdn_bwd")
+        return launch
+
+
+def bwd(q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_final_state=None, cu_seqlens=None,
+        initial_state=None, scale=1.0):
+    """One backward pass (allocates outputs and workspace with torch); returns
+    the dict of GdnBackward.grads()."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    num_seqs = None if cu_seqlens is None else cu_seqlens.numel() - 1
+    plan = GdnBackward(B, T, H, HV, K, V, q.dtype, q.device, num_seqs=num_seqs, scale=scale)
+    return plan(q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_final_state, cu_seqlens,
+                initial_state)

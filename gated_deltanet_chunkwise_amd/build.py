@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("gdn_common.h", "gdn_kernels.h", "gdn_kda.h", "gdn_decode.h")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("gdn_common.h", "gdn_kernels.h", "gdn_kda.h", "gdn_decode.h", "gdn_bwd.h")] + [
     os.path.join(INCLUDE, "gdn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

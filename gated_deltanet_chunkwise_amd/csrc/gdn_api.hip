@@ -10,6 +10,7 @@
 #include <utility>
 
 #include "gdn.h"
+#include "gdn_bwd.h"
 #include "gdn_decode.h"
 #include "gdn_kda.h"
 #include "gdn_kernels.h"
@@ -204,7 +205,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   mark(1);
   if (work && geo.slots > 0 && (mask & GDN_STAGE_WY))
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo, ke,
-              ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf));
+              ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf, nullptr));
   mark(2);
   if (work && (mask & GDN_STAGE_STATE)) {
     if (L.num_segs > 0) {
@@ -259,6 +260,173 @@ gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, 
   if (K == 128 && V == 64) return run_v<E, 128, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
   if (K == 64 && V == 128) return run_v<E, 64, 128>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
   return run_v<E, 64, 64>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu, h0, o, fin, ws, s, ev, m);
+}
+
+}  // namespace
+
+// ---- backward ----
+namespace {
+
+// Workspace of the backward pass: the forward layout (without segments), then
+// the backward's fp32 intermediates (see gdn_bwd.h).
+struct BwdLayout {
+  size_t tmat, hcp, vnp, qtf, wtf, kdf, dof, dvl, dhn, dvn, dqp, dkp, dwp, dgp, dAp, dbp, total;
+};
+
+gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayout* bl) {
+  if (!p) return GDN_ERR_NULL;
+  gdn_params_t q = *p;
+  q.seg_chunks = 0;
+  gdn_status_t st = make_plan(&q, varlen, pl);
+  if (st != GDN_OK) return st;
+  const size_t hsl = (size_t)p->HV * (size_t)pl->geo.slots, C = gdn::kChunk, K = p->K, V = p->V;
+  size_t off = pl->lay.total;
+  auto take = [&](size_t& field, size_t floats) {
+    field = off;
+    off = align_up(off + hsl * floats * 4);
+  };
+  take(bl->tmat, C * C);
+  take(bl->hcp, K * V);
+  take(bl->vnp, C * V);
+  take(bl->qtf, K * C);
+  take(bl->wtf, K * C);
+  take(bl->kdf, C * K);
+  take(bl->dof, C * V);
+  take(bl->dvl, C * V);
+  take(bl->dhn, K * V);
+  take(bl->dvn, C * V);
+  take(bl->dqp, C * K);
+  take(bl->dkp, C * K);
+  take(bl->dwp, C * K);
+  take(bl->dgp, C);
+  take(bl->dAp, 1);
+  take(bl->dbp, 1);
+  bl->total = off;
+  return GDN_OK;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *g_raw, *beta, *A_log, *dt_bias;
+  const int64_t* cu;
+  const float* h0;
+  const void* d_o;
+  const float* dht;
+  void *dq, *dk, *dv;
+  float *dg_raw, *dbeta, *dA_log, *ddt_bias, *dh0;
+};
+
+gdn_status_t check_bwd(const gdn_params_t* p, const BwdArgs& a, const void* ws, size_t ws_bytes,
+                       Plan* pl, BwdLayout* bl) {
+  if (!p) return GDN_ERR_NULL;
+  gdn_status_t st = make_bwd_plan(p, a.cu != nullptr, pl, bl);
+  if (st != GDN_OK) return st;
+  const bool tokens = pl->ntok > 0;
+  if (tokens && (!a.q || !a.k || !a.v || !a.g_raw || !a.beta || !a.A_log || !a.d_o || !a.dq ||
+                 !a.dk || !a.dv || !a.dg_raw || !a.dbeta))
+    return GDN_ERR_NULL;
+  if (!a.dA_log) return GDN_ERR_NULL;
+  if (bl->total > 0 && !ws) return GDN_ERR_NULL;
+  for (const void* x : {a.q, a.k, a.v, a.d_o, (const void*)a.dq, (const void*)a.dk, (const void*)a.dv})
+    if (!aligned(x, 16)) return GDN_ERR_ALIGN;
+  for (const void* x : {(const void*)a.g_raw, (const void*)a.beta, (const void*)a.A_log,
+                        (const void*)a.dt_bias, (const void*)a.h0, (const void*)a.dht,
+                        (const void*)a.dg_raw, (const void*)a.dbeta, (const void*)a.dA_log,
+                        (const void*)a.ddt_bias, (const void*)a.dh0})
+    if (!aligned(x, 4)) return GDN_ERR_ALIGN;
+  if (!aligned(a.cu, 8) || !aligned(ws, kWsAlign)) return GDN_ERR_ALIGN;
+  if (ws_bytes < bl->total) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+template <typename E, int K, int V, bool VARLEN>
+gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void* ws,
+                     hipStream_t s, void* const* events) {
+  using gdn::Frag;
+  using gdn::Quad;
+  const gdn::Geo& geo = pl.geo;
+  const gdn_workspace_layout_t& L = pl.lay;
+  char* w = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  float* gam = F(L.gamma);
+  float* bet = F(L.beta);
+  Frag<E>* wf = reinterpret_cast<Frag<E>*>(w + L.w);
+  Frag<E>* ktf = reinterpret_cast<Frag<E>*>(w + L.kt);
+  Quad<E>* uf = reinterpret_cast<Quad<E>*>(w + L.u);
+  int4* cmap = VARLEN ? reinterpret_cast<int4*>(w + L.chunk_map) : nullptr;
+  int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
+  auto FR = [&](size_t off) { return reinterpret_cast<Frag<float>*>(w + off); };
+  const E* qe = static_cast<const E*>(a.q);
+  const E* ke = static_cast<const E*>(a.k);
+  const E* ve = static_cast<const E*>(a.v);
+  const E* doe = static_cast<const E*>(a.d_o);
+
+  hipError_t err = hipSuccess;
+  auto ok = [&](hipError_t e) {
+    if (e != hipSuccess && err == hipSuccess) err = e;
+  };
+  auto mark = [&](int i) {
+    if (events) ok(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
+  };
+  const unsigned chunk_wgs = (unsigned)geo.slots * geo.HV;
+  const unsigned units = (unsigned)geo.N * geo.HV * (V / 16);
+  mark(0);
+  if (VARLEN && geo.N > 0)
+    ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, a.cu, geo.N, geo.T, geo.slots,
+              cmap, seq_slot));
+  if (chunk_wgs > 0)
+    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(256), s, geo, ke, ve,
+              a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat)));
+  if (units > 0 && geo.slots > 0)
+    ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN, gdn::CHAIN_PLAIN>, dim3(units), dim3(64), s,
+              geo, wf, ktf, uf, gam, seq_slot, a.h0, nullptr,
+              reinterpret_cast<Frag<E>*>(F(bl.hcp)), reinterpret_cast<Frag<E>*>(F(bl.vnp))));
+  mark(1);
+  if (chunk_wgs > 0)
+    ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,
+              doe, cmap, gam, wf, FR(bl.qtf), FR(bl.wtf), FR(bl.kdf), FR(bl.dof),
+              reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
+  mark(2);
+  if (units > 0)
+    ok(launch(gdn::gdn_bwd_chain_kernel<K, V, VARLEN>, dim3(units), dim3(64), s, geo, FR(bl.kdf),
+              reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FR(bl.qtf), FR(bl.dof), FR(bl.wtf),
+              gam, seq_slot, a.dht, a.dh0, F(bl.dhn), F(bl.dvn)));
+  mark(3);
+  if (chunk_wgs > 0)
+    ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,
+              doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
+              F(bl.dwp), F(bl.dgp)));
+  mark(4);
+  if (chunk_wgs > 0)
+    ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, ke, ve,
+              a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp), F(bl.dvn),
+              F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw, F(bl.dAp),
+              F(bl.dbp)));
+  mark(5);
+  if (geo.slots > 0)
+    ok(launch(gdn::gdn_bwd_qk_sum_kernel<E, K, VARLEN>, dim3((unsigned)geo.slots * geo.H),
+              dim3(256), s, geo, cmap, F(bl.dqp), F(bl.dkp), static_cast<E*>(a.dq),
+              static_cast<E*>(a.dk)));
+  ok(launch(gdn::gdn_bwd_param_kernel, dim3(geo.HV), dim3(256), s, geo, F(bl.dAp), F(bl.dbp),
+            a.dA_log, a.ddt_bias));
+  mark(6);
+  return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+template <typename E>
+gdn_status_t run_bwd_e(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void* ws,
+                       hipStream_t s, void* const* ev) {
+  const int kv = pl.geo.K * 1000 + pl.geo.V;
+  if (pl.varlen) {
+    if (kv == 128128) return run_bwd<E, 128, 128, true>(pl, bl, a, ws, s, ev);
+    if (kv == 128064) return run_bwd<E, 128, 64, true>(pl, bl, a, ws, s, ev);
+    if (kv == 64128) return run_bwd<E, 64, 128, true>(pl, bl, a, ws, s, ev);
+    return run_bwd<E, 64, 64, true>(pl, bl, a, ws, s, ev);
+  }
+  if (kv == 128128) return run_bwd<E, 128, 128, false>(pl, bl, a, ws, s, ev);
+  if (kv == 128064) return run_bwd<E, 128, 64, false>(pl, bl, a, ws, s, ev);
+  if (kv == 64128) return run_bwd<E, 64, 128, false>(pl, bl, a, ws, s, ev);
+  return run_bwd<E, 64, 64, false>(pl, bl, a, ws, s, ev);
 }
 
 }  // namespace
@@ -434,6 +602,44 @@ gdn_status_t gdn_kda_gate(const void* g, gdn_dtype_t g_dtype, const float* A_log
   if (g_dtype == GDN_F32) return kda_out<float>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
   if (g_dtype == GDN_BF16) return kda_out<gdn::bf16>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
   return kda_out<gdn::f16>(g, A_log, dt_bias, yg, yg_dtype, T, H, D, s);
+}
+
+size_t gdn_bwd_workspace_size(const gdn_params_t* p, int packed) {
+  Plan pl;
+  BwdLayout bl;
+  if (!p) return 0;
+  return make_bwd_plan(p, packed != 0, &pl, &bl) == GDN_OK ? bl.total : 0;
+}
+
+gdn_status_t gdn_bwd_timed(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                           const float* g_raw, const float* beta, const float* A_log,
+                           const float* dt_bias, const int64_t* cu_seqlens,
+                           const float* initial_state, const void* d_o,
+                           const float* d_final_state, void* dq, void* dk, void* dv,
+                           float* dg_raw, float* dbeta, float* dA_log, float* ddt_bias,
+                           float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events) {
+  const BwdArgs a{q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+                  d_final_state, dq, dk, dv, dg_raw, dbeta, dA_log, ddt_bias, d_initial_state};
+  Plan pl;
+  BwdLayout bl;
+  gdn_status_t st = check_bwd(p, a, workspace, workspace_bytes, &pl, &bl);
+  if (st != GDN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == GDN_BF16) return run_bwd_e<gdn::bf16>(pl, bl, a, workspace, s, events);
+  return run_bwd_e<float>(pl, bl, a, workspace, s, events);
+}
+
+gdn_status_t gdn_bwd(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                     const float* g_raw, const float* beta, const float* A_log,
+                     const float* dt_bias, const int64_t* cu_seqlens, const float* initial_state,
+                     const void* d_o, const float* d_final_state, void* dq, void* dk, void* dv,
+                     float* dg_raw, float* dbeta, float* dA_log, float* ddt_bias,
+                     float* d_initial_state, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return gdn_bwd_timed(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
+                       d_final_state, dq, dk, dv, dg_raw, dbeta, dA_log, ddt_bias,
+                       d_initial_state, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* gdn_status_string(gdn_status_t s) {

@@ -1,0 +1,769 @@
+// gdn_bwd.h -- chunkwise backward pass of the gated delta rule on gfx950.
+//
+// The pages name the backward kernels (a per-chunk dv, the dq/dk/dw/dg kernel,
+// the dg kernel, the WY backward and the dh/du pass of the state recurrence:
+// the Ascend GDN blog, "Ascend-affine tiling", and the G_T_CONTIG page, "fix")
+// without writing their formulas.  They follow from differentiating the
+// chunk form of the forward pass (per chunk, G the chunk-local cumulative
+// gate, natural log, e^{dG}_{ij} = e^{G_i - G_j}, M the causal mask j <= i):
+//     A = strictly_lower(beta_i e^{dG} K K^T),  T = (I + A)^{-1}
+//     w = T diag(beta e^G) K,   u = T diag(beta) V
+//     v_new = u - w H_c,        H_{c+1} = e^{G_last} H_c + kd^T v_new
+//     o = scale [(e^G * Q) H_c + P v_new],  P = (Q K^T) * M * e^{dG}
+// with kd = diag(e^{G_last - G}) K.  For L = sum <do, o> + <dht, H_final>:
+//   * dv_local = scale P^T do (prep kernel);
+//   * backwards over chunks, from dH = dht (state kernel):
+//       dv_new = dv_local + kd dH_{c+1},
+//       dH_c   = e^{G_last} dH_{c+1} + scale (e^G * Q)^T do - w^T dv_new;
+//   * per chunk (dq/dk kernel), with dPm = scale (do v_new^T) * M * e^{dG}:
+//       dq = scale e^G * (do H_c^T) + dPm K,
+//       dk = dPm^T Q + e^{G_last - G} * (v_new dH_{c+1}^T),   dw = -dv_new H_c^T,
+//       dG_i += sum_j R_ij - sum_j R_ji (R = dPm * Q K^T) + q_i . dq_inter_i
+//               - x_i,  x_i = k_i . dk_kd_i,
+//       dG_last += sum_i x_i + e^{G_last} <dH_{c+1}, H_c>;
+//   * WY backward (wy kernel), with dT = dw (diag(beta e^G) K)^T + dv_new (diag(beta) V)^T:
+//       X_w = T^T dw, X_u = T^T dv_new,  dk += beta e^G X_w,  dv = beta X_u,
+//       dbeta = e^G k . X_w + v . X_u + sum_j dA_ij e^{dG} (K K^T)_ij,
+//       dA = -strictly_lower(T^T dT T^T),  dS = dA * beta_i e^{dG},
+//       dk += (dS + dS^T) K,  dG_i += sum_j Z_ij - sum_j Z_ji (Z = dA * A)
+//              + beta_i e^{G_i} k_i . X_w_i;
+//   * dg_t = sum_{i >= t in the chunk} dG_i (the chunk-local cumsum reversed),
+//     then through the gate g = -exp(A_log) softplus(x), x = g_raw + dt_bias:
+//       dg_raw = dg (-exp(A_log)) softplus'(x),  dA_log = sum dg g,
+//       ddt_bias = sum dg_raw;
+//   * dq, dk of a key head sum its value heads (finalize kernel).
+// The forward intermediates are recomputed first by the forward kernels: WY
+// (also storing T) and the state pass in its CHAIN_PLAIN mode (fp32 H_c and
+// v_new).
+//
+// Arithmetic is fp32 throughout (fp32 MFMA v_mfma_f32_16x16x4f32, operands
+// staged as fp32 in LDS); only q, k, v, do are read, and dq, dk, dv written, in
+// the call's dtype.  Intermediates in the workspace are fp32 row-major:
+//   hcp, dhn [hv][slot][K][V]          H_c, dL/dH_{c+1}
+//   vnp, dvn [hv][slot][64][V]         v_new, dL/dv_new
+//   tmat     [hv][slot][64][64]        T
+//   dqp, dkp, dwp [hv][slot][64][K]    per value head dq, dk; dw
+//   dgp      [hv][slot][64]            dG from the dq/dk kernel
+//   dAp, dbp [hv][slot]                per-chunk sums for dA_log, ddt_bias
+// and fragment-major operands of the backward state pass (fp32 k32 fragments
+// as in the forward state pass, lane l = row l%16, k-slot group l/16):
+//   qtf, wtf [hv][slot][K/16][2][lane]  A operands (rows k, k over the chunk):
+//                                       scale e^G q^T and w^T
+//   kdf      [hv][slot][4][K/32][lane]  A operand (rows c, k over K): kd
+//   dof      [hv][slot][V/16][2][lane]  B operand (k over the chunk, column v): do
+//   dvl      [hv][slot][V/16][4][lane]  D tiles (rows c, column v): dv_local
+#pragma once
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+// fp32 LDS row stride for n columns: n + 4, so the 16 rows x 4 columns (or
+// 4 rows x 16 columns) that one MFMA operand read touches fall in distinct banks.
+template <int N> struct Pad { static constexpr int v = N + 4; };
+constexpr int kCP = kChunk + 4;  // stride of 64-column fp32 tiles
+
+// acc (one 16x16 fp32 D tile) += sum_{kk < KD} A(m, kk) B(kk, n), where
+// A(m, kk) = a[m * sam + kk * sak] and B(kk, n) = b[kk * sbk + n * sbn], with
+// a and b at the tile's origin (m, n in 0..15).  MFMA j of each 16-wide step
+// takes kk = s + 4 (lane / 16) + j in both operands.  D tile lane l holds rows
+// 4 (l / 16) + r, column l % 16.
+template <int KD>
+__device__ __forceinline__ void mm16(f32x4& acc, const float* a, int sam, int sak, const float* b,
+                                     int sbk, int sbn) {
+  const int lane = lane_id(), l16 = lane & 15, kq = lane >> 4;
+  const float* ap = a + l16 * sam;
+  const float* bp = b + l16 * sbn;
+#pragma unroll
+  for (int s = 0; s < KD; s += 16)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = s + 4 * kq + j;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[kk * sak], bp[kk * sbk], acc, 0, 0, 0);
+    }
+}
+
+// Sum over the 16 lanes of each lane group (the columns of a D tile row).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 16);
+  return x;
+}
+// Sum over the 4 lane groups (the rows 4g + r of a D tile column, per r).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float sum64(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Rows [0, ROWS) into an fp32 LDS tile (stride ld): row r reads
+// src + (t0 + r) * row_stride, rows >= len are zero.  N columns, 256 threads.
+template <int N, typename E, int ROWS = kChunk>
+__device__ __forceinline__ void stage_rows(float* dst, int ld, const E* src, int64_t t0,
+                                           int64_t row_stride, int len) {
+  constexpr int PER = ROWS * N / 8 / 256;  // 8-element pieces per thread
+  static_assert(PER * 8 * 256 == ROWS * N, "whole pieces per thread");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int m = tid + 256 * it, row = m / (N / 8), c0 = 8 * (m % (N / 8));
+    float e[8];
+    if (row < len) {
+      ld8(src + (t0 + row) * row_stride + c0, e);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = 0.f;
+    }
+    *reinterpret_cast<f32x4*>(dst + row * ld + c0) = f32x4{e[0], e[1], e[2], e[3]};
+    *reinterpret_cast<f32x4*>(dst + row * ld + c0 + 4) = f32x4{e[4], e[5], e[6], e[7]};
+  }
+}
+
+// The 8 elements of a k32 fragment in k-slot order (kslot(g, i), i = 0..7).
+__device__ __forceinline__ void frag_elems(const Frag<bf16>& f, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)f.x[i];
+}
+__device__ __forceinline__ void frag_elems(const Frag<float>& f, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = f.lo[i];
+    x[4 + i] = f.hi[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep, one workgroup per (chunk slot, value head): dv_local and the operand
+// fragments of the backward state pass.
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
+    Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
+    const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<E>* __restrict__ wf,
+    Frag<float>* __restrict__ qtf, Frag<float>* __restrict__ wtf, Frag<float>* __restrict__ kdf,
+    Frag<float>* __restrict__ dof, f32x4* __restrict__ dvl) {
+  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, KT = K / 16, KB = K / 32, NV = V / 16;
+  __shared__ __align__(16) float Qs[kChunk * KP];  // q, later w
+  __shared__ __align__(16) float Ks[kChunk * KP];
+  __shared__ __align__(16) float Ds[kChunk * VP];
+  __shared__ __align__(16) float Ps[kChunk * kCP];
+  __shared__ float sg[kChunk];
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+
+  stage_rows<K>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<V>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
+  __syncthreads();
+
+  // P = (Q K^T) * M * e^{dG}; wave = row tile.
+  {
+    const int it = wave;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= it) mm16<K>(acc, Qs + 16 * it * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g + r, j = 16 * jt + lc;
+        Ps[i * kCP + j] = j <= i ? acc[r] * fast_exp2(sg[i] - sg[j]) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // dv_local = scale P^T do: D tiles (rows c = 16 ct + .., column v).
+  {
+    const int ct = wave;
+    for (int vt = 0; vt < NV; ++vt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mm16<kChunk>(acc, Ps + 16 * ct, 1, kCP, Ds + 16 * vt, VP, 1);
+      dvl[((hs * NV + vt) * 4 + ct) * 64 + lane] = acc * geo.scale;
+    }
+  }
+  // (scale e^G q)^T fragments (rows k, k over the chunk).
+  for (int f = wave; f < KT * 2; f += 4) {
+    const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
+    Frag<float> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c0 = 32 * cb + 4 * g + i, c1 = c0 + 16;
+      x.lo[i] = geo.scale * fast_exp2(sg[c0]) * Qs[c0 * KP + kk];
+      x.hi[i] = geo.scale * fast_exp2(sg[c1]) * Qs[c1 * KP + kk];
+    }
+    qtf[(hs * KT * 2 + f) * 64 + lane] = x;
+  }
+  // kd fragments (rows c, k over K).
+  {
+    const float gl = sg[kChunk - 1];
+    for (int f = wave; f < 4 * KB; f += 4) {
+      const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
+      const float e = fast_exp2(gl - sg[c]);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(Ks + c * KP + 32 * kb + 4 * g);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(Ks + c * KP + 32 * kb + 16 + 4 * g);
+      kdf[((hs * 4 + ct) * KB + kb) * 64 + lane] = Frag<float>{lo * e, hi * e};
+    }
+  }
+  // do fragments (k over the chunk, column v).
+  for (int f = wave; f < NV * 2; f += 4) {
+    const int vt = f >> 1, cb = f & 1, vv = 16 * vt + lc;
+    Frag<float> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x.lo[i] = Ds[(32 * cb + 4 * g + i) * VP + vv];
+      x.hi[i] = Ds[(32 * cb + 16 + 4 * g + i) * VP + vv];
+    }
+    dof[(hs * NV * 2 + f) * 64 + lane] = x;
+  }
+  __syncthreads();
+  // w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
+  // into Qs, then w^T fragments (rows k, k over the chunk).
+  for (int f = wave; f < 4 * KB; f += 4) {
+    const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
+    float x[8];
+    frag_elems(wf[((hs * 4 + ct) * KB + kb) * 64 + lane], x);
+    *reinterpret_cast<f32x4*>(Qs + c * KP + 32 * kb + 4 * g) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(Qs + c * KP + 32 * kb + 16 + 4 * g) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+  __syncthreads();
+  for (int f = wave; f < KT * 2; f += 4) {
+    const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
+    Frag<float> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x.lo[i] = Qs[(32 * cb + 4 * g + i) * KP + kk];
+      x.hi[i] = Qs[(32 * cb + 16 + 4 * g + i) * KP + kk];
+    }
+    wtf[(hs * KT * 2 + f) * 64 + lane] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward state pass: one wave per (sequence, value head, 16 value columns),
+// chunks in reverse order; dL/dH (K x 16, fp32) lives in registers as K/16 D
+// tiles (rows k, column v).  Per chunk: store dH (= dL/dH_{c+1}), then
+//   dv_new = dv_local + kd dH,  dH <- e^{G_last} dH + (scale e^G q)^T do - w^T dv_new.
+// After the first chunk dH is dL/dh0.
+template <int K, int V, bool VARLEN>
+__global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
+    Geo geo, const Frag<float>* __restrict__ kdf, const f32x4* __restrict__ dvl,
+    const Frag<float>* __restrict__ qtf, const Frag<float>* __restrict__ dof,
+    const Frag<float>* __restrict__ wtf, const float* __restrict__ gam,
+    const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
+    float* __restrict__ dhn, float* __restrict__ dvn) {
+  constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+  const int n = rest / NV, vt = rest - n * NV;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int lane = lane_id(), g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+
+  f32x4 dH[KT];
+  load_state<K, V>(dH, dht, sbase, v, g);
+  for (int s = s1 - 1; s >= s0; --s) {
+    const size_t hs = (size_t)hv * geo.slots + s;
+    float* hp = dhn + hs * K * V + v;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hp[(size_t)(16 * mt + 4 * g + r) * V] = dH[mt][r];
+    const float dec = fast_exp2(gam[hs * kChunk + kChunk - 1]);
+    f32x4 dv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      dv[ct] = dvl[((hs * NV + vt) * 4 + ct) * 64 + lane];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma_k32(dv[ct], kdf[((hs * 4 + ct) * KB + kb) * 64 + lane], Frag<float>{dH[2 * kb], dH[2 * kb + 1]});
+    }
+    float* vp = dvn + hs * kChunk * V + v;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vp[(size_t)(16 * ct + 4 * g + r) * V] = dv[ct][r];
+    const Frag<float> nb[2] = {Frag<float>{-dv[0], -dv[1]}, Frag<float>{-dv[2], -dv[3]}};
+    Frag<float> db[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) db[cb] = dof[((hs * NV + vt) * 2 + cb) * 64 + lane];
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      dH[mt] *= dec;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        mma_k32(dH[mt], qtf[((hs * KT + mt) * 2 + cb) * 64 + lane], db[cb]);
+        mma_k32(dH[mt], wtf[((hs * KT + mt) * 2 + cb) * 64 + lane], nb[cb]);
+      }
+    }
+  }
+  if (dh0) {
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dh0[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = dH[mt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq / dk / dw / dG, one workgroup per (chunk slot, value head).  Wave w owns
+// key columns [w K/4, (w+1) K/4) of the 64 x K results and row tile w of the
+// 64 x 64 ones.  The products over V run in two LDS stagings: (do, dv_new,
+// H_c) for dq_inter and dw, then (do, v_new, dH_{c+1}) for dPm and dk_kd; the
+// products over K and over the chunk then stage q and k.
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
+    Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
+    const int4* __restrict__ cmap, const float* __restrict__ gam, const float* __restrict__ vnp,
+    const float* __restrict__ dvn, const float* __restrict__ hcp, const float* __restrict__ dhn,
+    float* __restrict__ dqp, float* __restrict__ dkp, float* __restrict__ dwp,
+    float* __restrict__ dgp) {
+  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64;
+  constexpr int PH1 = 2 * kChunk * VP + K * VP, PH2 = 2 * kChunk * KP + kChunk * kCP;
+  __shared__ __align__(16) float lds[PH1 > PH2 ? PH1 : PH2];
+  __shared__ float sg[kChunk], dG[kChunk], red[2];
+  float* const Ds = lds;                    // do
+  float* const Xs = lds + kChunk * VP;      // dv_new, then v_new
+  float* const Hs = lds + 2 * kChunk * VP;  // H_c, then dH_{c+1}  [K][V]
+  float* const Qs = lds;
+  float* const Ks = lds + kChunk * KP;
+  float* const Pd = lds + 2 * kChunk * KP;
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+  const int kc0 = wave * (K / 4);
+  const float* Hc = hcp + hs * K * V;
+  const float* dHn = dhn + hs * K * V;
+
+  stage_rows<V>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_rows<V>(Xs, VP, dvn + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<V, float, K>(Hs, VP, Hc, 0, V, K);
+  if (tid < kChunk) {
+    sg[tid] = gam[hs * kChunk + tid];
+    dG[tid] = 0.f;
+  }
+  if (tid < 2) red[tid] = 0.f;
+  // <dH_{c+1}, H_c>, streamed from the workspace
+  {
+    float acc = 0.f;
+    for (int e = 4 * tid; e < K * V; e += 4 * 256) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Hc + e);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(dHn + e);
+      acc += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    }
+    acc = sum64(acc);
+    __syncthreads();  // red[] initialised
+    if (lane == 0) atomicAdd(&red[0], acc);
+  }
+  __syncthreads();
+  const float gl = sg[kChunk - 1];
+
+  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T on this wave's key
+  // columns (B operand: H_c rows k, contiguous in v).
+  f32x4 dq[4][NKT], dk[4][NKT];
+#pragma unroll
+  for (int nt = 0; nt < NKT; ++nt) {
+    const int kc = kc0 + 16 * nt;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      dq[it][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 dw = {0.f, 0.f, 0.f, 0.f};
+      mm16<V>(dq[it][nt], Ds + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+      mm16<V>(dw, Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g + r;
+        dq[it][nt][r] *= geo.scale * fast_exp2(sg[i]);
+        dwp[(hs * kChunk + i) * K + kc + lc] = -dw[r];
+      }
+    }
+  }
+  __syncthreads();
+  stage_rows<V>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<V, float, K>(Hs, VP, dHn, 0, V, K);
+  __syncthreads();
+  // dPm = scale (do v_new^T) * M * e^{dG}: row tile `wave`.
+  f32x4 dPm[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    dPm[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (jt <= wave) mm16<V>(dPm[jt], Ds + 16 * wave * VP, VP, 1, Xs + 16 * jt * VP, 1, VP);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * wave + 4 * g + r, j = 16 * jt + lc;
+      dPm[jt][r] = j <= i ? dPm[jt][r] * geo.scale * fast_exp2(sg[i] - sg[j]) : 0.f;
+    }
+  }
+  // dk_kd = e^{G_last - G} (v_new dH_{c+1}^T) on this wave's key columns.
+#pragma unroll
+  for (int nt = 0; nt < NKT; ++nt) {
+    const int kc = kc0 + 16 * nt;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      dk[it][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mm16<V>(dk[it][nt], Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[it][nt][r] *= fast_exp2(gl - sg[16 * it + 4 * g + r]);
+    }
+  }
+  __syncthreads();
+
+  stage_rows<K>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  __syncthreads();
+  // R = dPm * (Q K^T): dG_i += row sums, dG_j -= column sums; dPm to LDS.
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= wave) mm16<K>(s, Qs + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+    float cs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rr = dPm[jt][r] * s[r];
+      cs += rr;
+      const float rs = sum16(rr);
+      if (lc == 0) atomicAdd(&dG[16 * wave + 4 * g + r], rs);
+      Pd[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dPm[jt][r];
+    }
+    cs = sum_groups(cs);
+    if (g == 0) atomicAdd(&dG[16 * jt + lc], -cs);
+  }
+  // dG_i += q_i . dq_inter_i;  x_j = k_j . dk_kd_j: dG_j -= x_j, sum x -> red[1].
+  {
+    float xs = 0.f;
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g + r;
+        float qd = 0.f, kx = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NKT; ++nt) {
+          const int kk = kc0 + 16 * nt + lc;
+          qd += Qs[i * KP + kk] * dq[it][nt][r];
+          kx += Ks[i * KP + kk] * dk[it][nt][r];
+        }
+        qd = sum16(qd);
+        kx = sum16(kx);
+        if (lc == 0) atomicAdd(&dG[i], qd - kx);
+        xs += lc == 0 ? kx : 0.f;
+      }
+    xs = sum64(xs);
+    if (lane == 0) atomicAdd(&red[1], xs);
+  }
+  __syncthreads();
+  // dq += dPm K;  dk += dPm^T Q.
+#pragma unroll
+  for (int nt = 0; nt < NKT; ++nt) {
+    const int kc = kc0 + 16 * nt;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      mm16<kChunk>(dq[it][nt], Pd + 16 * it * kCP, kCP, 1, Ks + kc, KP, 1);
+      mm16<kChunk>(dk[it][nt], Pd + 16 * it, 1, kCP, Qs + kc, KP, 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t o = (hs * kChunk + 16 * it + 4 * g + r) * K + kc + lc;
+        dqp[o] = dq[it][nt][r];
+        dkp[o] = dk[it][nt][r];
+      }
+    }
+  }
+  if (tid < kChunk) {
+    float x = dG[tid];
+    if (tid == kChunk - 1) x += red[1] + fast_exp2(gl) * red[0];
+    dgp[hs * kChunk + tid] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WY backward, the chunk-local dG scan and the gate backward, one workgroup
+// per (chunk slot, value head).  Adds its dk terms to dkp; writes dv (dtype),
+// dbeta and dg_raw (fp32) for the chunk's tokens and the chunk's sums for
+// dA_log and ddt_bias.
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
+    Geo geo, const E* __restrict__ kg, const E* __restrict__ vg, const float* __restrict__ g_raw,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const int4* __restrict__ cmap, const float* __restrict__ gam, const float* __restrict__ bet,
+    const float* __restrict__ tmat, const float* __restrict__ dwp, const float* __restrict__ dvn,
+    const float* __restrict__ dgp, float* __restrict__ dkp, E* __restrict__ dvg,
+    float* __restrict__ dbeta, float* __restrict__ dg_raw, float* __restrict__ dAp,
+    float* __restrict__ dbp) {
+  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, NVT = V / 64;
+  __shared__ __align__(16) float Ks[kChunk * KP];
+  __shared__ __align__(16) float Vs[kChunk * VP];  // later dT, dS
+  __shared__ __align__(16) float Wd[kChunk * KP];
+  __shared__ __align__(16) float Dv[kChunk * VP];  // later Y
+  __shared__ __align__(16) float Tt[kChunk * kCP];
+  __shared__ float sg[kChunk], sb[kChunk], dG[kChunk], dB[kChunk];
+  float* const dTs = Vs;
+  float* const Ys = Dv;
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  const size_t hs = (size_t)hv * geo.slots + slot;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) {
+    if (threadIdx.x == 0) {
+      dAp[hs] = 0.f;
+      dbp[hs] = 0.f;
+    }
+    return;
+  }
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const int kc0 = wave * (K / 4), vc0 = wave * (V / 4);
+
+  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<V>(Vs, VP, vg + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_rows<K>(Wd, KP, dwp + hs * kChunk * K, 0, K, kChunk);
+  stage_rows<V>(Dv, VP, dvn + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<kChunk>(Tt, kCP, tmat + hs * kChunk * kChunk, 0, kChunk, kChunk);
+  if (tid < kChunk) {
+    sg[tid] = gam[hs * kChunk + tid];
+    sb[tid] = bet[hs * kChunk + tid];
+    dG[tid] = 0.f;
+    dB[tid] = 0.f;
+  }
+  __syncthreads();
+
+  // dT (strictly lower part; the rest does not reach dA): row tile `wave`.
+  f32x4 dT[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= wave) {
+      mm16<K>(a, Wd + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+      mm16<V>(b, Dv + 16 * wave * VP, VP, 1, Vs + 16 * jt * VP, 1, VP);
+    }
+    const int j = 16 * jt + lc;
+    const float fw = sb[j] * fast_exp2(sg[j]), fu = sb[j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * wave + 4 * g + r;
+      dT[jt][r] = j < i ? a[r] * fw + b[r] * fu : 0.f;
+    }
+  }
+  // X_w = T^T dw (this wave's key columns): dk += beta e^G X_w and the
+  // k . X_w terms of dbeta and dG.
+  f32x4 dk[4][NKT];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      dk[jt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mm16<kChunk>(dk[jt][nt], Tt + 16 * jt, 1, kCP, Wd + kc0 + 16 * nt, KP, 1);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jt + 4 * g + r;
+      const float eg = fast_exp2(sg[j]);
+      float kx = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) kx += Ks[j * KP + kc0 + 16 * nt + lc] * dk[jt][nt][r];
+      kx = sum16(kx);
+      if (lc == 0) {
+        atomicAdd(&dB[j], eg * kx);
+        atomicAdd(&dG[j], sb[j] * eg * kx);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) dk[jt][nt][r] *= sb[j] * eg;
+    }
+  }
+  // X_u = T^T dv_new: dv = beta X_u, the v . X_u term of dbeta.
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 xu[NVT];
+#pragma unroll
+    for (int nv = 0; nv < NVT; ++nv) {
+      xu[nv] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mm16<kChunk>(xu[nv], Tt + 16 * jt, 1, kCP, Dv + vc0 + 16 * nv, VP, 1);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jt + 4 * g + r;
+      float vx = 0.f;
+#pragma unroll
+      for (int nv = 0; nv < NVT; ++nv) {
+        const int vv = vc0 + 16 * nv + lc;
+        vx += Vs[j * VP + vv] * xu[nv][r];
+        if (j < len) dvg[((t0 + j) * geo.HV + hv) * V + vv] = (E)(sb[j] * xu[nv][r]);
+      }
+      vx = sum16(vx);
+      if (lc == 0) atomicAdd(&dB[j], vx);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dTs[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dT[jt][r];
+  __syncthreads();
+  // Y = T^T dT (row tile `wave`).
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    mm16<kChunk>(y, Tt + 16 * wave, 1, kCP, dTs + 16 * jt, kCP, 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ys[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = y[r];
+  }
+  __syncthreads();
+  // dA = -strictly_lower(Y T^T); with S = K K^T and A = beta_i e^{dG} S:
+  // dG += rows - columns of dA * A, dbeta += rows of dA e^{dG} S, dS = dA beta e^{dG}.
+  f32x4 dS[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 y = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= wave) {
+      mm16<kChunk>(y, Ys + 16 * wave * kCP, kCP, 1, Tt + 16 * jt * kCP, 1, kCP);
+      mm16<K>(s, Ks + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+    }
+    const int c = 16 * jt + lc;
+    float cs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = 16 * wave + 4 * g + r;
+      // above the diagonal e^{G_a - G_c} can overflow: select, never multiply by 0
+      const float da = c < a ? -y[r] : 0.f;
+      const float e = c < a ? fast_exp2(sg[a] - sg[c]) : 0.f;
+      const float des = da * e * s[r];
+      const float z = des * sb[a];
+      cs += z;
+      const float rz = sum16(z), rb = sum16(des);
+      if (lc == 0) {
+        atomicAdd(&dG[a], rz);
+        atomicAdd(&dB[a], rb);
+      }
+      dS[jt][r] = da * sb[a] * e;
+    }
+    cs = sum_groups(cs);
+    if (g == 0) atomicAdd(&dG[c], -cs);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dTs[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dS[jt][r];
+  __syncthreads();
+  // dk += (dS + dS^T) K; add the dq/dk kernel's terms and store.
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const int kc = kc0 + 16 * nt;
+      mm16<kChunk>(dk[jt][nt], dTs + 16 * jt * kCP, kCP, 1, Ks + kc, KP, 1);
+      mm16<kChunk>(dk[jt][nt], dTs + 16 * jt, 1, kCP, Ks + kc, KP, 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t o = (hs * kChunk + 16 * jt + 4 * g + r) * K + kc + lc;
+        dkp[o] += dk[jt][nt][r];
+      }
+    }
+  __syncthreads();
+  // dg = reversed chunk-local cumsum of dG; gate backward.
+  if (wave == 0) {
+    float x = dG[lane] + dgp[hs * kChunk + lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (lane + off < 64) x += y;
+    }
+    float sa = 0.f, sbias = 0.f;
+    if (lane < len) {
+      const int64_t t = t0 + lane;
+      const float xr = g_raw[t * geo.HV + hv] + (dt_bias ? dt_bias[hv] : 0.f);
+      const float ea = expf(A_log[hv]);
+      const float gt = -ea * gate_softplus(xr);
+      const float slope = xr > 20.f ? 1.f : 1.f / (1.f + fast_exp2(-xr * kLog2e));
+      const float dgr = x * (-ea) * slope;
+      dbeta[t * geo.HV + hv] = dB[lane];
+      dg_raw[t * geo.HV + hv] = dgr;
+      sa = x * gt;
+      sbias = dgr;
+    }
+    sa = sum64(sa);
+    sbias = sum64(sbias);
+    if (lane == 0) {
+      dAp[hs] = sa;
+      dbp[hs] = sbias;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq, dk of key head h: the sum of its G value heads' terms, in head order,
+// rounded to the dtype.  One workgroup per (chunk slot, key head).
+template <typename E, int K, bool VARLEN>
+__global__ __launch_bounds__(256) void gdn_bwd_qk_sum_kernel(Geo geo, const int4* __restrict__ cmap,
+                                                             const float* __restrict__ dqp,
+                                                             const float* __restrict__ dkp,
+                                                             E* __restrict__ dqg, E* __restrict__ dkg) {
+  const int slot = blockIdx.x % geo.slots, h = blockIdx.x / geo.slots;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  for (int e = threadIdx.x; e < len * K; e += 256) {
+    const int c = e / K, kk = e - c * K;
+    float sq = 0.f, sk = 0.f;
+    for (int r = 0; r < geo.G; ++r) {
+      const size_t o = (((size_t)(h * geo.G + r) * geo.slots + slot) * kChunk + c) * K + kk;
+      sq += dqp[o];
+      sk += dkp[o];
+    }
+    const size_t d = ((t0 + c) * geo.H + h) * K + kk;
+    dqg[d] = (E)sq;
+    dkg[d] = (E)sk;
+  }
+}
+
+// dA_log[hv], ddt_bias[hv]: sums of the per-chunk terms over the slots in slot
+// order (a fixed tree per thread count), one workgroup per value head.
+__global__ __launch_bounds__(256) void gdn_bwd_param_kernel(Geo geo, const float* __restrict__ dAp,
+                                                            const float* __restrict__ dbp,
+                                                            float* __restrict__ dA_log,
+                                                            float* __restrict__ ddt_bias) {
+  __shared__ float sa[4], sb[4];
+  const int hv = blockIdx.x, tid = threadIdx.x;
+  float a = 0.f, b = 0.f;
+  for (int s = tid; s < geo.slots; s += 256) {
+    a += dAp[(size_t)hv * geo.slots + s];
+    b += dbp[(size_t)hv * geo.slots + s];
+  }
+  a = sum64(a);
+  b = sum64(b);
+  if ((tid & 63) == 0) {
+    sa[tid >> 6] = a;
+    sb[tid >> 6] = b;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dA_log[hv] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    if (ddt_bias) ddt_bias[hv] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+  }
+}
+
+}  // namespace gdn

@@ -174,7 +174,9 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 //   ktf [hv][slot][mt<K/16][cb<2][lane]   A operand of  kd^T v_new (rows K, k over c)
 //   uf  [hv][slot][vt<V/16][cp<2][lane][2] D tiles ct = 2cp, 2cp+1 of u (rows c, column v);
 //                                         a lane's pair is one fragment-sized block
-template <typename E, int K, int V, bool VARLEN>
+// With STORE_T, T itself (lower triangular, fp32, [hv][slot][64][64] row-major,
+// zeros above the diagonal) is also written to tmat, for the backward pass.
+template <typename E, int K, int V, bool VARLEN, bool STORE_T = false>
 __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
                                                      const float* __restrict__ g_raw,
@@ -186,7 +188,8 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
                                                      float* __restrict__ bet,
                                                      Frag<E>* __restrict__ wf,
                                                      Frag<E>* __restrict__ ktf,
-                                                     Quad<E>* __restrict__ uf) {
+                                                     Quad<E>* __restrict__ uf,
+                                                     float* __restrict__ tmat) {
   constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
   constexpr int KS = K + P;          // K natural row stride
   constexpr int CS = kChunk + P;     // K^T, V^T row stride
@@ -361,6 +364,17 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     __syncthreads();
   }
 
+  if constexpr (STORE_T) {
+#pragma unroll
+    for (int it = 0; it < kChunk * kChunk / 4 / 256; ++it) {
+      const int e4 = tid + 256 * it, i = e4 >> 4, j = (e4 & 15) << 2;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      // blocks right of the diagonal block were never written
+      const f32x4 x = (j >> 4) <= (i >> 4) ? *reinterpret_cast<const f32x4*>(Ts + i * FS + j) : zero;
+      *reinterpret_cast<f32x4*>(tmat + hs * kChunk * kChunk + i * kChunk + j) = x;
+    }
+  }
+
   // Wave w owns chunk rows 16w..16w+15.  Its k32 fragments of T diag(beta e^G)
   // and T diag(beta) over the chunk index (row 16w + lane%16, columns
   // 32cb + kslot(g, i)) are formed from T in registers.
@@ -443,7 +457,10 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 // CHAIN_END: the same arithmetic without those stores (only the end state is
 // kept).  CHAIN_MAP: u taken as 0 and no stores; started from the identity
 // (with V = K), the end state is the chunks' composed linear map M.
-enum { CHAIN_FULL = 0, CHAIN_END = 1, CHAIN_MAP = 2 };
+// CHAIN_PLAIN: the CHAIN_FULL arithmetic, storing H_c and v_new in fp32 plain
+// row-major layouts instead (hcf, vnf then point at float arrays
+// [hv][slot][K][V] and [hv][slot][64][V]); the backward pass reads them.
+enum { CHAIN_FULL = 0, CHAIN_END = 1, CHAIN_MAP = 2, CHAIN_PLAIN = 3 };
 
 template <typename E, int K, int V, int MODE = CHAIN_FULL>
 struct ChainStep {
@@ -482,9 +499,9 @@ struct ChainStep {
   // First half of a chunk: emits H_c (the state on entry) and v_new = u - w H_c
   // through the sinks put_hc(kb, fragment) / put_vn(cb, fragment), and returns
   // v_new as the two B fragments of the state update.  Uses w and u.
-  template <typename PutH, typename PutV>
+  template <typename PutH, typename PutV, typename PutVF>
   __device__ __forceinline__ void vnew(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2], PutH&& put_hc,
-                                       PutV&& put_vn) const {
+                                       PutV&& put_vn, PutVF&& put_vf) const {
     Frag<E> hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -501,23 +518,44 @@ struct ChainStep {
         mma_k32(p0, w[2 * cb][kb], hb[kb]);
         mma_k32(p1, w[2 * cb + 1][kb], hb[kb]);
       }
-      vb[cb] = frag_from_tiles<E>(quad_f32(u[2 * cb]) - p0, quad_f32(u[2 * cb + 1]) - p1);
+      const f32x4 d0 = quad_f32(u[2 * cb]) - p0, d1 = quad_f32(u[2 * cb + 1]) - p1;
+      vb[cb] = frag_from_tiles<E>(d0, d1);
       put_vn(cb, vb[cb]);
+      put_vf(cb, d0, d1);
     }
   }
 
   // vnew with H_c and v_new stored straight to their fragment-major arrays
-  // (CHAIN_FULL), or not stored at all (the other modes).
+  // (CHAIN_FULL), in fp32 plain layouts (CHAIN_PLAIN), or not stored at all
+  // (the other modes).
   __device__ __forceinline__ void vnew_global(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2],
                                               Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf,
                                               size_t hs, int vt, int lane) const {
+    auto none_f = [](int, const Frag<E>&) {};
+    auto none_t = [](int, const f32x4&, const f32x4&) {};
     if constexpr (MODE == CHAIN_FULL) {
       Frag<E>* hc = hcf + (hs * NV + vt) * KB * 64 + lane;
       Frag<E>* vn = vnf + (hs * NV + vt) * 2 * 64 + lane;
       vnew(Hs, vb, [&](int kb, const Frag<E>& f) { hc[kb * 64] = f; },
-           [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; });
+           [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; }, none_t);
+    } else if constexpr (MODE == CHAIN_PLAIN) {
+      // D tile element r of lane (lc, g) is row 4g + r of the tile, column lc.
+      const int g = lane >> 4, v = 16 * vt + (lane & 15);
+      float* hp = reinterpret_cast<float*>(hcf) + hs * K * V + v;
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hp[(size_t)(16 * mt + 4 * g + r) * V] = Hs[mt][r];
+      float* vp = reinterpret_cast<float*>(vnf) + hs * kChunk * V + v;
+      vnew(Hs, vb, none_f, none_f, [&](int cb, const f32x4& d0, const f32x4& d1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          vp[(size_t)(32 * cb + 4 * g + r) * V] = d0[r];
+          vp[(size_t)(32 * cb + 16 + 4 * g + r) * V] = d1[r];
+        }
+      });
     } else {
-      vnew(Hs, vb, [](int, const Frag<E>&) {}, [](int, const Frag<E>&) {});
+      vnew(Hs, vb, none_f, none_f, none_t);
     }
   }
 

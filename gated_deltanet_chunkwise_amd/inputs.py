@@ -14,6 +14,10 @@ dt_bias, h0, lengths):
   h0       ~ N(0, 0.1^2) fp32 [N,HV,K,V] when requested
   packed lengths: N-1 integers U[lo, hi]; the last is T - sum, accepted when
              it also lies in [lo, hi] (else all are redrawn).
+Backward seeds (make_grads, a second Generator seeded separately, draw order
+d_o, d_final_state):
+  d_o      ~ N(0,1), cast to the workload dtype   [B,T,HV,V]
+  d_final_state ~ N(0, 0.1^2) fp32                [N,HV,K,V] when requested
 """
 import dataclasses
 
@@ -123,3 +127,16 @@ def workload_inputs(name, **overrides):
     cfg.update(overrides)
     seed = cfg.pop("seed", SEEDS[name])
     return make_inputs(seed=seed, **cfg)
+
+
+def make_grads(inp, seed, final_state_grad=True):
+    """Seeded output gradients for the backward pass: (d_o, d_final_state or None)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    s = inp.shape
+    d_o = torch.randn((s["B"], s["T"], s["HV"], s["V"]), generator=gen,
+                      dtype=torch.float32).to(inp.q.dtype)
+    dht = None
+    if final_state_grad:
+        dht = 0.1 * torch.randn((s["N"], s["HV"], s["K"], s["V"]), generator=gen,
+                                dtype=torch.float32)
+    return d_o, dht

@@ -207,6 +207,70 @@ gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
                             float *final_state, void *workspace, size_t workspace_bytes,
                             unsigned stage_mask, void *stream);
 
+/* ---- Backward pass ------------------------------------------------------------
+ * Gradients of the forward pass for the scalar
+ *     L = sum_t <d_o_t, o_t> + <d_final_state, final_state>,
+ * i.e. given d_o = dL/do and d_final_state = dL/d(final state), returns
+ * dL/dq, dL/dk, dL/dv, dL/dg_raw, dL/dbeta, dL/dA_log, dL/ddt_bias and
+ * dL/d(initial state).  The pages list the kernels of this pass (per-chunk dv,
+ * dq/dk/dw/dg, dg, the WY backward and the state recurrence's dh/du: the Ascend
+ * GDN blog, "Ascend-affine tiling", and the G_T_CONTIG page, "fix" and
+ * "correctness gates", which checks it against automatic differentiation);
+ * their formulas are the derivative of the chunk form of the forward pass.  It
+ * recomputes the forward intermediates (WY, the state pass) and then runs, on
+ * `stream`: the per-chunk dv_local and operand preparation, the state-gradient
+ * pass backwards over each sequence's chunks, the per-chunk dq/dk/dw/dg, the
+ * WY backward with the gate backward, and the per-key-head dq/dk sums and
+ * per-head dA_log/ddt_bias sums.  Arithmetic is fp32 (fp32 MFMA).
+ *   p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state:
+ *            exactly as for gdn_fwd (p->seg_chunks is not used: both state
+ *            passes here run sequentially over each sequence)
+ *   d_o            [B][T][HV][V]   dtype
+ *   d_final_state  [N][HV][K][V]   fp32, or NULL (zero)
+ *   dq, dk         [B][T][H][K]    dtype, written (sums over the value heads
+ *                                  that read each key head)
+ *   dv             [B][T][HV][V]   dtype, written
+ *   dg_raw, dbeta  [B][T][HV]      fp32, written
+ *   dA_log         [HV]            fp32, written
+ *   ddt_bias       [HV]            fp32, written, or NULL (not computed); with
+ *                                  dt_bias NULL it is the gradient at a zero bias
+ *   d_initial_state [N][HV][K][V]  fp32, written, or NULL (not computed)
+ *   workspace      gdn_bwd_workspace_size() bytes, 256-byte aligned
+ * Alignment: q, k, v, d_o, dq, dk, dv 16 bytes; fp32 arrays 4 bytes;
+ * cu_seqlens 8; workspace 256.  Errors as for gdn_fwd (GDN_ERR_NULL also for
+ * d_o, dq, dk, dv, dg_raw, dbeta with tokens present, and for dA_log), all
+ * checked before anything is enqueued.  Outputs must not overlap inputs or
+ * each other.  Partial sums inside the workgroups use LDS atomics, so the low
+ * bits of the fp32 results may differ between runs.  Enqueued on `stream`
+ * (hipStream_t); returns without waiting; allocates nothing. */
+size_t gdn_bwd_workspace_size(const gdn_params_t *p, int packed);
+
+gdn_status_t gdn_bwd(const gdn_params_t *p, const void *q, const void *k, const void *v,
+                     const float *g_raw, const float *beta, const float *A_log,
+                     const float *dt_bias, const int64_t *cu_seqlens,
+                     const float *initial_state, const void *d_o,
+                     const float *d_final_state, void *dq, void *dk, void *dv,
+                     float *dg_raw, float *dbeta, float *dA_log, float *ddt_bias,
+                     float *d_initial_state, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Stages gdn_bwd_timed brackets with events: forward recompute (chunk map, WY,
+ * state pass), dv_local preparation, backward state pass, dq/dk, WY backward,
+ * sums. */
+#define GDN_BWD_NUM_STAGES 6
+
+/* gdn_bwd recording events[0] before the first kernel and events[i] after
+ * stage i (GDN_BWD_NUM_STAGES + 1 hipEvent_t created by the caller; NULL makes
+ * it gdn_bwd). */
+gdn_status_t gdn_bwd_timed(const gdn_params_t *p, const void *q, const void *k,
+                           const void *v, const float *g_raw, const float *beta,
+                           const float *A_log, const float *dt_bias,
+                           const int64_t *cu_seqlens, const float *initial_state,
+                           const void *d_o, const float *d_final_state, void *dq, void *dk,
+                           void *dv, float *dg_raw, float *dbeta, float *dA_log,
+                           float *ddt_bias, float *d_initial_state, void *workspace,
+                           size_t workspace_bytes, void *stream, void *const *events);
+
 /* ---- Recurrent step (decode) ---------------------------------------------------
  * The state updated token by token, as the Ascend GDN blog describes the
  * recurrence ("GDN sequence structure and Triton introduction": one state per

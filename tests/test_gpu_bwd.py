@@ -1,0 +1,157 @@
+"""Backward pass (gdn_bwd) vs the fp64 oracle's reverse-mode derivative, on the
+same rounded inputs and output gradients.
+
+Tolerances per gradient tensor: fp32 rel-L2 <= 1e-4; bf16 rel-L2 <= 1e-2 and
+max-abs <= 2e-2 relative to max(1, max |reference|) (gradients are not O(1) in
+scale the way o is).  dA_log[hv] and ddt_bias[hv] are sums over every token of
+the head, whose terms cancel: their error is bounded against the sum of the
+terms' magnitudes (the sum's condition), at the same relative tolerances.
+Outputs are NaN-filled before each call, so any element the kernels fail to
+write fails the comparison.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_chunkwise_amd as gdn
+import oracle
+from gated_deltanet_chunkwise_amd.inputs import make_grads, make_inputs, workload_inputs
+from gpu_helpers import f64, metrics, say
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = "bf16", "fp32"
+TOL = {torch.float32: (1e-4, None), torch.bfloat16: (1e-2, 2e-2)}
+NAMES = ("dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "ddt_bias", "dh0")
+
+
+def run_gpu_bwd(inp, d_o, dht):
+    d = inp.to("cuda")
+    s = inp.shape
+    plan = gdn.GdnBackward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype,
+                           d.q.device, num_seqs=None if d.cu_seqlens is None else s["N"],
+                           scale=d.scale)
+    for t in plan.grads().values():
+        t.fill_(float("nan"))
+    out = plan(d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d_o.cuda(),
+               None if dht is None else dht.cuda(), d.cu_seqlens, d.h0)
+    torch.cuda.synchronize()
+    return {n: f64(t) for n, t in out.items()}
+
+
+def run_oracle_bwd(inp, d_o, dht, units=None):
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    # without dt_bias the library returns the gradient at a zero bias
+    bias = f64(inp.dt_bias) if inp.dt_bias is not None else np.zeros(inp.shape["HV"])
+    return oracle.bwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.g_raw), f64(inp.beta),
+                      f64(inp.A_log), bias, f64(d_o), f64(dht), cu_seqlens=cu,
+                      h0=f64(inp.h0), scale=inp.scale, units=units)
+
+
+def param_term_scale(inp, ref):
+    """Per value head, the sums of |terms| of dA_log and ddt_bias.  Per token
+    ddt_bias gathers dg_raw and dA_log gathers dg g = dg_raw softplus(x) /
+    softplus'(x) (x = g_raw + dt_bias), from the oracle's dg_raw."""
+    HV = inp.shape["HV"]
+    x = f64(inp.g_raw).reshape(-1, HV)
+    if inp.dt_bias is not None:
+        x = x + f64(inp.dt_bias)[None, :]
+    sp = np.where(x > 20, x, np.log1p(np.exp(np.minimum(x, 20))))
+    slope = np.where(x > 20, 1.0, 1.0 / (1.0 + np.exp(-x)))
+    dgr = np.asarray(ref["dg_raw"]).reshape(-1, HV)
+    return dict(dA_log=np.sum(np.abs(dgr * sp / slope), 0), ddt_bias=np.sum(np.abs(dgr), 0))
+
+
+def compare(got, ref, dtype, tag, names=NAMES, term_scale=None):
+    """Every gradient is reported before the first failure is raised."""
+    rel, mab = TOL[dtype]
+    bad = []
+    for n in names:
+        x, r = np.asarray(got[n]), np.asarray(ref[n])
+        if not np.all(np.isfinite(x)):
+            bad.append((n, "non-finite values", int(np.sum(~np.isfinite(x)))))
+            continue
+        if term_scale is not None and n in term_scale:
+            err = np.max(np.abs(x - r) / np.maximum(term_scale[n], 1e-30))
+            say("  %-34s err/sum|terms|=%.3e" % (tag + " " + n, err))
+            if err > rel:
+                bad.append((n, float(err)))
+            continue
+        m = metrics(x, r)
+        scale = max(1.0, float(np.max(np.abs(r)))) if r.size else 1.0
+        say("  %-34s rel_l2=%.3e max_abs/scale=%.3e" % (tag + " " + n, m["rel_l2"],
+                                                        m["max_abs"] / scale))
+        if m["rel_l2"] > rel or (mab is not None and m["max_abs"] > mab * scale):
+            bad.append((n, m))
+    assert not bad, (tag, bad)
+
+
+def check_full(inp, tag, seed, dht=True):
+    say("case", tag, inp.shape)
+    d_o, d_ht = make_grads(inp, seed, final_state_grad=dht)
+    got = run_gpu_bwd(inp, d_o, d_ht)
+    ref = run_oracle_bwd(inp, d_o, d_ht)
+    compare(got, ref, inp.q.dtype, tag, term_scale=param_term_scale(inp, ref))
+
+
+def test_tiny_fp32_workload():
+    check_full(workload_inputs("tiny_fp32", h0=True), "bwd tiny_fp32", 501)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_ragged_gqa_h0(dtype, K, V):
+    # 300 = 4 full chunks + a 44-token tail; 2 value heads per key head
+    inp = make_inputs(B=2, T=300, H=2, HV=4, K=K, V=V, dtype=dtype, seed=600 + K + V, h0=True,
+                      scale=0.75)
+    check_full(inp, "bwd ragged_gqa_%s_K%d_V%d" % (dtype, K, V), 700 + K + V)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_packed_with_empty_sequence(dtype):
+    # lengths with an empty sequence, a 1-token one and ragged tails
+    inp = make_inputs(B=1, T=600, H=1, HV=2, K=128, V=128, dtype=dtype, seed=611, h0=True,
+                      lengths=[130, 0, 1, 64, 305, 100])
+    check_full(inp, "bwd packed_%s" % dtype, 612)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_no_state_no_bias(dtype):
+    # zero initial state, no final-state gradient, no dt_bias
+    inp = make_inputs(B=1, T=200, H=2, HV=2, K=64, V=64, dtype=dtype, seed=621)
+    inp.dt_bias = None
+    check_full(inp, "bwd plain_%s" % dtype, 622, dht=False)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_pages_workload_sampled_heads(dtype):
+    """The pages' shape (B=2, T=2048, H=HV=8, K=V=128; bf16 as benchmarked, and
+    fp32), every gradient of two sampled value heads (all sequences, so
+    dA_log/ddt_bias are complete)."""
+    inp = workload_inputs("pages_bf16", dtype=dtype)
+    s = inp.shape
+    d_o, dht = make_grads(inp, 631)
+    got = run_gpu_bwd(inp, d_o, dht)
+    for hv in (2, 7):
+        units = [n * s["HV"] + hv for n in range(s["N"])]
+        ref = run_oracle_bwd(inp, d_o, dht, units=units)
+        ts = {k: v[hv:hv + 1] for k, v in param_term_scale(inp, ref).items()}
+        sub = lambda d: dict(  # noqa: E731
+            dq=d["dq"][:, :, hv], dk=d["dk"][:, :, hv], dv=d["dv"][:, :, hv],
+            dg_raw=d["dg_raw"][:, :, hv], dbeta=d["dbeta"][:, :, hv],
+            dA_log=d["dA_log"][hv:hv + 1], ddt_bias=d["ddt_bias"][hv:hv + 1],
+            dh0=d["dh0"][:, hv])
+        compare(sub(got), sub(ref), inp.q.dtype, "bwd pages %s hv=%d" % (dtype, hv),
+                term_scale=ts)
+
+
+def test_repeat_calls_agree():
+    """Two calls on one plan (workspace reused) give the same gradients up to
+    the order of the in-workgroup fp32 atomics."""
+    inp = make_inputs(B=1, T=256, H=1, HV=1, K=64, V=64, dtype=F32, seed=641, h0=True)
+    d_o, dht = make_grads(inp, 642)
+    a = run_gpu_bwd(inp, d_o, dht)
+    b = run_gpu_bwd(inp, d_o, dht)
+    for n in NAMES:
+        m = metrics(a[n], b[n])
+        assert m["rel_l2"] <= 1e-6, (n, m)
