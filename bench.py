@@ -1,5 +1,6 @@
 #!/usr/bin/env python3
-"""Throughput of the GDN chunkwise forward pass on one MI355X.
+"""Throughput of the GDN chunkwise forward pass on one MI355X (--op selects
+the backward pass, the KDA gate or the decode step instead).
 
 One step = one gdn_fwd call (chunk map when packed, gate prologue, WY, state
 pass, output) over one batch of seeded synthetic inputs that are already
@@ -33,10 +34,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pages_bf16")
-    ap.add_argument("--op", default="gdn_fwd", choices=["gdn_fwd", "kda_gate", "decode"],
-                    help="gdn_fwd: the forward pass (headline); kda_gate: the KDA per-channel "
-                         "gate on the guide's timing shape; decode: one recurrent step for a "
-                         "batch of sequences")
+    ap.add_argument("--op", default="gdn_fwd", choices=["gdn_fwd", "gdn_bwd", "kda_gate", "decode"],
+                    help="gdn_fwd: the forward pass (headline); gdn_bwd: the backward pass "
+                         "(forward recompute included) on --workload; kda_gate: the KDA "
+                         "per-channel gate on the guide's timing shape; decode: one recurrent "
+                         "step for a batch of sequences")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-chunks", type=int, default=0,
                     help="segment-parallel state pass with segments of this many chunks (0: off)")
@@ -92,10 +94,51 @@ def algorithmic(shape, esz, has_h0, used_slots):
     return kern, path, ntok
 
 
+def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
+    """Algorithmic bytes and flops per launch of each backward stage (the
+    forward-recompute stage is two kernels, WY and the state pass), and of the
+    whole pass.  fp32 intermediates count at 4 bytes; triangular products by
+    their nonzero half."""
+    B, T, H, HV, K, V, N = (shape[k] for k in ("B", "T", "H", "HV", "K", "V", "N"))
+    ntok = T if shape.get("packed") else B * T
+    U = ntok * HV
+    Ck = used_slots * HV
+    state = N * HV * K * V * 4
+    C = CHUNK
+    k_in = ntok * H * K * esz
+    fwd, _, _ = algorithmic(shape, esz, has_h0, used_slots)
+    kern = {
+        "recompute": dict(
+            bytes=fwd["wy"]["bytes"] + Ck * C * C * 4 + U * (2 * K + V) * esz + Ck * 4
+            + (state if has_h0 else 0) + Ck * K * V * 4 + U * V * 4,
+            flops=fwd["wy"]["flops"] + U * 4 * K * V),
+        "prep": dict(bytes=2 * k_in + U * V * esz + U * 4 + U * K * esz + 2 * U * K * esz
+                     + Ck * K * V * 4 + U * V * 4,
+                     flops=U * C * (K + V) + U * 2 * K * V),
+        "bwd_chain": dict(bytes=2 * U * K * esz + Ck * K * V * 4 + U * V * 4 + Ck * 4
+                          + (state if has_dht else 0) + Ck * K * V * 4 + U * V * 4 + state,
+                          flops=U * 4 * K * V),
+        "dqk": dict(bytes=2 * k_in + U * V * esz + 2 * U * V * 4 + 2 * Ck * K * V * 4 + U * 4
+                    + 3 * U * K * 4 + U * 4,
+                    flops=U * (6 * K * V + C * V + 3 * C * K)),
+        "bwd_wy": dict(bytes=k_in + U * V * esz + 2 * U * K * 4 + U * V * 4 + Ck * C * C * 4
+                       + 4 * U * 4 + U * K * 4 + U * V * esz + 2 * U * 4 + 2 * Ck * 4,
+                       flops=U * (2 * C * (K + V) + 2 * C * C // 3 + 3 * C * K)),
+        "sums": dict(bytes=2 * U * K * 4 + 2 * k_in + 2 * Ck * 4 + 2 * HV * 4, flops=0),
+    }
+    path = dict(bytes=4 * k_in + 3 * U * V * esz + 4 * U * 4 + (state if has_h0 else 0)
+                + (state if has_dht else 0) + state,
+                flops=sum(v["flops"] for v in kern.values()))
+    return kern, path, ntok
+
+
 KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
                 ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
                 ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
-                ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"))
+                ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"),
+                ("gdn_bwd_prep_kernel", "prep"), ("gdn_bwd_chain_kernel", "bwd_chain"),
+                ("gdn_bwd_dqk_kernel", "dqk"), ("gdn_bwd_wy_kernel", "bwd_wy"),
+                ("gdn_bwd_qk_sum_kernel", "sums"))
 
 
 def counter_means(path):
@@ -361,6 +404,138 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_bwd(args):
+    """One JSON line for the backward pass on --workload: tokens/s, per-stage
+    durations (HIP events recorded by gdn_bwd_timed on the launch stream), the
+    roofline of the dominant stage, and the fp64 oracle's backward on the host."""
+    import ctypes
+    import numpy as np
+    import torch
+    import gated_deltanet_chunkwise_amd as gdn
+    from gated_deltanet_chunkwise_amd.inputs import WORKLOADS, make_grads, workload_inputs
+    wl = args.workload
+    cfg = WORKLOADS[wl]
+    inp_cpu = workload_inputs(wl)
+    d_o_cpu, dht_cpu = make_grads(inp_cpu, SEEDS_BWD)
+    inp = inp_cpu.to("cuda")
+    d_o, dht = d_o_cpu.cuda(), dht_cpu.cuda()
+    s = inp.shape
+    packed = inp.cu_seqlens is not None
+    plan = gdn.GdnBackward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], inp.q.dtype,
+                           "cuda", num_seqs=s["N"] if packed else None, scale=inp.scale)
+    stream = torch.cuda.current_stream()
+    step = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias, d_o, dht,
+                     inp.cu_seqlens, inp.h0, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # per-stage durations: gdn_bwd_timed records an event after each stage
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(gdn.BWD_NUM_STAGES + 1)]
+    for e in evs:
+        e.record(stream)  # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    acc = [0.0] * gdn.BWD_NUM_STAGES
+    reps = max(1, args.steps // 4)
+    for _ in range(reps):
+        plan(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias, d_o, dht,
+             inp.cu_seqlens, inp.h0, stream=stream, events=handles)
+        torch.cuda.synchronize()
+        for i in range(gdn.BWD_NUM_STAGES):
+            acc[i] += evs[i].elapsed_time(evs[i + 1])
+    stage_ms = [a / reps for a in acc]
+    dtype = cfg["dtype"]
+    esz = 2 if dtype == "bf16" else 4
+    sh = dict(s, packed=packed)
+    if packed:
+        lens = (inp_cpu.cu_seqlens[1:] - inp_cpu.cu_seqlens[:-1]).tolist()
+        used = sum((L + CHUNK - 1) // CHUNK for L in lens)
+    else:
+        used = s["B"] * ((s["T"] + CHUNK - 1) // CHUNK)
+    kern, path, ntok = algorithmic_bwd(sh, esz, inp.h0 is not None, True, used)
+    kernels = {}
+    for name, t in zip(gdn.BWD_STAGES, stage_ms):
+        a = kern[name]
+        sec = t / 1e3
+        # the recompute (forward kernels) and the backward state pass multiply in
+        # the call's dtype; the other backward kernels in fp32
+        mdt = dtype if name in ("recompute", "bwd_chain") else "fp32"
+        kernels[name] = dict(us=round(t * 1e3, 3), bytes=a["bytes"], flops=a["flops"],
+                             hbm_gbs=round(a["bytes"] / sec / 1e9, 1),
+                             hbm_frac=round(a["bytes"] / sec / HBM_PEAK, 4),
+                             mfma_tflops=round(a["flops"] / sec / 1e12, 2),
+                             mfma_frac=round(a["flops"] / sec / MFMA_PEAK[mdt], 4),
+                             mfma_dtype=mdt)
+    single = [n for n in kernels if n != "recompute"]  # stages of one kernel
+    dom = max(single, key=lambda n: kernels[n]["us"])
+    d = kernels[dom]
+    mpk = MFMA_PEAK[d["mfma_dtype"]]
+    if d["flops"] / d["bytes"] >= mpk / HBM_PEAK:
+        roof = dict(bound="mfma", achieved=d["mfma_tflops"], peak=mpk / 1e12,
+                    unit="TFLOP/s", frac=d["mfma_frac"], dtype=d["mfma_dtype"])
+    else:
+        roof = dict(bound="hbm", achieved=d["hbm_gbs"], peak=HBM_PEAK / 1e9, unit="GB/s",
+                    frac=d["hbm_frac"])
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    src = source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            ent = json.load(fh).get(wl + ":bwd", {}).get(dom)
+        if ent and ent.get("source_hash") == src:
+            roof["traffic"] = ent["bytes_per_launch"]
+    sec = ms / 1e3
+    out = {
+        "metric": "GDN chunk-bwd tokens/s (%s)" % wl, "value": round(ntok / sec, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": wl, "B": s["B"], "T": s["T"], "H": s["H"], "HV": s["HV"],
+                   "K": s["K"], "V": s["V"], "chunk": CHUNK,
+                   "packed_seqs": s["N"] if packed else None,
+                   "initial_state": inp.h0 is not None, "final_state_grad": True},
+        "roofline": roof,
+        "path_roofline": {"bytes": path["bytes"], "flops": path["flops"],
+                          "hbm_frac": round(path["bytes"] / sec / HBM_PEAK, 4),
+                          "mfma_frac_fp32": round(path["flops"] / sec / MFMA_PEAK["fp32"], 4)},
+        "kernels": kernels,
+        "kernel_source_hash": src,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: None if t is None else t.float().numpy().astype(np.float64)  # noqa: E731
+        a = [f(inp_cpu.q), f(inp_cpu.k), f(inp_cpu.v), f(inp_cpu.g_raw), f(inp_cpu.beta),
+             f(inp_cpu.A_log), f(inp_cpu.dt_bias), f(d_o_cpu), f(dht_cpu)]
+        cu = None if inp_cpu.cu_seqlens is None else inp_cpu.cu_seqlens.numpy()
+        threads = oracle.default_threads()
+        oracle.load()
+        reps, total = 0, 0.0
+        while total < args.cpu_seconds:
+            t0 = time.perf_counter()
+            oracle.bwd(*a, cu_seqlens=cu, h0=f(inp_cpu.h0), scale=inp_cpu.scale,
+                       nthreads=threads)
+            total += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": reps * ntok / total, "unit": "tokens/s",
+            "cores": min(threads, s["N"] * s["HV"]), "kind": "oracle",
+            "sample": "whole workload (%d tokens x %d value heads), %d run(s), %.1f s; "
+                      "threads=%d" % (ntok, s["HV"], reps, total, threads)}
+    print(json.dumps(out), flush=True)
+
+
+SEEDS_BWD = 20290  # output-gradient seed of the backward benchmark
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -379,6 +554,9 @@ def main():
         return
     if args.op == "decode":
         bench_decode(args)
+        return
+    if args.op == "gdn_bwd":
+        bench_bwd(args)
         return
     import gated_deltanet_chunkwise_amd as gdn
     from gated_deltanet_chunkwise_amd.inputs import WORKLOADS, workload_inputs

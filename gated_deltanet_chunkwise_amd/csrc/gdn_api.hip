@@ -270,7 +270,7 @@ namespace {
 // Workspace of the backward pass: the forward layout (without segments), then
 // the backward's fp32 intermediates (see gdn_bwd.h).
 struct BwdLayout {
-  size_t tmat, hcp, vnp, qtf, wtf, kdf, dof, dvl, dhn, dvn, dqp, dkp, dwp, dgp, dAp, dbp, total;
+  size_t tmat, hcp, vnp, wtf, kdf, bq, dvl, dhn, dvn, dqp, dkp, dwp, dgp, dAp, dbp, total;
 };
 
 gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayout* bl) {
@@ -288,10 +288,9 @@ gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayo
   take(bl->tmat, C * C);
   take(bl->hcp, K * V);
   take(bl->vnp, C * V);
-  take(bl->qtf, K * C);
-  take(bl->wtf, K * C);
+  take(bl->wtf, K * C);  // fp32 size: also holds the dtype's fragments
   take(bl->kdf, C * K);
-  take(bl->dof, C * V);
+  take(bl->bq, K * V);
   take(bl->dvl, C * V);
   take(bl->dhn, K * V);
   take(bl->dvn, C * V);
@@ -355,7 +354,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   Quad<E>* uf = reinterpret_cast<Quad<E>*>(w + L.u);
   int4* cmap = VARLEN ? reinterpret_cast<int4*>(w + L.chunk_map) : nullptr;
   int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
-  auto FR = [&](size_t off) { return reinterpret_cast<Frag<float>*>(w + off); };
+  auto FE = [&](size_t off) { return reinterpret_cast<Frag<E>*>(w + off); };
   const E* qe = static_cast<const E*>(a.q);
   const E* ke = static_cast<const E*>(a.k);
   const E* ve = static_cast<const E*>(a.v);
@@ -384,13 +383,14 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   mark(1);
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,
-              doe, cmap, gam, wf, FR(bl.qtf), FR(bl.wtf), FR(bl.kdf), FR(bl.dof),
+              doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::f32x4*>(w + bl.bq),
               reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
   mark(2);
   if (units > 0)
-    ok(launch(gdn::gdn_bwd_chain_kernel<K, V, VARLEN>, dim3(units), dim3(64), s, geo, FR(bl.kdf),
-              reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FR(bl.qtf), FR(bl.dof), FR(bl.wtf),
-              gam, seq_slot, a.dht, a.dh0, F(bl.dhn), F(bl.dvn)));
+    ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,
+              FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
+              reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
+              F(bl.dhn), F(bl.dvn)));
   mark(3);
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,

@@ -36,21 +36,25 @@
 // (also storing T) and the state pass in its CHAIN_PLAIN mode (fp32 H_c and
 // v_new).
 //
-// Arithmetic is fp32 throughout (fp32 MFMA v_mfma_f32_16x16x4f32, operands
-// staged as fp32 in LDS); only q, k, v, do are read, and dq, dk, dv written, in
-// the call's dtype.  Intermediates in the workspace are fp32 row-major:
+// Arithmetic is fp32 (fp32 MFMA v_mfma_f32_16x16x4f32, operands staged as fp32
+// in LDS), except in the backward state pass, whose products take their
+// operands in the call's dtype like the forward state pass's (bf16 MFMA for
+// bf16 calls; the state gradient itself accumulates in fp32).  q, k, v, do are
+// read, and dq, dk, dv written, in the call's dtype.  Intermediates in the
+// workspace are fp32 row-major:
 //   hcp, dhn [hv][slot][K][V]          H_c, dL/dH_{c+1}
 //   vnp, dvn [hv][slot][64][V]         v_new, dL/dv_new
 //   tmat     [hv][slot][64][64]        T
 //   dqp, dkp, dwp [hv][slot][64][K]    per value head dq, dk; dw
 //   dgp      [hv][slot][64]            dG from the dq/dk kernel
 //   dAp, dbp [hv][slot]                per-chunk sums for dA_log, ddt_bias
-// and fragment-major operands of the backward state pass (fp32 k32 fragments
-// as in the forward state pass, lane l = row l%16, k-slot group l/16):
-//   qtf, wtf [hv][slot][K/16][2][lane]  A operands (rows k, k over the chunk):
-//                                       scale e^G q^T and w^T
+// and fragment-major operands of the backward state pass (k32 fragments in
+// the call's dtype as in the forward state pass, lane l = row l%16, k-slot
+// group l/16; D tiles fp32):
+//   wtf      [hv][slot][K/16][2][lane]  A operand (rows k, k over the chunk): w^T
 //   kdf      [hv][slot][4][K/32][lane]  A operand (rows c, k over K): kd
-//   dof      [hv][slot][V/16][2][lane]  B operand (k over the chunk, column v): do
+//   bq       [hv][slot][V/16][K/16][lane] D tiles (rows k, column v):
+//                                       scale (e^G * Q)^T do
 //   dvl      [hv][slot][V/16][4][lane]  D tiles (rows c, column v): dv_local
 #pragma once
 #include "gdn_kernels.h"
@@ -137,18 +141,19 @@ __device__ __forceinline__ void frag_elems(const Frag<float>& f, float (&x)[8]) 
 }
 
 // ---------------------------------------------------------------------------
-// Prep, one workgroup per (chunk slot, value head): dv_local and the operand
-// fragments of the backward state pass.
+// Prep, one workgroup per (chunk slot, value head): dv_local, the state pass's
+// dH term bq = scale (e^G * Q)^T do, and its kd and w^T operand fragments
+// (dtype E, as the forward state pass's operands).
 template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
     Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<E>* __restrict__ wf,
-    Frag<float>* __restrict__ qtf, Frag<float>* __restrict__ wtf, Frag<float>* __restrict__ kdf,
-    Frag<float>* __restrict__ dof, f32x4* __restrict__ dvl) {
+    Frag<E>* __restrict__ wtf, Frag<E>* __restrict__ kdf, f32x4* __restrict__ bq,
+    f32x4* __restrict__ dvl) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, KT = K / 16, KB = K / 32, NV = V / 16;
   __shared__ __align__(16) float Qs[kChunk * KP];  // q, later w
   __shared__ __align__(16) float Ks[kChunk * KP];
-  __shared__ __align__(16) float Ds[kChunk * VP];
+  __shared__ __align__(16) float Ds[kChunk * VP];  // do, later scale e^G do
   __shared__ __align__(16) float Ps[kChunk * kCP];
   __shared__ float sg[kChunk];
 
@@ -192,18 +197,6 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
       dvl[((hs * NV + vt) * 4 + ct) * 64 + lane] = acc * geo.scale;
     }
   }
-  // (scale e^G q)^T fragments (rows k, k over the chunk).
-  for (int f = wave; f < KT * 2; f += 4) {
-    const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
-    Frag<float> x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c0 = 32 * cb + 4 * g + i, c1 = c0 + 16;
-      x.lo[i] = geo.scale * fast_exp2(sg[c0]) * Qs[c0 * KP + kk];
-      x.hi[i] = geo.scale * fast_exp2(sg[c1]) * Qs[c1 * KP + kk];
-    }
-    qtf[(hs * KT * 2 + f) * 64 + lane] = x;
-  }
   // kd fragments (rows c, k over K).
   {
     const float gl = sg[kChunk - 1];
@@ -212,19 +205,22 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
       const float e = fast_exp2(gl - sg[c]);
       const f32x4 lo = *reinterpret_cast<const f32x4*>(Ks + c * KP + 32 * kb + 4 * g);
       const f32x4 hi = *reinterpret_cast<const f32x4*>(Ks + c * KP + 32 * kb + 16 + 4 * g);
-      kdf[((hs * 4 + ct) * KB + kb) * 64 + lane] = Frag<float>{lo * e, hi * e};
+      kdf[((hs * 4 + ct) * KB + kb) * 64 + lane] = frag_from_tiles<E>(lo * e, hi * e);
     }
   }
-  // do fragments (k over the chunk, column v).
-  for (int f = wave; f < NV * 2; f += 4) {
-    const int vt = f >> 1, cb = f & 1, vv = 16 * vt + lc;
-    Frag<float> x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x.lo[i] = Ds[(32 * cb + 4 * g + i) * VP + vv];
-      x.hi[i] = Ds[(32 * cb + 16 + 4 * g + i) * VP + vv];
-    }
-    dof[(hs * NV * 2 + f) * 64 + lane] = x;
+  __syncthreads();
+  // do rows times scale e^{G_c}, then bq = Q^T (scale e^G do): D tiles
+  // (rows k, column v).
+  for (int e = tid; e < kChunk * (V / 4); e += 256) {
+    const int c = e / (V / 4), v4 = 4 * (e - c * (V / 4));
+    *reinterpret_cast<f32x4*>(Ds + c * VP + v4) *= geo.scale * fast_exp2(sg[c]);
+  }
+  __syncthreads();
+  for (int f = wave; f < KT * NV; f += 4) {
+    const int mt = f / NV, vt = f - mt * NV;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mm16<kChunk>(acc, Qs + 16 * mt, 1, KP, Ds + 16 * vt, VP, 1);
+    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = acc;
   }
   __syncthreads();
   // w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
@@ -239,13 +235,13 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
   __syncthreads();
   for (int f = wave; f < KT * 2; f += 4) {
     const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
-    Frag<float> x;
+    f32x4 lo, hi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x.lo[i] = Qs[(32 * cb + 4 * g + i) * KP + kk];
-      x.hi[i] = Qs[(32 * cb + 16 + 4 * g + i) * KP + kk];
+      lo[i] = Qs[(32 * cb + 4 * g + i) * KP + kk];
+      hi[i] = Qs[(32 * cb + 16 + 4 * g + i) * KP + kk];
     }
-    wtf[(hs * KT * 2 + f) * 64 + lane] = x;
+    wtf[(hs * KT * 2 + f) * 64 + lane] = frag_from_tiles<E>(lo, hi);
   }
 }
 
@@ -253,13 +249,16 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
 // Backward state pass: one wave per (sequence, value head, 16 value columns),
 // chunks in reverse order; dL/dH (K x 16, fp32) lives in registers as K/16 D
 // tiles (rows k, column v).  Per chunk: store dH (= dL/dH_{c+1}), then
-//   dv_new = dv_local + kd dH,  dH <- e^{G_last} dH + (scale e^G q)^T do - w^T dv_new.
-// After the first chunk dH is dL/dh0.
-template <int K, int V, bool VARLEN>
+//   dv_new = dv_local + kd dH,   dH <- e^{G_last} dH + bq - w^T dv_new,
+// with kd, w^T and dH, dv_new as MFMA operands in the dtype E (as in the
+// forward state pass).  After the first chunk dH is dL/dh0.  The operands are
+// loaded in two halves, each right after its previous use, so that a half's
+// loads overlap the other half's products: (kd, dv_local) for v_new's product,
+// (w^T, bq, e^{G_last}) for the update.
+template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
-    Geo geo, const Frag<float>* __restrict__ kdf, const f32x4* __restrict__ dvl,
-    const Frag<float>* __restrict__ qtf, const Frag<float>* __restrict__ dof,
-    const Frag<float>* __restrict__ wtf, const float* __restrict__ gam,
+    Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
+    const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
     float* __restrict__ dhn, float* __restrict__ dvn) {
   constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
@@ -276,43 +275,70 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
   }
   const int lane = lane_id(), g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
   const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+  const size_t hbase = (size_t)hv * geo.slots;
 
   f32x4 dH[KT];
   load_state<K, V>(dH, dht, sbase, v, g);
+  Frag<E> kd[4][KB], wt[KT][2];
+  f32x4 dl[4], b[KT];
+  float gl = 0.f;
+  auto load_a = [&](size_t hs) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      dl[ct] = dvl[((hs * NV + vt) * 4 + ct) * 64 + lane];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kd[ct][kb] = kdf[((hs * 4 + ct) * KB + kb) * 64 + lane];
+    }
+  };
+  auto load_b = [&](size_t hs) {
+    gl = gam[hs * kChunk + lane];  // lane 63 holds the chunk's last cumulative gate
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+      b[mt] = bq[((hs * NV + vt) * KT + mt) * 64 + lane];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) wt[mt][cb] = wtf[((hs * KT + mt) * 2 + cb) * 64 + lane];
+    }
+  };
+  if (s1 > s0) {
+    load_a(hbase + s1 - 1);
+    load_b(hbase + s1 - 1);
+  }
   for (int s = s1 - 1; s >= s0; --s) {
-    const size_t hs = (size_t)hv * geo.slots + s;
+    const size_t hs = hbase + s, nxt = hbase + (s > s0 ? s - 1 : s0);  // in bounds
     float* hp = dhn + hs * K * V + v;
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) hp[(size_t)(16 * mt + 4 * g + r) * V] = dH[mt][r];
-    const float dec = fast_exp2(gam[hs * kChunk + kChunk - 1]);
+    Frag<E> hb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[kb] = frag_from_tiles<E>(dH[2 * kb], dH[2 * kb + 1]);
     f32x4 dv[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      dv[ct] = dvl[((hs * NV + vt) * 4 + ct) * 64 + lane];
+      dv[ct] = dl[ct];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        mma_k32(dv[ct], kdf[((hs * 4 + ct) * KB + kb) * 64 + lane], Frag<float>{dH[2 * kb], dH[2 * kb + 1]});
+      for (int kb = 0; kb < KB; ++kb) mma_k32(dv[ct], kd[ct][kb], hb[kb]);
     }
+    asm volatile("" ::: "memory");
+    load_a(nxt);
+    asm volatile("" ::: "memory");
     float* vp = dvn + hs * kChunk * V + v;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) vp[(size_t)(16 * ct + 4 * g + r) * V] = dv[ct][r];
-    const Frag<float> nb[2] = {Frag<float>{-dv[0], -dv[1]}, Frag<float>{-dv[2], -dv[3]}};
-    Frag<float> db[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) db[cb] = dof[((hs * NV + vt) * 2 + cb) * 64 + lane];
+    const Frag<E> nb[2] = {frag_from_tiles<E>(-dv[0], -dv[1]), frag_from_tiles<E>(-dv[2], -dv[3])};
+    const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
-      dH[mt] *= dec;
+      dH[mt] = dH[mt] * dec + b[mt];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        mma_k32(dH[mt], qtf[((hs * KT + mt) * 2 + cb) * 64 + lane], db[cb]);
-        mma_k32(dH[mt], wtf[((hs * KT + mt) * 2 + cb) * 64 + lane], nb[cb]);
-      }
+      for (int cb = 0; cb < 2; ++cb) mma_k32(dH[mt], wt[mt][cb], nb[cb]);
     }
+    asm volatile("" ::: "memory");
+    load_b(nxt);
+    asm volatile("" ::: "memory");
   }
   if (dh0) {
 #pragma unroll
