@@ -393,12 +393,12 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
               F(bl.dhn), F(bl.dvn)));
   mark(3);
   if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,
+    ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe, ke,
               doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
               F(bl.dwp), F(bl.dgp)));
   mark(4);
   if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, ke, ve,
+    ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke, ve,
               a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp), F(bl.dvn),
               F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw, F(bl.dAp),
               F(bl.dbp)));

@@ -105,16 +105,16 @@ __device__ __forceinline__ float sum64(float x) {
 }
 
 // Rows [0, ROWS) into an fp32 LDS tile (stride ld): row r reads
-// src + (t0 + r) * row_stride, rows >= len are zero.  N columns, 256 threads.
-template <int N, typename E, int ROWS = kChunk>
+// src + (t0 + r) * row_stride, rows >= len are zero.  N columns, THREADS threads.
+template <int N, typename E, int ROWS = kChunk, int THREADS = 256>
 __device__ __forceinline__ void stage_rows(float* dst, int ld, const E* src, int64_t t0,
                                            int64_t row_stride, int len) {
-  constexpr int PER = ROWS * N / 8 / 256;  // 8-element pieces per thread
-  static_assert(PER * 8 * 256 == ROWS * N, "whole pieces per thread");
+  constexpr int PER = ROWS * N / 8 / THREADS;  // 8-element pieces per thread
+  static_assert(PER * 8 * THREADS == ROWS * N, "whole pieces per thread");
   const int tid = threadIdx.x;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int m = tid + 256 * it, row = m / (N / 8), c0 = 8 * (m % (N / 8));
+    const int m = tid + THREADS * it, row = m / (N / 8), c0 = 8 * (m % (N / 8));
     float e[8];
     if (row < len) {
       ld8(src + (t0 + row) * row_stride + c0, e);
@@ -349,19 +349,25 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dq / dk / dw / dG, one workgroup per (chunk slot, value head).  Wave w owns
-// key columns [w K/4, (w+1) K/4) of the 64 x K results and row tile w of the
-// 64 x 64 ones.  The products over V run in two LDS stagings: (do, dv_new,
-// H_c) for dq_inter and dw, then (do, v_new, dH_{c+1}) for dPm and dk_kd; the
-// products over K and over the chunk then stage q and k.
+// Eight waves per workgroup (two per SIMD, so one wave's LDS waits overlap the
+// other's MFMAs).  A 64 x N result (N = K or V) is split in row halves x column
+// quarters: wave w owns row tiles 2 (w/4), 2 (w/4) + 1 and columns
+// [(w%4) N/4, (w%4+1) N/4).  A 64 x 64 result: wave w owns row tile w/2 and
+// column tiles 2 (w%2), 2 (w%2) + 1.
+constexpr int kBwdThreads = 512;
+
+// dq / dk / dw / dG, one workgroup per (chunk slot, value head).  The products
+// over V run in two LDS stagings: (do, dv_new, H_c) for dq_inter and dw, then
+// (do, v_new, dH_{c+1}) for dPm and dk_kd; the products over K and over the
+// chunk then stage q and k.
 template <typename E, int K, int V, bool VARLEN>
-__global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
+__global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const float* __restrict__ vnp,
     const float* __restrict__ dvn, const float* __restrict__ hcp, const float* __restrict__ dhn,
     float* __restrict__ dqp, float* __restrict__ dkp, float* __restrict__ dwp,
     float* __restrict__ dgp) {
-  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64;
+  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, TH = kBwdThreads;
   constexpr int PH1 = 2 * kChunk * VP + K * VP, PH2 = 2 * kChunk * KP + kChunk * kCP;
   __shared__ __align__(16) float lds[PH1 > PH2 ? PH1 : PH2];
   __shared__ float sg[kChunk], dG[kChunk], red[2];
@@ -380,13 +386,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
   const int h = hv / geo.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
   const size_t hs = (size_t)hv * geo.slots + slot;
-  const int kc0 = wave * (K / 4);
+  const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4);  // 64 x K ownership
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);               // 64 x 64 ownership
   const float* Hc = hcp + hs * K * V;
   const float* dHn = dhn + hs * K * V;
 
-  stage_rows<V>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
-  stage_rows<V>(Xs, VP, dvn + hs * kChunk * V, 0, V, kChunk);
-  stage_rows<V, float, K>(Hs, VP, Hc, 0, V, K);
+  stage_rows<V, E, kChunk, TH>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_rows<V, float, kChunk, TH>(Xs, VP, dvn + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<V, float, K, TH>(Hs, VP, Hc, 0, V, K);
   if (tid < kChunk) {
     sg[tid] = gam[hs * kChunk + tid];
     dG[tid] = 0.f;
@@ -395,10 +402,10 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
   // <dH_{c+1}, H_c>, streamed from the workspace
   {
     float acc = 0.f;
-    for (int e = 4 * tid; e < K * V; e += 4 * 256) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(Hc + e);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(dHn + e);
-      acc += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    for (int e = 4 * tid; e < K * V; e += 4 * TH) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(Hc + e);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(dHn + e);
+      acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
     }
     acc = sum64(acc);
     __syncthreads();  // red[] initialised
@@ -407,72 +414,76 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
   __syncthreads();
   const float gl = sg[kChunk - 1];
 
-  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T on this wave's key
-  // columns (B operand: H_c rows k, contiguous in v).
-  f32x4 dq[4][NKT], dk[4][NKT];
+  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T (B operand: H_c
+  // rows k, contiguous in v).
+  f32x4 dq[2][NKT], dk[2][NKT];
 #pragma unroll
   for (int nt = 0; nt < NKT; ++nt) {
     const int kc = kc0 + 16 * nt;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      dq[it][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 2; ++a) {
+      const int it = rt0 + a;
+      dq[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 dw = {0.f, 0.f, 0.f, 0.f};
-      mm16<V>(dq[it][nt], Ds + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+      mm16<V>(dq[a][nt], Ds + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
       mm16<V>(dw, Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * it + 4 * g + r;
-        dq[it][nt][r] *= geo.scale * fast_exp2(sg[i]);
+        dq[a][nt][r] *= geo.scale * fast_exp2(sg[i]);
         dwp[(hs * kChunk + i) * K + kc + lc] = -dw[r];
       }
     }
   }
   __syncthreads();
-  stage_rows<V>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
-  stage_rows<V, float, K>(Hs, VP, dHn, 0, V, K);
+  stage_rows<V, float, kChunk, TH>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<V, float, K, TH>(Hs, VP, dHn, 0, V, K);
   __syncthreads();
-  // dPm = scale (do v_new^T) * M * e^{dG}: row tile `wave`.
-  f32x4 dPm[4];
+  // dPm = scale (do v_new^T) * M * e^{dG}
+  f32x4 dPm[2];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    dPm[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (jt <= wave) mm16<V>(dPm[jt], Ds + 16 * wave * VP, VP, 1, Xs + 16 * jt * VP, 1, VP);
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    dPm[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) mm16<V>(dPm[b], Ds + 16 * pit * VP, VP, 1, Xs + 16 * jt * VP, 1, VP);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = 16 * wave + 4 * g + r, j = 16 * jt + lc;
-      dPm[jt][r] = j <= i ? dPm[jt][r] * geo.scale * fast_exp2(sg[i] - sg[j]) : 0.f;
+      const int i = 16 * pit + 4 * g + r, j = 16 * jt + lc;
+      dPm[b][r] = j <= i ? dPm[b][r] * geo.scale * fast_exp2(sg[i] - sg[j]) : 0.f;
     }
   }
-  // dk_kd = e^{G_last - G} (v_new dH_{c+1}^T) on this wave's key columns.
+  // dk_kd = e^{G_last - G} (v_new dH_{c+1}^T)
 #pragma unroll
   for (int nt = 0; nt < NKT; ++nt) {
     const int kc = kc0 + 16 * nt;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      dk[it][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16<V>(dk[it][nt], Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+    for (int a = 0; a < 2; ++a) {
+      const int it = rt0 + a;
+      dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mm16<V>(dk[a][nt], Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dk[it][nt][r] *= fast_exp2(gl - sg[16 * it + 4 * g + r]);
+      for (int r = 0; r < 4; ++r) dk[a][nt][r] *= fast_exp2(gl - sg[16 * it + 4 * g + r]);
     }
   }
   __syncthreads();
 
-  stage_rows<K>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
-  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<K, E, kChunk, TH>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<K, E, kChunk, TH>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
   __syncthreads();
   // R = dPm * (Q K^T): dG_i += row sums, dG_j -= column sums; dPm to LDS.
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= wave) mm16<K>(s, Qs + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) mm16<K>(sq, Qs + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
     float cs = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float rr = dPm[jt][r] * s[r];
+      const float rr = dPm[b][r] * sq[r];
       cs += rr;
       const float rs = sum16(rr);
-      if (lc == 0) atomicAdd(&dG[16 * wave + 4 * g + r], rs);
-      Pd[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dPm[jt][r];
+      if (lc == 0) atomicAdd(&dG[16 * pit + 4 * g + r], rs);
+      Pd[(16 * pit + 4 * g + r) * kCP + 16 * jt + lc] = dPm[b][r];
     }
     cs = sum_groups(cs);
     if (g == 0) atomicAdd(&dG[16 * jt + lc], -cs);
@@ -481,16 +492,16 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
   {
     float xs = 0.f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * g + r;
+        const int i = 16 * (rt0 + a) + 4 * g + r;
         float qd = 0.f, kx = 0.f;
 #pragma unroll
         for (int nt = 0; nt < NKT; ++nt) {
           const int kk = kc0 + 16 * nt + lc;
-          qd += Qs[i * KP + kk] * dq[it][nt][r];
-          kx += Ks[i * KP + kk] * dk[it][nt][r];
+          qd += Qs[i * KP + kk] * dq[a][nt][r];
+          kx += Ks[i * KP + kk] * dk[a][nt][r];
         }
         qd = sum16(qd);
         kx = sum16(kx);
@@ -506,14 +517,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
   for (int nt = 0; nt < NKT; ++nt) {
     const int kc = kc0 + 16 * nt;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      mm16<kChunk>(dq[it][nt], Pd + 16 * it * kCP, kCP, 1, Ks + kc, KP, 1);
-      mm16<kChunk>(dk[it][nt], Pd + 16 * it, 1, kCP, Qs + kc, KP, 1);
+    for (int a = 0; a < 2; ++a) {
+      const int it = rt0 + a;
+      mm16<kChunk>(dq[a][nt], Pd + 16 * it * kCP, kCP, 1, Ks + kc, KP, 1);
+      mm16<kChunk>(dk[a][nt], Pd + 16 * it, 1, kCP, Qs + kc, KP, 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const size_t o = (hs * kChunk + 16 * it + 4 * g + r) * K + kc + lc;
-        dqp[o] = dq[it][nt][r];
-        dkp[o] = dk[it][nt][r];
+        dqp[o] = dq[a][nt][r];
+        dkp[o] = dk[a][nt][r];
       }
     }
   }
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_dqk_kernel(
 // dbeta and dg_raw (fp32) for the chunk's tokens and the chunk's sums for
 // dA_log and ddt_bias.
 template <typename E, int K, int V, bool VARLEN>
-__global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
+__global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     Geo geo, const E* __restrict__ kg, const E* __restrict__ vg, const float* __restrict__ g_raw,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const float* __restrict__ bet,
@@ -538,7 +550,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
     const float* __restrict__ dgp, float* __restrict__ dkp, E* __restrict__ dvg,
     float* __restrict__ dbeta, float* __restrict__ dg_raw, float* __restrict__ dAp,
     float* __restrict__ dbp) {
-  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, NVT = V / 64;
+  constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, NVT = V / 64, TH = kBwdThreads;
   __shared__ __align__(16) float Ks[kChunk * KP];
   __shared__ __align__(16) float Vs[kChunk * VP];  // later dT, dS
   __shared__ __align__(16) float Wd[kChunk * KP];
@@ -562,13 +574,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
   }
   const int h = hv / geo.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
-  const int kc0 = wave * (K / 4), vc0 = wave * (V / 4);
+  const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4), vc0 = (wave & 3) * (V / 4);
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);
 
-  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
-  stage_rows<V>(Vs, VP, vg + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
-  stage_rows<K>(Wd, KP, dwp + hs * kChunk * K, 0, K, kChunk);
-  stage_rows<V>(Dv, VP, dvn + hs * kChunk * V, 0, V, kChunk);
-  stage_rows<kChunk>(Tt, kCP, tmat + hs * kChunk * kChunk, 0, kChunk, kChunk);
+  stage_rows<K, E, kChunk, TH>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<V, E, kChunk, TH>(Vs, VP, vg + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_rows<K, float, kChunk, TH>(Wd, KP, dwp + hs * kChunk * K, 0, K, kChunk);
+  stage_rows<V, float, kChunk, TH>(Dv, VP, dvn + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<kChunk, float, kChunk, TH>(Tt, kCP, tmat + hs * kChunk * kChunk, 0, kChunk, kChunk);
   if (tid < kChunk) {
     sg[tid] = gam[hs * kChunk + tid];
     sb[tid] = bet[hs * kChunk + tid];
@@ -577,32 +590,33 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
   }
   __syncthreads();
 
-  // dT (strictly lower part; the rest does not reach dA): row tile `wave`.
-  f32x4 dT[4];
+  // dT (strictly lower part; the rest does not reach dA).
+  f32x4 dT[2];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= wave) {
-      mm16<K>(a, Wd + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
-      mm16<V>(b, Dv + 16 * wave * VP, VP, 1, Vs + 16 * jt * VP, 1, VP);
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) {
+      mm16<K>(x, Wd + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+      mm16<V>(y, Dv + 16 * pit * VP, VP, 1, Vs + 16 * jt * VP, 1, VP);
     }
     const int j = 16 * jt + lc;
     const float fw = sb[j] * fast_exp2(sg[j]), fu = sb[j];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = 16 * wave + 4 * g + r;
-      dT[jt][r] = j < i ? a[r] * fw + b[r] * fu : 0.f;
+      const int i = 16 * pit + 4 * g + r;
+      dT[b][r] = j < i ? x[r] * fw + y[r] * fu : 0.f;
     }
   }
-  // X_w = T^T dw (this wave's key columns): dk += beta e^G X_w and the
-  // k . X_w terms of dbeta and dG.
-  f32x4 dk[4][NKT];
+  // X_w = T^T dw: dk += beta e^G X_w and the k . X_w terms of dbeta and dG.
+  f32x4 dk[2][NKT];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
+  for (int a = 0; a < 2; ++a) {
+    const int jt = rt0 + a;
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
-      dk[jt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16<kChunk>(dk[jt][nt], Tt + 16 * jt, 1, kCP, Wd + kc0 + 16 * nt, KP, 1);
+      dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mm16<kChunk>(dk[a][nt], Tt + 16 * jt, 1, kCP, Wd + kc0 + 16 * nt, KP, 1);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -610,19 +624,20 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
       const float eg = fast_exp2(sg[j]);
       float kx = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NKT; ++nt) kx += Ks[j * KP + kc0 + 16 * nt + lc] * dk[jt][nt][r];
+      for (int nt = 0; nt < NKT; ++nt) kx += Ks[j * KP + kc0 + 16 * nt + lc] * dk[a][nt][r];
       kx = sum16(kx);
       if (lc == 0) {
         atomicAdd(&dB[j], eg * kx);
         atomicAdd(&dG[j], sb[j] * eg * kx);
       }
 #pragma unroll
-      for (int nt = 0; nt < NKT; ++nt) dk[jt][nt][r] *= sb[j] * eg;
+      for (int nt = 0; nt < NKT; ++nt) dk[a][nt][r] *= sb[j] * eg;
     }
   }
   // X_u = T^T dv_new: dv = beta X_u, the v . X_u term of dbeta.
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
+  for (int a = 0; a < 2; ++a) {
+    const int jt = rt0 + a;
     f32x4 xu[NVT];
 #pragma unroll
     for (int nv = 0; nv < NVT; ++nv) {
@@ -645,70 +660,74 @@ __global__ __launch_bounds__(256) void gdn_bwd_wy_kernel(
   }
   __syncthreads();
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dTs[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dT[jt][r];
+    for (int r = 0; r < 4; ++r) dTs[(16 * pit + 4 * g + r) * kCP + 16 * (pj0 + b) + lc] = dT[b][r];
   __syncthreads();
-  // Y = T^T dT (row tile `wave`).
+  // Y = T^T dT.
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
     f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    mm16<kChunk>(y, Tt + 16 * wave, 1, kCP, dTs + 16 * jt, kCP, 1);
+    mm16<kChunk>(y, Tt + 16 * pit, 1, kCP, dTs + 16 * jt, kCP, 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ys[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = y[r];
+    for (int r = 0; r < 4; ++r) Ys[(16 * pit + 4 * g + r) * kCP + 16 * jt + lc] = y[r];
   }
   __syncthreads();
   // dA = -strictly_lower(Y T^T); with S = K K^T and A = beta_i e^{dG} S:
   // dG += rows - columns of dA * A, dbeta += rows of dA e^{dG} S, dS = dA beta e^{dG}.
-  f32x4 dS[4];
+  f32x4 dS[2];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 y = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= wave) {
-      mm16<kChunk>(y, Ys + 16 * wave * kCP, kCP, 1, Tt + 16 * jt * kCP, 1, kCP);
-      mm16<K>(s, Ks + 16 * wave * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) {
+      mm16<kChunk>(y, Ys + 16 * pit * kCP, kCP, 1, Tt + 16 * jt * kCP, 1, kCP);
+      mm16<K>(sk, Ks + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
     }
     const int c = 16 * jt + lc;
     float cs = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int a = 16 * wave + 4 * g + r;
+      const int ar = 16 * pit + 4 * g + r;
       // above the diagonal e^{G_a - G_c} can overflow: select, never multiply by 0
-      const float da = c < a ? -y[r] : 0.f;
-      const float e = c < a ? fast_exp2(sg[a] - sg[c]) : 0.f;
-      const float des = da * e * s[r];
-      const float z = des * sb[a];
+      const float da = c < ar ? -y[r] : 0.f;
+      const float e = c < ar ? fast_exp2(sg[ar] - sg[c]) : 0.f;
+      const float des = da * e * sk[r];
+      const float z = des * sb[ar];
       cs += z;
       const float rz = sum16(z), rb = sum16(des);
       if (lc == 0) {
-        atomicAdd(&dG[a], rz);
-        atomicAdd(&dB[a], rb);
+        atomicAdd(&dG[ar], rz);
+        atomicAdd(&dB[ar], rb);
       }
-      dS[jt][r] = da * sb[a] * e;
+      dS[b][r] = da * sb[ar] * e;
     }
     cs = sum_groups(cs);
     if (g == 0) atomicAdd(&dG[c], -cs);
   }
   __syncthreads();
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dTs[(16 * wave + 4 * g + r) * kCP + 16 * jt + lc] = dS[jt][r];
+    for (int r = 0; r < 4; ++r) dTs[(16 * pit + 4 * g + r) * kCP + 16 * (pj0 + b) + lc] = dS[b][r];
   __syncthreads();
   // dk += (dS + dS^T) K; add the dq/dk kernel's terms and store.
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int a = 0; a < 2; ++a) {
+    const int jt = rt0 + a;
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
       const int kc = kc0 + 16 * nt;
-      mm16<kChunk>(dk[jt][nt], dTs + 16 * jt * kCP, kCP, 1, Ks + kc, KP, 1);
-      mm16<kChunk>(dk[jt][nt], dTs + 16 * jt, 1, kCP, Ks + kc, KP, 1);
+      mm16<kChunk>(dk[a][nt], dTs + 16 * jt * kCP, kCP, 1, Ks + kc, KP, 1);
+      mm16<kChunk>(dk[a][nt], dTs + 16 * jt, 1, kCP, Ks + kc, KP, 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const size_t o = (hs * kChunk + 16 * jt + 4 * g + r) * K + kc + lc;
-        dkp[o] += dk[jt][nt][r];
+        dkp[o] += dk[a][nt][r];
       }
     }
+  }
   __syncthreads();
   // dg = reversed chunk-local cumsum of dG; gate backward.
   if (wave == 0) {
