@@ -124,7 +124,10 @@ def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
         "bwd_wy": dict(bytes=k_in + U * V * esz + 2 * U * K * 4 + U * V * 4 + Ck * C * C * 4
                        + 4 * U * 4 + U * K * 4 + U * V * esz + 2 * U * 4 + 2 * Ck * 4,
                        flops=U * (2 * C * (K + V) + 2 * C * C // 3 + 3 * C * K)),
-        "sums": dict(bytes=2 * U * K * 4 + 2 * k_in + 2 * Ck * 4 + 2 * HV * 4, flops=0),
+        # per-head parameter sums, plus the key-head dq/dk sums when value heads
+        # share a key head (else dq, dk are written by the dq/dk and WY kernels)
+        "sums": dict(bytes=2 * Ck * 4 + 2 * HV * 4 + (2 * U * K * 4 + 2 * k_in if HV > H else 0),
+                     flops=0),
     }
     path = dict(bytes=4 * k_in + 3 * U * V * esz + 4 * U * 4 + (state if has_h0 else 0)
                 + (state if has_dht else 0) + state,

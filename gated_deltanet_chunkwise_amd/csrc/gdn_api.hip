@@ -377,12 +377,12 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(256), s, geo, ke, ve,
               a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat)));
   if (units > 0 && geo.slots > 0)
-    ok(launch(gdn::gdn_chain_kernel<E, K, V, VARLEN, gdn::CHAIN_PLAIN>, dim3(units), dim3(64), s,
-              geo, wf, ktf, uf, gam, seq_slot, a.h0, nullptr,
-              reinterpret_cast<Frag<E>*>(F(bl.hcp)), reinterpret_cast<Frag<E>*>(F(bl.vnp))));
+    ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_PLAIN>(
+        geo, s, wf, ktf, uf, gam, seq_slot, a.h0, nullptr, reinterpret_cast<Frag<E>*>(F(bl.hcp)),
+        reinterpret_cast<Frag<E>*>(F(bl.vnp))));
   mark(1);
   if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(256), s, geo, qe, ke,
+    ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe, ke,
               doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::f32x4*>(w + bl.bq),
               reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
   mark(2);
@@ -395,15 +395,15 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe, ke,
               doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
-              F(bl.dwp), F(bl.dgp)));
+              F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
   mark(4);
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke, ve,
               a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp), F(bl.dvn),
               F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw, F(bl.dAp),
-              F(bl.dbp)));
+              F(bl.dbp), static_cast<E*>(a.dk)));
   mark(5);
-  if (geo.slots > 0)
+  if (geo.slots > 0 && geo.G > 1)
     ok(launch(gdn::gdn_bwd_qk_sum_kernel<E, K, VARLEN>, dim3((unsigned)geo.slots * geo.H),
               dim3(256), s, geo, cmap, F(bl.dqp), F(bl.dkp), static_cast<E*>(a.dq),
               static_cast<E*>(a.dk)));

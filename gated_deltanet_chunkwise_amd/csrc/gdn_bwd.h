@@ -66,6 +66,13 @@ namespace gdn {
 template <int N> struct Pad { static constexpr int v = N + 4; };
 constexpr int kCP = kChunk + 4;  // stride of 64-column fp32 tiles
 
+// The per-chunk backward kernels run eight waves per workgroup (two per SIMD,
+// so one wave's LDS waits overlap the other's MFMAs).  A 64 x N result (N = K
+// or V) is split in row halves x column quarters: wave w owns row tiles
+// 2 (w/4), 2 (w/4) + 1 and columns [(w%4) N/4, (w%4+1) N/4).  A 64 x 64 result:
+// wave w owns row tile w/2 and column tiles 2 (w%2), 2 (w%2) + 1.
+constexpr int kBwdThreads = 512;
+
 // acc (one 16x16 fp32 D tile) += sum_{kk < KD} A(m, kk) B(kk, n), where
 // A(m, kk) = a[m * sam + kk * sak] and B(kk, n) = b[kk * sbk + n * sbn], with
 // a and b at the tile's origin (m, n in 0..15).  MFMA j of each 16-wide step
@@ -84,6 +91,49 @@ __device__ __forceinline__ void mm16(f32x4& acc, const float* a, int sam, int sa
       const int kk = s + 4 * kq + j;
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[kk * sak], bp[kk * sbk], acc, 0, 0, 0);
     }
+}
+
+// acc[r][c] (MR x NR D tiles) += sum_{kk < KD} A_r(m, kk) B_c(kk, n), with A_r
+// the row tile r of A (origin a + 16 r sam) and B_c the column tile c of B
+// (origin b + 16 c sbn); each kk's operands are loaded once for all MR x NR
+// products, which also gives MR x NR independent accumulation chains.
+template <int KD, int MR, int NR>
+__device__ __forceinline__ void mm_block(f32x4 (&acc)[MR][NR], const float* a, int sam, int sak,
+                                         const float* b, int sbk, int sbn) {
+  const int lane = lane_id(), l16 = lane & 15, kq = lane >> 4;
+  const float* ap = a + l16 * sam;
+  const float* bp = b + l16 * sbn;
+#pragma unroll
+  for (int s = 0; s < KD; s += 16)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = s + 4 * kq + j;
+      float av[MR], bv[NR];
+#pragma unroll
+      for (int r = 0; r < MR; ++r) av[r] = ap[16 * r * sam + kk * sak];
+#pragma unroll
+      for (int c = 0; c < NR; ++c) bv[c] = bp[16 * c * sbn + kk * sbk];
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[c], acc[r][c], 0, 0, 0);
+    }
+}
+
+// The first `ncols` (0, 1 or 2; uniform per wave) of two column tiles of one
+// row tile: acc[c] += A B_c.
+template <int KD>
+__device__ __forceinline__ void mm_pair(f32x4 (&acc)[2], int ncols, const float* a, int sam,
+                                        int sak, const float* b, int sbk, int sbn) {
+  if (ncols >= 2) {
+    f32x4 t[1][2] = {{acc[0], acc[1]}};
+    mm_block<KD, 1, 2>(t, a, sam, sak, b, sbk, sbn);
+    acc[0] = t[0][0];
+    acc[1] = t[0][1];
+  } else if (ncols == 1) {
+    mm16<KD>(acc[0], a, sam, sak, b, sbk, sbn);
+  }
 }
 
 // Sum over the 16 lanes of each lane group (the columns of a D tile row).
@@ -145,12 +195,13 @@ __device__ __forceinline__ void frag_elems(const Frag<float>& f, float (&x)[8]) 
 // dH term bq = scale (e^G * Q)^T do, and its kd and w^T operand fragments
 // (dtype E, as the forward state pass's operands).
 template <typename E, int K, int V, bool VARLEN>
-__global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
+__global__ __launch_bounds__(kBwdThreads) void gdn_bwd_prep_kernel(
     Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<E>* __restrict__ wf,
     Frag<E>* __restrict__ wtf, Frag<E>* __restrict__ kdf, f32x4* __restrict__ bq,
     f32x4* __restrict__ dvl) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, KT = K / 16, KB = K / 32, NV = V / 16;
+  constexpr int TH = kBwdThreads, NW = TH / 64;
   __shared__ __align__(16) float Qs[kChunk * KP];  // q, later w
   __shared__ __align__(16) float Ks[kChunk * KP];
   __shared__ __align__(16) float Ds[kChunk * VP];  // do, later scale e^G do
@@ -165,42 +216,39 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
   const int h = hv / geo.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
   const size_t hs = (size_t)hv * geo.slots + slot;
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);
 
-  stage_rows<K>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
-  stage_rows<K>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
-  stage_rows<V>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_rows<K, E, kChunk, TH>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<K, E, kChunk, TH>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows<V, E, kChunk, TH>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
   if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
   __syncthreads();
 
-  // P = (Q K^T) * M * e^{dG}; wave = row tile.
-  {
-    const int it = wave;
+  // P = (Q K^T) * M * e^{dG}
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (jt <= it) mm16<K>(acc, Qs + 16 * it * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) mm16<K>(acc, Qs + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * g + r, j = 16 * jt + lc;
-        Ps[i * kCP + j] = j <= i ? acc[r] * fast_exp2(sg[i] - sg[j]) : 0.f;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * pit + 4 * g + r, j = 16 * jt + lc;
+      Ps[i * kCP + j] = j <= i ? acc[r] * fast_exp2(sg[i] - sg[j]) : 0.f;
     }
   }
   __syncthreads();
 
   // dv_local = scale P^T do: D tiles (rows c = 16 ct + .., column v).
-  {
-    const int ct = wave;
-    for (int vt = 0; vt < NV; ++vt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm16<kChunk>(acc, Ps + 16 * ct, 1, kCP, Ds + 16 * vt, VP, 1);
-      dvl[((hs * NV + vt) * 4 + ct) * 64 + lane] = acc * geo.scale;
-    }
+  for (int f = wave; f < 4 * NV; f += NW) {
+    const int ct = f / NV, vt = f - ct * NV;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mm16<kChunk>(acc, Ps + 16 * ct, 1, kCP, Ds + 16 * vt, VP, 1);
+    dvl[((hs * NV + vt) * 4 + ct) * 64 + lane] = acc * geo.scale;
   }
   // kd fragments (rows c, k over K).
   {
     const float gl = sg[kChunk - 1];
-    for (int f = wave; f < 4 * KB; f += 4) {
+    for (int f = wave; f < 4 * KB; f += NW) {
       const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
       const float e = fast_exp2(gl - sg[c]);
       const f32x4 lo = *reinterpret_cast<const f32x4*>(Ks + c * KP + 32 * kb + 4 * g);
@@ -211,12 +259,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
   __syncthreads();
   // do rows times scale e^{G_c}, then bq = Q^T (scale e^G do): D tiles
   // (rows k, column v).
-  for (int e = tid; e < kChunk * (V / 4); e += 256) {
+  for (int e = tid; e < kChunk * (V / 4); e += TH) {
     const int c = e / (V / 4), v4 = 4 * (e - c * (V / 4));
     *reinterpret_cast<f32x4*>(Ds + c * VP + v4) *= geo.scale * fast_exp2(sg[c]);
   }
   __syncthreads();
-  for (int f = wave; f < KT * NV; f += 4) {
+  for (int f = wave; f < KT * NV; f += NW) {
     const int mt = f / NV, vt = f - mt * NV;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mm16<kChunk>(acc, Qs + 16 * mt, 1, KP, Ds + 16 * vt, VP, 1);
@@ -225,7 +273,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
   __syncthreads();
   // w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
   // into Qs, then w^T fragments (rows k, k over the chunk).
-  for (int f = wave; f < 4 * KB; f += 4) {
+  for (int f = wave; f < 4 * KB; f += NW) {
     const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
     float x[8];
     frag_elems(wf[((hs * 4 + ct) * KB + kb) * 64 + lane], x);
@@ -233,7 +281,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(
     *reinterpret_cast<f32x4*>(Qs + c * KP + 32 * kb + 16 + 4 * g) = f32x4{x[4], x[5], x[6], x[7]};
   }
   __syncthreads();
-  for (int f = wave; f < KT * 2; f += 4) {
+  for (int f = wave; f < KT * 2; f += NW) {
     const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
     f32x4 lo, hi;
 #pragma unroll
@@ -348,15 +396,8 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Eight waves per workgroup (two per SIMD, so one wave's LDS waits overlap the
-// other's MFMAs).  A 64 x N result (N = K or V) is split in row halves x column
-// quarters: wave w owns row tiles 2 (w/4), 2 (w/4) + 1 and columns
-// [(w%4) N/4, (w%4+1) N/4).  A 64 x 64 result: wave w owns row tile w/2 and
-// column tiles 2 (w%2), 2 (w%2) + 1.
-constexpr int kBwdThreads = 512;
-
-// dq / dk / dw / dG, one workgroup per (chunk slot, value head).  The products
+// dq / dk / dw / dG, one workgroup per (chunk slot, value head); with one value
+// head per key head dq is written final, else per value head.  The products
 // over V run in two LDS stagings: (do, dv_new, H_c) for dq_inter and dw, then
 // (do, v_new, dH_{c+1}) for dPm and dk_kd; the products over K and over the
 // chunk then stage q and k.
@@ -366,7 +407,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     const int4* __restrict__ cmap, const float* __restrict__ gam, const float* __restrict__ vnp,
     const float* __restrict__ dvn, const float* __restrict__ hcp, const float* __restrict__ dhn,
     float* __restrict__ dqp, float* __restrict__ dkp, float* __restrict__ dwp,
-    float* __restrict__ dgp) {
+    float* __restrict__ dgp, E* __restrict__ dqg) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, TH = kBwdThreads;
   constexpr int PH1 = 2 * kChunk * VP + K * VP, PH2 = 2 * kChunk * KP + kChunk * kCP;
   __shared__ __align__(16) float lds[PH1 > PH2 ? PH1 : PH2];
@@ -416,36 +457,38 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
 
   // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T (B operand: H_c
   // rows k, contiguous in v).
+  // (ncols of a 64 x 64 row tile's column pair below or on the diagonal)
+  const int npair = pit >= pj0 + 1 ? 2 : pit >= pj0 ? 1 : 0;
   f32x4 dq[2][NKT], dk[2][NKT];
+  {
+    f32x4 dw[2][NKT];
 #pragma unroll
-  for (int nt = 0; nt < NKT; ++nt) {
-    const int kc = kc0 + 16 * nt;
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int it = rt0 + a;
-      dq[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 dw = {0.f, 0.f, 0.f, 0.f};
-      mm16<V>(dq[a][nt], Ds + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
-      mm16<V>(dw, Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+      for (int nt = 0; nt < NKT; ++nt) dq[a][nt] = dw[a][nt] = dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mm_block<V, 2, NKT>(dq, Ds + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
+    mm_block<V, 2, NKT>(dw, Xs + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * g + r;
-        dq[a][nt][r] *= geo.scale * fast_exp2(sg[i]);
-        dwp[(hs * kChunk + i) * K + kc + lc] = -dw[r];
-      }
-    }
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (rt0 + a) + 4 * g + r;
+          dq[a][nt][r] *= geo.scale * fast_exp2(sg[i]);
+          dwp[(hs * kChunk + i) * K + kc0 + 16 * nt + lc] = -dw[a][nt][r];
+        }
   }
   __syncthreads();
   stage_rows<V, float, kChunk, TH>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
   stage_rows<V, float, K, TH>(Hs, VP, dHn, 0, V, K);
   __syncthreads();
   // dPm = scale (do v_new^T) * M * e^{dG}
-  f32x4 dPm[2];
+  f32x4 dPm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  mm_pair<V>(dPm, npair, Ds + 16 * pit * VP, VP, 1, Xs + 16 * pj0 * VP, 1, VP);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int jt = pj0 + b;
-    dPm[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (jt <= pit) mm16<V>(dPm[b], Ds + 16 * pit * VP, VP, 1, Xs + 16 * jt * VP, 1, VP);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * pit + 4 * g + r, j = 16 * jt + lc;
@@ -453,33 +496,28 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     }
   }
   // dk_kd = e^{G_last - G} (v_new dH_{c+1}^T)
+  mm_block<V, 2, NKT>(dk, Xs + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
 #pragma unroll
-  for (int nt = 0; nt < NKT; ++nt) {
-    const int kc = kc0 + 16 * nt;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int it = rt0 + a;
-      dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16<V>(dk[a][nt], Xs + 16 * it * VP, VP, 1, Hs + kc * VP, 1, VP);
+    for (int nt = 0; nt < NKT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dk[a][nt][r] *= fast_exp2(gl - sg[16 * it + 4 * g + r]);
-    }
-  }
+      for (int r = 0; r < 4; ++r) dk[a][nt][r] *= fast_exp2(gl - sg[16 * (rt0 + a) + 4 * g + r]);
   __syncthreads();
 
   stage_rows<K, E, kChunk, TH>(Qs, KP, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
   stage_rows<K, E, kChunk, TH>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
   __syncthreads();
   // R = dPm * (Q K^T): dG_i += row sums, dG_j -= column sums; dPm to LDS.
+  f32x4 sq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  mm_pair<K>(sq, npair, Qs + 16 * pit * KP, KP, 1, Ks + 16 * pj0 * KP, 1, KP);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int jt = pj0 + b;
-    f32x4 sq = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= pit) mm16<K>(sq, Qs + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
     float cs = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float rr = dPm[b][r] * sq[r];
+      const float rr = dPm[b][r] * sq[b][r];
       cs += rr;
       const float rs = sum16(rr);
       if (lc == 0) atomicAdd(&dG[16 * pit + 4 * g + r], rs);
@@ -513,18 +551,24 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   }
   __syncthreads();
   // dq += dPm K;  dk += dPm^T Q.
+  mm_block<kChunk, 2, NKT>(dq, Pd + 16 * rt0 * kCP, kCP, 1, Ks + kc0, KP, 1);
+  mm_block<kChunk, 2, NKT>(dk, Pd + 16 * rt0, 1, kCP, Qs + kc0, KP, 1);
 #pragma unroll
   for (int nt = 0; nt < NKT; ++nt) {
     const int kc = kc0 + 16 * nt;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int it = rt0 + a;
-      mm16<kChunk>(dq[a][nt], Pd + 16 * it * kCP, kCP, 1, Ks + kc, KP, 1);
-      mm16<kChunk>(dk[a][nt], Pd + 16 * it, 1, kCP, Qs + kc, KP, 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const size_t o = (hs * kChunk + 16 * it + 4 * g + r) * K + kc + lc;
-        dqp[o] = dq[a][nt][r];
+        const int i = 16 * it + 4 * g + r;
+        const size_t o = (hs * kChunk + i) * K + kc + lc;
+        // one value head per key head: dq is final here
+        if (geo.G == 1) {
+          if (i < len) dqg[((t0 + i) * geo.H + h) * K + kc + lc] = (E)dq[a][nt][r];
+        } else {
+          dqp[o] = dq[a][nt][r];
+        }
         dkp[o] = dk[a][nt][r];
       }
     }
@@ -538,9 +582,9 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
 
 // ---------------------------------------------------------------------------
 // WY backward, the chunk-local dG scan and the gate backward, one workgroup
-// per (chunk slot, value head).  Adds its dk terms to dkp; writes dv (dtype),
-// dbeta and dg_raw (fp32) for the chunk's tokens and the chunk's sums for
-// dA_log and ddt_bias.
+// per (chunk slot, value head).  Adds its dk terms to dkp (or, with one value
+// head per key head, writes the final dk); writes dv (dtype), dbeta and dg_raw
+// (fp32) for the chunk's tokens and the chunk's sums for dA_log and ddt_bias.
 template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     Geo geo, const E* __restrict__ kg, const E* __restrict__ vg, const float* __restrict__ g_raw,
@@ -549,7 +593,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     const float* __restrict__ tmat, const float* __restrict__ dwp, const float* __restrict__ dvn,
     const float* __restrict__ dgp, float* __restrict__ dkp, E* __restrict__ dvg,
     float* __restrict__ dbeta, float* __restrict__ dg_raw, float* __restrict__ dAp,
-    float* __restrict__ dbp) {
+    float* __restrict__ dbp, E* __restrict__ dkg) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, NVT = V / 64, TH = kBwdThreads;
   __shared__ __align__(16) float Ks[kChunk * KP];
   __shared__ __align__(16) float Vs[kChunk * VP];  // later dT, dS
@@ -591,33 +635,34 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
   __syncthreads();
 
   // dT (strictly lower part; the rest does not reach dA).
+  const int npair = pit >= pj0 + 1 ? 2 : pit >= pj0 ? 1 : 0;
   f32x4 dT[2];
+  {
+    f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    mm_pair<K>(x, npair, Wd + 16 * pit * KP, KP, 1, Ks + 16 * pj0 * KP, 1, KP);
+    mm_pair<V>(y, npair, Dv + 16 * pit * VP, VP, 1, Vs + 16 * pj0 * VP, 1, VP);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int jt = pj0 + b;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= pit) {
-      mm16<K>(x, Wd + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
-      mm16<V>(y, Dv + 16 * pit * VP, VP, 1, Vs + 16 * jt * VP, 1, VP);
-    }
-    const int j = 16 * jt + lc;
-    const float fw = sb[j] * fast_exp2(sg[j]), fu = sb[j];
+    for (int b = 0; b < 2; ++b) {
+      const int j = 16 * (pj0 + b) + lc;
+      const float fw = sb[j] * fast_exp2(sg[j]), fu = sb[j];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * pit + 4 * g + r;
-      dT[b][r] = j < i ? x[r] * fw + y[r] * fu : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * pit + 4 * g + r;
+        dT[b][r] = j < i ? x[b][r] * fw + y[b][r] * fu : 0.f;
+      }
     }
   }
   // X_w = T^T dw: dk += beta e^G X_w and the k . X_w terms of dbeta and dG.
   f32x4 dk[2][NKT];
 #pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mm_block<kChunk, 2, NKT>(dk, Tt + 16 * rt0, 1, kCP, Wd + kc0, KP, 1);
+#pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int jt = rt0 + a;
-#pragma unroll
-    for (int nt = 0; nt < NKT; ++nt) {
-      dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16<kChunk>(dk[a][nt], Tt + 16 * jt, 1, kCP, Wd + kc0 + 16 * nt, KP, 1);
-    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 16 * jt + 4 * g + r;
@@ -635,15 +680,15 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     }
   }
   // X_u = T^T dv_new: dv = beta X_u, the v . X_u term of dbeta.
+  f32x4 xu[2][NVT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nv = 0; nv < NVT; ++nv) xu[a][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mm_block<kChunk, 2, NVT>(xu, Tt + 16 * rt0, 1, kCP, Dv + vc0, VP, 1);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int jt = rt0 + a;
-    f32x4 xu[NVT];
-#pragma unroll
-    for (int nv = 0; nv < NVT; ++nv) {
-      xu[nv] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mm16<kChunk>(xu[nv], Tt + 16 * jt, 1, kCP, Dv + vc0 + 16 * nv, VP, 1);
-    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 16 * jt + 4 * g + r;
@@ -651,8 +696,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
 #pragma unroll
       for (int nv = 0; nv < NVT; ++nv) {
         const int vv = vc0 + 16 * nv + lc;
-        vx += Vs[j * VP + vv] * xu[nv][r];
-        if (j < len) dvg[((t0 + j) * geo.HV + hv) * V + vv] = (E)(sb[j] * xu[nv][r]);
+        vx += Vs[j * VP + vv] * xu[a][nv][r];
+        if (j < len) dvg[((t0 + j) * geo.HV + hv) * V + vv] = (E)(sb[j] * xu[a][nv][r]);
       }
       vx = sum16(vx);
       if (lc == 0) atomicAdd(&dB[j], vx);
@@ -665,26 +710,26 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     for (int r = 0; r < 4; ++r) dTs[(16 * pit + 4 * g + r) * kCP + 16 * (pj0 + b) + lc] = dT[b][r];
   __syncthreads();
   // Y = T^T dT.
+  {
+    f32x4 y[1][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
+    mm_block<kChunk, 1, 2>(y, Tt + 16 * pit, 1, kCP, dTs + 16 * pj0, kCP, 1);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int jt = pj0 + b;
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    mm16<kChunk>(y, Tt + 16 * pit, 1, kCP, dTs + 16 * jt, kCP, 1);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ys[(16 * pit + 4 * g + r) * kCP + 16 * jt + lc] = y[r];
+      for (int r = 0; r < 4; ++r) Ys[(16 * pit + 4 * g + r) * kCP + 16 * (pj0 + b) + lc] = y[0][b][r];
   }
   __syncthreads();
   // dA = -strictly_lower(Y T^T); with S = K K^T and A = beta_i e^{dG} S:
   // dG += rows - columns of dA * A, dbeta += rows of dA e^{dG} S, dS = dA beta e^{dG}.
   f32x4 dS[2];
+  f32x4 yy[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 ss[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  mm_pair<kChunk>(yy, npair, Ys + 16 * pit * kCP, kCP, 1, Tt + 16 * pj0 * kCP, 1, kCP);
+  mm_pair<K>(ss, npair, Ks + 16 * pit * KP, KP, 1, Ks + 16 * pj0 * KP, 1, KP);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int jt = pj0 + b;
-    f32x4 y = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= pit) {
-      mm16<kChunk>(y, Ys + 16 * pit * kCP, kCP, 1, Tt + 16 * jt * kCP, 1, kCP);
-      mm16<K>(sk, Ks + 16 * pit * KP, KP, 1, Ks + 16 * jt * KP, 1, KP);
-    }
+    const f32x4 y = yy[b], sk = ss[b];
     const int c = 16 * jt + lc;
     float cs = 0.f;
 #pragma unroll
@@ -713,18 +758,24 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     for (int r = 0; r < 4; ++r) dTs[(16 * pit + 4 * g + r) * kCP + 16 * (pj0 + b) + lc] = dS[b][r];
   __syncthreads();
   // dk += (dS + dS^T) K; add the dq/dk kernel's terms and store.
+  mm_block<kChunk, 2, NKT>(dk, dTs + 16 * rt0 * kCP, kCP, 1, Ks + kc0, KP, 1);
+  mm_block<kChunk, 2, NKT>(dk, dTs + 16 * rt0, 1, kCP, Ks + kc0, KP, 1);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int jt = rt0 + a;
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
       const int kc = kc0 + 16 * nt;
-      mm16<kChunk>(dk[a][nt], dTs + 16 * jt * kCP, kCP, 1, Ks + kc, KP, 1);
-      mm16<kChunk>(dk[a][nt], dTs + 16 * jt, 1, kCP, Ks + kc, KP, 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const size_t o = (hs * kChunk + 16 * jt + 4 * g + r) * K + kc + lc;
-        dkp[o] += dk[a][nt][r];
+        const int j = 16 * jt + 4 * g + r;
+        const size_t o = (hs * kChunk + j) * K + kc + lc;
+        // one value head per key head: dk is final here
+        if (geo.G == 1) {
+          if (j < len) dkg[((t0 + j) * geo.H + h) * K + kc + lc] = (E)(dkp[o] + dk[a][nt][r]);
+        } else {
+          dkp[o] += dk[a][nt][r];
+        }
       }
     }
   }
