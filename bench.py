@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="no GPU: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE passes under DIR "
                          "(fetch/, write/, copy_fetch/, copy_write/) into profiles/traffic.json "
-                         "for --workload")
+                         "for --workload (with --op gdn_bwd: the backward's kernels, under "
+                         "'<workload>:bwd')")
     return ap.parse_args()
 
 
@@ -542,7 +543,8 @@ SEEDS_BWD = 20290  # output-gradient seed of the backward benchmark
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(args.write_traffic, args.workload, args.copy_mib << 20)
+        key = args.workload + (":bwd" if args.op == "gdn_bwd" else "")
+        write_traffic(args.write_traffic, key, args.copy_mib << 20)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

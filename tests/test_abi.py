@@ -227,3 +227,49 @@ def test_segment_layout():
     lp = gdn.workspace_layout(P(B=1, T=1000, num_seqs=3, seg_chunks=2), packed=True)
     assert lp.num_segs == (1000 // 64 + 3) // 2 + 3
     assert gdn.check(P(seg_chunks=-1), ptrs(), 1 << 40) == ESHAPE
+
+
+def _bwd_call(lib, p, ws_bytes, **over):
+    """gdn_bwd with fake, aligned device addresses (never dereferenced: every
+    case below fails validation, or has no work)."""
+    names = ("q", "k", "v", "g_raw", "beta", "A_log", "dt_bias", "cu_seqlens", "h0", "d_o",
+             "dht", "dq", "dk", "dv", "dg_raw", "dbeta", "dA_log", "ddt_bias", "dh0", "ws")
+    addr = {n: 0x100000 * (i + 1) for i, n in enumerate(names)}
+    addr.update(cu_seqlens=0, h0=0, dht=0)
+    addr.update(over)
+    vp = [ctypes.c_void_p(addr[n]) if addr[n] else None for n in names[:-1]]
+    ws = ctypes.c_void_p(addr["ws"]) if addr["ws"] else None
+    return lib.gdn_bwd(ctypes.byref(p), *vp, ws, ws_bytes, None)
+
+
+def test_bwd_validation():
+    lib = gdn.load_library()
+    p = P()
+    ws = lib.gdn_bwd_workspace_size(ctypes.byref(p), 0)
+    assert ws > gdn.workspace_size(p)  # the forward layout plus the backward's buffers
+    for name in ("q", "k", "v", "g_raw", "beta", "A_log", "d_o", "dq", "dk", "dv", "dg_raw",
+                 "dbeta", "dA_log", "ws"):
+        assert _bwd_call(lib, p, ws, **{name: 0}) == ENULL, name
+    for name, addr in (("q", 0x100008), ("d_o", 0x100004), ("dq", 0x100002),
+                       ("dv", 0x100008), ("dg_raw", 0x100002), ("dh0", 0x100001),
+                       ("ddt_bias", 0x100003), ("ws", 0x100080)):
+        assert _bwd_call(lib, p, ws, **{name: addr}) == EALIGN, name
+    assert _bwd_call(lib, p, ws - 256) == EWS
+    bad = P(K=96)
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(bad), 0) == 0
+    assert _bwd_call(lib, bad, ws) == EUNSUP
+    assert _bwd_call(lib, P(HV=3, H=2), ws) == ESHAPE
+    assert _bwd_call(lib, P(num_seqs=2), ws, cu_seqlens=0x90000) == ESHAPE  # packed needs B == 1
+    # no tokens: token pointers may be NULL (dA_log is still required)
+    e = P(T=0)
+    null = dict(q=0, k=0, v=0, g_raw=0, beta=0, d_o=0, dq=0, dk=0, dv=0, dg_raw=0, dbeta=0)
+    assert _bwd_call(lib, e, lib.gdn_bwd_workspace_size(ctypes.byref(e), 0),
+                     **dict(null, dA_log=0)) == ENULL
+
+
+def test_bwd_workspace_grows_with_the_problem():
+    lib = gdn.load_library()
+    sizes = [lib.gdn_bwd_workspace_size(ctypes.byref(P(T=t)), 0) for t in (64, 128, 1000)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    pk = P(B=1, T=1000, num_seqs=5)
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(pk), 1) > gdn.workspace_size(pk, packed=True)

@@ -155,3 +155,22 @@ def test_repeat_calls_agree():
     for n in NAMES:
         m = metrics(a[n], b[n])
         assert m["rel_l2"] <= 1e-6, (n, m)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_chunk_edges(T):
+    # one token, a chunk minus one, exactly one chunk, one past, two chunks + 1
+    inp = make_inputs(B=2, T=T, H=1, HV=1, K=64, V=128, dtype=F32, seed=650 + T, h0=True)
+    check_full(inp, "bwd edge_T%d" % T, 660 + T)
+
+
+def test_wide_gqa_group():
+    # four value heads per key head, bf16 (dq, dk summed by the key-head kernel)
+    inp = make_inputs(B=1, T=256, H=2, HV=8, K=128, V=128, dtype=BF, seed=671, h0=True)
+    check_full(inp, "bwd gqa4", 672)
+
+
+def test_packed_mostly_empty():
+    inp = make_inputs(B=1, T=70, H=1, HV=2, K=64, V=64, dtype=F32, seed=681, h0=True,
+                      lengths=[0, 0, 70, 0])
+    check_full(inp, "bwd packed_mostly_empty", 682)
