@@ -78,47 +78,54 @@ constexpr int kBwdThreads = 512;
 // a and b at the tile's origin (m, n in 0..15).  MFMA j of each 16-wide step
 // takes kk = s + 4 (lane / 16) + j in both operands.  D tile lane l holds rows
 // 4 (l / 16) + r, column l % 16.
+template <int KD, int MR, int NR>
+__device__ __forceinline__ void mm_block(f32x4 (&acc)[MR][NR], const float* a, int sam, int sak,
+                                         const float* b, int sbk, int sbn);
 template <int KD>
 __device__ __forceinline__ void mm16(f32x4& acc, const float* a, int sam, int sak, const float* b,
                                      int sbk, int sbn) {
-  const int lane = lane_id(), l16 = lane & 15, kq = lane >> 4;
-  const float* ap = a + l16 * sam;
-  const float* bp = b + l16 * sbn;
-#pragma unroll
-  for (int s = 0; s < KD; s += 16)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = s + 4 * kq + j;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[kk * sak], bp[kk * sbk], acc, 0, 0, 0);
-    }
+  f32x4 t[1][1] = {{acc}};
+  mm_block<KD, 1, 1>(t, a, sam, sak, b, sbk, sbn);
+  acc = t[0][0];
 }
 
 // acc[r][c] (MR x NR D tiles) += sum_{kk < KD} A_r(m, kk) B_c(kk, n), with A_r
 // the row tile r of A (origin a + 16 r sam) and B_c the column tile c of B
 // (origin b + 16 c sbn); each kk's operands are loaded once for all MR x NR
 // products, which also gives MR x NR independent accumulation chains.
+// The operands of a 16-wide k step are loaded one step ahead (two register
+// buffers), so each LDS wait covers a whole step's reads while the previous
+// step's MFMAs run.
 template <int KD, int MR, int NR>
 __device__ __forceinline__ void mm_block(f32x4 (&acc)[MR][NR], const float* a, int sam, int sak,
                                          const float* b, int sbk, int sbn) {
   const int lane = lane_id(), l16 = lane & 15, kq = lane >> 4;
-  const float* ap = a + l16 * sam;
-  const float* bp = b + l16 * sbn;
-#pragma unroll
-  for (int s = 0; s < KD; s += 16)
+  const float* ap = a + l16 * sam + 4 * kq * sak;
+  const float* bp = b + l16 * sbn + 4 * kq * sbk;
+  constexpr int NS = KD / 16;
+  float av[2][4][MR], bv[2][4][NR];
+  auto load = [&](int buf, int s) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int kk = s + 4 * kq + j;
-      float av[MR], bv[NR];
 #pragma unroll
-      for (int r = 0; r < MR; ++r) av[r] = ap[16 * r * sam + kk * sak];
+      for (int r = 0; r < MR; ++r) av[buf][j][r] = ap[16 * r * sam + (16 * s + j) * sak];
 #pragma unroll
-      for (int c = 0; c < NR; ++c) bv[c] = bp[16 * c * sbn + kk * sbk];
+      for (int c = 0; c < NR; ++c) bv[buf][j][c] = bp[16 * c * sbn + (16 * s + j) * sbk];
+    }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s + 1 < NS) load((s + 1) & 1, s + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < MR; ++r)
 #pragma unroll
         for (int c = 0; c < NR; ++c)
-          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[c], acc[r][c], 0, 0, 0);
-    }
+          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s & 1][j][r], bv[s & 1][j][c],
+                                                           acc[r][c], 0, 0, 0);
+  }
 }
 
 // The first `ncols` (0, 1 or 2; uniform per wave) of two column tiles of one
@@ -136,10 +143,22 @@ __device__ __forceinline__ void mm_pair(f32x4 (&acc)[2], int ncols, const float*
   }
 }
 
-// Sum over the 16 lanes of each lane group (the columns of a D tile row).
+// x from another lane of the same 16-lane row, by a DPP control (a VALU
+// operand modifier: no LDS round trip, unlike a shuffle).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each lane group (the columns of a D tile row), in
+// every lane of the group: quad_perm [1,0,3,2] and [2,3,0,1] sum each quad,
+// row_half_mirror adds the other quad of the half row, row_mirror the other
+// half row.
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 16);
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
   return x;
 }
 // Sum over the 4 lane groups (the rows 4g + r of a D tile column, per r).
@@ -440,18 +459,6 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     dG[tid] = 0.f;
   }
   if (tid < 2) red[tid] = 0.f;
-  // <dH_{c+1}, H_c>, streamed from the workspace
-  {
-    float acc = 0.f;
-    for (int e = 4 * tid; e < K * V; e += 4 * TH) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(Hc + e);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(dHn + e);
-      acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-    }
-    acc = sum64(acc);
-    __syncthreads();  // red[] initialised
-    if (lane == 0) atomicAdd(&red[0], acc);
-  }
   __syncthreads();
   const float gl = sg[kChunk - 1];
 
@@ -481,7 +488,27 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   }
   __syncthreads();
   stage_rows<V, float, kChunk, TH>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
-  stage_rows<V, float, K, TH>(Hs, VP, dHn, 0, V, K);
+  // dH_{c+1} replaces H_c in LDS; each thread first reads the H_c values at the
+  // positions it overwrites, for <dH_{c+1}, H_c>.
+  {
+    constexpr int PER = K * V / 8 / TH;
+    float acc = 0.f;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int m = tid + TH * it, row = m / (V / 8), c0 = 8 * (m % (V / 8));
+      float e[8];
+      ld8(dHn + (size_t)row * V + c0, e);
+      float* dst = Hs + row * VP + c0;
+      const f32x4 h0 = *reinterpret_cast<const f32x4*>(dst);
+      const f32x4 h1 = *reinterpret_cast<const f32x4*>(dst + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += h0[j] * e[j] + h1[j] * e[4 + j];
+      *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], e[1], e[2], e[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[4], e[5], e[6], e[7]};
+    }
+    acc = sum64(acc);
+    if (lane == 0) atomicAdd(&red[0], acc);
+  }
   __syncthreads();
   // dPm = scale (do v_new^T) * M * e^{dG}
   f32x4 dPm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
