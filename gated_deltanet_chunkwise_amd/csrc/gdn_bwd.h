@@ -659,6 +659,16 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     dG[tid] = 0.f;
     dB[tid] = 0.f;
   }
+  // the dq/dk kernel's dk terms of this wave's tiles, loaded now and used at
+  // the end (their latency hides behind the whole kernel)
+  float dk0[2][NKT][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dk0[a][nt][r] = dkp[(hs * kChunk + 16 * (rt0 + a) + 4 * g + r) * K + kc0 + 16 * nt + lc];
   __syncthreads();
 
   // dT (strictly lower part; the rest does not reach dA).
@@ -799,9 +809,9 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
         const size_t o = (hs * kChunk + j) * K + kc + lc;
         // one value head per key head: dk is final here
         if (geo.G == 1) {
-          if (j < len) dkg[((t0 + j) * geo.H + h) * K + kc + lc] = (E)(dkp[o] + dk[a][nt][r]);
+          if (j < len) dkg[((t0 + j) * geo.H + h) * K + kc + lc] = (E)(dk0[a][nt][r] + dk[a][nt][r]);
         } else {
-          dkp[o] += dk[a][nt][r];
+          dkp[o] = dk0[a][nt][r] + dk[a][nt][r];
         }
       }
     }
