@@ -119,11 +119,14 @@ def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
         "bwd_chain": dict(bytes=2 * U * K * esz + Ck * K * V * 4 + U * V * 4 + Ck * 4
                           + (state if has_dht else 0) + Ck * K * V * 4 + U * V * 4 + state,
                           flops=U * 4 * K * V),
+        # with one value head per key head dq and dk are written at the dtype by
+        # these two kernels, else as fp32 partials per value head
         "dqk": dict(bytes=2 * k_in + U * V * esz + 2 * U * V * 4 + 2 * Ck * K * V * 4 + U * 4
-                    + 3 * U * K * 4 + U * 4,
+                    + U * K * (esz if HV == H else 4) + 2 * U * K * 4 + U * 4,
                     flops=U * (6 * K * V + C * V + 3 * C * K)),
         "bwd_wy": dict(bytes=k_in + U * V * esz + 2 * U * K * 4 + U * V * 4 + Ck * C * C * 4
-                       + 4 * U * 4 + U * K * 4 + U * V * esz + 2 * U * 4 + 2 * Ck * 4,
+                       + 4 * U * 4 + U * K * (esz if HV == H else 4) + U * V * esz + 2 * U * 4
+                       + 2 * Ck * 4,
                        flops=U * (2 * C * (K + V) + 2 * C * C // 3 + 3 * C * K)),
         # per-head parameter sums, plus the key-head dq/dk sums when value heads
         # share a key head (else dq, dk are written by the dq/dk and WY kernels)
