@@ -204,7 +204,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               geo.slots, cmap, seq_slot));
   mark(1);
   if (work && geo.slots > 0 && (mask & GDN_STAGE_WY))
-    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo, ke,
+    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(gdn::kWyThreads), s, geo, ke,
               ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf, nullptr));
   mark(2);
   if (work && (mask & GDN_STAGE_STATE)) {
@@ -374,7 +374,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
     ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, a.cu, geo.N, geo.T, geo.slots,
               cmap, seq_slot));
   if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(256), s, geo, ke, ve,
+    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(gdn::kWyThreads), s, geo, ke, ve,
               a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat)));
   if (units > 0 && geo.slots > 0)
     ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_PLAIN>(

@@ -174,10 +174,13 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 //   ktf [hv][slot][mt<K/16][cb<2][lane]   A operand of  kd^T v_new (rows K, k over c)
 //   uf  [hv][slot][vt<V/16][cp<2][lane][2] D tiles ct = 2cp, 2cp+1 of u (rows c, column v);
 //                                         a lane's pair is one fragment-sized block
+// Eight waves per WY workgroup.
+constexpr int kWyThreads = 512;
+
 // With STORE_T, T itself (lower triangular, fp32, [hv][slot][64][64] row-major,
 // zeros above the diagonal) is also written to tmat, for the backward pass.
 template <typename E, int K, int V, bool VARLEN, bool STORE_T = false>
-__global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
+__global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
                                                      const float* __restrict__ g_raw,
                                                      const float* __restrict__ beta,
@@ -215,41 +218,38 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   const size_t hs = (size_t)hv * geo.slots + slot;
 
   // All global loads first (one memory latency for K, V and the gate inputs):
-  // thread t owns the 4x8 micro-tile t of K and of V; wave 0 also reads this
-  // head's 64 raw gates and betas (stride HV along T).
+  // thread t < 256 owns the 4x8 micro-tile t of K, thread 256 + t that of V;
+  // wave 0 also reads this head's 64 raw gates and betas (stride HV along T).
   float graw = 0.f, braw = 0.f;
   if (wave == 0 && lane < len) {
     graw = g_raw[(t0 + lane) * geo.HV + hv];
     braw = beta[(t0 + lane) * geo.HV + hv];
   }
   constexpr int NKM = 16 * (K / 8), NVM = 16 * (V / 8);  // micro-tiles (<= 256 each)
-  float ek[4][8], ev[4][8];
-  const int krb = 4 * (tid / (K / 8)), kc0 = 8 * (tid % (K / 8));
-  const int vrb = 4 * (tid / (V / 8)), vc0 = 8 * (tid % (V / 8));
+  const bool kside = tid < 256;
+  const int mtile = tid & 255, W8 = (kside ? K : V) / 8;
+  const int rb = 4 * (mtile / W8), c0 = 8 * (mtile % W8);
+  const bool owns = mtile < (kside ? NKM : NVM);
+  float e[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if (tid < NKM && krb + r < len) ld8(kg + ((t0 + krb + r) * geo.H + h) * K + kc0, ek[r]);
-    else {
+    if (owns && rb + r < len) {
+      if (kside) ld8(kg + ((t0 + rb + r) * geo.H + h) * K + c0, e[r]);
+      else ld8(vg + ((t0 + rb + r) * geo.HV + hv) * V + c0, e[r]);
+    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ek[r][j] = 0.f;
-    }
-    if (tid < NVM && vrb + r < len) ld8(vg + ((t0 + vrb + r) * geo.HV + hv) * V + vc0, ev[r]);
-    else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ev[r][j] = 0.f;
+      for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
     }
   }
-  if (tid < NKM) {
+  if (owns) {
+    if (kside) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st8(Ks + (krb + r) * KS + kc0, ek[r]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st4(Kt + (kc0 + j) * CS + (krb ^ tswz(kc0 + j)), ek[0][j], ek[1][j], ek[2][j], ek[3][j]);
-  }
-  if (tid < NVM) {
+      for (int r = 0; r < 4; ++r) st8(Ks + (rb + r) * KS + c0, e[r]);
+    }
+    E* const tr = kside ? Kt : Vt;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      st4(Vt + (vc0 + j) * CS + (vrb ^ tswz(vc0 + j)), ev[0][j], ev[1][j], ev[2][j], ev[3][j]);
+      st4(tr + (c0 + j) * CS + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
   }
   // Gate prologue (wave 0, lane = token): g in fp32 with the softplus
   // threshold of the KDA gate guide ("core computation logic"), the chunk-local
@@ -276,14 +276,14 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   __syncthreads();
 
   // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)).  The 10 tiles on or
-  // below the diagonal go 3/3/2/2 to the waves; the products finish before A
-  // overwrites K natural in region 0.
+  // below the diagonal go 2/2/1/1/1/1/1/1 to the waves; the products finish
+  // before A overwrites K natural in region 0.
   {
-    f32x4 acc[3];
-    int ti[3], tj[3];
+    f32x4 acc[2];
+    int ti[2], tj[2];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int t = wave + 4 * q;  // tile index in (0,0),(1,0),(1,1),(2,0),...
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 8 * q;  // tile index in (0,0),(1,0),(1,1),(2,0),...
       const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
       ti[q] = it;
       tj[q] = t - it * (it + 1) / 2;
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (wave + 4 * q < 10) {
+    for (int q = 0; q < 2; ++q) {
+      if (wave + 8 * q < 10) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * ti[q] + 4 * g + r, col = 16 * tj[q] + lc;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   // triangular, and the reads below take those blocks as zero.
   {
     const int b = wave;
-    if (lane < 16) {
+    if (b < 4 && lane < 16) {
       float a[16][16];
 #pragma unroll
       for (int i = 1; i < 16; ++i) {
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
 
   if constexpr (STORE_T) {
 #pragma unroll
-    for (int it = 0; it < kChunk * kChunk / 4 / 256; ++it) {
-      const int e4 = tid + 256 * it, i = e4 >> 4, j = (e4 & 15) << 2;
+    for (int it = 0; it < kChunk * kChunk / 4 / kWyThreads; ++it) {
+      const int e4 = tid + kWyThreads * it, i = e4 >> 4, j = (e4 & 15) << 2;
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       // blocks right of the diagonal block were never written
       const f32x4 x = (j >> 4) <= (i >> 4) ? *reinterpret_cast<const f32x4*>(Ts + i * FS + j) : zero;
@@ -375,10 +375,11 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
     }
   }
 
-  // Wave w owns chunk rows 16w..16w+15.  Its k32 fragments of T diag(beta e^G)
-  // and T diag(beta) over the chunk index (row 16w + lane%16, columns
-  // 32cb + kslot(g, i)) are formed from T in registers.
-  const int ct = wave;
+  // Waves w and w + 4 own chunk rows 16w..16w+15 (w < 4), each half of the
+  // output tiles.  Their k32 fragments of T diag(beta e^G) and T diag(beta)
+  // over the chunk index (row 16w + lane%16, columns 32cb + kslot(g, i)) are
+  // formed from T in registers.
+  const int ct = wave & 3, half = wave >> 2;
   Frag<E> bw[2], bu[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -403,22 +404,27 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   // w^T = K^T T_w^T: D tile (mt) holds w[16ct + lane%16][16mt + 4g + r], so
   // tile pairs are the state pass's A fragments.
   {
-    f32x4 acc[K / 16];
+    constexpr int MTH = K / 32;  // row tiles of w^T per half
+    f32x4 acc[MTH];
 #pragma unroll
-    for (int mt = 0; mt < K / 16; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MTH; ++m) {
+      const int mt = half * MTH + m;
+      acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mma_k32(acc[mt], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
+      for (int cb = 0; cb < 2; ++cb) mma_k32(acc[m], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
     }
     Frag<E>* dst = wf + (hs * 4 + ct) * (K / 32) * 64;
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) dst[kb * 64 + lane] = frag_from_tiles<E>(acc[2 * kb], acc[2 * kb + 1]);
+    for (int b2 = 0; b2 < MTH / 2; ++b2)
+      dst[(half * (MTH / 2) + b2) * 64 + lane] = frag_from_tiles<E>(acc[2 * b2], acc[2 * b2 + 1]);
   }
-  // u = T_u V (A operand: this wave's rows of T_u).
+  // u = T_u V (A operand: this wave's rows of T_u; each half takes half of
+  // the value tiles).
   {
     Quad<E>* dst = uf + hs * (V / 16) * 4 * 64;
 #pragma unroll
-    for (int vt = 0; vt < V / 16; ++vt) {
+    for (int m = 0; m < V / 32; ++m) {
+      const int vt = half * (V / 32) + m;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CS, 32 * cb));
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(256) void gdn_wy_kernel(Geo geo, const E* __restric
   {
     Frag<E>* dst = ktf + hs * (K / 16) * 2 * 64;
     const float gl = sg[kChunk - 1];
-    for (int f = wave; f < (K / 16) * 2; f += 4) {
+    for (int f = wave; f < (K / 16) * 2; f += kWyThreads / 64) {
       const int mt = f >> 1, cb = f & 1;
       float sc[8];
 #pragma unroll
