@@ -550,7 +550,7 @@ def main():
         write_traffic(args.write_traffic, key, args.copy_mib << 20)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr, flush=True)
         sys.exit(2)
     import torch
