@@ -174,3 +174,19 @@ def test_packed_mostly_empty():
     inp = make_inputs(B=1, T=70, H=1, HV=2, K=64, V=64, dtype=F32, seed=681, h0=True,
                       lengths=[0, 0, 70, 0])
     check_full(inp, "bwd packed_mostly_empty", 682)
+
+
+def test_long_gqa_sampled_key_head():
+    """A long sequence (T=16384, 256 chunks) with two value heads per key head,
+    bf16: every gradient of key head 1's two value heads (the oracle keeps each
+    unit's 16384 states, 2 GiB per unit)."""
+    inp = make_inputs(B=1, T=16384, H=2, HV=4, K=128, V=128, dtype=BF, seed=691, h0=True)
+    d_o, dht = make_grads(inp, 692)
+    got = run_gpu_bwd(inp, d_o, dht)
+    ref = run_oracle_bwd(inp, d_o, dht, units=[2, 3])
+    ts = {k: v[2:4] for k, v in param_term_scale(inp, ref).items()}
+    sub = lambda d: dict(  # noqa: E731
+        dq=d["dq"][:, :, 1], dk=d["dk"][:, :, 1], dv=d["dv"][:, :, 2:4],
+        dg_raw=d["dg_raw"][:, :, 2:4], dbeta=d["dbeta"][:, :, 2:4],
+        dA_log=d["dA_log"][2:4], ddt_bias=d["ddt_bias"][2:4], dh0=d["dh0"][:, 2:4])
+    compare(sub(got), sub(ref), inp.q.dtype, "bwd long_gqa", term_scale=ts)
