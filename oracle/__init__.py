@@ -11,8 +11,9 @@ from gated_deltanet_chunkwise_amd).
 * ``bwd``        -- reverse-mode derivative of ``fwd`` (C, fp64, pthreads) for
                     L = sum <do, o> + <dht, final state>.
 * ``chunkwise``  -- numpy fp64 chunkwise (WY) reformulation with per-chunk
-                    intermediates; a second, independent derivation used to
-                    pin the token oracle and to expose intermediates.
+                    intermediates, and its backward (``chunkwise.bwd``); a
+                    second, independent derivation used to pin the token
+                    oracle and to expose intermediates.
 
 Functions marked "parity unpinned" in their module docstring: none.
 """

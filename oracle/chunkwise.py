@@ -170,3 +170,119 @@ def segment_scan(q, k, v, g, beta, cu_seqlens=None, h0=None, chunk=64, seg_chunk
                                             bf[s:e, hv], Hc, scale)
                     o[s:e, hv] = o_c
     return o.reshape(B, T, HV, V), fin
+
+
+# ---------------------------------------------------------------------------
+# Backward.  The derivative of the chunk form above for
+# L = sum <do, o> + <dht, H_final>, chunk by chunk (a second derivation,
+# independent of the token oracle's reverse sweep).  Per chunk, with
+# M the causal mask j <= i, P = (Q K^T) * M * e^{dG}, kd = diag(e^{G_last - G}) K:
+#   dv_local = scale P^T do;      dv_new = dv_local + kd dH_{c+1}
+#   dH_c     = e^{G_last} dH_{c+1} + scale (e^G * Q)^T do - w^T dv_new
+#   dPm      = scale (do v_new^T) * M * e^{dG}
+#   dq       = scale e^G * (do H_c^T) + dPm K
+#   dk       = dPm^T Q + e^{G_last - G} * (v_new dH_{c+1}^T) + [WY terms]
+#   dw       = -dv_new H_c^T;  dT = dw (diag(beta e^G) K)^T + dv_new (diag(beta) V)^T
+#   dv       = beta * (Tinv^T dv_new)
+#   dA       = -strictly_lower(Tinv^T dT Tinv^T)
+# and dG collects every exp(G) factor's derivative; dg is its reversed
+# chunk-local cumsum.  Returns the gradients with respect to q, k, v, beta and
+# the log-decay g (not g_raw), and dh0.
+
+def chunk_step_bwd(Qc, Kc, Vc, gc, bc, H0, dO, dHn, scale=1.0):
+    """Gradients of one chunk.  dHn is dL/dH_next.  Returns
+    (dq, dk, dv, dbeta, dg, dH0) for the chunk's rows and its start state."""
+    C = Kc.shape[0]
+    G = np.cumsum(gc)
+    diff = G[:, None] - G[None, :]
+    lower_incl = np.tril(np.ones((C, C), dtype=bool))
+    strict = np.tril(np.ones((C, C), dtype=bool), -1)
+    E = np.zeros((C, C))
+    E[lower_incl] = np.exp(diff[lower_incl])
+    S = Kc @ Kc.T
+    A = np.where(strict, bc[:, None] * S * E, 0.0)
+    Tinv = np.linalg.solve(np.eye(C) + A, np.eye(C))
+    eG = np.exp(G)
+    Gl = G[-1]
+    w = Tinv @ ((bc * eG)[:, None] * Kc)
+    u = Tinv @ (bc[:, None] * Vc)
+    v_new = u - w @ H0
+    kd = np.exp(Gl - G)[:, None] * Kc
+    QK = Qc @ Kc.T
+    P = QK * E
+    # state pass (reverse)
+    dv_new = scale * P.T @ dO + kd @ dHn
+    dH0 = np.exp(Gl) * dHn + scale * (eG[:, None] * Qc).T @ dO - w.T @ dv_new
+    # output and state-update terms
+    dPm = scale * (dO @ v_new.T) * E
+    R = dPm * QK
+    dG = R.sum(1) - R.sum(0)
+    dq_inter = scale * eG[:, None] * (dO @ H0.T)
+    dG += np.sum(Qc * dq_inter, 1)
+    dq = dq_inter + dPm @ Kc
+    dk_kd = np.exp(Gl - G)[:, None] * (v_new @ dHn.T)
+    x = np.sum(Kc * dk_kd, 1)
+    dG -= x
+    dG[-1] += x.sum() + np.exp(Gl) * np.sum(dHn * H0)
+    dk = dPm.T @ Qc + dk_kd
+    # WY terms
+    dw = -dv_new @ H0.T
+    dT = dw @ ((bc * eG)[:, None] * Kc).T + dv_new @ (bc[:, None] * Vc).T
+    Xw = Tinv.T @ dw
+    Xu = Tinv.T @ dv_new
+    dk += (bc * eG)[:, None] * Xw
+    dbeta = eG * np.sum(Kc * Xw, 1) + np.sum(Vc * Xu, 1)
+    dG += bc * eG * np.sum(Kc * Xw, 1)
+    dv = bc[:, None] * Xu
+    dA = -np.where(strict, Tinv.T @ dT @ Tinv.T, 0.0)
+    dS = dA * bc[:, None] * E
+    dk += (dS + dS.T) @ Kc
+    dbeta += np.sum(dA * E * S, 1)
+    Z = dA * A
+    dG += Z.sum(1) - Z.sum(0)
+    dg = np.cumsum(dG[::-1])[::-1]
+    return dq, dk, dv, dbeta, dg, dH0
+
+
+def bwd(q, k, v, g, beta, do, dht=None, cu_seqlens=None, h0=None, chunk=64, scale=1.0):
+    """Chunkwise backward from a given log-decay g [B,T,HV] (fp64).  Returns a
+    dict: dq, dk [B,T,H,K]; dv [B,T,HV,V]; dbeta, dg [B,T,HV]; dh0 [N,HV,K,V]."""
+    q, k, v, g, beta, do = (np.asarray(x, np.float64) for x in (q, k, v, g, beta, do))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    G = HV // H
+    bounds = _seq_bounds(B, T, cu_seqlens)
+    N = len(bounds)
+    flat = lambda x: x.reshape((B * T,) + x.shape[2:])  # noqa: E731
+    qf, kf, vf, gf, bf, df = (flat(x) for x in (q, k, v, g, beta, do))
+    out = dict(dq=np.zeros((B * T, H, K)), dk=np.zeros((B * T, H, K)),
+               dv=np.zeros((B * T, HV, V)), dbeta=np.zeros((B * T, HV)),
+               dg=np.zeros((B * T, HV)), dh0=np.zeros((N, HV, K, V)))
+    for n, (s, e) in enumerate(bounds):
+        if cu_seqlens is None:
+            s, e = n * T, (n + 1) * T
+        for hv in range(HV):
+            h = hv // G
+            Hs = [np.zeros((K, V)) if h0 is None else np.asarray(h0[n, hv], np.float64)]
+            cs = list(range(s, e, chunk))
+            for c0 in cs:  # forward, keeping each chunk's start state
+                c1 = min(c0 + chunk, e)
+                _, Hn, _ = chunk_step(qf[c0:c1, h], kf[c0:c1, h], vf[c0:c1, hv], gf[c0:c1, hv],
+                                      bf[c0:c1, hv], Hs[-1], scale)
+                Hs.append(Hn)
+            dH = np.zeros((K, V)) if dht is None else np.asarray(dht[n, hv], np.float64)
+            for ci in reversed(range(len(cs))):
+                c0 = cs[ci]
+                c1 = min(c0 + chunk, e)
+                dq, dk, dv, db, dg, dH = chunk_step_bwd(
+                    qf[c0:c1, h], kf[c0:c1, h], vf[c0:c1, hv], gf[c0:c1, hv], bf[c0:c1, hv],
+                    Hs[ci], df[c0:c1, hv], dH, scale)
+                out["dq"][c0:c1, h] += dq
+                out["dk"][c0:c1, h] += dk
+                out["dv"][c0:c1, hv] = dv
+                out["dbeta"][c0:c1, hv] = db
+                out["dg"][c0:c1, hv] = dg
+            out["dh0"][n, hv] = dH
+    for key in ("dq", "dk", "dv", "dbeta", "dg"):
+        out[key] = out[key].reshape((B, T) + out[key].shape[1:])
+    return out

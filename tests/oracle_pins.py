@@ -17,8 +17,10 @@ planted mistake) and raises AssertionError when the oracle disagrees with:
   * invariants: packed = separate sequences, state passing, grouped heads =
     repeated heads, causality, joint linearity in (v, h0), scale;
   * for the backward: central finite differences of the forward oracle's
-    L = sum <do, o> + <dht, final state> in every input, and the closed form
-    of the gradients when all keys are zero (the state then only decays).
+    L = sum <do, o> + <dht, final state> in every input, the closed form of
+    the gradients when all keys are zero (the state then only decays), and
+    the independent chunkwise derivation of the gradient at several chunk
+    sizes.
 """
 import math
 
@@ -482,6 +484,31 @@ def pin_bwd_no_keys(lib):
            "no keys: ddt_bias")
 
 
+def pin_bwd_chunkwise(lib):
+    """The chunkwise backward (a chunk-by-chunk derivation of the WY form's
+    gradient, oracle/chunkwise.py) equals the token oracle's reverse sweep, at
+    chunk sizes 8, 16 and 64 over packed ragged sequences (one empty), grouped
+    heads, h0 and dht.  dg_raw is compared through the gate's own derivative."""
+    rng = np.random.default_rng(33)
+    lengths = [37, 0, 70]
+    cu = np.cumsum([0] + lengths)
+    B, T, H, HV, K, V = 1, int(cu[-1]), 1, 2, 5, 4
+    x, do, dht = _bwd_case(rng, B, T, H, HV, K, V, len(lengths))
+    scale = 0.9
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g_raw"], x["beta"], x["A_log"], x["dt_bias"],
+                     do, dht, cu_seqlens=cu, h0=x["h0"], scale=scale, lib=lib)
+    g = oracle.gate(x["g_raw"], x["A_log"], x["dt_bias"], lib=lib)
+    xr = x["g_raw"] + x["dt_bias"]
+    slope = np.where(xr > 20, 1.0, 1.0 / (1.0 + np.exp(-np.minimum(xr, 20))))
+    for C in (8, 16, 64):
+        cw = chunkwise.bwd(x["q"], x["k"], x["v"], g, x["beta"], do, dht, cu_seqlens=cu,
+                           h0=x["h0"], chunk=C, scale=scale)
+        for name in ("dq", "dk", "dv", "dbeta", "dh0"):
+            _close(cw[name], ref[name], 1e-10, "chunkwise bwd %s (C=%d)" % (name, C))
+        _close(cw["dg"] * (-np.exp(x["A_log"])) * slope, ref["dg_raw"], 1e-10,
+               "chunkwise bwd dg (C=%d)" % C)
+
+
 ALL_PINS = [pin_gate, pin_kda_gate, pin_brute_force, pin_transition_product, pin_identities,
             pin_chunkwise, pin_invariants, pin_full_forward, pin_segment_scan,
-            pin_bwd_finite_differences, pin_bwd_no_keys]
+            pin_bwd_finite_differences, pin_bwd_no_keys, pin_bwd_chunkwise]
