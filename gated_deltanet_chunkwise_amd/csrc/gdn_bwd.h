@@ -31,7 +31,8 @@
 //     then through the gate g = -exp(A_log) softplus(x), x = g_raw + dt_bias:
 //       dg_raw = dg (-exp(A_log)) softplus'(x),  dA_log = sum dg g,
 //       ddt_bias = sum dg_raw;
-//   * dq, dk of a key head sum its value heads (finalize kernel).
+//   * dq, dk of a key head sum its value heads (a key-head sum kernel; with one
+//     value head per key head the dq/dk and WY kernels write them directly).
 // The forward intermediates are recomputed first by the forward kernels: WY
 // (also storing T) and the state pass in its CHAIN_PLAIN mode (fp32 H_c and
 // v_new).
@@ -42,10 +43,11 @@
 // bf16 calls; the state gradient itself accumulates in fp32).  q, k, v, do are
 // read, and dq, dk, dv written, in the call's dtype.  Intermediates in the
 // workspace are fp32 row-major:
-//   hcp, dhn [hv][slot][K][V]          H_c, dL/dH_{c+1}
-//   vnp, dvn [hv][slot][64][V]         v_new, dL/dv_new
+//   hcp, dhn [hv][slot][V][K]          H_c^T, (dL/dH_{c+1})^T
+//   vnp, dvn [hv][slot][V][64]         v_new^T, (dL/dv_new)^T
 //   tmat     [hv][slot][64][64]        T
-//   dqp, dkp, dwp [hv][slot][64][K]    per value head dq, dk; dw
+//   dqp, dkp, dwp [hv][slot][64][K]    per value head dq (several value heads
+//                                      per key head only), dk; dw
 //   dgp      [hv][slot][64]            dG from the dq/dk kernel
 //   dAp, dbp [hv][slot]                per-chunk sums for dA_log, ddt_bias
 // and fragment-major operands of the backward state pass (k32 fragments in
@@ -372,11 +374,10 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
   }
   for (int s = s1 - 1; s >= s0; --s) {
     const size_t hs = hbase + s, nxt = hbase + (s > s0 ? s - 1 : s0);  // in bounds
-    float* hp = dhn + hs * K * V + v;
+    // transposed: lane (v, g) holds rows 4g..4g+3 of each tile, contiguous in dH^T
+    f32x4* hp = reinterpret_cast<f32x4*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hp[(size_t)(16 * mt + 4 * g + r) * V] = dH[mt][r];
+    for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = dH[mt];
     Frag<E> hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) hb[kb] = frag_from_tiles<E>(dH[2 * kb], dH[2 * kb + 1]);
@@ -390,11 +391,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
     asm volatile("" ::: "memory");
     load_a(nxt);
     asm volatile("" ::: "memory");
-    float* vp = dvn + hs * kChunk * V + v;
+    f32x4* vp = reinterpret_cast<f32x4*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vp[(size_t)(16 * ct + 4 * g + r) * V] = dv[ct][r];
+    for (int ct = 0; ct < 4; ++ct) vp[4 * ct] = dv[ct];
     const Frag<E> nb[2] = {frag_from_tiles<E>(-dv[0], -dv[1]), frag_from_tiles<E>(-dv[2], -dv[3])};
     const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
 #pragma unroll
@@ -428,12 +427,12 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     float* __restrict__ dqp, float* __restrict__ dkp, float* __restrict__ dwp,
     float* __restrict__ dgp, E* __restrict__ dqg) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, NKT = K / 64, TH = kBwdThreads;
-  constexpr int PH1 = 2 * kChunk * VP + K * VP, PH2 = 2 * kChunk * KP + kChunk * kCP;
+  constexpr int PH1 = kChunk * VP + V * kCP + V * KP, PH2 = 2 * kChunk * KP + kChunk * kCP;
   __shared__ __align__(16) float lds[PH1 > PH2 ? PH1 : PH2];
   __shared__ float sg[kChunk], dG[kChunk], red[2];
-  float* const Ds = lds;                    // do
-  float* const Xs = lds + kChunk * VP;      // dv_new, then v_new
-  float* const Hs = lds + 2 * kChunk * VP;  // H_c, then dH_{c+1}  [K][V]
+  float* const Ds = lds;                                // do            [64][V]
+  float* const Xs = lds + kChunk * VP;                  // dv_new^T, then v_new^T  [V][64]
+  float* const Hs = lds + kChunk * VP + V * kCP;        // H_c^T, then dH_{c+1}^T  [V][K]
   float* const Qs = lds;
   float* const Ks = lds + kChunk * KP;
   float* const Pd = lds + 2 * kChunk * KP;
@@ -452,8 +451,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   const float* dHn = dhn + hs * K * V;
 
   stage_rows<V, E, kChunk, TH>(Ds, VP, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
-  stage_rows<V, float, kChunk, TH>(Xs, VP, dvn + hs * kChunk * V, 0, V, kChunk);
-  stage_rows<V, float, K, TH>(Hs, VP, Hc, 0, V, K);
+  stage_rows<kChunk, float, V, TH>(Xs, kCP, dvn + hs * kChunk * V, 0, kChunk, V);
+  stage_rows<K, float, V, TH>(Hs, KP, Hc, 0, K, V);
   if (tid < kChunk) {
     sg[tid] = gam[hs * kChunk + tid];
     dG[tid] = 0.f;
@@ -462,8 +461,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   __syncthreads();
   const float gl = sg[kChunk - 1];
 
-  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T (B operand: H_c
-  // rows k, contiguous in v).
+  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T (B operand: H_c^T,
+  // rows v).
   // (ncols of a 64 x 64 row tile's column pair below or on the diagonal)
   const int npair = pit >= pj0 + 1 ? 2 : pit >= pj0 ? 1 : 0;
   f32x4 dq[2][NKT], dk[2][NKT];
@@ -473,8 +472,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int nt = 0; nt < NKT; ++nt) dq[a][nt] = dw[a][nt] = dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mm_block<V, 2, NKT>(dq, Ds + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
-    mm_block<V, 2, NKT>(dw, Xs + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
+    mm_block<V, 2, NKT>(dq, Ds + 16 * rt0 * VP, VP, 1, Hs + kc0, KP, 1);
+    mm_block<V, 2, NKT>(dw, Xs + 16 * rt0, 1, kCP, Hs + kc0, KP, 1);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -487,7 +486,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
         }
   }
   __syncthreads();
-  stage_rows<V, float, kChunk, TH>(Xs, VP, vnp + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<kChunk, float, V, TH>(Xs, kCP, vnp + hs * kChunk * V, 0, kChunk, V);
   // dH_{c+1} replaces H_c in LDS; each thread first reads the H_c values at the
   // positions it overwrites, for <dH_{c+1}, H_c>.
   {
@@ -495,10 +494,10 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     float acc = 0.f;
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int m = tid + TH * it, row = m / (V / 8), c0 = 8 * (m % (V / 8));
+      const int m = tid + TH * it, row = m / (K / 8), c0 = 8 * (m % (K / 8));
       float e[8];
-      ld8(dHn + (size_t)row * V + c0, e);
-      float* dst = Hs + row * VP + c0;
+      ld8(dHn + (size_t)row * K + c0, e);
+      float* dst = Hs + row * KP + c0;
       const f32x4 h0 = *reinterpret_cast<const f32x4*>(dst);
       const f32x4 h1 = *reinterpret_cast<const f32x4*>(dst + 4);
 #pragma unroll
@@ -512,7 +511,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   __syncthreads();
   // dPm = scale (do v_new^T) * M * e^{dG}
   f32x4 dPm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  mm_pair<V>(dPm, npair, Ds + 16 * pit * VP, VP, 1, Xs + 16 * pj0 * VP, 1, VP);
+  mm_pair<V>(dPm, npair, Ds + 16 * pit * VP, VP, 1, Xs + 16 * pj0, kCP, 1);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int jt = pj0 + b;
@@ -523,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
     }
   }
   // dk_kd = e^{G_last - G} (v_new dH_{c+1}^T)
-  mm_block<V, 2, NKT>(dk, Xs + 16 * rt0 * VP, VP, 1, Hs + kc0 * VP, 1, VP);
+  mm_block<V, 2, NKT>(dk, Xs + 16 * rt0, 1, kCP, Hs + kc0, KP, 1);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -625,7 +624,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
   __shared__ __align__(16) float Ks[kChunk * KP];
   __shared__ __align__(16) float Vs[kChunk * VP];  // later dT, dS
   __shared__ __align__(16) float Wd[kChunk * KP];
-  __shared__ __align__(16) float Dv[kChunk * VP];  // later Y
+  __shared__ __align__(16) float Dv[V * kCP];      // dv_new^T [V][64], later Y
   __shared__ __align__(16) float Tt[kChunk * kCP];
   __shared__ float sg[kChunk], sb[kChunk], dG[kChunk], dB[kChunk];
   float* const dTs = Vs;
@@ -651,7 +650,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
   stage_rows<K, E, kChunk, TH>(Ks, KP, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
   stage_rows<V, E, kChunk, TH>(Vs, VP, vg + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
   stage_rows<K, float, kChunk, TH>(Wd, KP, dwp + hs * kChunk * K, 0, K, kChunk);
-  stage_rows<V, float, kChunk, TH>(Dv, VP, dvn + hs * kChunk * V, 0, V, kChunk);
+  stage_rows<kChunk, float, V, TH>(Dv, kCP, dvn + hs * kChunk * V, 0, kChunk, V);
   stage_rows<kChunk, float, kChunk, TH>(Tt, kCP, tmat + hs * kChunk * kChunk, 0, kChunk, kChunk);
   if (tid < kChunk) {
     sg[tid] = gam[hs * kChunk + tid];
@@ -678,7 +677,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
     f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     mm_pair<K>(x, npair, Wd + 16 * pit * KP, KP, 1, Ks + 16 * pj0 * KP, 1, KP);
-    mm_pair<V>(y, npair, Dv + 16 * pit * VP, VP, 1, Vs + 16 * pj0 * VP, 1, VP);
+    mm_pair<V>(y, npair, Dv + 16 * pit, 1, kCP, Vs + 16 * pj0 * VP, 1, VP);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int j = 16 * (pj0 + b) + lc;
@@ -722,7 +721,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int nv = 0; nv < NVT; ++nv) xu[a][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mm_block<kChunk, 2, NVT>(xu, Tt + 16 * rt0, 1, kCP, Dv + vc0, VP, 1);
+  mm_block<kChunk, 2, NVT>(xu, Tt + 16 * rt0, 1, kCP, Dv + vc0 * kCP, 1, kCP);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int jt = rt0 + a;

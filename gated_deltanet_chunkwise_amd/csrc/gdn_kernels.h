@@ -463,9 +463,10 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
 // CHAIN_END: the same arithmetic without those stores (only the end state is
 // kept).  CHAIN_MAP: u taken as 0 and no stores; started from the identity
 // (with V = K), the end state is the chunks' composed linear map M.
-// CHAIN_PLAIN: the CHAIN_FULL arithmetic, storing H_c and v_new in fp32 plain
-// row-major layouts instead (hcf, vnf then point at float arrays
-// [hv][slot][K][V] and [hv][slot][64][V]); the backward pass reads them.
+// CHAIN_PLAIN: the CHAIN_FULL arithmetic, storing H_c and v_new transposed in
+// fp32 row-major layouts instead (hcf, vnf then point at float arrays
+// [hv][slot][V][K] = H_c^T and [hv][slot][V][64] = v_new^T); the backward pass
+// reads them.
 enum { CHAIN_FULL = 0, CHAIN_END = 1, CHAIN_MAP = 2, CHAIN_PLAIN = 3 };
 
 template <typename E, int K, int V, int MODE = CHAIN_FULL>
@@ -545,20 +546,16 @@ struct ChainStep {
       vnew(Hs, vb, [&](int kb, const Frag<E>& f) { hc[kb * 64] = f; },
            [&](int cb, const Frag<E>& f) { vn[cb * 64] = f; }, none_t);
     } else if constexpr (MODE == CHAIN_PLAIN) {
-      // D tile element r of lane (lc, g) is row 4g + r of the tile, column lc.
+      // D tile element r of lane (lc, g) is row 4g + r of the tile, column lc:
+      // four consecutive elements of row v of the transposed layouts.
       const int g = lane >> 4, v = 16 * vt + (lane & 15);
-      float* hp = reinterpret_cast<float*>(hcf) + hs * K * V + v;
+      f32x4* hp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hcf) + hs * K * V + (size_t)v * K + 4 * g);
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hp[(size_t)(16 * mt + 4 * g + r) * V] = Hs[mt][r];
-      float* vp = reinterpret_cast<float*>(vnf) + hs * kChunk * V + v;
+      for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = Hs[mt];
+      f32x4* vp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(vnf) + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
       vnew(Hs, vb, none_f, none_f, [&](int cb, const f32x4& d0, const f32x4& d1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          vp[(size_t)(32 * cb + 4 * g + r) * V] = d0[r];
-          vp[(size_t)(32 * cb + 16 + 4 * g + r) * V] = d1[r];
-        }
+        vp[8 * cb] = d0;
+        vp[8 * cb + 4] = d1;
       });
     } else {
       vnew(Hs, vb, none_f, none_f, none_t);
