@@ -144,7 +144,8 @@ KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
                 ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
                 ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"),
                 ("gdn_bwd_prep_kernel", "prep"), ("gdn_bwd_chain_kernel", "bwd_chain"),
-                ("gdn_bwd_dqk_kernel", "dqk"), ("gdn_bwd_wy_kernel", "bwd_wy"),
+                ("gdn_bwd_dqk_kernel", "dqk"), ("gdn_bwd_dqk_bf16_kernel", "dqk"),
+                ("gdn_bwd_wy_kernel", "bwd_wy"),
                 ("gdn_bwd_qk_sum_kernel", "sums"))
 
 
@@ -472,9 +473,9 @@ def bench_bwd(args):
     for name, t in zip(gdn.BWD_STAGES, stage_ms):
         a = kern[name]
         sec = t / 1e3
-        # the recompute (forward kernels) and the backward state pass multiply in
-        # the call's dtype; the other backward kernels in fp32
-        mdt = dtype if name in ("recompute", "bwd_chain") else "fp32"
+        # the recompute (forward kernels), the backward state pass and the dq/dk
+        # kernel multiply in the call's dtype; the other backward kernels in fp32
+        mdt = dtype if name in ("recompute", "bwd_chain", "dqk") else "fp32"
         kernels[name] = dict(us=round(t * 1e3, 3), bytes=a["bytes"], flops=a["flops"],
                              hbm_gbs=round(a["bytes"] / sec / 1e9, 1),
                              hbm_frac=round(a["bytes"] / sec / HBM_PEAK, 4),

@@ -392,10 +392,17 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
               reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
               F(bl.dhn), F(bl.dvn)));
   mark(3);
-  if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe, ke,
-              doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
-              F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
+  if (chunk_wgs > 0) {
+    // bf16 calls take the bf16-MFMA variant, fp32 calls the fp32 one
+    if constexpr (std::is_same<E, gdn::bf16>::value)
+      ok(launch(gdn::gdn_bwd_dqk_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo,
+                qe, ke, doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp),
+                F(bl.dkp), F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
+    else
+      ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe,
+                ke, doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
+                F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
+  }
   mark(4);
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke, ve,

@@ -40,7 +40,9 @@
 // Arithmetic is fp32 (fp32 MFMA v_mfma_f32_16x16x4f32, operands staged as fp32
 // in LDS), except in the backward state pass, whose products take their
 // operands in the call's dtype like the forward state pass's (bf16 MFMA for
-// bf16 calls; the state gradient itself accumulates in fp32).  q, k, v, do are
+// bf16 calls; the state gradient itself accumulates in fp32), and in the
+// dq/dk kernel of bf16 calls, whose operands are staged as bf16 for the bf16
+// MFMA (fp32 accumulation; gdn_bwd_dqk_bf16_kernel).  q, k, v, do are
 // read, and dq, dk, dv written, in the call's dtype.  Intermediates in the
 // workspace are fp32 row-major:
 //   hcp, dhn [hv][slot][V][K]          H_c^T, (dL/dH_{c+1})^T
@@ -173,6 +175,14 @@ __device__ __forceinline__ float sum64(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
+}
+// The wave's sum, uniform: DPP row sums, then the four rows' sums read from
+// lanes 0, 16, 32, 48 (no LDS permutes, no per-lane address registers).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum16(x);
+  const int b = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
 // Rows [0, ROWS) into an fp32 LDS tile (stride ld): row r reads
@@ -598,6 +608,369 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
         dkp[o] = dk[a][nt][r];
       }
     }
+  }
+  if (tid < kChunk) {
+    float x = dG[tid];
+    if (tid == kChunk - 1) x += red[1] + fast_exp2(gl) * red[0];
+    dgp[hs * kChunk + tid] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The dq / dk / dw / dG kernel for bf16 calls: the same products on the bf16
+// MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation), with every operand
+// staged in LDS as bf16.  q, k and do are bf16 already; H_c, dH_{c+1}, v_new,
+// dv_new and dPm are rounded to bf16 once, when staged (the forward output
+// kernel takes H_c and v_new the same way); <dH_{c+1}, H_c> is summed from the
+// fp32 values.  A k32 operand needs its 32 reduction indices contiguous in a
+// tile row, so tiles whose reduction index is a column of the stored layout
+// are written transposed (4 x 4 or 4 x 8 blocks per thread, one 8-byte LDS
+// store per transposed row piece, column groups swizzled by tswz) and read
+// with frag_from_trow; the others are copied row by row and read with
+// frag_from_row.  LDS is ~72 KB (two workgroups per CU).
+
+// bf16 LDS row stride for N columns: N + 8 elements (a multiple of 16 bytes).
+template <int N> struct PadB { static constexpr int v = N + 8; };
+
+// Rows [0, kChunk) of a bf16 source into a bf16 LDS tile (stride ld), rows
+// >= len zero; 16 bytes per thread per piece.
+template <int N, int THREADS>
+__device__ __forceinline__ void stage_rows_b(bf16* dst, int ld, const bf16* src, int64_t t0,
+                                             int64_t row_stride, int len) {
+  constexpr int PER = kChunk * N / 8 / THREADS;
+  static_assert(PER * 8 * THREADS == kChunk * N, "whole pieces per thread");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int m = tid + THREADS * it, row = m / (N / 8), c0 = 8 * (m % (N / 8));
+    bf16x8 x = {};
+    if (row < len) x = *reinterpret_cast<const bf16x8*>(src + (t0 + row) * row_stride + c0);
+    *reinterpret_cast<bf16x8*>(dst + row * ld + c0) = x;
+  }
+}
+
+// dst[c][r] = src[r][c] for r < SR, c < SC: fp32 source (row stride SC) into
+// a transposed bf16 LDS tile (row stride DS, column groups swizzled by
+// tswz(c)).  One 4 x 4 block per thread and step.
+template <int SR, int SC, int DS, int THREADS>
+__device__ __forceinline__ void stage_t(bf16* dst, const float* src) {
+  constexpr int BC = SC / 4, NB = (SR / 4) * BC, PER = (NB + THREADS - 1) / THREADS;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int b = threadIdx.x + THREADS * it;
+    if (NB % THREADS == 0 || b < NB) {
+      const int r0 = 4 * (b / BC), c0 = 4 * (b % BC);
+      f32x4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const f32x4*>(src + (size_t)(r0 + j) * SC + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st4(dst + (c0 + j) * DS + (r0 ^ tswz(c0 + j)), x[0][j], x[1][j], x[2][j], x[3][j]);
+    }
+  }
+}
+
+// (at most 128 VGPRs: two eight-wave workgroups per CU)
+template <int K, int V, bool VARLEN>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_dqk_bf16_kernel(
+    Geo geo, const bf16* __restrict__ qg, const bf16* __restrict__ kg,
+    const bf16* __restrict__ dog, const int4* __restrict__ cmap, const float* __restrict__ gam,
+    const float* __restrict__ vnp, const float* __restrict__ dvn, const float* __restrict__ hcp,
+    const float* __restrict__ dhn, float* __restrict__ dqp, float* __restrict__ dkp,
+    float* __restrict__ dwp, float* __restrict__ dgp, bf16* __restrict__ dqg) {
+  constexpr int SK = PadB<K>::v, SV = PadB<V>::v, SC = PadB<kChunk>::v;
+  constexpr int NKT = K / 64, TH = kBwdThreads;
+  constexpr int P12 = 2 * kChunk * SV + K * SV, P3 = 2 * kChunk * SK + 2 * K * SC;
+  static_assert(kChunk * SC <= kChunk * SK, "dPm tiles fit in the q / k tiles");
+  __shared__ __align__(16) bf16 lds[P12 > P3 ? P12 : P3];
+  __shared__ float sg[kChunk], dG[kChunk], red[2];
+  bf16* const Ds = lds;                        // do [64][V]
+  bf16* const Xs = lds + kChunk * SV;          // dv_new, then v_new [64][V] (transposed-written)
+  bf16* const Hs = lds + 2 * kChunk * SV;      // H_c, then dH_{c+1} [K][V] (transposed-written)
+  bf16* const Qs = lds;                        // q [64][K], then dPm [64][64]
+  bf16* const Ks = lds + kChunk * SK;          // k [64][K], then dPm^T [64][64] (transposed-written)
+  bf16* const Qt = lds + 2 * kChunk * SK;      // q^T [K][64] (transposed-written)
+  bf16* const Kt = Qt + K * SC;                // k^T [K][64] (transposed-written)
+  bf16* const Pd = Qs;
+  bf16* const Pt = Ks;
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+  const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4);  // 64 x K ownership
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);               // 64 x 64 ownership
+  const float* Hc = hcp + hs * K * V;
+  const float* dHn = dhn + hs * K * V;
+
+  // H_c^T and dH_{c+1}^T ([V][K] fp32) in 4 x 4 blocks: their dot in fp32;
+  // H_c goes to LDS now, dH_{c+1} stays in registers (already rounded to bf16,
+  // transposed) until the second staging.
+  constexpr int HBC = K / 4, HNB = (V / 4) * HBC, HPER = (HNB + TH - 1) / TH;
+  bf16x4 hd[HPER][4];
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int it = 0; it < HPER; ++it) {
+      const int b = tid + TH * it;
+      if (HNB % TH == 0 || b < HNB) {
+        const int r0 = 4 * (b / HBC), c0 = 4 * (b % HBC);
+        f32x4 hc[4], dh[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hc[j] = *reinterpret_cast<const f32x4*>(Hc + (size_t)(r0 + j) * K + c0);
+          dh[j] = *reinterpret_cast<const f32x4*>(dHn + (size_t)(r0 + j) * K + c0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 p = hc[j] * dh[j];
+          acc += (p[0] + p[1]) + (p[2] + p[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          st4(Hs + (c0 + j) * SV + (r0 ^ tswz(c0 + j)), hc[0][j], hc[1][j], hc[2][j], hc[3][j]);
+          hd[it][j] = to_bf16x4(f32x4{dh[0][j], dh[1][j], dh[2][j], dh[3][j]});
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (tid < kChunk) {
+      sg[tid] = gam[hs * kChunk + tid];
+      dG[tid] = 0.f;
+    }
+    if (tid == 0) red[1] = 0.f;
+    if (tid == 64) red[0] = 0.f;
+    __syncthreads();
+    if (lane == 0) atomicAdd(&red[0], acc);
+  }
+  stage_rows_b<V, TH>(Ds, SV, dog + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  stage_t<V, kChunk, SV, TH>(Xs, dvn + hs * kChunk * V);
+  __syncthreads();
+  const float gl = sg[kChunk - 1];
+
+  // dq_inter = scale e^G (do H_c^T) and dw = -dv_new H_c^T.
+  const int npair = pit >= pj0 + 1 ? 2 : pit >= pj0 ? 1 : 0;
+  f32x4 dq[2][NKT], dk[2][NKT];
+  {
+    f32x4 dw[2][NKT];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) dq[a][nt] = dw[a][nt] = dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int vb = 0; vb < V / 32; ++vb) {
+      Frag<bf16> da[2], xa[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        da[a] = frag_from_row(Ds + (16 * (rt0 + a) + lc) * SV + 32 * vb);
+        xa[a] = frag_from_trow(Xs, 16 * (rt0 + a) + lc, SV, 32 * vb);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) {
+        const Frag<bf16> hb = frag_from_trow(Hs, kc0 + 16 * nt + lc, SV, 32 * vb);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          mma_k32(dq[a][nt], da[a], hb);
+          mma_k32(dw[a][nt], xa[a], hb);
+        }
+      }
+    }
+    // (lane base + constant offsets: no per-store 64-bit address arithmetic)
+    float* const dwl = dwp + (hs * kChunk + 16 * rt0 + 4 * g) * K + kc0 + lc;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = geo.scale * fast_exp2(sg[16 * (rt0 + a) + 4 * g + r]);
+#pragma unroll
+        for (int nt = 0; nt < NKT; ++nt) {
+          dq[a][nt][r] *= e;
+          dwl[(16 * a + r) * K + 16 * nt] = -dw[a][nt][r];
+        }
+      }
+    // scaled here, not deferred to the end (which would keep the factors live)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) asm volatile("" : "+v"(dq[a][nt]));
+  }
+  __syncthreads();
+  // v_new and dH_{c+1} replace dv_new and H_c.
+  stage_t<V, kChunk, SV, TH>(Xs, vnp + hs * kChunk * V);
+#pragma unroll
+  for (int it = 0; it < HPER; ++it) {
+    const int b = tid + TH * it;
+    if (HNB % TH == 0 || b < HNB) {
+      const int r0 = 4 * (b / HBC), c0 = 4 * (b % HBC);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x4*>(Hs + (c0 + j) * SV + (r0 ^ tswz(c0 + j))) = hd[it][j];
+    }
+  }
+  __syncthreads();
+  // dPm = scale (do v_new^T) * M * e^{dG};  dk_kd = e^{G_last - G} (v_new dH_{c+1}^T)
+  f32x4 dPm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 1
+  for (int vb = 0; vb < V / 32; ++vb) {
+    const Frag<bf16> da = frag_from_row(Ds + (16 * pit + lc) * SV + 32 * vb);
+    if (npair >= 1) mma_k32(dPm[0], da, frag_from_trow(Xs, 16 * pj0 + lc, SV, 32 * vb));
+    if (npair >= 2) mma_k32(dPm[1], da, frag_from_trow(Xs, 16 * (pj0 + 1) + lc, SV, 32 * vb));
+    Frag<bf16> xa[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) xa[a] = frag_from_trow(Xs, 16 * (rt0 + a) + lc, SV, 32 * vb);
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const Frag<bf16> hb = frag_from_trow(Hs, kc0 + 16 * nt + lc, SV, 32 * vb);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) mma_k32(dk[a][nt], xa[a], hb);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * pit + 4 * g + r, j = 16 * jt + lc;
+      dPm[b][r] = j <= i ? dPm[b][r] * geo.scale * fast_exp2(sg[i] - sg[j]) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fast_exp2(gl - sg[16 * (rt0 + a) + 4 * g + r]);
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) dk[a][nt][r] *= e;
+    }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) asm volatile("" : "+v"(dk[a][nt]));
+  __syncthreads();
+
+  // q and k: rows [64][K] and transposed [K][64] from one load of 4 rows x 8
+  // columns per thread (q on threads 0..255, k on 256..511).
+  {
+    constexpr int CB = K / 8, NB = (kChunk / 4) * CB;
+    static_assert(NB <= 256, "one block per thread");
+    const int half = tid >> 8, t = tid & 255;
+    if (t < NB) {
+      const bf16* src = (half ? kg : qg) + (size_t)h * K;
+      bf16* nat = half ? Ks : Qs;
+      bf16* tr = half ? Kt : Qt;
+      const int r0 = 4 * (t / CB), c0 = 8 * (t % CB);
+      bf16x8 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = bf16x8{};
+        if (r0 + j < len) x[j] = *reinterpret_cast<const bf16x8*>(src + ((t0 + r0 + j) * geo.H) * K + c0);
+        *reinterpret_cast<bf16x8*>(nat + (r0 + j) * SK + c0) = x[j];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<bf16x4*>(tr + (c0 + e) * SC + (r0 ^ tswz(c0 + e))) =
+            bf16x4{x[0][e], x[1][e], x[2][e], x[3][e]};
+    }
+  }
+  __syncthreads();
+  // R = dPm * (Q K^T): dG_i += row sums, dG_j -= column sums.
+  f32x4 sq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) {
+    const Frag<bf16> qa = frag_from_row(Qs + (16 * pit + lc) * SK + 32 * kb);
+    if (npair >= 1) mma_k32(sq[0], qa, frag_from_row(Ks + (16 * pj0 + lc) * SK + 32 * kb));
+    if (npair >= 2) mma_k32(sq[1], qa, frag_from_row(Ks + (16 * (pj0 + 1) + lc) * SK + 32 * kb));
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    float cs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rr = dPm[b][r] * sq[b][r];
+      cs += rr;
+      const float rs = sum16(rr);
+      if (lc == 0) atomicAdd(&dG[16 * pit + 4 * g + r], rs);
+    }
+    cs = sum_groups(cs);
+    if (g == 0) atomicAdd(&dG[16 * jt + lc], -cs);
+  }
+  // dG_i += q_i . dq_inter_i;  x_j = k_j . dk_kd_j: dG_j -= x_j, sum x -> red[1].
+  {
+    float xs = 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * (rt0 + a) + 4 * g + r;
+        float qd = 0.f, kx = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NKT; ++nt) {
+          const int kk = kc0 + 16 * nt + lc;
+          qd += (float)Qs[i * SK + kk] * dq[a][nt][r];
+          kx += (float)Ks[i * SK + kk] * dk[a][nt][r];
+        }
+        qd = sum16(qd);
+        kx = sum16(kx);
+        if (lc == 0) atomicAdd(&dG[i], qd - kx);
+        xs += lc == 0 ? kx : 0.f;
+      }
+    xs = wave_sum(xs);
+    if (lane == 0) atomicAdd(&red[1], xs);
+  }
+  __syncthreads();
+  // dPm (rows i) over q's tile, dPm^T (rows j, transposed-written) over k's.
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = 16 * (pj0 + b) + lc, i0 = 16 * pit + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Pd[(i0 + r) * SC + j] = (bf16)dPm[b][r];
+    st4(Pt + j * SC + (i0 ^ tswz(j)), dPm[b][0], dPm[b][1], dPm[b][2], dPm[b][3]);
+  }
+  __syncthreads();
+  // dq += dPm K;  dk += dPm^T Q.
+#pragma unroll
+  for (int cb = 0; cb < kChunk / 32; ++cb) {
+    Frag<bf16> pa[2], pta[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      pa[a] = frag_from_row(Pd + (16 * (rt0 + a) + lc) * SC + 32 * cb);
+      pta[a] = frag_from_trow(Pt, 16 * (rt0 + a) + lc, SC, 32 * cb);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const Frag<bf16> kb = frag_from_trow(Kt, kc0 + 16 * nt + lc, SC, 32 * cb);
+      const Frag<bf16> qb = frag_from_trow(Qt, kc0 + 16 * nt + lc, SC, 32 * cb);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        mma_k32(dq[a][nt], pa[a], kb);
+        mma_k32(dk[a][nt], pta[a], qb);
+      }
+    }
+  }
+  {
+    const size_t o = (hs * kChunk + 16 * rt0 + 4 * g) * K + kc0 + lc;
+    float* const dkl = dkp + o;
+    float* const dql = dqp + o;
+    const int i0 = 16 * rt0 + 4 * g;
+    bf16* const dqo = dqg + ((t0 + i0) * geo.H + h) * K + kc0 + lc;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nt = 0; nt < NKT; ++nt) {
+          const int off = (16 * a + r) * K + 16 * nt;
+          // one value head per key head: dq is final here
+          if (geo.G == 1) {
+            if (i0 + 16 * a + r < len) dqo[(size_t)(16 * a + r) * geo.H * K + 16 * nt] = (bf16)dq[a][nt][r];
+          } else {
+            dql[off] = dq[a][nt][r];
+          }
+          dkl[off] = dk[a][nt][r];
+        }
   }
   if (tid < kChunk) {
     float x = dG[tid];
