@@ -64,11 +64,14 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic(shape, esz, has_h0, used_slots):
+def algorithmic(shape, esz, has_h0, used_slots, fused=False):
     """Algorithmic bytes and flops per launch of each kernel and of the whole pass.
 
     Each tensor a kernel consumes or produces counts once at its stored width;
-    flops count the triangular products by their nonzero half.
+    flops count the triangular products by their nonzero half.  fused: the
+    output stage runs inside the state pass ("chain_out"), and WY also reads Q
+    and writes the masked, decayed Q K^T (six 1 KB bf16 fragments per chunk and
+    head at bf16).
     """
     B, T, H, HV, K, V, N = (shape[k] for k in ("B", "T", "H", "HV", "K", "V", "N"))
     ntok = T if shape.get("packed") else B * T
@@ -89,6 +92,15 @@ def algorithmic(shape, esz, has_h0, used_slots):
         "output": dict(bytes=2 * k_in + Ck * K * V * esz + U * V * esz + U * 4 + U * V * esz,
                        flops=U * (C * K + C * V + 2 * K * V)),
     }
+    if fused:
+        p_bytes = Ck * 6 * 64 * 8 * esz        # the P^T fragments WY writes and chain_out reads
+        kern["wy"] = dict(bytes=kern["wy"]["bytes"] + k_in + p_bytes,
+                          flops=kern["wy"]["flops"] + U * C * K)
+        kern["chain_out"] = dict(
+            bytes=U * (2 * K + V) * esz + U * 4 + k_in + p_bytes + U * V * esz
+            + (state if has_h0 else 0) + state,
+            flops=U * (4 * K * V + C * V + 2 * K * V))
+        del kern["chain"], kern["output"]
     path = dict(bytes=2 * k_in + ntok * HV * V * esz + U * 8 + U * V * esz
                 + (state if has_h0 else 0) + state,
                 flops=U * (C * (3 * K + 2 * V) + 6 * K * V))
@@ -140,6 +152,7 @@ def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
 
 
 KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
+                ("gdn_chain_out_kernel", "chain_out"),
                 ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
                 ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
                 ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"),
@@ -624,13 +637,21 @@ def main():
     # per-kernel durations: each kernel alone, K back-to-back launches between two
     # events on the launch stream (gdn_fwd_stages re-runs one stage on the
     # workspace the full steps above left; results are unchanged by it)
+    # (with the output fused into the state pass, the two run as one kernel,
+    # "chain_out", timed with both stage bits)
+    fused = gdn.fuses_output(plan.params, packed)
+    B = gdn.STAGE_BITS
+    stage_list = [(n, B[n]) for n in gdn.STAGES]
+    if fused:
+        stage_list = [("chunk_map", B["chunk_map"]), ("wy", B["wy"]),
+                      ("chain_out", B["chain"] | B["output"])]
     stage_ms = []
-    for name in gdn.STAGES:
+    for name, bits in stage_list:
         if name == "chunk_map" and not packed:
             stage_ms.append(0.0)
             continue
         one = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias,
-                        inp.cu_seqlens, inp.h0, stream=stream, stage_mask=gdn.STAGE_BITS[name])
+                        inp.cu_seqlens, inp.h0, stream=stream, stage_mask=bits)
         for _ in range(max(1, args.warmup)):
             one()
         stage_ms.append(timed(one, args.steps))
@@ -642,9 +663,9 @@ def main():
     if packed:
         lens = (inp_cpu.cu_seqlens[1:] - inp_cpu.cu_seqlens[:-1]).tolist()
         used = sum((L + CHUNK - 1) // CHUNK for L in lens)
-    kern, path, ntok = algorithmic(sh, esz, inp.h0 is not None, used)
+    kern, path, ntok = algorithmic(sh, esz, inp.h0 is not None, used, fused)
     kernels = {}
-    for name, t in zip(gdn.STAGES, stage_ms):
+    for (name, _), t in zip(stage_list, stage_ms):
         if name == "chunk_map" and not packed:
             continue
         a = kern[name]
@@ -693,6 +714,7 @@ def main():
                    "K": s["K"], "V": s["V"], "chunk": CHUNK, "packed_seqs": s["N"] if packed
                    else None, "initial_state": inp.h0 is not None,
                    "seg_chunks": args.seg_chunks},
+        "output_fused": fused,
         "roofline": roof,
         "path_roofline": {"bytes": path["bytes"], "flops": path["flops"],
                           "hbm_frac": round(path["bytes"] / sec / HBM_PEAK, 4),

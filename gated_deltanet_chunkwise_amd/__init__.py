@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     check,
     decode,
     decode_launcher,
+    fuses_output,
     fwd,
     kda_gate,
     kda_gate_launcher,
@@ -39,6 +40,6 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "BWD_NUM_STAGES", "BWD_STAGES", "GdnBackward", "bwd",
     "GDN_BF16", "GDN_F16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
-    "check", "decode", "decode_launcher", "fwd", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
+    "check", "decode", "decode_launcher", "fuses_output", "fwd", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
     "workspace_layout", "workspace_size",
 ]

@@ -16,7 +16,8 @@ GDN_F16 = 2  # KDA gate only
 
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
            "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_decode", "gdn_kda_gate",
-           "gdn_bwd_workspace_size", "gdn_bwd", "gdn_bwd_timed", "gdn_status_string")
+           "gdn_bwd_workspace_size", "gdn_bwd", "gdn_bwd_timed", "gdn_status_string",
+           "gdn_fwd_fuses_output")
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
 # gdn_fwd_stages bits, one per entry of STAGES
@@ -37,7 +38,7 @@ class Params(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     """gdn_workspace_layout_t."""
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gamma", "beta", "w", "kt", "u", "hc", "vn", "chunk_map", "seq_slot",
+                ("gamma", "beta", "w", "kt", "u", "hc", "vn", "pm", "chunk_map", "seq_slot",
                  "seg_slot", "seq_seg", "seg_e", "seg_m", "seg_h", "total")] + [
                     ("num_slots", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                     ("num_segs", ctypes.c_int32)]
@@ -92,6 +93,8 @@ def _declare(lib):
     lib.gdn_bwd.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp]
     lib.gdn_bwd_timed.restype = ctypes.c_int
     lib.gdn_bwd_timed.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp, ctypes.c_void_p]
+    lib.gdn_fwd_fuses_output.restype = ctypes.c_int
+    lib.gdn_fwd_fuses_output.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -117,6 +120,17 @@ def workspace_layout(params, packed=False):
     if st:
         raise GdnError(st, "gdn_fwd_workspace_layout")
     return lay
+
+
+def fuses_output(params, packed=False):
+    """gdn_fwd_fuses_output: True when gdn_fwd runs the output stage inside the
+    state pass for these parameters on the current device."""
+    f = ctypes.c_int32(0)
+    st = load_library().gdn_fwd_fuses_output(ctypes.byref(params), int(bool(packed)),
+                                             ctypes.byref(f))
+    if st:
+        raise GdnError(st, "gdn_fwd_fuses_output")
+    return bool(f.value)
 
 
 def check(params, ptrs, workspace_bytes):

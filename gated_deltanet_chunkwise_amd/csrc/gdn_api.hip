@@ -83,6 +83,7 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   L.u = off;     off = align_up(off + hsl * gdn::kChunk * p->V * esz);
   L.hc = off;    off = align_up(off + hsl * (size_t)p->K * p->V * esz);
   L.vn = off;    off = align_up(off + hsl * gdn::kChunk * p->V * esz);
+  L.pm = off;    off = align_up(off + hsl * gdn::kChunk * gdn::kChunk * esz);  // [4][2] k32 fragments
   L.chunk_map = off; off = align_up(off + (varlen ? (size_t)slots * 16 : 0));
   L.seq_slot = off;  off = align_up(off + (varlen ? (size_t)(N + 1) * 4 : 0));
   // segments: at most ceil(c_n / L) per sequence, summing to <= slots / L + N
@@ -166,6 +167,26 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
                 ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
 }
 
+// Whether the output stage runs fused into the state pass (see
+// gdn_fwd_fuses_output): bf16, no segments, and the units of the state pass
+// filling the compute units once over but not twice, so that the ring form
+// runs two compute waves per workgroup.  Measured on MI355X: with two value
+// tiles per workgroup the fused kernel beats the state pass and output kernel
+// together (B=4, T=8192, H=16: 0.50 against 0.58 ms per forward step); with
+// one, the output waves' operand loads (Q rows and P^T, ~20 KB per chunk and
+// workgroup, mostly from the last-level cache) outlast the ~0.66 us chunk step
+// and hold up the state pass (B=2, T=2048, H=8: 45 us against 33 us).
+template <typename E, int K, int V>
+bool fuses_output(const Plan& pl) {
+  if constexpr (!gdn::ChainOutCfg<E, K, V, 2>::FITS || sizeof(E) != 2) {
+    return false;
+  } else {
+    const int64_t units = (int64_t)pl.geo.N * pl.geo.HV * (V / 16);
+    const int64_t cus = device_cus();
+    return pl.lay.num_segs == 0 && pl.seg_chunks == 0 && units > cus && units <= 2 * cus;
+  }
+}
+
 template <typename E, int K, int V, bool VARLEN>
 gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                  const float* beta, const float* A_log, const float* dt_bias,
@@ -203,10 +224,38 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
     ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
               geo.slots, cmap, seq_slot));
   mark(1);
-  if (work && geo.slots > 0 && (mask & GDN_STAGE_WY))
-    ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(gdn::kWyThreads), s, geo, ke,
-              ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf, nullptr));
+  const bool fused = fuses_output<E, K, V>(pl);
+  Frag<E>* pmf = reinterpret_cast<Frag<E>*>(w + L.pm);
+  if (work && geo.slots > 0 && (mask & GDN_STAGE_WY)) {
+    bool done = false;
+    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS && sizeof(E) == 2) {
+      if (fused) {
+        ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, false, true>, dim3(geo.slots * geo.HV),
+                  dim3(gdn::kWyThreads), s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam,
+                  bet, wf, ktf, uf, nullptr, qe, pmf));
+        done = true;
+      }
+    }
+    if (!done)
+      ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(gdn::kWyThreads),
+                s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam, bet, wf, ktf, uf, nullptr,
+                nullptr, nullptr));
+  }
   mark(2);
+  const unsigned so = GDN_STAGE_STATE | GDN_STAGE_OUTPUT;
+  if (fused && (mask & so) == so) {
+    // the state pass with the output stage in the same workgroups
+    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS && sizeof(E) == 2) {
+      const int units = geo.N * geo.HV * (V / 16);
+      if (work && units > 0)
+        ok(launch(gdn::gdn_chain_out_kernel<E, K, V, VARLEN, 2>, dim3(units / 2),
+                  dim3(64 * gdn::ChainOutCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam,
+                  seq_slot, cmap, h0, fin, qe, pmf, oe));
+    }
+    mark(3);
+    mark(4);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+  }
   if (work && (mask & GDN_STAGE_STATE)) {
     if (L.num_segs > 0) {
       // segment-parallel: E_s and M_s per segment, start states in order, then
@@ -375,7 +424,8 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
               cmap, seq_slot));
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(gdn::kWyThreads), s, geo, ke, ve,
-              a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat)));
+              a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat),
+              nullptr, nullptr));
   if (units > 0 && geo.slots > 0)
     ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_PLAIN>(
         geo, s, wf, ktf, uf, gam, seq_slot, a.h0, nullptr, reinterpret_cast<Frag<E>*>(F(bl.hcp)),
@@ -489,6 +539,21 @@ gdn_status_t gdn_fwd_workspace_layout(const gdn_params_t* p, int packed,
   gdn_status_t st = make_plan(p, packed != 0, &pl);
   if (st == GDN_OK) *out = pl.lay;
   return st;
+}
+
+gdn_status_t gdn_fwd_fuses_output(const gdn_params_t* p, int packed, int32_t* fused) {
+  if (!p || !fused) return GDN_ERR_NULL;
+  Plan pl;
+  gdn_status_t st = make_plan(p, packed != 0, &pl);
+  if (st != GDN_OK) return st;
+  bool f;
+  const bool bf = p->dtype == GDN_BF16;
+  if (p->K == 128 && p->V == 128) f = bf ? fuses_output<gdn::bf16, 128, 128>(pl) : fuses_output<float, 128, 128>(pl);
+  else if (p->K == 128 && p->V == 64) f = bf ? fuses_output<gdn::bf16, 128, 64>(pl) : fuses_output<float, 128, 64>(pl);
+  else if (p->K == 64 && p->V == 128) f = bf ? fuses_output<gdn::bf16, 64, 128>(pl) : fuses_output<float, 64, 128>(pl);
+  else f = bf ? fuses_output<gdn::bf16, 64, 64>(pl) : fuses_output<float, 64, 64>(pl);
+  *fused = f ? 1 : 0;
+  return GDN_OK;
 }
 
 gdn_status_t gdn_fwd_check(const gdn_params_t* p, const void* q, const void* k, const void* v,

@@ -179,7 +179,22 @@ constexpr int kWyThreads = 512;
 
 // With STORE_T, T itself (lower triangular, fp32, [hv][slot][64][64] row-major,
 // zeros above the diagonal) is also written to tmat, for the backward pass.
-template <typename E, int K, int V, bool VARLEN, bool STORE_T = false>
+//
+// With EMIT_P the workgroup also forms the chunk's intra-chunk output matrix
+// P^T = (K Q^T) * [j <= i] * e^{G_i - G_j} (rows j: keys, columns i: queries;
+// diagonal included), the intra-chunk term of the output stage, and stores it
+// for the fused state-and-output pass as the B operands of v_new^T P^T:
+//   pf [hv][slot][it<4][jb<2][lane]   k32 fragment over key rows 32jb.., query
+//                                     column 16it + lane%16 (written for
+//                                     jb <= it/2 only; the rest is all zero)
+// Q is staged in the LDS of T, which is free until the diagonal blocks of T
+// are solved.
+template <typename E, int K>
+constexpr bool wy_q_fits() {
+  return kChunk * (K + 16 / (int)sizeof(E)) * (int)sizeof(E) <= kChunk * (kChunk + 4) * 4;
+}
+
+template <typename E, int K, int V, bool VARLEN, bool STORE_T = false, bool EMIT_P = false>
 __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
                                                      const float* __restrict__ g_raw,
@@ -192,7 +207,10 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
                                                      Frag<E>* __restrict__ wf,
                                                      Frag<E>* __restrict__ ktf,
                                                      Quad<E>* __restrict__ uf,
-                                                     float* __restrict__ tmat) {
+                                                     float* __restrict__ tmat,
+                                                     const E* __restrict__ qg,
+                                                     Frag<E>* __restrict__ pf) {
+  static_assert(!EMIT_P || wy_q_fits<E, K>(), "Q rows must fit the LDS of T");
   constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
   constexpr int KS = K + P;          // K natural row stride
   constexpr int CS = kChunk + P;     // K^T, V^T row stride
@@ -207,6 +225,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   __shared__ float sg[kChunk], sb[kChunk];
   E* const Ks = reinterpret_cast<E*>(r0);
   float* const As = reinterpret_cast<float*>(r0);
+  E* const Qs = reinterpret_cast<E*>(Ts);  // EMIT_P: Q natural [64][KS], until T is formed
 
   int hv, slot;
   head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
@@ -241,6 +260,19 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
     }
   }
+  // EMIT_P: thread t also loads 8-element pieces t and t + 512 of Q's rows.
+  constexpr int NQP = EMIT_P ? (kChunk * (K / 8) + kWyThreads - 1) / kWyThreads : 0;
+  float eq[NQP > 0 ? NQP : 1][8];
+#pragma unroll
+  for (int it = 0; it < NQP; ++it) {
+    const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
+    if (row < kChunk && row < len) {
+      ld8(qg + ((t0 + row) * geo.H + h) * K + qc, eq[it]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) eq[it][j] = 0.f;
+    }
+  }
   if (owns) {
     if (kside) {
 #pragma unroll
@@ -250,6 +282,11 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       st4(tr + (c0 + j) * CS + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
+  }
+#pragma unroll
+  for (int it = 0; it < NQP; ++it) {
+    const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
+    if (row < kChunk) st8(Qs + row * KS + qc, eq[it]);
   }
   // Gate prologue (wave 0, lane = token): g in fp32 with the softplus
   // threshold of the KDA gate guide ("core computation logic"), the chunk-local
@@ -295,7 +332,41 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
                   frag_from_row(Ks + (16 * tj[q] + lc) * KS + 32 * kb));
       }
     }
+    // EMIT_P: fragment job j = wave - 2 (waves 2..7) of P^T: query tile it,
+    // key rows 32jb..32jb+31 (key tiles 2jb, 2jb+1; a key tile past it is 0).
+    f32x4 pt[2];
+    int pit = 0, pjb = 0;
+    if constexpr (EMIT_P) {
+      const int j = wave - 2;
+      pit = j < 1 ? 0 : j < 2 ? 1 : j < 4 ? 2 : 3;
+      pjb = (j == 3 || j == 5) ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int jt = 2 * pjb + q;
+        pt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (wave >= 2 && jt <= pit) {
+#pragma unroll
+          for (int kb = 0; kb < K / 32; ++kb)
+            mma_k32(pt[q], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
+                    frag_from_row(Qs + (16 * pit + lc) * KS + 32 * kb));
+        }
+      }
+    }
     __syncthreads();
+    if constexpr (EMIT_P) {
+      if (wave >= 2) {
+        const int i = 16 * pit + lc;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * (2 * pjb + q) + 4 * g + r;
+            pt[q][r] = j <= i ? pt[q][r] * fast_exp2(sg[i] - sg[j]) : 0.f;
+          }
+        }
+        pf[((hs * 4 + pit) * 2 + pjb) * 64 + lane] = frag_from_tiles<E>(pt[0], pt[1]);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       if (wave + 8 * q < 10) {
@@ -712,7 +783,7 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
 // B_{-1} (before the loop) certifies chunk 0.  The barrier is s_barrier
 // between compiler-level memory fences; the explicit waits named above are
 // the only ones it relies on.
-template <typename E, int K, int V, int NC_, bool HAS_U = true>
+template <typename E, int K, int V, int NC_, bool HAS_U = true, int RESERVE = 0>
 struct RingCfg {
   static constexpr int FB = (int)sizeof(Frag<E>);      // bytes per lane per fragment
   static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
@@ -726,7 +797,7 @@ struct RingCfg {
   static constexpr int NLOAD = NFRAG * SUB;            // 1 KB loads per chunk
   static constexpr int PER = NLOAD / 2;                // per loader wave; the first
                                                        // loader also loads the gate row
-  static constexpr int D0 = (160 * 1024) / STEP;
+  static constexpr int D0 = (160 * 1024 - RESERVE) / STEP;  // RESERVE: other LDS of the kernel
   static constexpr int D = D0 > 6 ? 6 : D0;            // ring stages
   static constexpr int LDS = D * STEP;
   // fp32 fragments at K = 128 do not fit the pipelined registers in 256 VGPRs
@@ -796,6 +867,69 @@ __device__ __forceinline__ void split_pair(const Frag<float>& f, Quad<float>& a,
 __device__ __forceinline__ void wait_lgkm0() {
   // gfx9 s_waitcnt with lgkmcnt = 0 and vmcnt / expcnt at their maxima
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Loader role of the LDS-ring state passes: loader lw (0 or 1) issues loads
+// lw*PER .. lw*PER + PER-1 of each chunk (1 KB blocks of the fragments);
+// loader 0 also loads the gate row.  It takes part in the ring's barriers
+// B_{-1} .. B_{nsteps-1}, refilling stage i % D with chunk i + D after B_i.
+template <typename R, typename E, int K, int V, int NC>
+__device__ __forceinline__ void ring_loader(char* ring, int lw, const Geo& geo,
+                                            const Frag<E>* __restrict__ wf,
+                                            const Frag<E>* __restrict__ ktf,
+                                            const Quad<E>* __restrict__ uf,
+                                            const float* __restrict__ gam, size_t hbase, int vp,
+                                            int nsteps) {
+  constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D;
+  const int lane = threadIdx.x & 63;
+  // Loader l issues loads l*PER .. l*PER + PER-1 of each chunk (1 KB blocks
+  // of the fragments); loader 0 also loads the gate row.  Sources at chunk 0
+  // (per lane); a chunk later every source has advanced by one slot of its
+  // array.
+  const int j0 = lw * R::PER;
+  const char* src0[R::PER];
+  size_t adv[R::PER];
+#pragma unroll
+  for (int jj = 0; jj < R::PER; ++jj) {
+    const int j = j0 + jj;
+    const int f = j / R::SUB, h = j - f * R::SUB;
+    const char* base;
+    if (f < 4 * KB) {
+      const int ct = f / KB, kb = f - ct * KB;
+      base = reinterpret_cast<const char*>(wf + ((hbase * 4 + ct) * KB + kb) * 64);
+      adv[jj] = (size_t)4 * KB * 64 * R::FB;
+    } else if (f < R::FU) {
+      const int f2 = f - 4 * KB, mt = f2 >> 1, cb = f2 & 1;
+      base = reinterpret_cast<const char*>(ktf + ((hbase * KT + mt) * 2 + cb) * 64);
+      adv[jj] = (size_t)KT * 2 * 64 * R::FB;
+    } else {
+      const int q = f - R::FU, vt = NC * vp + (q >> 1), cp = q & 1;
+      base = reinterpret_cast<const char*>(uf + ((hbase * NV + vt) * 2 + cp) * 64 * 2);
+      adv[jj] = (size_t)NV * 2 * 64 * R::FB;
+    }
+    src0[jj] = base + lane * R::FB + 16 * h;
+  }
+  const float* gsrc0 = gam + hbase * kChunk + lane;
+  auto issue = [&](int c) {
+    char* stage = ring + (c % D) * R::STEP;
+#pragma unroll
+    for (int jj = 0; jj < R::PER; ++jj) dma16(src0[jj] + (size_t)c * adv[jj], stage + (j0 + jj) * 1024);
+    if (lw == 0)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc0 + (size_t)c * kChunk),
+                                       (lds_void_t*)(stage + R::GOFF), 4, 0, 0);
+  };
+  for (int c = 0; c < D - 1 && c < nsteps; ++c) issue(c);
+  for (int i = -1; i < nsteps; ++i) {
+    if (i + 1 < nsteps) {
+      // chunk i+1 must have landed; chunks i+2 .. min(nsteps, i+D) - 1 may be in flight
+      const int later = nsteps - 2 - i;
+      const int ahead = later < D - 2 ? later : D - 2;
+      if (lw == 0) wait_ahead<R::PER + 1, D>(ahead);  // also loads the gate row
+      else wait_ahead<R::PER, D>(ahead);
+    }
+    ring_barrier();  // B_i
+    if (i + D < nsteps) issue(i + D);
+  }
 }
 
 template <typename E, int K, int V, bool VARLEN, int NC, int MODE = CHAIN_FULL>
@@ -879,55 +1013,205 @@ __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_
         for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
     }
   } else {
-    // Loader l issues loads l*PER .. l*PER + PER-1 of each chunk (1 KB blocks
-    // of the fragments); loader 0 also loads the gate row.  Sources at chunk 0
-    // (per lane); a chunk later every source has advanced by one slot of its
-    // array.
-    const int lw = wave - NC;  // loader index 0 / 1
-    const int j0 = lw * R::PER;
-    const char* src0[R::PER];
-    size_t adv[R::PER];
+    ring_loader<R, E, K, V, NC>(ring, wave - NC, geo, wf, ktf, uf, gam, hbase, vp, nsteps);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State pass with the output stage fused in (LDS-ring variant).  The chunk
+// states never leave the CU: a workgroup is
+//   NC compute waves -- as in gdn_chain_ring_kernel, except that H_c and v_new
+//                       go to an LDS exchange (two buffers, by chunk parity)
+//                       instead of memory;
+//   two output waves -- output wave ow owns query tiles 2ow and 2ow+1 of every
+//                       chunk: after B_i it takes chunk i's H_c and v_new
+//                       fragments from the exchange and computes, for its
+//                       tiles and the workgroup's NC value tiles,
+//                         o^T = scale (e^{G_i} (H_c^T Q^T) + v_new^T P^T)
+//                       with Q rows read from q and P^T from the WY stage
+//                       (pf), both loaded two chunks ahead into registers;
+//   two loader waves -- as in gdn_chain_ring_kernel.
+// Exchange timing: compute writes buffer i%2 before B_i (its LDS writes have
+// completed when it reaches the barrier); the output waves read it between B_i
+// and B_{i+1} (completed before they reach B_{i+1}); compute writes it again
+// only after B_{i+1}.  Every wave passes the same nsteps + 1 barriers.
+template <typename E, int K, int V, int NC>
+struct ChainOutCfg {
+  static constexpr int FB = (int)sizeof(Frag<E>);
+  static constexpr int XF = K / 32 + 2;                 // exchange fragments per compute wave
+  static constexpr int XBYTES = 2 * NC * XF * 64 * FB;  // both buffers
+  using R = RingCfg<E, K, V, NC, true, XBYTES>;
+  static constexpr int WAVES = NC + 4;                  // compute, two output, two loaders
+  // the ring's registers hold bf16 fragments at any K, fp32 ones at K = 64
+  static constexpr bool FITS = (FB == 16 || K <= 64) && wy_q_fits<E, K>();
+};
+
+template <typename E, int K, int V, bool VARLEN, int NC>
+__global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_chain_out_kernel(
+    Geo geo, const Frag<E>* __restrict__ wf, const Frag<E>* __restrict__ ktf,
+    const Quad<E>* __restrict__ uf, const float* __restrict__ gam,
+    const int* __restrict__ seq_slot, const int4* __restrict__ cmap,
+    const float* __restrict__ h0, float* __restrict__ fin, const E* __restrict__ qg,
+    const Frag<E>* __restrict__ pf, E* __restrict__ og) {
+  using C = ChainOutCfg<E, K, V, NC>;
+  using R = typename C::R;
+  using Step = ChainStep<E, K, V, CHAIN_FULL>;
+  constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D, XF = C::XF;
+  __shared__ __align__(16) char ring[R::LDS];
+  __shared__ __align__(16) Frag<E> xch[2][NC][XF][64];
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
+  const int n = rest / (NV / NC), vp = rest - n * (NV / NC);
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int nsteps = s1 - s0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int g = lane >> 4, lc = lane & 15;
+  const size_t hbase = (size_t)hv * geo.slots + s0;
+
+  if (wave < NC) {
+    const int vt = NC * vp + wave;
+    const int v = 16 * vt + lc;
+    const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+    f32x4 Hs[KT];
+    init_state<K, V, CHAIN_FULL>(Hs, h0, sbase, v, g);
+    Step st;
+    auto read_w = [&](const char* stage) {
 #pragma unroll
-    for (int jj = 0; jj < R::PER; ++jj) {
-      const int j = j0 + jj;
-      const int f = j / R::SUB, h = j - f * R::SUB;
-      const char* base;
-      if (f < 4 * KB) {
-        const int ct = f / KB, kb = f - ct * KB;
-        base = reinterpret_cast<const char*>(wf + ((hbase * 4 + ct) * KB + kb) * 64);
-        adv[jj] = (size_t)4 * KB * 64 * R::FB;
-      } else if (f < R::FU) {
-        const int f2 = f - 4 * KB, mt = f2 >> 1, cb = f2 & 1;
-        base = reinterpret_cast<const char*>(ktf + ((hbase * KT + mt) * 2 + cb) * 64);
-        adv[jj] = (size_t)KT * 2 * 64 * R::FB;
-      } else {
-        const int q = f - R::FU, vt = NC * vp + (q >> 1), cp = q & 1;
-        base = reinterpret_cast<const char*>(uf + ((hbase * NV + vt) * 2 + cp) * 64 * 2);
-        adv[jj] = (size_t)NV * 2 * 64 * R::FB;
-      }
-      src0[jj] = base + lane * R::FB + 16 * h;
-    }
-    const float* gsrc0 = gam + hbase * kChunk + lane;
-    auto issue = [&](int c) {
-      char* stage = ring + (c % D) * R::STEP;
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int jj = 0; jj < R::PER; ++jj) dma16(src0[jj] + (size_t)c * adv[jj], stage + (j0 + jj) * 1024);
-      if (lw == 0)
-        __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc0 + (size_t)c * kChunk),
-                                         (lds_void_t*)(stage + R::GOFF), 4, 0, 0);
+        for (int kb = 0; kb < KB; ++kb) st.w[ct][kb] = ring_frag(stage, ct * KB + kb, lane, (E*)nullptr);
     };
-    for (int c = 0; c < D - 1 && c < nsteps; ++c) issue(c);
-    for (int i = -1; i < nsteps; ++i) {
-      if (i + 1 < nsteps) {
-        // chunk i+1 must have landed; chunks i+2 .. min(nsteps, i+D) - 1 may be in flight
-        const int later = nsteps - 2 - i;
-        const int ahead = later < D - 2 ? later : D - 2;
-        if (lw == 0) wait_ahead<R::PER + 1, D>(ahead);  // also loads the gate row
-        else wait_ahead<R::PER, D>(ahead);
+    auto none_t = [](int, const f32x4&, const f32x4&) {};
+    ring_barrier();  // B_{-1}
+    if (nsteps > 0) read_w(ring);
+    for (int i = 0; i < nsteps; ++i) {
+      const char* stage = ring + (i % D) * R::STEP;
+      const float glast = reinterpret_cast<const float*>(stage + R::GOFF)[kChunk - 1];
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        split_pair(ring_frag(stage, R::FU + 2 * wave + cp, lane, (E*)nullptr), st.u[2 * cp],
+                   st.u[2 * cp + 1]);
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          st.kt[mt][cb] = ring_frag(stage, 4 * KB + 2 * mt + cb, lane, (E*)nullptr);
+      Frag<E> vb[2];
+      Frag<E>* x = &xch[i & 1][wave][0][lane];
+      st.vnew(Hs, vb, [&](int kb, const Frag<E>& f) { x[kb * 64] = f; },
+              [&](int cb, const Frag<E>& f) { x[(KB + cb) * 64] = f; }, none_t);
+      const float dec = fast_exp2(glast);
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) {
+        Hs[mt] *= dec;
+        asm volatile("" : "+v"(Hs[mt]));
       }
+      wait_lgkm0();    // stage i % D read, exchange i % 2 written
       ring_barrier();  // B_i
-      if (i + D < nsteps) issue(i + D);
+      if (i + 1 < nsteps) read_w(ring + ((i + 1) % D) * R::STEP);
+      st.update(Hs, vb);
     }
+    if (fin) {
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
+    }
+  } else if (wave < NC + 2) {
+    // output wave OW (0 or 1) as a compile-time constant, so that every load
+    // count is fixed
+    auto role = [&](auto ow_c) {
+      constexpr int OW = decltype(ow_c)::value;
+      const int h = hv / geo.G;
+      // the sequence's token range: chunk c covers bos + 64c .. min(bos + 64c + 64, eos)
+      int64_t bos = 0, eos = 0;
+      if (nsteps > 0) {
+        if constexpr (VARLEN) {
+          const int4 a = cmap[s0], b = cmap[s1 - 1];
+          bos = a.y;
+          eos = (int64_t)b.y + b.z;
+        } else {
+          bos = (int64_t)n * geo.T;
+          eos = bos + geo.T;
+        }
+      }
+      struct Ops {
+        Frag<E> q[2][KB];  // Q rows of query tiles 2OW, 2OW+1 (B operands over K)
+        Frag<E> p[2][2];   // P^T fragments (it, jb), jb <= it/2
+        float gq[2];       // cumulative gate (log2 units) of the lane's query in each tile
+      };
+      // Every load is unconditional (in bounds): a query row past the chunk's
+      // end reads the chunk's last row instead; only output rows that are not
+      // stored depend on it.  (A load skipped on some path would make the
+      // compiler's wait counts fall back to draining every load.)
+      auto load = [&](Ops& o, int c) {
+        const int64_t t0 = bos + (int64_t)kChunk * c;
+        const int len = (int)min((int64_t)kChunk, eos - t0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          constexpr int it0 = 2 * OW;
+          const int it = it0 + t, row = 16 * it + lc;
+          const E* qr = qg + ((t0 + min(row, len - 1)) * geo.H + h) * K;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) o.q[t][kb] = frag_from_row(qr + 32 * kb);
+#pragma unroll
+          for (int jb = 0; jb <= ((it0 + 1) >> 1); ++jb)
+            if (jb <= ((2 * OW + t) >> 1)) o.p[t][jb] = pf[(((hbase + c) * 4 + it) * 2 + jb) * 64 + lane];
+          o.gq[t] = gam[(hbase + c) * kChunk + row];
+        }
+      };
+      auto out = [&](const Ops& o, int i) {
+        const int64_t t0 = bos + (int64_t)kChunk * i;
+        const int len = (int)min((int64_t)kChunk, eos - t0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const Frag<E>* x = &xch[i & 1][c][0][lane];
+          Frag<E> hc[KB], vn[2];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) hc[kb] = x[kb * 64];
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) vn[jb] = x[(KB + jb) * 64];
+          const int vt = NC * vp + c;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int it = 2 * OW + t;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[kb], o.q[t][kb]);
+            acc *= fast_exp2(o.gq[t]);
+#pragma unroll
+            for (int jb = 0; jb <= ((2 * OW + 1) >> 1); ++jb)
+              if (jb <= ((2 * OW + t) >> 1)) mma_k32(acc, vn[jb], o.p[t][jb]);
+            acc *= geo.scale;
+            const int row = 16 * it + lc;
+            if (row < len)
+              st4(og + ((t0 + row) * geo.HV + hv) * V + 16 * vt + 4 * g, acc[0], acc[1], acc[2],
+                  acc[3]);
+          }
+        }
+      };
+      // One register set: chunk i's operands are loaded at the top of its
+      // step, before B_i, and consumed after it.
+      ring_barrier();  // B_{-1}
+      for (int i = 0; i < nsteps; ++i) {
+        Ops cur;
+        load(cur, i);
+        ring_barrier();  // B_i
+        out(cur, i);
+        wait_lgkm0();    // exchange i % 2 read before B_{i+1}
+      }
+    };
+    if (wave == NC) role(std::integral_constant<int, 0>{});
+    else role(std::integral_constant<int, 1>{});
+  } else {
+    ring_loader<R, E, K, V, NC>(ring, wave - NC - 2, geo, wf, ktf, uf, gam, hbase, vp, nsteps);
   }
 }
 

@@ -122,8 +122,12 @@ typedef struct {
  * cu_seqlens (num_slots = floor(T/64) + N is an upper bound there).
  *   gamma [HV][num_slots][64] fp32  chunk-local cumsum of g, times log2(e)
  *   beta  [HV][num_slots][64] fp32  beta in the same layout (0 past a chunk's end)
- *   w, kt, u, hc, vn                 MFMA-fragment-ordered dtype tensors (see
- *                                    the kernel sources for the lane order)
+ *   w, kt, u, hc, vn, pm             MFMA-fragment-ordered dtype tensors (see
+ *                                    the kernel sources for the lane order);
+ *                                    pm holds the masked, decayed Q K^T of every
+ *                                    chunk, written only when the output stage is
+ *                                    fused into the state pass (below), which then
+ *                                    leaves hc and vn unwritten
  *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32 (cu_seqlens only)
  * With seg_chunks > 0 (num_segs = an upper bound on the segment count):
  *   seg_slot [num_segs+1] int32    first slot of each segment, sequence order
@@ -132,7 +136,7 @@ typedef struct {
  *   seg_m    [num_segs][HV][K][K] fp32        M_s
  * (their offsets are 0 and num_segs is 0 without segments). */
 typedef struct {
-  size_t gamma, beta, w, kt, u, hc, vn, chunk_map, seq_slot;
+  size_t gamma, beta, w, kt, u, hc, vn, pm, chunk_map, seq_slot;
   size_t seg_slot, seq_seg, seg_e, seg_m, seg_h, total;
   int32_t num_slots;
   int32_t num_seqs;
@@ -166,8 +170,24 @@ gdn_status_t gdn_fwd(const gdn_params_t *p, const void *q, const void *k, const 
                      const float *initial_state, void *o, float *final_state,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Whether gdn_fwd, for these parameters on the current device, runs the output
+ * stage fused into the state pass (one kernel) instead of as a kernel of its
+ * own.  It does so for bf16 without segments when the state pass has more
+ * (sequence, value head, 16-column) units than the device has compute units but
+ * at most twice as many, so that each state-pass workgroup holds two of them:
+ * each chunk's start state and v_new then pass from the state-pass waves to
+ * two output waves of the same workgroup through LDS instead of memory, and WY
+ * also emits the chunk's masked, decayed Q K^T (the intra-chunk term of the
+ * output).  The results are bit-identical either way: the same products in the
+ * same order and rounding.  *fused is set to 1 or 0.  Queries the device's
+ * compute-unit count (no GPU work); GDN_ERR_NULL / the gdn_fwd_check shape
+ * errors. */
+gdn_status_t gdn_fwd_fuses_output(const gdn_params_t *p, int packed, int32_t *fused);
+
 /* Number of stages gdn_fwd_timed brackets with events: chunk map, WY (with
- * the gate prologue), state pass, output. */
+ * the gate prologue), state pass, output.  With the output fused into the
+ * state pass (gdn_fwd_fuses_output), the state-pass event follows the fused
+ * kernel and the output event is recorded right after it. */
 #define GDN_NUM_STAGES 4
 
 /* gdn_fwd that also records timing events on `stream`, for profiling:
@@ -198,8 +218,12 @@ gdn_status_t gdn_fwd_timed(const gdn_params_t *p, const void *q, const void *k,
  * results only on a workspace that already holds a full call with the same
  * arguments; the stages are deterministic, so re-running any subset on such a
  * workspace leaves o, final_state and the workspace as they were.
- * GDN_STAGE_ALL is gdn_fwd.  Same validation and errors as gdn_fwd, plus
- * GDN_ERR_UNSUPPORTED for bits outside GDN_STAGE_ALL. */
+ * GDN_STAGE_ALL is gdn_fwd.  When the output is fused into the state pass,
+ * a mask with both GDN_STAGE_STATE and GDN_STAGE_OUTPUT runs the fused kernel;
+ * either bit alone runs the unfused kernel of that stage (the state pass then
+ * writes the chunk states hc and v_new vn, which the unfused output reads).
+ * Same validation and errors as gdn_fwd, plus GDN_ERR_UNSUPPORTED for bits
+ * outside GDN_STAGE_ALL. */
 gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
                             const void *v, const float *g_raw, const float *beta,
                             const float *A_log, const float *dt_bias,

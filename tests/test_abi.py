@@ -141,8 +141,8 @@ def test_workspace_layout():
             assert lay.num_slots == slots
             HV, K, V = 8, 128, 64
             hsl = HV * slots
-            offs = [lay.gamma, lay.beta, lay.w, lay.kt, lay.u, lay.hc, lay.vn, lay.chunk_map,
-                    lay.seq_slot, lay.total]
+            offs = [lay.gamma, lay.beta, lay.w, lay.kt, lay.u, lay.hc, lay.vn, lay.pm,
+                    lay.chunk_map, lay.seq_slot, lay.total]
             assert all(o % 256 == 0 for o in offs)
             assert offs == sorted(offs)
             assert lay.beta - lay.gamma >= hsl * 64 * 4
@@ -150,7 +150,9 @@ def test_workspace_layout():
             assert lay.u - lay.kt >= hsl * 64 * K * esz
             assert lay.hc - lay.u >= hsl * 64 * V * esz
             assert lay.vn - lay.hc >= hsl * K * V * esz
-            assert lay.chunk_map - lay.vn >= hsl * 64 * V * esz
+            assert lay.pm - lay.vn >= hsl * 64 * V * esz
+            # P^T fragments: [it 4][jb 2][lane 64] of 8 elements per chunk and head
+            assert lay.chunk_map - lay.pm >= hsl * 4 * 2 * 64 * 8 * esz
             if packed:
                 assert lay.seq_slot - lay.chunk_map >= slots * 16
                 assert lay.total - lay.seq_slot >= (5 + 1) * 4

@@ -123,6 +123,46 @@ def test_stages_one_at_a_time_match_one_call(packed):
     plan.bind(*args, stage_mask=gdn.STAGE_BITS["output"])()
     torch.cuda.synchronize()
     assert np.array_equal(f64(plan.o), o_ref) and np.array_equal(f64(plan.final_state), f_ref)
+    # the state pass and output together (the fused kernel when the plan fuses
+    # them) give the same bits as the two unfused kernels above
+    say("  output fused into the state pass:", gdn.fuses_output(plan.params, plan.packed))
+    plan.o.fill_(float("nan"))
+    plan.final_state.fill_(float("nan"))
+    plan.bind(*args, stage_mask=gdn.STAGE_BITS["chain"] | gdn.STAGE_BITS["output"])()
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(plan.o), o_ref) and np.array_equal(f64(plan.final_state), f_ref)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fused_output_path(packed):
+    """Shapes whose state pass holds two value tiles per workgroup, where the
+    output stage runs inside the state pass: parity with the oracle, and the
+    same bits as the unfused kernels launched stage by stage."""
+    if packed:
+        lengths = [1, 300, 0, 64, 65, 129, 200]       # 7 sequences x 8 heads x 8 tiles
+        inp = make_inputs(B=1, T=sum(lengths), H=4, HV=8, K=128, V=128, dtype=BF, seed=31,
+                          lengths=lengths, h0=True, scale=0.5)
+    else:
+        inp = make_inputs(B=5, T=300, H=4, HV=8, K=128, V=128, dtype=BF, seed=32, h0=True)
+    s = inp.shape
+    d = inp.to("cuda")
+    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
+                          num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale)
+    fused = gdn.fuses_output(plan.params, plan.packed)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    say("case fused_output", "packed" if packed else "fixed", s, "units", units, "cus", cus,
+        "fused", fused)
+    assert fused == (cus < units <= 2 * cus)
+    check_full(inp, "fused_output_%s" % ("packed" if packed else "fixed"))
+    o_ref, f_ref = run_gpu(inp)
+    plan.o.fill_(float("nan"))
+    plan.final_state.fill_(float("nan"))
+    args = (d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
+    for name in gdn.STAGES:
+        plan.bind(*args, stage_mask=gdn.STAGE_BITS[name])()
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(plan.o), o_ref) and np.array_equal(f64(plan.final_state), f_ref)
 
 
 def test_split_and_resume_matches_one_call():

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import gated_deltanet_chunkwise_amd as gdn
 from gated_deltanet_chunkwise_amd.inputs import make_inputs
 from gpu_helpers import f64, metrics, run_gpu, say
 import oracle
@@ -89,6 +90,18 @@ def decode_vn(buf, HV, slots, V):
     return out
 
 
+def decode_pm(buf, HV, slots):
+    """pf [hv][slot][it<4][jb<2][lane][8] (P^T fragments, jb <= it/2 written)
+    -> P[hv][slot][i][j] (query row i, key column j)."""
+    f = buf.reshape(HV, slots, 4, 2, 64, 8)
+    out = np.zeros((HV, slots, 64, 64))
+    for it in range(4):
+        for jb in range(it // 2 + 1):
+            for i in range(8):
+                out[:, :, 16 * it + LC, 32 * jb + KSLOT[G_OF_LANE, i]] = f[:, :, it, jb, :, i]
+    return out
+
+
 def cmp(x, r, tol, what):
     m = metrics(x, r)
     say("  %-22s rel_l2=%.3e max_abs=%.3e" % (what, m["rel_l2"], m["max_abs"]))
@@ -116,6 +129,17 @@ def test_intermediates(dtype, tol, packed):
     HV, slots = s["HV"], lay.num_slots
     ws = plan.workspace
     et = inp.q.dtype
+    fused = gdn.fuses_output(plan.params, plan.packed)
+    say("  output fused into the state pass:", fused)
+    pm = None
+    if fused:
+        # the full call left the masked, decayed Q K^T of every chunk (from WY)
+        # and no chunk states; the state pass alone writes those
+        pm = decode_pm(read(ws, lay.pm, HV * slots * 64 * 64, et), HV, slots)
+        d = inp.to("cuda")
+        plan.bind(d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0,
+                  stage_mask=gdn.STAGE_BITS["chain"])()
+        torch.cuda.synchronize()
     gam = read(ws, lay.gamma, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
     bet = read(ws, lay.beta, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
     w = decode_w(read(ws, lay.w, HV * slots * 64 * K, et), HV, slots, K)
@@ -146,6 +170,10 @@ def test_intermediates(dtype, tol, packed):
                 cmp(kd[hv, slot, :L], st["kdecay"], tol, tag + " kdecay")
                 cmp(hc[hv, slot], st["H0"], tol, tag + " chunk-start state")
                 cmp(vn[hv, slot, :L], st["v_new"], tol, tag + " v_new")
+                if pm is not None:
+                    cmp(pm[hv, slot, :L, :L], st["P"], tol, tag + " P (masked QK^T)")
+                    assert not np.any(pm[hv, slot, L:]), tag + " P rows past the end"
+                    assert not np.any(pm[hv, slot, :, L:]), tag + " P columns past the end"
                 for name, arr in (("w", w), ("u", u), ("kd", kd), ("vn", vn)):
                     assert not np.any(arr[hv, slot, L:]), tag + " %s rows past the end" % name
             slot += 1
