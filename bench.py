@@ -54,11 +54,21 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash():
-    """Hash of the kernel sources (traffic counters are only valid for this code)."""
+# The sources each op's kernels and launches are built from: traffic counters
+# taken for an op stay valid while these files are unchanged.
+OP_SOURCES = {
+    "gdn_fwd": ("gdn_api.hip", "gdn_common.h", "gdn_kernels.h"),
+    "gdn_bwd": ("gdn_api.hip", "gdn_bwd.h", "gdn_common.h", "gdn_kernels.h"),
+    "kda_gate": ("gdn_common.h", "gdn_kda.h"),
+    "decode": ("gdn_common.h", "gdn_decode.h"),
+}
+
+
+def source_hash(op="gdn_fwd"):
+    """Hash of the sources of one op (traffic counters are only valid for this code)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_chunkwise_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in OP_SOURCES[op]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -180,7 +190,7 @@ def counter_means(path):
     return {k: sum(v) / len(v) for k, v in vals.items()}, (max(copies) if copies else None)
 
 
-def write_traffic(d, workload, copy_bytes):
+def write_traffic(d, workload, copy_bytes, op="gdn_fwd"):
     """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by copy_bytes / (the same counter for a plain copy of
     copy_bytes bytes read and copy_bytes written)."""
@@ -197,7 +207,7 @@ def write_traffic(d, workload, copy_bytes):
     _, copy_write = one("copy_write")
     kf = copy_bytes / (copy_fetch * 1024.0)
     kw = copy_bytes / (copy_write * 1024.0)
-    src = source_hash()
+    src = source_hash(op)
     tr = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
@@ -300,7 +310,7 @@ def bench_kda(args):
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(nbytes / sec / HBM_PEAK, 4), "kernel": "kda_gate",
                      "traffic": None},
-        "kernel_source_hash": source_hash(),
+        "kernel_source_hash": source_hash("kda_gate"),
     }
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
@@ -396,7 +406,7 @@ def bench_decode(args):
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(nbytes / sec / HBM_PEAK, 4), "kernel": "decode",
                      "traffic": None},
-        "kernel_source_hash": source_hash(),
+        "kernel_source_hash": source_hash("decode"),
     }
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
@@ -507,7 +517,7 @@ def bench_bwd(args):
                     frac=d["hbm_frac"])
     roof["kernel"] = dom
     roof["traffic"] = None
-    src = source_hash()
+    src = source_hash("gdn_bwd")
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             ent = json.load(fh).get(wl + ":bwd", {}).get(dom)
@@ -561,7 +571,9 @@ def main():
     args = parse()
     if args.write_traffic:
         key = args.workload + (":bwd" if args.op == "gdn_bwd" else "")
-        write_traffic(args.write_traffic, key, args.copy_mib << 20)
+        op = {"kda_gate": "kda_gate", "decode": "decode"}.get(
+            args.workload, "gdn_bwd" if args.op == "gdn_bwd" else "gdn_fwd")
+        write_traffic(args.write_traffic, key, args.copy_mib << 20, op)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
