@@ -190,6 +190,39 @@ def counter_means(path):
     return {k: sum(v) / len(v) for k, v in vals.items()}, (max(copies) if copies else None)
 
 
+def counters_by_name(path):
+    """Mean value per dispatch of every counter in one rocprofv3
+    counter_collection.csv, per stage: {stage: {counter: mean}}."""
+    import csv
+    vals = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            for key, stage in KERNEL_STAGE:
+                if key in r["Kernel_Name"]:
+                    vals.setdefault(stage, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+                    break
+    return {st: {c: sum(v) / len(v) for c, v in cs.items()} for st, cs in vals.items()}
+
+
+# Optional counter passes read by --write-traffic besides the byte counters:
+# MFMA-busy cycles over active SIMD cycles, and matrix flops counted by the
+# SQ (512 per MFMA "mop").
+MFMA_PASSES = (("mfma_util", "MfmaUtil"), ("mfma_flops", "MfmaFlopsBF16 MfmaFlopsF32"))
+
+
+def kernel_counters(ent):
+    """The MFMA figures of one traffic.json kernel entry, if its passes ran."""
+    c = ent.get("counters", {})
+    out = {}
+    if "MfmaUtil" in c:
+        out["mfma_util"] = round(c["MfmaUtil"] / 100.0, 4)
+    fl = [c[k] for k in ("MfmaFlopsBF16", "MfmaFlopsF32") if k in c]
+    if fl:
+        out["mfma_flops"] = int(round(sum(fl)))
+    return out
+
+
 def write_traffic(d, workload, copy_bytes, op="gdn_fwd"):
     """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by copy_bytes / (the same counter for a plain copy of
@@ -220,6 +253,13 @@ def write_traffic(d, workload, copy_bytes, op="gdn_fwd"):
                       "write_kib_raw": round(write.get(stage, 0.0), 2),
                       "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
                       "source_hash": src}
+    for sub, _ in MFMA_PASSES:
+        f = glob.glob(os.path.join(d, sub, "*_counter_collection.csv"))
+        if len(f) == 1:
+            for stage, cs in counters_by_name(f[0]).items():
+                if stage in ent:
+                    ent[stage].setdefault("counters", {}).update(
+                        {k: round(v, 2) for k, v in cs.items()})
     tr[workload] = ent
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(tr, fh, indent=1, sort_keys=True)
@@ -520,9 +560,15 @@ def bench_bwd(args):
     src = source_hash("gdn_bwd")
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
-            ent = json.load(fh).get(wl + ":bwd", {}).get(dom)
+            tr = json.load(fh).get(wl + ":bwd", {})
+        ent = tr.get(dom)
         if ent and ent.get("source_hash") == src:
             roof["traffic"] = ent["bytes_per_launch"]
+            roof.update(kernel_counters(ent))
+        for name, k in kernels.items():
+            e = tr.get(name)
+            if e and e.get("source_hash") == src:
+                k.update({"counters_" + a: b for a, b in kernel_counters(e).items()})
     sec = ms / 1e3
     out = {
         "metric": "GDN chunk-bwd tokens/s (%s)" % wl, "value": round(ntok / sec, 1),
@@ -707,6 +753,12 @@ def main():
         ent = tr.get(wl, {}).get(dom)
         if ent and ent.get("source_hash") == src:
             roof["traffic"] = ent["bytes_per_launch"]
+            roof.update(kernel_counters(ent))
+        # counter-measured MFMA utilisation and matrix flops of every kernel
+        for name, k in kernels.items():
+            e = tr.get(wl, {}).get(name)
+            if e and e.get("source_hash") == src:
+                k.update({"counters_" + a: b for a, b in kernel_counters(e).items()})
     sec = ms / 1e3
     out = {
         "metric": METRIC,
