@@ -165,6 +165,25 @@ def test_fused_output_path(packed):
     assert np.array_equal(f64(plan.o), o_ref) and np.array_equal(f64(plan.final_state), f_ref)
 
 
+@pytest.mark.parametrize("K,V,B,T,HV,h0", [(64, 64, 5, 130, 16, False), (64, 128, 5, 40, 8, True),
+                                            (128, 64, 5, 200, 16, True), (128, 128, 3, 64, 16, False)])
+def test_fused_output_head_sizes(K, V, B, T, HV, h0):
+    """The output fused into the state pass at every supported head size, with
+    ragged tails, a sequence shorter than one chunk and an exact single chunk
+    (units = B * HV * V/16 between one and two times the CU count of the
+    256-CU device)."""
+    inp = make_inputs(B=B, T=T, H=HV // 2, HV=HV, K=K, V=V, dtype=BF, seed=40 + K + V + T,
+                      h0=h0, scale=0.9)
+    s = inp.shape
+    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], torch.bfloat16, "cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    path = gdn.fuses_output(plan.params, False)
+    say("case fused_heads", s, "units", units, "path", path)
+    assert path == (cus < units <= 2 * cus)
+    check_full(inp, "fused_heads_K%d_V%d_T%d" % (K, V, T))
+
+
 def test_split_and_resume_matches_one_call():
     # the final state is a checkpoint: run [0, s) then [s, T) from it
     inp = make_inputs(B=1, T=640, H=2, HV=2, K=128, V=128, dtype=F32, seed=7,
