@@ -454,11 +454,18 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
                 F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
   }
   mark(4);
-  if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke, ve,
-              a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp), F(bl.dvn),
-              F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw, F(bl.dAp),
-              F(bl.dbp), static_cast<E*>(a.dk)));
+  if (chunk_wgs > 0) {
+    if constexpr (std::is_same<E, gdn::bf16>::value)
+      ok(launch(gdn::gdn_bwd_wy_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s,
+                geo, ke, ve, a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp),
+                F(bl.dvn), F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw,
+                F(bl.dAp), F(bl.dbp), static_cast<E*>(a.dk)));
+    else
+      ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke,
+                ve, a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp), F(bl.dvn),
+                F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw, F(bl.dAp),
+                F(bl.dbp), static_cast<E*>(a.dk)));
+  }
   mark(5);
   if (geo.slots > 0 && geo.G > 1)
     ok(launch(gdn::gdn_bwd_qk_sum_kernel<E, K, VARLEN>, dim3((unsigned)geo.slots * geo.H),

@@ -1220,6 +1220,414 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The WY backward for bf16 calls: the products of gdn_bwd_wy_kernel on the bf16
+// MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation) with every operand staged
+// in LDS as bf16: k and v exactly, dw, dv_new, T, dT, Y and dS rounded once
+// when staged.  The masks, decays, dbeta / dG sums and the gate backward are
+// the fp32 kernel's.  Operands whose reduction index is a column of the stored
+// layout are written transposed (swizzled by tswz, read with frag_from_trow);
+// the others as natural rows (frag_from_row).  LDS is K natural plus one pool
+// reused phase by phase (~70 KB at K = V = 128: two workgroups per CU):
+//   1 (dT):        dw [64][K], v [64][V], dv_new [64][V] (transposed-written)
+//   2 (X_w, X_u):  dw^T [K][64] (t-w), dv_new^T [V][64], T^T [64][64] (t-w)
+//   3 (Y):         dT^T (t-w), T^T; then Y natural
+//   4 (dA, dS):    Y, T natural, K
+//   5 (dk):        K^T (t-w), dS natural, dS^T (t-w)
+// dw, dv_new and T are read from memory once, at the start, into registers (as
+// bf16), and written to LDS in each layout when its phase comes.
+template <int R, int C>
+struct Blk4 {  // 4 x 4 blocks of an R x C matrix, one per thread and step
+  static constexpr int BC = C / 4, NB = (R / 4) * BC, PER = (NB + kBwdThreads - 1) / kBwdThreads;
+};
+
+// (at most 128 VGPRs: two eight-wave workgroups per CU)
+template <int K, int V, bool VARLEN>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_wy_bf16_kernel(
+    Geo geo, const bf16* __restrict__ kg, const bf16* __restrict__ vg,
+    const float* __restrict__ g_raw, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const int4* __restrict__ cmap,
+    const float* __restrict__ gam, const float* __restrict__ bet, const float* __restrict__ tmat,
+    const float* __restrict__ dwp, const float* __restrict__ dvn, const float* __restrict__ dgp,
+    float* __restrict__ dkp, bf16* __restrict__ dvg, float* __restrict__ dbeta,
+    float* __restrict__ dg_raw, float* __restrict__ dAp, float* __restrict__ dbp,
+    bf16* __restrict__ dkg) {
+  constexpr int SK = PadB<K>::v, SV = PadB<V>::v, SC = PadB<kChunk>::v;
+  constexpr int NKT = K / 64, NVT = V / 64, TH = kBwdThreads;
+  constexpr int KN = kChunk * SK;
+  constexpr int P1 = kChunk * SK + 2 * kChunk * SV;
+  constexpr int P2 = (K + V + kChunk) * SC;
+  constexpr int P5 = (K + 2 * kChunk) * SC;
+  constexpr int POOL = P1 > P2 ? (P1 > P5 ? P1 : P5) : (P2 > P5 ? P2 : P5);
+  constexpr int TT = (K + V) * SC;  // T^T, phases 2-3
+  static_assert(TT >= 2 * kChunk * SC, "dT^T and Y fit below T^T");
+  __shared__ __align__(16) bf16 lds[KN + POOL];
+  __shared__ float sg[kChunk], sb[kChunk], dG[kChunk], dB[kChunk];
+  bf16* const Kn = lds;
+  bf16* const pool = lds + KN;
+  bf16* const Wn = pool;                    // 1: dw
+  bf16* const Vn = pool + kChunk * SK;      // 1: v
+  bf16* const Dn = Vn + kChunk * SV;        // 1: dv_new (t-w from [V][64])
+  bf16* const Wt = pool;                    // 2: dw^T (t-w)
+  bf16* const Dt = pool + K * SC;           // 2: dv_new^T rows
+  bf16* const Tt = pool + TT;               // 2-3: T^T (t-w)
+  bf16* const dTt = pool;                   // 3: dT^T (t-w)
+  bf16* const Yn = pool + kChunk * SC;      // 3-4: Y
+  bf16* const Tn = pool;                    // 4: T
+  bf16* const Kt = pool;                    // 5: K^T (t-w)
+  bf16* const Sn = pool + K * SC;           // 5: dS
+  bf16* const St = Sn + kChunk * SC;        // 5: dS^T (t-w)
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  const size_t hs = (size_t)hv * geo.slots + slot;
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) {
+    if (threadIdx.x == 0) {
+      dAp[hs] = 0.f;
+      dbp[hs] = 0.f;
+    }
+    return;
+  }
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4), vc0 = (wave & 3) * (V / 4);
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);
+
+  // dw [64][K], dv_new^T [V][64] and T [64][64] (fp32) into registers as bf16,
+  // 4 x 4 blocks per thread: row j of block b is w[b][j].
+  using BW = Blk4<kChunk, K>;
+  using BD = Blk4<V, kChunk>;
+  using BT = Blk4<kChunk, kChunk>;
+  bf16x4 wr[BW::PER][4], dr[BD::PER][4], tr[BT::PER][4];
+  auto fetch = [&](auto B, bf16x4 (&dst)[decltype(B)::PER][4], const float* src, int C) {
+    using Bk = decltype(B);
+#pragma unroll
+    for (int it = 0; it < Bk::PER; ++it) {
+      const int b = tid + TH * it;
+      if (Bk::NB % TH == 0 || b < Bk::NB) {
+        const int r0 = 4 * (b / Bk::BC), c0 = 4 * (b % Bk::BC);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          dst[it][j] = to_bf16x4(*reinterpret_cast<const f32x4*>(src + (size_t)(r0 + j) * C + c0));
+      }
+    }
+  };
+  fetch(BW{}, wr, dwp + hs * kChunk * K, K);
+  fetch(BD{}, dr, dvn + hs * kChunk * V, kChunk);
+  fetch(BT{}, tr, tmat + hs * kChunk * kChunk, kChunk);
+  // natural rows of a held block matrix: dst[(r0 + j) * ld + c0 ..] = row j
+  auto put_nat = [&](auto B, const bf16x4 (&src)[decltype(B)::PER][4], bf16* dst, int ld) {
+    using Bk = decltype(B);
+#pragma unroll
+    for (int it = 0; it < Bk::PER; ++it) {
+      const int b = tid + TH * it;
+      if (Bk::NB % TH == 0 || b < Bk::NB) {
+        const int r0 = 4 * (b / Bk::BC), c0 = 4 * (b % Bk::BC);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x4*>(dst + (r0 + j) * ld + c0) = src[it][j];
+      }
+    }
+  };
+  // transposed, swizzled: dst[c][r] = m[r][c]
+  auto put_tr = [&](auto B, const bf16x4 (&src)[decltype(B)::PER][4], bf16* dst, int ld) {
+    using Bk = decltype(B);
+#pragma unroll
+    for (int it = 0; it < Bk::PER; ++it) {
+      const int b = tid + TH * it;
+      if (Bk::NB % TH == 0 || b < Bk::NB) {
+        const int r0 = 4 * (b / Bk::BC), c0 = 4 * (b % Bk::BC);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) col[i] = src[it][i][j];
+          *reinterpret_cast<bf16x4*>(dst + (c0 + j) * ld + (r0 ^ tswz(c0 + j))) = col;
+        }
+      }
+    }
+  };
+
+  stage_rows_b<K, TH>(Kn, SK, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows_b<V, TH>(Vn, SV, vg + (size_t)hv * V, t0, (int64_t)geo.HV * V, len);
+  put_nat(BW{}, wr, Wn, SK);
+  put_tr(BD{}, dr, Dn, SV);
+  if (tid < kChunk) {
+    sg[tid] = gam[hs * kChunk + tid];
+    sb[tid] = bet[hs * kChunk + tid];
+    dG[tid] = 0.f;
+    dB[tid] = 0.f;
+  }
+  __syncthreads();
+
+  // 1. dT (strictly lower part): x = dw K^T, y = dv_new V^T.
+  const int npair = pit >= pj0 + 1 ? 2 : pit >= pj0 ? 1 : 0;
+  f32x4 dT[2];
+  {
+    f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (npair > 0) {
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        const Frag<bf16> a = frag_from_row(Wn + (16 * pit + lc) * SK + 32 * kb);
+        mma_k32(x[0], a, frag_from_row(Kn + (16 * pj0 + lc) * SK + 32 * kb));
+        if (npair > 1) mma_k32(x[1], a, frag_from_row(Kn + (16 * (pj0 + 1) + lc) * SK + 32 * kb));
+      }
+#pragma unroll
+      for (int vb = 0; vb < V / 32; ++vb) {
+        const Frag<bf16> a = frag_from_trow(Dn, 16 * pit + lc, SV, 32 * vb);
+        mma_k32(y[0], a, frag_from_row(Vn + (16 * pj0 + lc) * SV + 32 * vb));
+        if (npair > 1) mma_k32(y[1], a, frag_from_row(Vn + (16 * (pj0 + 1) + lc) * SV + 32 * vb));
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j = 16 * (pj0 + b) + lc;
+      const float fw = sb[j] * fast_exp2(sg[j]), fu = sb[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * pit + 4 * g + r;
+        dT[b][r] = j < i ? x[b][r] * fw + y[b][r] * fu : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  put_tr(BW{}, wr, Wt, SC);
+  put_nat(BD{}, dr, Dt, SC);
+  put_tr(BT{}, tr, Tt, SC);
+  __syncthreads();
+
+  // 2. X_w = T^T dw: dk += beta e^G X_w and the k . X_w terms of dbeta, dG;
+  //    X_u = T^T dv_new: dv = beta X_u and the v . X_u term of dbeta.
+  f32x4 dk[2][NKT], xu[2][NVT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) dk[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nv = 0; nv < NVT; ++nv) xu[a][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll 1
+  for (int ib = 0; ib < 2; ++ib) {
+    Frag<bf16> ta[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) ta[a] = frag_from_trow(Tt, 16 * (rt0 + a) + lc, SC, 32 * ib);
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const Frag<bf16> wb = frag_from_trow(Wt, kc0 + 16 * nt + lc, SC, 32 * ib);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) mma_k32(dk[a][nt], ta[a], wb);
+    }
+#pragma unroll
+    for (int nv = 0; nv < NVT; ++nv) {
+      const Frag<bf16> db = frag_from_row(Dt + (vc0 + 16 * nv + lc) * SC + 32 * ib);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) mma_k32(xu[a][nv], ta[a], db);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int jt = rt0 + a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jt + 4 * g + r;
+      const float eg = fast_exp2(sg[j]);
+      float kx = 0.f, vx = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) kx += (float)Kn[j * SK + kc0 + 16 * nt + lc] * dk[a][nt][r];
+#pragma unroll
+      for (int nv = 0; nv < NVT; ++nv) {
+        const int vv = vc0 + 16 * nv + lc;
+        if (j < len) {
+          vx += (float)vg[((t0 + j) * geo.HV + hv) * V + vv] * xu[a][nv][r];
+          dvg[((t0 + j) * geo.HV + hv) * V + vv] = (bf16)(sb[j] * xu[a][nv][r]);
+        }
+      }
+      kx = sum16(kx);
+      vx = sum16(vx);
+      if (lc == 0) {
+        atomicAdd(&dB[j], eg * kx + vx);
+        atomicAdd(&dG[j], sb[j] * eg * kx);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NKT; ++nt) dk[a][nt][r] *= sb[j] * eg;
+    }
+  }
+  __syncthreads();
+  // 3. Y = T^T dT.
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = 16 * (pj0 + b) + lc;
+    *reinterpret_cast<bf16x4*>(dTt + j * SC + ((16 * pit + 4 * g) ^ tswz(j))) = to_bf16x4(dT[b]);
+  }
+  __syncthreads();
+  {
+    f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const Frag<bf16> ta = frag_from_trow(Tt, 16 * pit + lc, SC, 32 * ib);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) mma_k32(y[b], ta, frag_from_trow(dTt, 16 * (pj0 + b) + lc, SC, 32 * ib));
+    }
+    // Y natural (below T^T, apart from dT^T)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Yn[(16 * pit + 4 * g + r) * SC + 16 * (pj0 + b) + lc] = (bf16)y[b][r];
+  }
+  __syncthreads();
+  put_nat(BT{}, tr, Tn, SC);
+  __syncthreads();
+  // 4. dA = -strictly_lower(Y T^T); with S = K K^T and A = beta_i e^{dG} S:
+  //    dG += rows - columns of dA * A, dbeta += rows of dA e^{dG} S, dS = dA beta e^{dG}.
+  f32x4 dS[2];
+  {
+    f32x4 yy[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 ss[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (npair > 0) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const Frag<bf16> a = frag_from_row(Yn + (16 * pit + lc) * SC + 32 * mb);
+        mma_k32(yy[0], a, frag_from_row(Tn + (16 * pj0 + lc) * SC + 32 * mb));
+        if (npair > 1) mma_k32(yy[1], a, frag_from_row(Tn + (16 * (pj0 + 1) + lc) * SC + 32 * mb));
+      }
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        const Frag<bf16> a = frag_from_row(Kn + (16 * pit + lc) * SK + 32 * kb);
+        mma_k32(ss[0], a, frag_from_row(Kn + (16 * pj0 + lc) * SK + 32 * kb));
+        if (npair > 1) mma_k32(ss[1], a, frag_from_row(Kn + (16 * (pj0 + 1) + lc) * SK + 32 * kb));
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int jt = pj0 + b;
+      const f32x4 y = yy[b], sk = ss[b];
+      const int c = 16 * jt + lc;
+      float cs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ar = 16 * pit + 4 * g + r;
+        // above the diagonal e^{G_a - G_c} can overflow: select, never multiply by 0
+        const float da = c < ar ? -y[r] : 0.f;
+        const float e = c < ar ? fast_exp2(sg[ar] - sg[c]) : 0.f;
+        const float des = da * e * sk[r];
+        const float z = des * sb[ar];
+        cs += z;
+        const float rz = sum16(z), rb = sum16(des);
+        if (lc == 0) {
+          atomicAdd(&dG[ar], rz);
+          atomicAdd(&dB[ar], rb);
+        }
+        dS[b][r] = da * sb[ar] * e;
+      }
+      cs = sum_groups(cs);
+      if (g == 0) atomicAdd(&dG[c], -cs);
+    }
+  }
+  __syncthreads();
+  // the dq/dk kernel's dk terms of this wave's tiles (loaded here, not at the
+  // start, to keep 16 registers free through the phases before)
+  float dk0[2][NKT][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dk0[a][nt][r] = dkp[(hs * kChunk + 16 * (rt0 + a) + 4 * g + r) * K + kc0 + 16 * nt + lc];
+  // 5. dk += (dS + dS^T) K.  K^T from the natural rows (4 rows x 8 columns per thread).
+  {
+    constexpr int CB = K / 8, NB = (kChunk / 4) * CB;
+#pragma unroll
+    for (int b = tid; b < NB; b += TH) {
+      const int r0 = 4 * (b / CB), c0 = 8 * (b % CB);
+      bf16x8 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const bf16x8*>(Kn + (r0 + j) * SK + c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
+        *reinterpret_cast<bf16x4*>(Kt + (c0 + e) * SC + (r0 ^ tswz(c0 + e))) = col;
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = 16 * (pj0 + b) + lc;
+    *reinterpret_cast<bf16x4*>(St + j * SC + ((16 * pit + 4 * g) ^ tswz(j))) = to_bf16x4(dS[b]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sn[(16 * pit + 4 * g + r) * SC + j] = (bf16)dS[b][r];
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int ib = 0; ib < 2; ++ib) {
+    Frag<bf16> sa[2], sat[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      sa[a] = frag_from_row(Sn + (16 * (rt0 + a) + lc) * SC + 32 * ib);
+      sat[a] = frag_from_trow(St, 16 * (rt0 + a) + lc, SC, 32 * ib);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const Frag<bf16> kb = frag_from_trow(Kt, kc0 + 16 * nt + lc, SC, 32 * ib);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        mma_k32(dk[a][nt], sa[a], kb);
+        mma_k32(dk[a][nt], sat[a], kb);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int jt = rt0 + a;
+#pragma unroll
+    for (int nt = 0; nt < NKT; ++nt) {
+      const int kc = kc0 + 16 * nt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jt + 4 * g + r;
+        const size_t o = (hs * kChunk + j) * K + kc + lc;
+        // one value head per key head: dk is final here
+        if (geo.G == 1) {
+          if (j < len) dkg[((t0 + j) * geo.H + h) * K + kc + lc] = (bf16)(dk0[a][nt][r] + dk[a][nt][r]);
+        } else {
+          dkp[o] = dk0[a][nt][r] + dk[a][nt][r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // dg = reversed chunk-local cumsum of dG; gate backward.
+  if (wave == 0) {
+    float x = dG[lane] + dgp[hs * kChunk + lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (lane + off < 64) x += y;
+    }
+    float sa = 0.f, sbias = 0.f;
+    if (lane < len) {
+      const int64_t t = t0 + lane;
+      const float xr = g_raw[t * geo.HV + hv] + (dt_bias ? dt_bias[hv] : 0.f);
+      const float ea = expf(A_log[hv]);
+      const float gt = -ea * gate_softplus(xr);
+      const float slope = xr > 20.f ? 1.f : 1.f / (1.f + fast_exp2(-xr * kLog2e));
+      const float dgr = x * (-ea) * slope;
+      dbeta[t * geo.HV + hv] = dB[lane];
+      dg_raw[t * geo.HV + hv] = dgr;
+      sa = x * gt;
+      sbias = dgr;
+    }
+    sa = sum64(sa);
+    sbias = sum64(sbias);
+    if (lane == 0) {
+      dAp[hs] = sa;
+      dbp[hs] = sbias;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dq, dk of key head h: the sum of its G value heads' terms, in head order,
 // rounded to the dtype.  One workgroup per (chunk slot, key head).
 template <typename E, int K, bool VARLEN>
