@@ -163,6 +163,13 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
                     dim3(64 * gdn::RingCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
                     h0, fin, hcf, vnf);
   }
+  // bf16, beyond the ring variant: two value tiles per wave while the waves
+  // (one per SIMD) are all resident at once
+  if constexpr (MODE == gdn::CHAIN_FULL && sizeof(E) == 2 && (V / 16) % 2 == 0) {
+    if (units <= 8 * cus)
+      return launch(gdn::gdn_chain2_kernel<E, K, V, VARLEN>, dim3(units / 2), dim3(64), s, geo, wf,
+                    ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
+  }
   return launch(gdn::gdn_chain_kernel<E, K, V, VARLEN, MODE>, dim3(units), dim3(64), s, geo, wf,
                 ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
 }

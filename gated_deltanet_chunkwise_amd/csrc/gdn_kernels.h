@@ -754,6 +754,139 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(Geo geo, const Frag<E>* _
 }
 
 // ---------------------------------------------------------------------------
+// State pass, register variant with two value tiles per wave (bf16, CHAIN_FULL):
+// one wave per (sequence, value head, 32 value columns).  The chunk's w and
+// kd^T fragments are loaded once for both tiles (34 KB per chunk per wave, as
+// for one tile), which halves the operand stream per value column of the
+// one-tile register variant; used when the units are too many for the ring
+// variant's workgroups to be resident at once.  The next chunk's operands are
+// loaded one chunk ahead (two register sets).
+template <typename E, int K, int V>
+struct ChainStep2 {
+  static constexpr int KB = K / 32, KT = K / 16, NV = V / 16;
+  Frag<E> w[4][KB];
+  Frag<E> kt[KT][2];
+  Quad<E> u[2][4];
+  float gl;  // lane l: entry l of the chunk's (log2-scaled) cumulative gate row
+
+  __device__ __forceinline__ void load(const Frag<E>* __restrict__ wf,
+                                       const Frag<E>* __restrict__ ktf,
+                                       const Quad<E>* __restrict__ uf,
+                                       const float* __restrict__ gam, size_t hs, int vt0,
+                                       int lane) {
+    gl = gam[hs * kChunk + lane];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) w[ct][kb] = wf[((hs * 4 + ct) * KB + kb) * 64 + lane];
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) kt[mt][cb] = ktf[((hs * KT + mt) * 2 + cb) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        u[t][ct] = uf[(((hs * NV + vt0 + t) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
+  }
+
+  // One chunk for both tiles: store H_c and v_new, then
+  // H <- e^{G_last} H + kd^T v_new.
+  __device__ __forceinline__ void compute(f32x4 (&Hs)[2][KT], Frag<E>* __restrict__ hcf,
+                                          Frag<E>* __restrict__ vnf, size_t hs, int vt0,
+                                          int lane) const {
+    Frag<E> vb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      Frag<E> hb[KB];
+      Frag<E>* hc = hcf + (hs * NV + vt0 + t) * KB * 64 + lane;
+      Frag<E>* vn = vnf + (hs * NV + vt0 + t) * 2 * 64 + lane;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        hb[kb] = frag_from_tiles<E>(Hs[t][2 * kb], Hs[t][2 * kb + 1]);
+        hc[kb * 64] = hb[kb];
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          mma_k32(p0, w[2 * cb][kb], hb[kb]);
+          mma_k32(p1, w[2 * cb + 1][kb], hb[kb]);
+        }
+        vb[t][cb] = frag_from_tiles<E>(quad_f32(u[t][2 * cb]) - p0, quad_f32(u[t][2 * cb + 1]) - p1);
+        vn[cb * 64] = vb[t][cb];
+      }
+    }
+    const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt) Hs[t][mt] *= dec;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) mma_k32(Hs[t][mt], kt[mt][cb], vb[t][cb]);
+  }
+};
+
+template <typename E, int K, int V, bool VARLEN>
+__global__ __launch_bounds__(64) void gdn_chain2_kernel(Geo geo, const Frag<E>* __restrict__ wf,
+                                                        const Frag<E>* __restrict__ ktf,
+                                                        const Quad<E>* __restrict__ uf,
+                                                        const float* __restrict__ gam,
+                                                        const int* __restrict__ seq_slot,
+                                                        const float* __restrict__ h0,
+                                                        float* __restrict__ fin,
+                                                        Frag<E>* __restrict__ hcf,
+                                                        Frag<E>* __restrict__ vnf) {
+  using Step = ChainStep2<E, K, V>;
+  constexpr int NV = V / 16, KT = K / 16, NP = NV / 2;
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NP, hv, rest);
+  const int n = rest / NP, vt0 = 2 * (rest - n * NP);
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const int lane = lane_id(), g = lane >> 4, lc = lane & 15;
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+  const size_t hbase = (size_t)hv * geo.slots;
+  f32x4 Hs[2][KT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) load_state<K, V>(Hs[t], h0, sbase, 16 * (vt0 + t) + lc, g);
+  // The next chunk's loads are issued unconditionally (the last chunk reloads
+  // itself, in bounds), so the compiler's wait counts stay exact across the loop.
+  Step A, B;
+  const int last = s1 - 1;
+  if (s0 < s1) A.load(wf, ktf, uf, gam, hbase + s0, vt0, lane);
+  for (int s = s0; s < s1; s += 2) {
+    B.load(wf, ktf, uf, gam, hbase + min(s + 1, last), vt0, lane);
+    asm volatile("" ::: "memory");
+    A.compute(Hs, hcf, vnf, hbase + s, vt0, lane);
+    if (s + 1 >= s1) break;
+    A.load(wf, ktf, uf, gam, hbase + min(s + 2, last), vt0, lane);
+    asm volatile("" ::: "memory");
+    B.compute(Hs, hcf, vnf, hbase + s + 1, vt0, lane);
+  }
+  if (fin) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + 16 * (vt0 + t) + lc] = Hs[t][mt][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // State pass, LDS-ring variant (used when its workgroups fit one per CU).
 // Same arithmetic as gdn_chain_kernel; only the operand supply differs.  A
 // workgroup is:

@@ -184,6 +184,26 @@ def test_fused_output_head_sizes(K, V, B, T, HV, h0):
     check_full(inp, "fused_heads_K%d_V%d_T%d" % (K, V, T))
 
 
+@pytest.mark.parametrize("K,V,HV,packed", [(128, 128, 8, False), (64, 64, 16, False),
+                                           (128, 64, 16, True)])
+def test_many_units_two_tile_state_pass(K, V, HV, packed):
+    """More (sequence, head, 16-column) units than two per compute unit on the
+    256-CU device: the bf16 state pass runs one wave per two value tiles."""
+    if packed:
+        lengths = [130, 0, 64, 1, 65, 200, 7, 128, 63, 90]   # 10 sequences
+        inp = make_inputs(B=1, T=sum(lengths), H=HV // 2, HV=HV, K=K, V=V, dtype=BF, seed=50,
+                          lengths=lengths, h0=True)
+    else:
+        inp = make_inputs(B=9, T=130, H=HV // 2, HV=HV, K=K, V=V, dtype=BF, seed=51 + K + V,
+                          h0=True, A_log_range=(-4.0, 0.0))
+    s = inp.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    say("case two_tile_state_pass", s, "units", units, "cus", cus)
+    assert units > 2 * cus or cus != 256
+    check_full(inp, "two_tile_K%d_V%d%s" % (K, V, "_packed" if packed else ""))
+
+
 def test_split_and_resume_matches_one_call():
     # the final state is a checkpoint: run [0, s) then [s, T) from it
     inp = make_inputs(B=1, T=640, H=2, HV=2, K=128, V=128, dtype=F32, seed=7,
