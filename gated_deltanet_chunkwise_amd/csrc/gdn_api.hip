@@ -439,9 +439,16 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
         reinterpret_cast<Frag<E>*>(F(bl.vnp))));
   mark(1);
   if (chunk_wgs > 0)
-    ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe, ke,
-              doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::f32x4*>(w + bl.bq),
-              reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
+    {
+      if constexpr (std::is_same<E, gdn::bf16>::value)
+        ok(launch(gdn::gdn_bwd_prep_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo,
+                  qe, ke, doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf),
+                  reinterpret_cast<gdn::f32x4*>(w + bl.bq), reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
+      else
+        ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe,
+                  ke, doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::f32x4*>(w + bl.bq),
+                  reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
+    }
   mark(2);
   if (units > 0)
     ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,

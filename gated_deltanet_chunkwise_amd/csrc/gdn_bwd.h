@@ -669,6 +669,174 @@ __device__ __forceinline__ void stage_t(bf16* dst, const float* src) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The prep kernel for bf16 calls: the products of gdn_bwd_prep_kernel on the
+// bf16 MFMA (fp32 accumulation).  q, k and do are staged exactly; P (for
+// dv_local) and scale e^G do (for the dH term) are rounded to bf16 once.
+// LDS (~73 KB at K = V = 128: two workgroups per CU), phase by phase:
+//   A: q, k natural rows            -> P (registers), kd fragments
+//   B: P^T (t-w) over k's rows; do^T and (scale e^G do)^T (t-w) -> dv_local
+//   C: q^T (t-w) over P^T           -> bq = q^T (scale e^G do)
+//   D: w natural over q             -> w^T fragments
+template <int K, int V, bool VARLEN>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_prep_bf16_kernel(
+    Geo geo, const bf16* __restrict__ qg, const bf16* __restrict__ kg, const bf16* __restrict__ dog,
+    const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<bf16>* __restrict__ wf,
+    Frag<bf16>* __restrict__ wtf, Frag<bf16>* __restrict__ kdf, f32x4* __restrict__ bq,
+    f32x4* __restrict__ dvl) {
+  constexpr int SK = PadB<K>::v, SC = PadB<kChunk>::v;
+  constexpr int KT = K / 16, KB = K / 32, NV = V / 16, TH = kBwdThreads, NW = TH / 64;
+  constexpr int RX = kChunk * SK;                                  // q, then w
+  constexpr int RY = kChunk * SK > K * SC ? kChunk * SK : K * SC;  // k, then P^T, then q^T
+  constexpr int RZ = 2 * V * SC;                                   // do^T, (s do)^T
+  __shared__ __align__(16) bf16 lds[RX + RY + RZ];
+  __shared__ float sg[kChunk];
+  bf16* const Qn = lds;
+  bf16* const Wn = lds;
+  bf16* const Kn = lds + RX;
+  bf16* const Pt = lds + RX;
+  bf16* const Qt = lds + RX;
+  bf16* const Dt = lds + RX + RY;
+  bf16* const Dst = Dt + V * SC;
+
+  int hv, slot;
+  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  int n, len;
+  int64_t t0;
+  if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
+  const int h = hv / geo.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
+  const size_t hs = (size_t)hv * geo.slots + slot;
+  const int pit = wave >> 1, pj0 = 2 * (wave & 1);
+
+  // do rows: 4 rows x 8 columns per thread, loaded now, staged in B
+  constexpr int DCB = V / 8, DNB = (kChunk / 4) * DCB, DPER = (DNB + TH - 1) / TH;
+  bf16x8 dx[DPER][4];
+#pragma unroll
+  for (int it = 0; it < DPER; ++it) {
+    const int b = tid + TH * it;
+    if (DNB % TH == 0 || b < DNB) {
+      const int r0 = 4 * (b / DCB), c0 = 8 * (b % DCB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dx[it][j] = bf16x8{};
+        if (r0 + j < len) dx[it][j] = *reinterpret_cast<const bf16x8*>(dog + ((t0 + r0 + j) * geo.HV + hv) * V + c0);
+      }
+    }
+  }
+  stage_rows_b<K, TH>(Qn, SK, qg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  stage_rows_b<K, TH>(Kn, SK, kg + (size_t)h * K, t0, (int64_t)geo.H * K, len);
+  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
+  __syncthreads();
+
+  // A. P = (Q K^T) * M * e^{dG} (registers), and the kd fragments.
+  f32x4 pm[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int jt = pj0 + b;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= pit) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma_k32(acc, frag_from_row(Qn + (16 * pit + lc) * SK + 32 * kb),
+                frag_from_row(Kn + (16 * jt + lc) * SK + 32 * kb));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * pit + 4 * g + r, j = 16 * jt + lc;
+      pm[b][r] = j <= i ? acc[r] * fast_exp2(sg[i] - sg[j]) : 0.f;
+    }
+  }
+  {
+    const float gl = sg[kChunk - 1];
+    for (int f = wave; f < 4 * KB; f += NW) {
+      const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
+      const float e = fast_exp2(gl - sg[c]);
+      const f32x4 lo = to_f32x4(*reinterpret_cast<const bf16x4*>(Kn + c * SK + 32 * kb + 4 * g));
+      const f32x4 hi = to_f32x4(*reinterpret_cast<const bf16x4*>(Kn + c * SK + 32 * kb + 16 + 4 * g));
+      kdf[((hs * 4 + ct) * KB + kb) * 64 + lane] = frag_from_tiles<bf16>(lo * e, hi * e);
+    }
+  }
+  __syncthreads();
+  // B. P^T, do^T and (scale e^G do)^T; dv_local = scale P^T do.
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = 16 * (pj0 + b) + lc;
+    *reinterpret_cast<bf16x4*>(Pt + j * SC + ((16 * pit + 4 * g) ^ tswz(j))) = to_bf16x4(pm[b]);
+  }
+#pragma unroll
+  for (int it = 0; it < DPER; ++it) {
+    const int b = tid + TH * it;
+    if (DNB % TH == 0 || b < DNB) {
+      const int r0 = 4 * (b / DCB), c0 = 8 * (b % DCB);
+      float sc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[j] = geo.scale * fast_exp2(sg[r0 + j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = c0 + e, col = r0 ^ tswz(c0 + e);
+        const bf16x4 d = {dx[it][0][e], dx[it][1][e], dx[it][2][e], dx[it][3][e]};
+        *reinterpret_cast<bf16x4*>(Dt + row * SC + col) = d;
+        *reinterpret_cast<bf16x4*>(Dst + row * SC + col) =
+            to_bf16x4(f32x4{(float)d[0] * sc[0], (float)d[1] * sc[1], (float)d[2] * sc[2], (float)d[3] * sc[3]});
+      }
+    }
+  }
+  __syncthreads();
+  for (int f = wave; f < 4 * NV; f += NW) {
+    const int ct = f / NV, vt = f - ct * NV;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+      mma_k32(acc, frag_from_trow(Pt, 16 * ct + lc, SC, 32 * ib), frag_from_trow(Dt, 16 * vt + lc, SC, 32 * ib));
+    dvl[((hs * NV + vt) * 4 + ct) * 64 + lane] = acc * geo.scale;
+  }
+  __syncthreads();
+  // C. q^T from the natural rows (4 rows x 8 columns per thread); bq.
+  {
+    constexpr int CB = K / 8, NB = (kChunk / 4) * CB;
+    for (int b = tid; b < NB; b += TH) {
+      const int r0 = 4 * (b / CB), c0 = 8 * (b % CB);
+      bf16x8 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const bf16x8*>(Qn + (r0 + j) * SK + c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
+        *reinterpret_cast<bf16x4*>(Qt + (c0 + e) * SC + (r0 ^ tswz(c0 + e))) = col;
+      }
+    }
+  }
+  __syncthreads();
+  for (int f = wave; f < KT * NV; f += NW) {
+    const int mt = f / NV, vt = f - mt * NV;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      mma_k32(acc, frag_from_trow(Qt, 16 * mt + lc, SC, 32 * cb), frag_from_trow(Dst, 16 * vt + lc, SC, 32 * cb));
+    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = acc;
+  }
+  // D. w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
+  // into the q rows' space (free since q^T was built), then w^T fragments.
+  for (int f = wave; f < 4 * KB; f += NW) {
+    const int ct = f / KB, kb = f - ct * KB, c = 16 * ct + lc;
+    const Frag<bf16> x = wf[((hs * 4 + ct) * KB + kb) * 64 + lane];
+    *reinterpret_cast<bf16x4*>(Wn + c * SK + 32 * kb + 4 * g) = __builtin_shufflevector(x.x, x.x, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(Wn + c * SK + 32 * kb + 16 + 4 * g) = __builtin_shufflevector(x.x, x.x, 4, 5, 6, 7);
+  }
+  __syncthreads();
+  for (int f = wave; f < KT * 2; f += NW) {
+    const int mt = f >> 1, cb = f & 1, kk = 16 * mt + lc;
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = Wn[(32 * cb + 4 * g + i) * SK + kk];
+      y[4 + i] = Wn[(32 * cb + 16 + 4 * g + i) * SK + kk];
+    }
+    wtf[(hs * KT * 2 + f) * 64 + lane] = Frag<bf16>{y};
+  }
+}
+
 // (at most 128 VGPRs: two eight-wave workgroups per CU)
 template <int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_dqk_bf16_kernel(
