@@ -1,0 +1,92 @@
+"""bench.py host logic on the CPU: the one-GPU rule, the algorithmic byte and
+flop counts the roofline uses, and the parsing of rocprofv3 counter CSVs into
+traffic and MFMA figures (synthetic CSV files, no GPU)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_counts_at_the_pages_shape():
+    # B=2, T=2048, H=HV=8, K=V=128, bf16, no initial state: 64 slots of 64 tokens
+    shape = dict(B=2, T=2048, H=8, HV=8, K=128, V=128, N=2)
+    kern, path, ntok = bench.algorithmic(shape, 2, False, 64)
+    assert ntok == 4096
+    U = 4096 * 8
+    # the whole pass: q, k (per key head), v, o at 2 bytes, gates and beta, final state
+    assert path["bytes"] == 2 * 4096 * 8 * 128 * 2 + U * 128 * 2 + U * 8 + U * 128 * 2 + 2 * 8 * 128 * 128 * 4
+    # C(3K + 2V) + 6KV flops per token-head: 139,264 at C = 64, K = V = 128
+    assert path["flops"] == U * 139264
+    assert kern["chain"]["flops"] == U * 4 * 128 * 128
+    # fused: the output's bytes move into the state pass, P^T and q into WY
+    fk, fpath, _ = bench.algorithmic(shape, 2, False, 64, fused=True)
+    assert set(fk) == {"chunk_map", "wy", "chain_out"}
+    assert fpath == path
+    p_bytes = 64 * 8 * 6 * 64 * 8 * 2
+    assert fk["wy"]["bytes"] == kern["wy"]["bytes"] + 4096 * 8 * 128 * 2 + p_bytes
+
+
+def _counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (kernel, counter, value) in enumerate(rows):
+            w.writerow([i, kernel, counter, value])
+
+
+def test_write_traffic_scales_counters_and_reads_mfma_passes(tmp_path, monkeypatch):
+    d = str(tmp_path)
+    wy = "_ZN3gdn13gdn_wy_kernelIDF16bLi128ELi128ELb0ELb0ELb0EEEv"
+    chain = "_ZN3gdn21gdn_chain_ring_kernelIDF16bLi128ELi128ELb0ELi1ELi0EEEv"
+    copy = "__amd_rocclr_copyBuffer"
+    mib = 256 << 20
+    # the copy reads FETCH_SIZE = half its bytes and WRITE_SIZE = all of them (KiB)
+    _counter_csv(os.path.join(d, "copy_fetch", "c_counter_collection.csv"),
+                 [(copy, "FETCH_SIZE", mib / 2048.0)])
+    _counter_csv(os.path.join(d, "copy_write", "c_counter_collection.csv"),
+                 [(copy, "WRITE_SIZE", mib / 1024.0)])
+    _counter_csv(os.path.join(d, "fetch", "f_counter_collection.csv"),
+                 [(wy, "FETCH_SIZE", 100.0), (wy, "FETCH_SIZE", 300.0), (chain, "FETCH_SIZE", 50.0)])
+    _counter_csv(os.path.join(d, "write", "w_counter_collection.csv"),
+                 [(wy, "WRITE_SIZE", 400.0), (chain, "WRITE_SIZE", 10.0)])
+    _counter_csv(os.path.join(d, "mfma_util", "u_counter_collection.csv"),
+                 [(wy, "MfmaUtil", 4.0), (wy, "MfmaUtil", 6.0), (chain, "MfmaUtil", 2.5)])
+    _counter_csv(os.path.join(d, "mfma_flops", "m_counter_collection.csv"),
+                 [(wy, "MfmaFlopsBF16", 1000.0), (wy, "MfmaFlopsF32", 24.0),
+                  (chain, "MfmaFlopsBF16", 512.0)])
+    out = os.path.join(d, "traffic.json")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", out)
+    bench.write_traffic(d, "wl", mib)
+    ent = json.load(open(out))["wl"]
+    # mean per dispatch (KiB) x 1024 x calibration (2 for FETCH_SIZE, 1 for WRITE_SIZE)
+    assert ent["wy"]["fetch_bytes"] == 200.0 * 1024 * 2
+    assert ent["wy"]["write_bytes"] == 400.0 * 1024
+    assert ent["wy"]["bytes_per_launch"] == 200 * 1024 * 2 + 400 * 1024
+    assert ent["chain"]["bytes_per_launch"] == 50 * 1024 * 2 + 10 * 1024
+    assert ent["wy"]["source_hash"] == bench.source_hash("gdn_fwd")
+    assert bench.kernel_counters(ent["wy"]) == {"mfma_util": 0.05, "mfma_flops": 1024}
+    assert bench.kernel_counters(ent["chain"]) == {"mfma_util": 0.025, "mfma_flops": 512}
+
+
+def test_source_hash_covers_each_op_only_with_its_sources():
+    ops = ("gdn_fwd", "gdn_bwd", "kda_gate", "decode")
+    hashes = {op: bench.source_hash(op) for op in ops}
+    assert len(set(hashes.values())) == len(ops)
+    for op in ops:
+        for f in bench.OP_SOURCES[op]:
+            assert os.path.exists(os.path.join(ROOT, "gated_deltanet_chunkwise_amd", "csrc", f))
