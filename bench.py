@@ -40,6 +40,9 @@ def parse():
                          "per-channel gate on the guide's timing shape; decode: one recurrent "
                          "step for a batch of sequences")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="forward: also time this many steps each after touching 1 GiB on the "
+                         "stream (inputs and intermediates out of the 256 MB last-level cache)")
     ap.add_argument("--seg-chunks", type=int, default=0,
                     help="segment-parallel state pass with segments of this many chunks (0: off)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -674,6 +677,25 @@ def main():
     # headline: K eager steps, events on the launch stream, synchronized on both sides
     ms = timed(step, args.steps)
 
+    # cold: each step timed alone after an untimed pass over 1 GiB on the same
+    # stream, so that its inputs and intermediates come from HBM rather than the
+    # last-level cache (the pages' working set fits in it)
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        total = 0.0
+        for _ in range(args.cold_steps):
+            flush.add_(1.0)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        cold_ms = total / args.cold_steps
+        del flush
+
     # the same step captured once in a HIP graph and replayed (launch overhead view)
     graph_ms = None
     try:
@@ -771,6 +793,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
+        "cold_tokens_per_s": None if cold_ms is None else round(ntok / (cold_ms / 1e3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
