@@ -153,6 +153,18 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
   const int units = geo.N * geo.HV * (V / 16);
   if (units == 0) return hipSuccess;
   const int cus = device_cus();
+  // fp32 operands, one unit per CU or fewer: the K rows split over K/32
+  // waves, each reading a K/32-th of the chunk's (doubled-width) fragments.
+  // Measured on MI355X: B=1, T=256, H=2, K=V=64 state pass 7.6 us against
+  // 11.7 for the one-wave ring.  Not for bf16, whose one-wave operand stream
+  // is half as wide: B=2, T=2048, H=8, K=V=128 took 27.0 us against 21.5,
+  // the two barriers and LDS round trips per chunk outlasting the intake
+  // they save.
+  if constexpr (MODE == gdn::CHAIN_FULL && sizeof(E) == 4 && (K == 64 || K == 128)) {
+    if (units <= cus)
+      return launch(gdn::gdn_chain_ks_kernel<E, K, V, VARLEN, 2>, dim3(units),
+                    dim3(64 * (K / 32)), s, geo, wf, ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
+  }
   if constexpr (gdn::RingCfg<E, K, V, 1>::FITS) {
     if (units <= cus)
       return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1, MODE>, dim3(units),

@@ -1151,6 +1151,191 @@ __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_
 }
 
 // ---------------------------------------------------------------------------
+// State pass with the K rows split over K/32 waves (CHAIN_FULL): one workgroup
+// per (sequence, value head, 16 value columns).  Wave q holds rows
+// 32q .. 32q+31 of the K x 16 state (two D tiles) and reads only the w and
+// kd^T fragments of those rows: a quarter of the one-wave variant's operand
+// stream at K = 128, and a quarter of its products.  Per chunk:
+//   store the wave's H_c fragment (k block q, the one-wave variant's layout);
+//   partial products P_q = w[:, rows of q] H_c[rows of q], four 16-row tiles;
+//   reduce-scatter through LDS: the wave owning chunk-row tile ct
+//   (ct mod KB = q) forms v_new tile ct = u - (P_0 + P_1 + ...), summed in
+//   wave order and rounded to the dtype;
+//   exchange the v_new tiles, so every wave holds v_new; store v_new;
+//   H[rows of q] <- e^{G_last} H[rows of q] + kd^T[rows of q] v_new.
+// Two workgroup barriers per chunk.  Each wave loads its operands (about 65
+// VGPRs per chunk for fp32 at K = 128) D chunks ahead into registers.  Used
+// for fp32 operands, whose one-wave stream is twice the bf16 one.
+template <typename E, int K, int V>
+struct ChainKsStep {
+  static constexpr int KB = K / 32, KT = K / 16, NV = V / 16, OWN = 4 / KB;
+  Frag<E> w[4];      // w, chunk-row tile ct, k block q
+  Frag<E> kt[2][2];  // kd^T, row tile 2q + j, chunk block cb
+  Quad<E> u[OWN];    // u, chunk-row tiles q + KB j
+  float gl;          // lane l: entry l of the chunk's gate row
+
+  template <int Q>
+  __device__ __forceinline__ void load(const Frag<E>* __restrict__ wf,
+                                       const Frag<E>* __restrict__ ktf,
+                                       const Quad<E>* __restrict__ uf,
+                                       const float* __restrict__ gam, size_t hs, int vt,
+                                       int lane) {
+    gl = gam[hs * kChunk + lane];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) w[ct] = wf[((hs * 4 + ct) * KB + Q) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) kt[j][cb] = ktf[((hs * KT + 2 * Q + j) * 2 + cb) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+      const int ct = Q + KB * j;
+      u[j] = uf[(((hs * NV + vt) * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)];
+    }
+  }
+};
+
+__device__ __forceinline__ Frag<bf16> frag_join(const Quad<bf16>& a, const Quad<bf16>& b) {
+  return {__builtin_shufflevector(a.x, b.x, 0, 1, 2, 3, 4, 5, 6, 7)};
+}
+__device__ __forceinline__ Frag<float> frag_join(const Quad<float>& a, const Quad<float>& b) {
+  return {a.x, b.x};
+}
+
+template <typename E, int K, int V>
+struct ChainKsLds {
+  f32x4 part[K / 32][4][64];  // partial products, by wave and chunk-row tile
+  Quad<E> vx[4][64];          // v_new tiles, rounded
+};
+
+// Wave Q's part of gdn_chain_ks_kernel (Q is the wave index, uniform).
+template <typename E, int K, int V, int D, int Q>
+__device__ __forceinline__ void chain_ks_wave(ChainKsLds<E, K, V>& sh, const Frag<E>* __restrict__ wf,
+                                              const Frag<E>* __restrict__ ktf,
+                                              const Quad<E>* __restrict__ uf,
+                                              const float* __restrict__ gam, const float* __restrict__ h0,
+                                              float* __restrict__ fin, Frag<E>* __restrict__ hcf,
+                                              Frag<E>* __restrict__ vnf, int s0, int s1, size_t hbase,
+                                              size_t sbase, int vt) {
+  using Step = ChainKsStep<E, K, V>;
+  constexpr int KB = Step::KB, NV = Step::NV, OWN = Step::OWN, HALF = KB / 2;
+  const int lane = lane_id(), g = lane >> 4, v = 16 * vt + (lane & 15);
+  f32x4 Hs[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Hs[j][r] = h0 ? h0[sbase + (size_t)(32 * Q + 16 * j + 4 * g + r) * V + v] : 0.f;
+
+  auto chunk = [&](const Step& S, size_t hs) {
+    const Frag<E> hb = frag_from_tiles<E>(Hs[0], Hs[1]);
+    hcf[((hs * NV + vt) * KB + Q) * 64 + lane] = hb;
+    f32x4 p[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      p[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_k32(p[ct], S.w[ct], hb);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (ct % KB != Q) sh.part[Q][ct][lane] = p[ct];
+    wait_lgkm0();
+    ring_barrier();
+    Quad<E> own[OWN];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+      const int ct = Q + KB * j;
+      f32x4 acc = Q == 0 ? p[ct] : sh.part[0][ct][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < KB; ++w2) acc += (w2 == Q ? p[ct] : sh.part[w2][ct][lane]);
+      own[j] = make_quad<E>(quad_f32(S.u[j]) - acc);
+      sh.vx[ct][lane] = own[j];
+    }
+    wait_lgkm0();
+    ring_barrier();
+    Quad<E> vq[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) vq[ct] = (ct % KB == Q) ? own[ct / KB] : sh.vx[ct][lane];
+    Frag<E> vb[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) vb[cb] = frag_join(vq[2 * cb], vq[2 * cb + 1]);
+    if constexpr (Q % HALF == HALF - 1) vnf[((hs * NV + vt) * 2 + Q / HALF) * 64 + lane] = vb[Q / HALF];
+    const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.gl), kChunk - 1)));
+    Hs[0] *= dec;
+    Hs[1] *= dec;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mma_k32(Hs[j], S.kt[j][cb], vb[cb]);
+  };
+
+  if (s0 < s1) {
+    // The loads are issued unconditionally (clamped to the last chunk, in
+    // bounds), so the compiler's wait counts stay exact around the loop; the
+    // exit jumps past it.
+    Step buf[D];
+    const int last = s1 - 1;
+#pragma unroll
+    for (int j = 0; j < D; ++j) buf[j].template load<Q>(wf, ktf, uf, gam, hbase + min(s0 + j, last), vt, lane);
+    for (int s = s0;; s += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (s + j >= s1) goto done;
+        chunk(buf[j], hbase + s + j);
+        buf[j].template load<Q>(wf, ktf, uf, gam, hbase + min(s + j + D, last), vt, lane);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+done:
+  if (fin) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(32 * Q + 16 * j + 4 * g + r) * V + v] = Hs[j][r];
+  }
+}
+
+template <typename E, int K, int V, bool VARLEN, int D>
+__global__ __launch_bounds__(64 * (K / 32)) void gdn_chain_ks_kernel(Geo geo, const Frag<E>* __restrict__ wf,
+                                                                    const Frag<E>* __restrict__ ktf,
+                                                                    const Quad<E>* __restrict__ uf,
+                                                                    const float* __restrict__ gam,
+                                                                    const int* __restrict__ seq_slot,
+                                                                    const float* __restrict__ h0,
+                                                                    float* __restrict__ fin,
+                                                                    Frag<E>* __restrict__ hcf,
+                                                                    Frag<E>* __restrict__ vnf) {
+  static_assert(K == 64 || K == 128, "two or four waves");
+  constexpr int NV = V / 16;
+  __shared__ ChainKsLds<E, K, V> sh;
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+  const int n = rest / NV, vt = rest - n * NV;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+  const size_t hbase = (size_t)hv * geo.slots;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 0)
+    chain_ks_wave<E, K, V, D, 0>(sh, wf, ktf, uf, gam, h0, fin, hcf, vnf, s0, s1, hbase, sbase, vt);
+  else if (wave == 1)
+    chain_ks_wave<E, K, V, D, 1>(sh, wf, ktf, uf, gam, h0, fin, hcf, vnf, s0, s1, hbase, sbase, vt);
+  if constexpr (K == 128) {
+    if (wave == 2)
+      chain_ks_wave<E, K, V, D, 2>(sh, wf, ktf, uf, gam, h0, fin, hcf, vnf, s0, s1, hbase, sbase, vt);
+    else if (wave == 3)
+      chain_ks_wave<E, K, V, D, 3>(sh, wf, ktf, uf, gam, h0, fin, hcf, vnf, s0, s1, hbase, sbase, vt);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // State pass with the output stage fused in (LDS-ring variant).  The chunk
 // states never leave the CU: a workgroup is
 //   NC compute waves -- as in gdn_chain_ring_kernel, except that H_c and v_new
