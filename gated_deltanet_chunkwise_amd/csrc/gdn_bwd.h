@@ -1807,17 +1807,18 @@ __global__ __launch_bounds__(256) void gdn_bwd_qk_sum_kernel(Geo geo, const int4
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
-  for (int e = threadIdx.x; e < len * K; e += 256) {
+  // four consecutive k per thread: 16-byte loads, one 8- or 16-byte store
+  for (int e = 4 * threadIdx.x; e < len * K; e += 4 * 256) {
     const int c = e / K, kk = e - c * K;
-    float sq = 0.f, sk = 0.f;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < geo.G; ++r) {
       const size_t o = (((size_t)(h * geo.G + r) * geo.slots + slot) * kChunk + c) * K + kk;
-      sq += dqp[o];
-      sk += dkp[o];
+      sq += *reinterpret_cast<const f32x4*>(dqp + o);
+      sk += *reinterpret_cast<const f32x4*>(dkp + o);
     }
     const size_t d = ((t0 + c) * geo.H + h) * K + kk;
-    dqg[d] = (E)sq;
-    dkg[d] = (E)sk;
+    st4(dqg + d, sq[0], sq[1], sq[2], sq[3]);
+    st4(dkg + d, sk[0], sk[1], sk[2], sk[3]);
   }
 }
 
