@@ -462,7 +462,13 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
                   reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
     }
   mark(2);
-  if (units > 0)
+  if (units > 0 && units <= device_cus())
+    // one unit per CU or fewer: the K rows split over K/32 waves
+    ok(launch(gdn::gdn_bwd_chain_ks_kernel<E, K, V, VARLEN, 2>, dim3(units), dim3(64 * (K / 32)), s, geo,
+              FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
+              reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
+              F(bl.dhn), F(bl.dvn)));
+  else if (units > 0)
     ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
               reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,

@@ -424,6 +424,171 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward state pass with the K rows split over K/32 waves: one workgroup per
+// (sequence, value head, 16 value columns); wave q holds rows 32q..32q+31 of
+// dL/dH and reads only those rows' kd and w^T fragments and bq tiles (a
+// quarter of the one-wave variant's operand stream at K = 128).  Per chunk,
+// in reverse order:
+//   store the wave's rows of dH;
+//   partial products kd[:, rows of q] dH[rows of q], four 16-row tiles;
+//   reduce-scatter through LDS: the owner of chunk-row tile ct (ct mod KB = q)
+//   forms dv_new tile ct = dv_local + (P_0 + P_1 + ...), summed in wave order,
+//   stores it and exchanges -dv_new rounded to the dtype;
+//   dH[rows of q] <- e^{G_last} dH[rows of q] + bq[rows of q] - w^T[rows of q] dv_new.
+// Two workgroup barriers per chunk; operands loaded two chunks ahead.
+template <typename E, int K, int V>
+struct BwdKsStep {
+  static constexpr int KB = K / 32, KT = K / 16, NV = V / 16, OWN = 4 / KB;
+  Frag<E> kd[4];      // kd, chunk-row tile ct, k block q
+  Frag<E> wt[2][2];   // w^T, row tile 2q + j, chunk block cb
+  f32x4 dl[OWN];      // dv_local, chunk-row tiles q + KB j
+  f32x4 b[2];         // bq, row tiles 2q + j
+  float gl;           // lane l: entry l of the chunk's gate row
+
+  template <int Q>
+  __device__ __forceinline__ void load(const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
+                                       const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq,
+                                       const float* __restrict__ gam, size_t hs, int vt, int lane) {
+    gl = gam[hs * kChunk + lane];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) kd[ct] = kdf[((hs * 4 + ct) * KB + Q) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) dl[j] = dvl[((hs * NV + vt) * 4 + Q + KB * j) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      b[j] = bq[((hs * NV + vt) * KT + 2 * Q + j) * 64 + lane];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) wt[j][cb] = wtf[((hs * KT + 2 * Q + j) * 2 + cb) * 64 + lane];
+    }
+  }
+};
+
+template <typename E, int K, int V, int D, int Q>
+__device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const Frag<E>* __restrict__ kdf,
+                                                  const f32x4* __restrict__ dvl,
+                                                  const Frag<E>* __restrict__ wtf,
+                                                  const f32x4* __restrict__ bq, const float* __restrict__ gam,
+                                                  const float* __restrict__ dht, float* __restrict__ dh0,
+                                                  float* __restrict__ dhn, float* __restrict__ dvn, int s0,
+                                                  int s1, size_t hbase, size_t sbase, int vt) {
+  using Step = BwdKsStep<E, K, V>;
+  constexpr int KB = Step::KB, OWN = Step::OWN;
+  const int lane = lane_id(), g = lane >> 4, v = 16 * vt + (lane & 15);
+  f32x4 dH[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dH[j][r] = dht ? dht[sbase + (size_t)(32 * Q + 16 * j + 4 * g + r) * V + v] : 0.f;
+
+  auto chunk = [&](const Step& S, size_t hs) {
+    // transposed: lane (v, g) holds rows 4g..4g+3 of each tile, contiguous in dH^T
+    f32x4* hp = reinterpret_cast<f32x4*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
+    hp[4 * (2 * Q)] = dH[0];
+    hp[4 * (2 * Q + 1)] = dH[1];
+    const Frag<E> hb = frag_from_tiles<E>(dH[0], dH[1]);
+    f32x4 p[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      p[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_k32(p[ct], S.kd[ct], hb);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (ct % KB != Q) sh.part[Q][ct][lane] = p[ct];
+    wait_lgkm0();
+    ring_barrier();
+    Quad<E> own[OWN];
+    f32x4* vp = reinterpret_cast<f32x4*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+      const int ct = Q + KB * j;
+      f32x4 acc = Q == 0 ? p[ct] : sh.part[0][ct][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < KB; ++w2) acc += (w2 == Q ? p[ct] : sh.part[w2][ct][lane]);
+      const f32x4 dv = S.dl[j] + acc;
+      vp[4 * ct] = dv;
+      own[j] = make_quad<E>(-dv);
+      sh.vx[ct][lane] = own[j];
+    }
+    wait_lgkm0();
+    ring_barrier();
+    Quad<E> vq[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) vq[ct] = (ct % KB == Q) ? own[ct / KB] : sh.vx[ct][lane];
+    Frag<E> nb[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) nb[cb] = frag_join(vq[2 * cb], vq[2 * cb + 1]);
+    const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.gl), kChunk - 1)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dH[j] = dH[j] * dec + S.b[j];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) mma_k32(dH[j], S.wt[j][cb], nb[cb]);
+    }
+  };
+
+  if (s0 < s1) {
+    // chunks s1-1 down to s0; loads clamped to s0 (in bounds), the exit
+    // jumps past the loop
+    Step buf[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) buf[j].template load<Q>(kdf, dvl, wtf, bq, gam, hbase + max(s1 - 1 - j, s0), vt, lane);
+    for (int s = s1 - 1;; s -= D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (s - j < s0) goto done;
+        chunk(buf[j], hbase + s - j);
+        buf[j].template load<Q>(kdf, dvl, wtf, bq, gam, hbase + max(s - j - D, s0), vt, lane);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+done:
+  if (dh0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dh0[sbase + (size_t)(32 * Q + 16 * j + 4 * g + r) * V + v] = dH[j][r];
+  }
+}
+
+template <typename E, int K, int V, bool VARLEN, int D>
+__global__ __launch_bounds__(64 * (K / 32)) void gdn_bwd_chain_ks_kernel(
+    Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
+    const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq, const float* __restrict__ gam,
+    const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
+    float* __restrict__ dhn, float* __restrict__ dvn) {
+  static_assert(K == 64 || K == 128, "two or four waves");
+  constexpr int NV = V / 16;
+  __shared__ ChainKsLds<E, K, V> sh;
+  int hv, rest;
+  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+  const int n = rest / NV, vt = rest - n * NV;
+  int s0, s1;
+  if constexpr (VARLEN) {
+    s0 = seq_slot[n];
+    s1 = seq_slot[n + 1];
+  } else {
+    s0 = n * geo.NT;
+    s1 = s0 + geo.NT;
+  }
+  const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
+  const size_t hbase = (size_t)hv * geo.slots;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 0)
+    bwd_chain_ks_wave<E, K, V, D, 0>(sh, kdf, dvl, wtf, bq, gam, dht, dh0, dhn, dvn, s0, s1, hbase, sbase, vt);
+  else if (wave == 1)
+    bwd_chain_ks_wave<E, K, V, D, 1>(sh, kdf, dvl, wtf, bq, gam, dht, dh0, dhn, dvn, s0, s1, hbase, sbase, vt);
+  if constexpr (K == 128) {
+    if (wave == 2)
+      bwd_chain_ks_wave<E, K, V, D, 2>(sh, kdf, dvl, wtf, bq, gam, dht, dh0, dhn, dvn, s0, s1, hbase, sbase, vt);
+    else if (wave == 3)
+      bwd_chain_ks_wave<E, K, V, D, 3>(sh, kdf, dvl, wtf, bq, gam, dht, dh0, dhn, dvn, s0, s1, hbase, sbase, vt);
+  }
+}
+
 // dq / dk / dw / dG, one workgroup per (chunk slot, value head); with one value
 // head per key head dq is written final, else per value head.  The products
 // over V run in two LDS stagings: (do, dv_new, H_c) for dq_inter and dw, then
