@@ -167,11 +167,11 @@ def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
 KERNEL_STAGE = (("gdn_chunk_map_kernel", "chunk_map"), ("gdn_wy_kernel", "wy"),
                 ("gdn_chain_out_kernel", "chain_out"),
                 ("gdn_chain_ring_kernel", "chain"), ("gdn_chain_kernel", "chain"),
-                ("gdn_chain2_kernel", "chain"),
+                ("gdn_chain2_kernel", "chain"), ("gdn_chain_ks_kernel", "chain"),
                 ("gdn_output_kernel", "output"), ("gdn_kda_gate_vec_kernel", "kda_gate"),
                 ("gdn_kda_gate_scalar_kernel", "kda_gate"), ("gdn_decode_kernel", "decode"),
                 ("gdn_bwd_prep_kernel", "prep"), ("gdn_bwd_prep_bf16_kernel", "prep"),
-                ("gdn_bwd_chain_kernel", "bwd_chain"),
+                ("gdn_bwd_chain_kernel", "bwd_chain"), ("gdn_bwd_chain_ks_kernel", "bwd_chain"),
                 ("gdn_bwd_dqk_kernel", "dqk"), ("gdn_bwd_dqk_bf16_kernel", "dqk"),
                 ("gdn_bwd_wy_kernel", "bwd_wy"), ("gdn_bwd_wy_bf16_kernel", "bwd_wy"),
                 ("gdn_bwd_qk_sum_kernel", "sums"))

@@ -90,3 +90,22 @@ def test_source_hash_covers_each_op_only_with_its_sources():
     for op in ops:
         for f in bench.OP_SOURCES[op]:
             assert os.path.exists(os.path.join(ROOT, "gated_deltanet_chunkwise_amd", "csrc", f))
+
+
+def test_every_state_pass_variant_maps_to_its_stage(tmp_path):
+    # each launchable state-pass kernel's counters must land on its stage, or
+    # the bench line's traffic for that stage would be null
+    names = {
+        "_ZN3gdn21gdn_chain_ring_kernelIDF16bLi128ELi128ELb0ELi1ELi0EEEv": "chain",
+        "_ZN3gdn16gdn_chain_kernelIDF16bLi128ELi128ELb0ELi0EEEv": "chain",
+        "_ZN3gdn17gdn_chain2_kernelIDF16bLi128ELi128ELb0EEEv": "chain",
+        "_ZN3gdn19gdn_chain_ks_kernelIfLi64ELi64ELb0ELi2EEEv": "chain",
+        "_ZN3gdn20gdn_chain_out_kernelIDF16bLi128ELi128ELb0ELi2EEEv": "chain_out",
+        "_ZN3gdn20gdn_bwd_chain_kernelIDF16bLi128ELi128ELb0EEEv": "bwd_chain",
+        "_ZN3gdn23gdn_bwd_chain_ks_kernelIDF16bLi128ELi128ELb0ELi2EEEv": "bwd_chain",
+    }
+    for i, (kernel, stage) in enumerate(names.items()):
+        path = os.path.join(str(tmp_path), "k%d.csv" % i)
+        _counter_csv(path, [(kernel, "FETCH_SIZE", 8.0)])
+        means, _ = bench.counter_means(path)
+        assert means == {stage: 8.0}, kernel
