@@ -190,3 +190,17 @@ def test_long_gqa_sampled_key_head():
         dg_raw=d["dg_raw"][:, :, 2:4], dbeta=d["dbeta"][:, :, 2:4],
         dA_log=d["dA_log"][2:4], ddt_bias=d["ddt_bias"][2:4], dh0=d["dh0"][:, 2:4])
     compare(sub(got), sub(ref), inp.q.dtype, "bwd long_gqa", term_scale=ts)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_many_units_one_wave_state_pass(dtype):
+    """More (sequence, head, 16-column) units than compute units on the 256-CU
+    device: the backward state pass runs one wave per unit instead of splitting
+    the K rows over waves."""
+    inp = make_inputs(B=9, T=130, H=2, HV=4, K=128, V=128, dtype=dtype, seed=701, h0=True)
+    s = inp.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    say("case bwd one_wave_state_pass", s, "units", units, "cus", cus)
+    assert units > cus or cus != 256
+    check_full(inp, "bwd many_units_%s" % dtype, 702)

@@ -247,3 +247,17 @@ def test_full_size_workload_sampled(name, count):
         assert_close(fin[n, hv], f_r, dt, "%s final[n=%d,hv=%d]" % (name, n, hv))
     # every element written (outputs are NaN-filled before the call) and finite
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(fin))
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
+def test_many_units_fp32_state_pass(K, V):
+    """fp32 with more (sequence, head, 16-column) units than compute units on
+    the 256-CU device: not the K-split state pass, but one wave per unit (the
+    register variant at K = 128, the two-wave LDS ring at K = 64)."""
+    inp = make_inputs(B=9, T=130, H=2, HV=4, K=K, V=V, dtype=F32, seed=61 + K, h0=True)
+    s = inp.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    say("case fp32_many_units", s, "units", units, "cus", cus)
+    assert units > cus or cus != 256
+    check_full(inp, "fp32_many_units_K%d_V%d" % (K, V))
