@@ -455,10 +455,10 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
       if constexpr (std::is_same<E, gdn::bf16>::value)
         ok(launch(gdn::gdn_bwd_prep_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo,
                   qe, ke, doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf),
-                  reinterpret_cast<gdn::f32x4*>(w + bl.bq), reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
+                  reinterpret_cast<gdn::Quad<E>*>(w + bl.bq), reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
       else
         ok(launch(gdn::gdn_bwd_prep_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe,
-                  ke, doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::f32x4*>(w + bl.bq),
+                  ke, doe, cmap, gam, wf, FE(bl.wtf), FE(bl.kdf), reinterpret_cast<gdn::Quad<E>*>(w + bl.bq),
                   reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
     }
   mark(2);
@@ -466,12 +466,12 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
     // one unit per CU or fewer: the K rows split over K/32 waves
     ok(launch(gdn::gdn_bwd_chain_ks_kernel<E, K, V, VARLEN, 2>, dim3(units), dim3(64 * (K / 32)), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
-              reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
+              reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
               F(bl.dhn), F(bl.dvn)));
   else if (units > 0)
     ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
-              reinterpret_cast<const gdn::f32x4*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
+              reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
               F(bl.dhn), F(bl.dvn)));
   mark(3);
   if (chunk_wgs > 0) {

@@ -57,8 +57,8 @@
 // group l/16; D tiles fp32):
 //   wtf      [hv][slot][K/16][2][lane]  A operand (rows k, k over the chunk): w^T
 //   kdf      [hv][slot][4][K/32][lane]  A operand (rows c, k over K): kd
-//   bq       [hv][slot][V/16][K/16][lane] D tiles (rows k, column v):
-//                                       scale (e^G * Q)^T do
+//   bq       [hv][slot][V/16][K/16][lane] D tiles (rows k, column v) in the
+//                                       call's dtype: scale (e^G * Q)^T do
 //   dvl      [hv][slot][V/16][4][lane]  D tiles (rows c, column v): dv_local
 #pragma once
 #include "gdn_kernels.h"
@@ -229,7 +229,7 @@ template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_prep_kernel(
     Geo geo, const E* __restrict__ qg, const E* __restrict__ kg, const E* __restrict__ dog,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<E>* __restrict__ wf,
-    Frag<E>* __restrict__ wtf, Frag<E>* __restrict__ kdf, f32x4* __restrict__ bq,
+    Frag<E>* __restrict__ wtf, Frag<E>* __restrict__ kdf, Quad<E>* __restrict__ bq,
     f32x4* __restrict__ dvl) {
   constexpr int KP = Pad<K>::v, VP = Pad<V>::v, KT = K / 16, KB = K / 32, NV = V / 16;
   constexpr int TH = kBwdThreads, NW = TH / 64;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_prep_kernel(
     const int mt = f / NV, vt = f - mt * NV;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mm16<kChunk>(acc, Qs + 16 * mt, 1, KP, Ds + 16 * vt, VP, 1);
-    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = acc;
+    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = make_quad<E>(acc);
   }
   __syncthreads();
   // w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_prep_kernel(
 template <typename E, int K, int V, bool VARLEN>
 __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
     Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
-    const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq, const float* __restrict__ gam,
+    const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
     float* __restrict__ dhn, float* __restrict__ dvn) {
   constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
     gl = gam[hs * kChunk + lane];  // lane 63 holds the chunk's last cumulative gate
 #pragma unroll
     for (int mt = 0; mt < KT; ++mt) {
-      b[mt] = bq[((hs * NV + vt) * KT + mt) * 64 + lane];
+      b[mt] = quad_f32(bq[((hs * NV + vt) * KT + mt) * 64 + lane]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) wt[mt][cb] = wtf[((hs * KT + mt) * 2 + cb) * 64 + lane];
     }
@@ -443,12 +443,12 @@ struct BwdKsStep {
   Frag<E> kd[4];      // kd, chunk-row tile ct, k block q
   Frag<E> wt[2][2];   // w^T, row tile 2q + j, chunk block cb
   f32x4 dl[OWN];      // dv_local, chunk-row tiles q + KB j
-  f32x4 b[2];         // bq, row tiles 2q + j
+  Quad<E> b[2];       // bq, row tiles 2q + j
   float gl;           // lane l: entry l of the chunk's gate row
 
   template <int Q>
   __device__ __forceinline__ void load(const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
-                                       const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq,
+                                       const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq,
                                        const float* __restrict__ gam, size_t hs, int vt, int lane) {
     gl = gam[hs * kChunk + lane];
 #pragma unroll
@@ -468,7 +468,7 @@ template <typename E, int K, int V, int D, int Q>
 __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const Frag<E>* __restrict__ kdf,
                                                   const f32x4* __restrict__ dvl,
                                                   const Frag<E>* __restrict__ wtf,
-                                                  const f32x4* __restrict__ bq, const float* __restrict__ gam,
+                                                  const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
                                                   const float* __restrict__ dht, float* __restrict__ dh0,
                                                   float* __restrict__ dhn, float* __restrict__ dvn, int s0,
                                                   int s1, size_t hbase, size_t sbase, int vt) {
@@ -523,7 +523,7 @@ __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const
     const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.gl), kChunk - 1)));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      dH[j] = dH[j] * dec + S.b[j];
+      dH[j] = dH[j] * dec + quad_f32(S.b[j]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) mma_k32(dH[j], S.wt[j][cb], nb[cb]);
     }
@@ -557,7 +557,7 @@ done:
 template <typename E, int K, int V, bool VARLEN, int D>
 __global__ __launch_bounds__(64 * (K / 32)) void gdn_bwd_chain_ks_kernel(
     Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
-    const Frag<E>* __restrict__ wtf, const f32x4* __restrict__ bq, const float* __restrict__ gam,
+    const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
     float* __restrict__ dhn, float* __restrict__ dvn) {
   static_assert(K == 64 || K == 128, "two or four waves");
@@ -847,7 +847,7 @@ template <int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_prep_bf16_kernel(
     Geo geo, const bf16* __restrict__ qg, const bf16* __restrict__ kg, const bf16* __restrict__ dog,
     const int4* __restrict__ cmap, const float* __restrict__ gam, const Frag<bf16>* __restrict__ wf,
-    Frag<bf16>* __restrict__ wtf, Frag<bf16>* __restrict__ kdf, f32x4* __restrict__ bq,
+    Frag<bf16>* __restrict__ wtf, Frag<bf16>* __restrict__ kdf, Quad<bf16>* __restrict__ bq,
     f32x4* __restrict__ dvl) {
   constexpr int SK = PadB<K>::v, SC = PadB<kChunk>::v;
   constexpr int KT = K / 16, KB = K / 32, NV = V / 16, TH = kBwdThreads, NW = TH / 64;
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
       mma_k32(acc, frag_from_trow(Qt, 16 * mt + lc, SC, 32 * cb), frag_from_trow(Dst, 16 * vt + lc, SC, 32 * cb));
-    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = acc;
+    bq[((hs * NV + vt) * KT + mt) * 64 + lane] = make_quad<bf16>(acc);
   }
   // D. w from its forward fragments (rows c = 16 ct + lane%16, k = 32 kb + kslot)
   // into the q rows' space (free since q^T was built), then w^T fragments.
