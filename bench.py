@@ -25,7 +25,41 @@ METRIC = "GDN chunk-fwd tokens/s (B=2,T=2048,H=8,K=V=128 bf16); % MFMA/HBM peak"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "fp32": 157.3e12}  # dense flop/s
 CHUNK = 64
+GRAPH_PER = 10               # steps per HIP graph in the many-steps graph view
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def metric_label(op, cfg):
+    """The metric string of a forward or backward line, named after the workload
+    it measures: B, T, heads (HV only when it differs from H), head sizes and
+    dtype, or the packed total and sequence count.  For the forward pass at
+    B=2, T=2048, H=HV=8, K=V=128 bf16 this is METRIC exactly."""
+    kind = {"gdn_fwd": "chunk-fwd", "gdn_bwd": "chunk-bwd"}[op]
+    heads = "H=%d" % cfg["H"] + ("" if cfg["HV"] == cfg["H"] else ",HV=%d" % cfg["HV"])
+    dims = ("K=V=%d" % cfg["K"]) if cfg["K"] == cfg["V"] else "K=%d,V=%d" % (cfg["K"], cfg["V"])
+    if cfg.get("num_seqs"):
+        seqs = "packed T=%d in %d seqs" % (cfg["T"], cfg["num_seqs"])
+    else:
+        seqs = "B=%d,T=%d" % (cfg["B"], cfg["T"])
+    extra = ",h0" if cfg.get("h0") else ""
+    return "GDN %s tokens/s (%s,%s,%s%s %s); %% MFMA/HBM peak" % (kind, seqs, heads, dims, extra,
+                                                                cfg["dtype"])
+
+
+def kernel_figures(a, t_ms, dtype):
+    """Rates of one kernel (algorithmic bytes and flops `a`, average duration
+    t_ms) against the HBM peak and the MFMA peak of the dtype its products
+    take: the call's dtype, for every forward and backward kernel (a bf16 call
+    runs all of its products on the bf16 MFMA, an fp32 call on the fp32 MFMA)."""
+    sec = t_ms / 1e3
+    if sec <= 0:
+        return dict(us=round(t_ms * 1e3, 3), bytes=a["bytes"], flops=a["flops"], hbm_gbs=None,
+                    hbm_frac=None, mfma_tflops=None, mfma_frac=None, mfma_dtype=dtype)
+    return dict(us=round(t_ms * 1e3, 3), bytes=a["bytes"], flops=a["flops"],
+                hbm_gbs=round(a["bytes"] / sec / 1e9, 1),
+                hbm_frac=round(a["bytes"] / sec / HBM_PEAK, 4),
+                mfma_tflops=round(a["flops"] / sec / 1e12, 2),
+                mfma_frac=round(a["flops"] / sec / MFMA_PEAK[dtype], 4), mfma_dtype=dtype)
 
 
 def parse():
@@ -539,17 +573,7 @@ def bench_bwd(args):
     kern, path, ntok = algorithmic_bwd(sh, esz, inp.h0 is not None, True, used)
     kernels = {}
     for name, t in zip(gdn.BWD_STAGES, stage_ms):
-        a = kern[name]
-        sec = t / 1e3
-        # the recompute (forward kernels), the backward state pass and the dq/dk
-        # kernel multiply in the call's dtype; the other backward kernels in fp32
-        mdt = dtype if name in ("recompute", "bwd_chain", "dqk") else "fp32"
-        kernels[name] = dict(us=round(t * 1e3, 3), bytes=a["bytes"], flops=a["flops"],
-                             hbm_gbs=round(a["bytes"] / sec / 1e9, 1),
-                             hbm_frac=round(a["bytes"] / sec / HBM_PEAK, 4),
-                             mfma_tflops=round(a["flops"] / sec / 1e12, 2),
-                             mfma_frac=round(a["flops"] / sec / MFMA_PEAK[mdt], 4),
-                             mfma_dtype=mdt)
+        kernels[name] = kernel_figures(kern[name], t, dtype)
     single = [n for n in kernels if n != "recompute"]  # stages of one kernel
     dom = max(single, key=lambda n: kernels[n]["us"])
     d = kernels[dom]
@@ -576,7 +600,7 @@ def bench_bwd(args):
                 k.update({"counters_" + a: b for a, b in kernel_counters(e).items()})
     sec = ms / 1e3
     out = {
-        "metric": "GDN chunk-bwd tokens/s (%s)" % wl, "value": round(ntok / sec, 1),
+        "metric": metric_label("gdn_bwd", cfg), "value": round(ntok / sec, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
@@ -587,7 +611,7 @@ def bench_bwd(args):
         "roofline": roof,
         "path_roofline": {"bytes": path["bytes"], "flops": path["flops"],
                           "hbm_frac": round(path["bytes"] / sec / HBM_PEAK, 4),
-                          "mfma_frac_fp32": round(path["flops"] / sec / MFMA_PEAK["fp32"], 4)},
+                          "mfma_frac": round(path["flops"] / sec / MFMA_PEAK[dtype], 4)},
         "kernels": kernels,
         "kernel_source_hash": src,
         "cpu_baseline": None,
@@ -696,23 +720,36 @@ def main():
         cold_ms = total / args.cold_steps
         del flush
 
-    # the same step captured once in a HIP graph and replayed (launch overhead view)
-    graph_ms = None
+    # the same step captured in HIP graphs and replayed (launch overhead view):
+    # one step per graph, and GRAPH_PER steps per graph (per step: the
+    # difference between the two is the cost of one graph launch); each
+    # replay's o must equal the eager step's bit for bit (the same work)
+    graph_ms = graph_many_ms = None
     try:
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            gstep = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log, inp.dt_bias,
-                              inp.cu_seqlens, inp.h0, stream=cap)
-            with torch.cuda.graph(g, stream=cap):
-                gstep()
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        for _ in range(3):
+        o_eager = plan.o.clone()
+        graphs = {}
+        for per in (1, GRAPH_PER):
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                gstep = plan.bind(inp.q, inp.k, inp.v, inp.g_raw, inp.beta, inp.A_log,
+                                  inp.dt_bias, inp.cu_seqlens, inp.h0, stream=cap)
+                with torch.cuda.graph(g, stream=cap):
+                    for _ in range(per):
+                        gstep()
+            stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            graphs[per] = g
+        for per, g in graphs.items():
+            plan.o.fill_(float("nan"))
             g.replay()
-        torch.cuda.synchronize()
-        graph_ms = timed(g.replay, args.steps)
+            torch.cuda.synchronize()
+            if not torch.equal(plan.o, o_eager):
+                raise RuntimeError("graph replay (%d steps) differs from the eager step" % per)
+        graph_ms = timed(graphs[1].replay, args.steps)
+        reps = max(1, args.steps // GRAPH_PER)
+        graph_many_ms = timed(graphs[GRAPH_PER].replay, reps) / GRAPH_PER
     except Exception as exc:  # graph capture is an extra view, not the headline
         print("graph timing skipped: %s" % exc, file=sys.stderr, flush=True)
 
@@ -750,14 +787,7 @@ def main():
     for (name, _), t in zip(stage_list, stage_ms):
         if name == "chunk_map" and not packed:
             continue
-        a = kern[name]
-        sec = t / 1e3
-        kernels[name] = dict(us=round(t * 1e3, 3), bytes=a["bytes"], flops=a["flops"],
-                             hbm_gbs=round(a["bytes"] / sec / 1e9, 1) if sec > 0 else None,
-                             hbm_frac=round(a["bytes"] / sec / HBM_PEAK, 4) if sec > 0 else None,
-                             mfma_tflops=round(a["flops"] / sec / 1e12, 2) if sec > 0 else None,
-                             mfma_frac=round(a["flops"] / sec / MFMA_PEAK[dtype], 4)
-                             if sec > 0 else None)
+        kernels[name] = kernel_figures(kern[name], t, dtype)
     dom = max(kernels, key=lambda n: kernels[n]["us"])
     d = kernels[dom]
     ai = d["flops"] / d["bytes"]
@@ -785,7 +815,7 @@ def main():
                 k.update({"counters_" + a: b for a, b in kernel_counters(e).items()})
     sec = ms / 1e3
     out = {
-        "metric": METRIC,
+        "metric": metric_label("gdn_fwd", cfg),
         "value": round(ntok / sec, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -793,6 +823,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "graph%d_ms_per_step" % GRAPH_PER: None if graph_many_ms is None
+        else round(graph_many_ms, 5),
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "cold_tokens_per_s": None if cold_ms is None else round(ntok / (cold_ms / 1e3), 1),
         "higher_is_better": True,

@@ -150,6 +150,51 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_tensor(name, t, shape, dtype, required=True):
+    """Raise ValueError / TypeError unless `t` has exactly `shape` and `dtype`
+    (None is accepted when not required)."""
+    if t is None:
+        if required:
+            raise ValueError("%s is required" % name)
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _check_placement(named, device):
+    """Every given tensor contiguous and on `device` (checked after the shapes)."""
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError("%s must be a GPU tensor on %s, got %s" % (name, device, t.device))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _check_forward_inputs(plan, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                          initial_state):
+    """The forward inputs against a plan's sizes and dtype (include/gdn.h layouts)."""
+    torch = _torch()
+    B, T, H, HV, K, V = plan.dims
+    f32 = torch.float32
+    if (cu_seqlens is not None) != plan.packed:
+        raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
+    _check_tensor("q", q, (B, T, H, K), plan.dtype)
+    _check_tensor("k", k, (B, T, H, K), plan.dtype)
+    _check_tensor("v", v, (B, T, HV, V), plan.dtype)
+    _check_tensor("g_raw", g_raw, (B, T, HV), f32)
+    _check_tensor("beta", beta, (B, T, HV), f32)
+    _check_tensor("A_log", A_log, (HV,), f32)
+    _check_tensor("dt_bias", dt_bias, (HV,), f32, required=False)
+    _check_tensor("cu_seqlens", cu_seqlens, (plan.N + 1,), torch.int64, required=plan.packed)
+    _check_tensor("initial_state", initial_state, (plan.N, HV, K, V), f32, required=False)
+    return [("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta), ("A_log", A_log),
+            ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens), ("initial_state", initial_state)]
+
+
 def _dtype_code(dt):
     torch = _torch()
     if dt == torch.bfloat16:
@@ -173,6 +218,8 @@ class GdnForward:
         torch = _torch()
         self.packed = num_seqs is not None
         self.N = num_seqs if self.packed else B
+        self.dims = (B, T, H, HV, K, V)
+        self.dtype = dtype
         self.params = make_params(B, T, H, HV, K, V, _dtype_code(dtype),
                                   num_seqs if self.packed else 0, scale, seg_chunks)
         self.lib = load_library()
@@ -185,15 +232,13 @@ class GdnForward:
                             if final_state else None)
 
     def _args(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream):
-        """Checked ctypes argument tuple of gdn_fwd (host-side checks only)."""
+        """Checked ctypes argument tuple of gdn_fwd (host-side checks only): every
+        tensor's shape and dtype against the plan, then device and contiguity,
+        then gdn_fwd_check; raises before anything is launched."""
         torch = _torch()
-        if (cu_seqlens is not None) != self.packed:
-            raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
-        for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta),
-                        ("A_log", A_log), ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
-                        ("initial_state", initial_state)):
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError("%s must be a contiguous GPU tensor" % name)
+        named = _check_forward_inputs(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                                      initial_state)
+        _check_placement(named, self.o.device)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         args = (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),
@@ -264,6 +309,10 @@ def decode_launcher(q, k, v, g_raw, beta, A_log, state, dt_bias=None, scale=1.0,
         raise ValueError("q, k, v shapes or dtypes disagree")
     if g_raw.shape != (B, T, HV) or beta.shape != (B, T, HV) or state.shape != (B, HV, K, V):
         raise ValueError("g_raw, beta must be [B,T,HV] and state [B,HV,K,V]")
+    if A_log.shape != (HV,) or (dt_bias is not None and dt_bias.shape != (HV,)):
+        raise ValueError("A_log and dt_bias must be [HV]")
+    if out is not None and (out.shape != (B, T, HV, V) or out.dtype != q.dtype):
+        raise ValueError("out must be [B,T,HV,V] in q's dtype")
     for name, t in (("g_raw", g_raw), ("beta", beta), ("A_log", A_log), ("dt_bias", dt_bias),
                     ("state", state)):
         if t is not None and t.dtype != torch.float32:
@@ -381,6 +430,8 @@ class GdnBackward:
         torch = _torch()
         self.packed = num_seqs is not None
         self.N = num_seqs if self.packed else B
+        self.dims = (B, T, H, HV, K, V)
+        self.dtype = dtype
         self.params = make_params(B, T, H, HV, K, V, _dtype_code(dtype),
                                   num_seqs if self.packed else 0, scale)
         self.lib = load_library()
@@ -405,16 +456,14 @@ class GdnBackward:
     def _args(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, d_o,
               d_final_state, stream):
         torch = _torch()
-        if (cu_seqlens is not None) != self.packed:
-            raise ValueError("cu_seqlens given/omitted inconsistently with the plan")
-        for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta", beta),
-                        ("A_log", A_log), ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
-                        ("initial_state", initial_state), ("d_o", d_o),
-                        ("d_final_state", d_final_state)):
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError("%s must be a contiguous GPU tensor" % name)
-        if d_o.shape != self.dv.shape or d_o.dtype != self.dv.dtype:
-            raise ValueError("d_o must match o's shape and dtype")
+        B, T, H, HV, K, V = self.dims
+        named = _check_forward_inputs(self, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                                      initial_state)
+        _check_tensor("d_o", d_o, (B, T, HV, V), self.dtype)
+        _check_tensor("d_final_state", d_final_state, (self.N, HV, K, V), torch.float32,
+                      required=False)
+        _check_placement(named + [("d_o", d_o), ("d_final_state", d_final_state)],
+                         self.dq.device)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         return (ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta),

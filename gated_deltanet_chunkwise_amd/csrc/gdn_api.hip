@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <cstring>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -30,6 +31,17 @@ struct Plan {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The int a C caller passed for an enum-typed argument.  C lets any int
+// through; loading an enum object that holds a value outside the enumerators'
+// range is undefined in C++, so the bits are read instead of the enum.
+template <typename Enum>
+int enum_bits(const Enum& e) {
+  static_assert(sizeof(Enum) == sizeof(int), "enum arguments are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // Compute units of the current device (cached per device id; a benign race
 // at worst stores the same value twice).
 int device_cus() {
@@ -54,6 +66,9 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   if (p->HV % p->H) return GDN_ERR_SHAPE;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDN_ERR_UNSUPPORTED;
   if (varlen && (p->B != 1 || p->num_seqs < 0)) return GDN_ERR_SHAPE;
+  // tokens but no sequence: cu_seqlens = {0} cannot end at T > 0, and every
+  // per-chunk launch would read a chunk map that nothing wrote
+  if (varlen && p->num_seqs == 0 && p->T > 0) return GDN_ERR_SHAPE;
   if (p->seg_chunks < 0) return GDN_ERR_SHAPE;
   const int64_t N = varlen ? p->num_seqs : p->B;
   const int64_t NT = ((int64_t)p->T + gdn::kChunk - 1) / gdn::kChunk;
@@ -697,13 +712,14 @@ gdn_status_t gdn_decode(const gdn_params_t* p, const void* q, const void* k, con
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-gdn_status_t gdn_kda_gate(const void* g, gdn_dtype_t g_dtype, const float* A_log,
-                          const float* dt_bias, void* yg, gdn_dtype_t yg_dtype, int64_t T,
+gdn_status_t gdn_kda_gate(const void* g, gdn_dtype_t g_dtype_arg, const float* A_log,
+                          const float* dt_bias, void* yg, gdn_dtype_t yg_dtype_arg, int64_t T,
                           int32_t H, int32_t D, void* stream) {
   if (T < 0 || H < 1 || D < 1) return GDN_ERR_SHAPE;
   if ((int64_t)H * D > INT64_MAX / (T > 0 ? T : 1)) return GDN_ERR_SHAPE;
-  auto known = [](gdn_dtype_t t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; };
-  if (!known(g_dtype) || !known(yg_dtype)) return GDN_ERR_DTYPE;
+  auto known = [](int t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; };
+  if (!known(enum_bits(g_dtype_arg)) || !known(enum_bits(yg_dtype_arg))) return GDN_ERR_DTYPE;
+  const gdn_dtype_t g_dtype = g_dtype_arg, yg_dtype = yg_dtype_arg;  // now in range
   if (T == 0) return GDN_OK;
   if (!g || !A_log || !yg) return GDN_ERR_NULL;
   if (!aligned_to(g, elem_size(g_dtype)) || !aligned_to(yg, elem_size(yg_dtype)) ||
@@ -754,7 +770,7 @@ gdn_status_t gdn_bwd(const gdn_params_t* p, const void* q, const void* k, const 
 }
 
 const char* gdn_status_string(gdn_status_t s) {
-  switch (s) {
+  switch (enum_bits(s)) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "a required pointer is NULL";
     case GDN_ERR_SHAPE: return "invalid shape";

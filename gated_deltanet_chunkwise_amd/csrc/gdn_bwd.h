@@ -37,14 +37,20 @@
 // (also storing T) and the state pass in its CHAIN_PLAIN mode (fp32 H_c and
 // v_new).
 //
-// Arithmetic is fp32 (fp32 MFMA v_mfma_f32_16x16x4f32, operands staged as fp32
-// in LDS), except in the backward state pass, whose products take their
-// operands in the call's dtype like the forward state pass's (bf16 MFMA for
-// bf16 calls; the state gradient itself accumulates in fp32), and in the
-// dq/dk kernel of bf16 calls, whose operands are staged as bf16 for the bf16
-// MFMA (fp32 accumulation; gdn_bwd_dqk_bf16_kernel).  q, k, v, do are
-// read, and dq, dk, dv written, in the call's dtype.  Intermediates in the
-// workspace are fp32 row-major:
+// Arithmetic.  fp32 calls run every product on the fp32 MFMA
+// (v_mfma_f32_16x16x4f32, operands staged as fp32 in LDS).  bf16 calls run
+// every product on the bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32
+// accumulation: the forward recompute (WY, state pass), the prep kernel
+// (gdn_bwd_prep_bf16_kernel: q, k, do exact, P and scale e^G do rounded to
+// bf16 once), the backward state pass (operands in the call's dtype, the state
+// gradient accumulating in fp32), dq/dk (gdn_bwd_dqk_bf16_kernel) and the WY
+// backward (gdn_bwd_wy_bf16_kernel: k, v exact; dw, dv_new, T, dT, Y and dS
+// rounded to bf16 once each).  The gate backward, the chunk-local reductions
+// and the sums are fp32 VALU work.  q, k, v, do are read, and dq, dk, dv
+// written, in the call's dtype.  Workspace intermediates: T, H_c, v_new and
+// the gradients below are fp32 row-major; the state pass's operands (wtf, kdf)
+// and the dO term bq are fragments in the call's dtype (bq is rounded to it
+// once per chunk, before the state pass adds it to the fp32 dH):
 //   hcp, dhn [hv][slot][V][K]          H_c^T, (dL/dH_{c+1})^T
 //   vnp, dvn [hv][slot][V][64]         v_new^T, (dL/dv_new)^T
 //   tmat     [hv][slot][64][64]        T

@@ -66,7 +66,9 @@
  * (not checked, to avoid a device-to-host sync): cu_seqlens[0] == 0,
  * cu_seqlens[N] == T, non-decreasing.  Offsets that break it are clamped on the
  * device so that no access leaves the buffers; the results are then undefined.
- * Empty sequences are allowed (final state = initial state).
+ * Empty sequences are allowed (final state = initial state).  N = 0 is
+ * allowed only with T = 0 (GDN_ERR_SHAPE otherwise: tokens with no sequence to
+ * hold them).
  *
  * Ownership.  The caller owns every buffer.  The library never allocates,
  * frees or synchronizes; gdn_fwd only enqueues kernels on `stream` (a
@@ -154,7 +156,12 @@ gdn_status_t gdn_fwd_workspace_layout(const gdn_params_t *p, int packed,
 /* Validate a gdn_fwd call without touching the GPU or dereferencing any device
  * pointer: sizes, dtype, NULL-ness and alignment (q, k, v, o: 16 bytes;
  * g_raw, beta, A_log, dt_bias, initial_state, final_state: 4 bytes;
- * cu_seqlens: 8 bytes; workspace: 256 bytes) and workspace_bytes. */
+ * cu_seqlens: 8 bytes; workspace: 256 bytes) and workspace_bytes.  These are
+ * the checks the KDA gate guide's API layer makes with asserts on ndim, shape
+ * and element count before it dispatches (MindSpeed-Ops issue page, "API
+ * layer"), returned here as status codes; the packed-sequence rules are those
+ * of the G_T_CONTIG page, "varlen checklist".  gdn_fwd runs the same checks
+ * first and enqueues nothing when one fails. */
 gdn_status_t gdn_fwd_check(const gdn_params_t *p, const void *q, const void *k,
                            const void *v, const float *g_raw, const float *beta,
                            const float *A_log, const float *dt_bias,
@@ -245,7 +252,11 @@ gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
  * `stream`: the per-chunk dv_local and operand preparation, the state-gradient
  * pass backwards over each sequence's chunks, the per-chunk dq/dk/dw/dg, the
  * WY backward with the gate backward, and the per-key-head dq/dk sums and
- * per-head dA_log/ddt_bias sums.  Arithmetic is fp32 (fp32 MFMA).
+ * per-head dA_log/ddt_bias sums.  Arithmetic: fp32 calls multiply on the fp32
+ * MFMA; bf16 calls multiply every product (recompute, dv_local preparation,
+ * state-gradient pass, dq/dk, WY backward) on the bf16 MFMA with fp32
+ * accumulation, their operands rounded to bf16 once (the per-chunk dO term of
+ * the state gradient included); the gate backward and the sums are fp32.
  *   p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state:
  *            exactly as for gdn_fwd (p->seg_chunks is not used: both state
  *            passes here run sequentially over each sequence)

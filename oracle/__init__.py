@@ -6,6 +6,8 @@ the HIP library (no shared code, headers or helpers, and it imports nothing
 from gated_deltanet_chunkwise_amd).
 
 * ``fwd``        -- token-by-token recurrence (C, fp64, pthreads), the oracle.
+* ``ref_fwd``    -- the same through ``gdn_ref_fwd``, the C twin of the
+                    library's gdn_fwd (same argument order, fp64 host arrays).
 * ``gate``       -- the gate activation alone (C, fp64).
 * ``recurrence`` -- the recurrence from a given log-decay g (C, fp64).
 * ``bwd``        -- reverse-mode derivative of ``fwd`` (C, fp64, pthreads) for
@@ -42,6 +44,9 @@ def _declare(lib):
     lib.gdn_oracle_recurrence.argtypes = common + [_dp, _dp, _dp] + tail
     lib.gdn_oracle_fwd.restype = ctypes.c_int
     lib.gdn_oracle_fwd.argtypes = common + [_dp, _dp, _dp, _dp, _dp] + tail
+    lib.gdn_ref_fwd.restype = ctypes.c_int
+    lib.gdn_ref_fwd.argtypes = ([ctypes.c_int] * 7 + [ctypes.c_double] + [_dp] * 7 + [_i64p]
+                                + [_dp] * 3 + [ctypes.c_int])
     lib.gdn_oracle_bwd.restype = ctypes.c_int
     lib.gdn_oracle_bwd.argtypes = (common + [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp,
                                              _i32p, ctypes.c_int] + [_dp] * 8 + [ctypes.c_int])
@@ -165,6 +170,27 @@ def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, h0=None,
     """
     return _run("gdn_oracle_fwd", q, k, v, [g_raw, A_log, dt_bias], beta,
                 cu_seqlens, h0, scale, units, nthreads, lib)
+
+
+def ref_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_state=None,
+            scale=1.0, nthreads=None, lib=None):
+    """gdn_ref_fwd: the oracle forward pass called with gdn_fwd's argument
+    order (q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state ->
+    o, final_state).  Same arrays and results as ``fwd``."""
+    lib = lib or load()
+    B, T, H, HV, K, V, N = _shapes(q, v, cu_seqlens)
+    q, k, v, g_raw, beta, A_log, dt_bias, h0 = (
+        _f64(x) for x in (q, k, v, g_raw, beta, A_log, dt_bias, initial_state))
+    cu = None if cu_seqlens is None else np.ascontiguousarray(np.asarray(cu_seqlens, np.int64))
+    o = np.zeros((B, T, HV, V), np.float64)
+    fin = np.zeros((N, HV, K, V), np.float64)
+    rc = lib.gdn_ref_fwd(B, T, H, HV, K, V, N if cu is not None else 0, float(scale),
+                         _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log),
+                         _ptr(dt_bias), _ptr(cu, _i64p), _ptr(h0), _ptr(o), _ptr(fin),
+                         int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle returned error code %d" % rc)
+    return o, fin
 
 
 def recurrence(q, k, v, g, beta, cu_seqlens=None, h0=None, scale=1.0,

@@ -257,6 +257,33 @@ int gdn_oracle_fwd(int B, int T, int H, int HV, int K, int V,
   return rc;
 }
 
+/*
+ * Host twin of the library's gdn_fwd, with its argument order: the sizes
+ * (B, T, H, HV, K, V, num_seqs, scale standing in for its parameter struct),
+ * then q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+ * final_state, all fp64 host arrays in the library's layouts; the workspace
+ * and stream have no counterpart, nthreads takes their place.  cu_seqlens
+ * NULL: B sequences of T tokens; otherwise num_seqs packed sequences (B = 1).
+ * dt_bias and initial_state may be NULL (zero); final_state may be NULL (not
+ * written).  Returns ORACLE_* codes.
+ */
+int gdn_ref_fwd(int B, int T, int H, int HV, int K, int V, int num_seqs, double scale,
+                const double *q, const double *k, const double *v, const double *g_raw,
+                const double *beta, const double *A_log, const double *dt_bias,
+                const int64_t *cu_seqlens, const double *initial_state, double *o,
+                double *final_state, int nthreads) {
+  int N = cu_seqlens ? num_seqs : B;
+  double *fin = final_state;
+  if (!fin && N > 0 && HV > 0 && K > 0 && V > 0) {
+    fin = (double *)malloc(sizeof(double) * (size_t)N * HV * K * V);
+    if (!fin) return ORACLE_ENOMEM;
+  }
+  int rc = gdn_oracle_fwd(B, T, H, HV, K, V, cu_seqlens, N, q, k, v, g_raw, beta, A_log,
+                          dt_bias, initial_state, scale, NULL, 0, o, fin, nthreads);
+  if (fin != final_state) free(fin);
+  return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Backward: reverse-mode derivative of the token recurrence (see the top).  */
 

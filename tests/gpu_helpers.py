@@ -23,8 +23,9 @@ def f64(t):
     return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, plan_out=None):
-    """Run the library on `inp` (CPU GdnInputs); returns (o, final) as fp64 numpy."""
+def run_gpu(inp, plan_out=None, ws_fill=None):
+    """Run the library on `inp` (CPU GdnInputs); returns (o, final) as fp64 numpy.
+    ws_fill: a byte value the workspace is filled with first."""
     d = inp.to("cuda")
     s = inp.shape
     plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
@@ -32,6 +33,8 @@ def run_gpu(inp, plan_out=None):
     # NaN-fill the outputs so that any element the kernels fail to write shows up
     plan.o.fill_(float("nan"))
     plan.final_state.fill_(float("nan"))
+    if ws_fill is not None:
+        plan.workspace.fill_(ws_fill)
     o, fin = plan(d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
     torch.cuda.synchronize()
     if plan_out is not None:
@@ -88,3 +91,63 @@ def assert_close(x, r, dtype, what):
     if tol["max_abs"] is not None:
         assert m["max_abs"] <= tol["max_abs"], (what, m)
     return m
+
+
+def _sub_problem(inp, b, h_lo, h_hi):
+    """Inputs restricted to batch row b (None: all rows, packed input) and key
+    heads [h_lo, h_hi) with the value heads that read them: the same GQA
+    structure on fewer heads."""
+    s = inp.shape
+    G = s["HV"] // s["H"]
+    hv_lo, hv_hi = h_lo * G, h_hi * G
+    rows = slice(None) if b is None else slice(b, b + 1)
+    kh = lambda t: t[rows, :, h_lo:h_hi]  # noqa: E731
+    vh = lambda t: t[rows, :, hv_lo:hv_hi]  # noqa: E731
+    if inp.h0 is None:
+        h0 = None
+    else:
+        n_rows = slice(None) if b is None else slice(b, b + 1)
+        h0 = inp.h0[n_rows, hv_lo:hv_hi]
+    return dict(q=kh(inp.q), k=kh(inp.k), v=vh(inp.v), g_raw=vh(inp.g_raw), beta=vh(inp.beta),
+                A_log=inp.A_log[hv_lo:hv_hi], dt_bias=inp.dt_bias[hv_lo:hv_hi], h0=h0), \
+        (rows, slice(hv_lo, hv_hi))
+
+
+def full_oracle_metrics(inp, o, fin, heads_per_batch=None):
+    """rel-L2 and max-abs of the GPU outputs (o [B,T,HV,V], fin [N,HV,K,V], fp64
+    numpy) against the oracle over EVERY element, each tensor as a whole.  The
+    oracle runs in batches (one sequence of a fixed-length batch, or the whole
+    packed batch, times a group of key heads) so that host memory stays bounded;
+    the sums of squares and the maximum are accumulated across batches."""
+    s = inp.shape
+    H = s["H"]
+    hb = heads_per_batch or H
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    acc = {"o": [0.0, 0.0, 0.0], "final": [0.0, 0.0, 0.0]}
+    rows = [None] if cu is not None else list(range(s["B"]))
+    for b in rows:
+        for h_lo in range(0, H, hb):
+            sub, (rsl, hsl) = _sub_problem(inp, b, h_lo, min(H, h_lo + hb))
+            o_r, f_r = oracle.fwd(f64(sub["q"]), f64(sub["k"]), f64(sub["v"]), f64(sub["g_raw"]),
+                                  f64(sub["beta"]), f64(sub["A_log"]), f64(sub["dt_bias"]),
+                                  cu_seqlens=cu, h0=f64(sub["h0"]), scale=inp.scale)
+            n_rows = slice(None) if b is None else slice(b, b + 1)
+            for key, x, r in (("o", o[rsl, :, hsl], o_r), ("final", fin[n_rows, hsl], f_r)):
+                d = x - r
+                a = acc[key]
+                a[0] += float(np.sum(d * d))
+                a[1] += float(np.sum(r * r))
+                a[2] = max(a[2], float(np.max(np.abs(d))) if d.size else 0.0)
+    out = {}
+    for key, (dd, rr, mx) in acc.items():
+        out[key] = dict(rel_l2=float(np.sqrt(dd / rr)) if rr > 0 else float(np.sqrt(dd)),
+                        max_abs=mx)
+    return out
+
+
+def assert_metrics(m, dtype, what):
+    tol = TOL[dtype]
+    say("  %-28s rel_l2=%.3e max_abs=%.3e" % (what, m["rel_l2"], m["max_abs"]))
+    assert m["rel_l2"] <= tol["rel_l2"], (what, m)
+    if tol["max_abs"] is not None:
+        assert m["max_abs"] <= tol["max_abs"], (what, m)

@@ -275,3 +275,21 @@ def test_bwd_workspace_grows_with_the_problem():
     assert sizes[0] < sizes[1] < sizes[2]
     pk = P(B=1, T=1000, num_seqs=5)
     assert lib.gdn_bwd_workspace_size(ctypes.byref(pk), 1) > gdn.workspace_size(pk, packed=True)
+
+
+def test_packed_call_without_sequences():
+    """A packed call with no sequence but tokens is rejected before anything is
+    enqueued, forward and backward (every per-chunk launch would otherwise read
+    a chunk map nothing wrote); no sequence and no token is a valid no-op."""
+    lib = gdn.load_library()
+    bad = P(B=1, T=64, num_seqs=0)
+    assert gdn.workspace_size(bad, packed=True) == 0
+    assert gdn.check(bad, ptrs(cu_seqlens=0x90000), 1 << 40) == ESHAPE
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(bad), 1) == 0
+    assert _bwd_call(lib, bad, 1 << 40, cu_seqlens=0x90000) == ESHAPE
+    empty = P(B=1, T=0, num_seqs=0)
+    ws = gdn.workspace_size(empty, packed=True)
+    null = dict(q=None, k=None, v=None, g_raw=None, beta=None, A_log=None, o=None)
+    assert gdn.check(empty, ptrs(cu_seqlens=0x90000, **null), ws) == OK
+    # the same sizes without cu_seqlens are a fixed-length call (N = B = 1)
+    assert gdn.check(bad, ptrs(), 1 << 40) == OK

@@ -109,3 +109,36 @@ def test_every_state_pass_variant_maps_to_its_stage(tmp_path):
         _counter_csv(path, [(kernel, "FETCH_SIZE", 8.0)])
         means, _ = bench.counter_means(path)
         assert means == {stage: 8.0}, kernel
+
+
+def test_metric_names_the_measured_workload():
+    from gated_deltanet_chunkwise_amd.inputs import WORKLOADS
+    # the forward pass at the pages' shape carries the headline metric string
+    assert bench.metric_label("gdn_fwd", WORKLOADS["pages_bf16"]) == bench.METRIC
+    labels = {(op, wl): bench.metric_label(op, WORKLOADS[wl])
+              for op in ("gdn_fwd", "gdn_bwd") for wl in WORKLOADS}
+    assert len(set(labels.values())) == len(labels)
+    assert labels[("gdn_bwd", "pages_bf16")].startswith("GDN chunk-bwd tokens/s (B=2,T=2048,H=8,")
+    assert "B=4,T=8192,H=16,K=V=128,h0 bf16" in labels[("gdn_fwd", "wide_bf16_h0")]
+    assert "packed T=32768 in 12 seqs,H=16" in labels[("gdn_fwd", "packed_bf16")]
+    assert "B=1,T=65536,H=16,HV=32,K=V=128 bf16" in labels[("gdn_fwd", "long_gqa_bf16")]
+    assert "K=V=64 fp32" in labels[("gdn_fwd", "tiny_fp32")]
+
+
+@pytest.mark.parametrize("dtype,peak", [("bf16", 2.5e15), ("fp32", 157.3e12)])
+def test_every_kernel_is_rated_against_its_own_dtype_peak(dtype, peak):
+    """bf16 calls run every forward and backward product on the bf16 MFMA, so
+    each stage's MFMA fraction is taken against the bf16 peak (and fp32 calls
+    against the fp32 one)."""
+    shape = dict(B=2, T=2048, H=8, HV=8, K=128, V=128, N=2)
+    esz = 2 if dtype == "bf16" else 4
+    kern, _, _ = bench.algorithmic_bwd(shape, esz, False, True, 64)
+    for name in ("recompute", "prep", "bwd_chain", "dqk", "bwd_wy"):
+        f = bench.kernel_figures(kern[name], 0.02, dtype)
+        assert f["mfma_dtype"] == dtype
+        assert f["mfma_frac"] == round(kern[name]["flops"] / 2e-5 / peak, 4), name
+        assert f["hbm_frac"] == round(kern[name]["bytes"] / 2e-5 / 8.0e12, 4), name
+    fwd, _, _ = bench.algorithmic(shape, esz, False, 64)
+    for name in ("wy", "chain", "output"):
+        assert bench.kernel_figures(fwd[name], 0.01, dtype)["mfma_frac"] == round(
+            fwd[name]["flops"] / 1e-5 / peak, 4)

@@ -27,10 +27,14 @@ LC = LANE % 16
 KSLOT = np.array([[4 * g + i if i < 4 else 12 + 4 * g + i for i in range(8)] for g in range(4)])
 
 
-def read(ws, off, count, dtype):
-    nbytes = count * (2 if dtype == torch.bfloat16 else 4)
-    raw = ws[off:off + nbytes]
-    return raw.view(dtype).float().cpu().numpy().astype(np.float64)
+def read(ws, off, HV, slots, used, per_slot, dtype):
+    """The first `used` chunk slots of each head of a [HV][slots][per_slot]
+    workspace array, as fp64 [HV][used][per_slot].  Slots past `used` (the
+    packed layout's slot count is an upper bound) were never written and are
+    not read."""
+    esz = 2 if dtype == torch.bfloat16 else 4
+    raw = ws[off:off + HV * slots * per_slot * esz].view(HV, slots, per_slot * esz)
+    return raw[:, :used].contiguous().view(dtype).float().cpu().numpy().astype(np.float64)
 
 
 def decode_w(buf, HV, slots, K):
@@ -122,12 +126,18 @@ def test_intermediates(dtype, tol, packed):
                           A_log_range=(-4.0, 0.0))
     say("case intermediates", dtype, "packed" if packed else "fixed", inp.shape)
     plans = []
-    run_gpu(inp, plans)
+    # NaN bytes first: a used slot the kernels failed to write does not pass
+    run_gpu(inp, plans, ws_fill=0xFF)
     plan = plans[0]
     lay = plan.layout
     s = inp.shape
-    HV, slots = s["HV"], lay.num_slots
+    HV = s["HV"]
+    lens = ([s["T"]] * s["B"] if inp.cu_seqlens is None
+            else (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1]).tolist())
+    used = sum((n + 63) // 64 for n in lens)
     ws = plan.workspace
+    rd = lambda off, per, dt: read(ws, off, HV, lay.num_slots, used, per, dt)  # noqa: E731
+    slots = used
     et = inp.q.dtype
     fused = gdn.fuses_output(plan.params, plan.packed)
     say("  output fused into the state pass:", fused)
@@ -135,18 +145,18 @@ def test_intermediates(dtype, tol, packed):
     if fused:
         # the full call left the masked, decayed Q K^T of every chunk (from WY)
         # and no chunk states; the state pass alone writes those
-        pm = decode_pm(read(ws, lay.pm, HV * slots * 64 * 64, et), HV, slots)
+        pm = decode_pm(rd(lay.pm, 64 * 64, et), HV, slots)
         d = inp.to("cuda")
         plan.bind(d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0,
                   stage_mask=gdn.STAGE_BITS["chain"])()
         torch.cuda.synchronize()
-    gam = read(ws, lay.gamma, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
-    bet = read(ws, lay.beta, HV * slots * 64, torch.float32).reshape(HV, slots, 64)
-    w = decode_w(read(ws, lay.w, HV * slots * 64 * K, et), HV, slots, K)
-    kd = decode_kt(read(ws, lay.kt, HV * slots * 64 * K, et), HV, slots, K)
-    u = decode_u(read(ws, lay.u, HV * slots * 64 * V, et), HV, slots, V)
-    hc = decode_hc(read(ws, lay.hc, HV * slots * K * V, et), HV, slots, K, V)
-    vn = decode_vn(read(ws, lay.vn, HV * slots * 64 * V, et), HV, slots, V)
+    gam = rd(lay.gamma, 64, torch.float32).reshape(HV, slots, 64)
+    bet = rd(lay.beta, 64, torch.float32).reshape(HV, slots, 64)
+    w = decode_w(rd(lay.w, 64 * K, et), HV, slots, K)
+    kd = decode_kt(rd(lay.kt, 64 * K, et), HV, slots, K)
+    u = decode_u(rd(lay.u, 64 * V, et), HV, slots, V)
+    hc = decode_hc(rd(lay.hc, K * V, et), HV, slots, K, V)
+    vn = decode_vn(rd(lay.vn, 64 * V, et), HV, slots, V)
 
     q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)
     g = oracle.gate(f64(inp.g_raw), f64(inp.A_log), f64(inp.dt_bias))

@@ -57,3 +57,26 @@ def test_bwd_threads_and_units_do_not_change_results():
         assert np.array_equal(ru[name][1], r1[name][1]), name
         assert not ru[name][0].any(), name
     assert np.array_equal(ru["dh0"][1], r1["dh0"][1]) and not ru["dh0"][0].any()
+
+
+def test_ref_fwd_twin_matches_fwd():
+    """gdn_ref_fwd (gdn_fwd's argument order) gives fwd's results bit for bit,
+    fixed-length and packed, with and without a bias and an initial state."""
+    rng = np.random.default_rng(6)
+    q, k, v, _, beta = oracle_pins._rand(rng, 2, 40, 2, 4, 8, 6)
+    g_raw = rng.normal(size=(2, 40, 4))
+    A_log = rng.uniform(0, 2, 4)
+    dt_bias = rng.normal(0, 0.1, 4)
+    h0 = rng.normal(size=(2, 4, 8, 6))
+    for b, h in ((dt_bias, h0), (None, None)):
+        o1, f1 = oracle.fwd(q, k, v, g_raw, beta, A_log, b, h0=h, scale=0.5)
+        o2, f2 = oracle.ref_fwd(q, k, v, g_raw, beta, A_log, b, initial_state=h, scale=0.5)
+        assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    cu = np.array([0, 30, 30, 80])
+    one = lambda t: t.reshape(1, 80, *t.shape[2:])  # noqa: E731
+    h3 = rng.normal(size=(3, 4, 8, 6))
+    o1, f1 = oracle.fwd(one(q), one(k), one(v), one(g_raw), one(beta), A_log, dt_bias,
+                        cu_seqlens=cu, h0=h3)
+    o2, f2 = oracle.ref_fwd(one(q), one(k), one(v), one(g_raw), one(beta), A_log, dt_bias,
+                            cu_seqlens=cu, initial_state=h3)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
