@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     GDN_BF16,
     GDN_F16,
     GDN_F32,
+    GDN_SCRATCH_BYTES,
     GdnBackward,
     GdnError,
     GdnForward,
@@ -27,6 +28,7 @@ from ._binding import (  # noqa: F401
     decode_launcher,
     fuses_output,
     fwd,
+    fwd_noalloc,
     kda_gate,
     kda_gate_launcher,
     lib_path,
@@ -39,7 +41,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "BWD_NUM_STAGES", "BWD_STAGES", "GdnBackward", "bwd",
-    "GDN_BF16", "GDN_F16", "GDN_F32", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
-    "check", "decode", "decode_launcher", "fuses_output", "fwd", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
+    "GDN_BF16", "GDN_F16", "GDN_F32", "GDN_SCRATCH_BYTES", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
+    "check", "decode", "decode_launcher", "fuses_output", "fwd", "fwd_noalloc", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
     "workspace_layout", "workspace_size",
 ]

@@ -17,7 +17,8 @@ GDN_F16 = 2  # KDA gate only
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
            "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_decode", "gdn_kda_gate",
            "gdn_bwd_workspace_size", "gdn_bwd", "gdn_bwd_timed", "gdn_status_string",
-           "gdn_fwd_fuses_output")
+           "gdn_fwd_fuses_output", "gdn_fwd_noalloc")
+GDN_SCRATCH_BYTES = 64 << 20  # include/gdn.h: the static workspace of gdn_fwd_noalloc
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
 # gdn_fwd_stages bits, one per entry of STAGES
@@ -95,6 +96,8 @@ def _declare(lib):
     lib.gdn_bwd_timed.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp, ctypes.c_void_p]
     lib.gdn_fwd_fuses_output.restype = ctypes.c_int
     lib.gdn_fwd_fuses_output.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
+    lib.gdn_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_fwd_noalloc.argtypes = [P] + [vp] * 11 + [fp]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -389,6 +392,43 @@ def kda_gate_launcher(g, A_log, dt_bias=None, output_dtype=None, out=None, strea
         if st:
             raise GdnError(st, "gdn_kda_gate")
     return launch, out
+
+
+class _Dims:
+    """The sizes _check_forward_inputs reads from a plan."""
+
+    def __init__(self, B, T, H, HV, K, V, dtype, N, packed):
+        self.dims, self.dtype, self.N, self.packed = (B, T, H, HV, K, V), dtype, N, packed
+
+
+def fwd_noalloc(q, k, v, g_raw, beta, A_log, o, dt_bias=None, cu_seqlens=None,
+                initial_state=None, final_state=None, scale=1.0, stream=None):
+    """gdn_fwd_noalloc: the forward pass into caller-owned o [B,T,HV,V] (q's
+    dtype) and final_state [N,HV,K,V] fp32 (or None), with the library's static
+    device scratch as workspace: nothing is allocated.  Raises GdnError with
+    GDN_ERR_SCRATCH when the problem needs more than GDN_SCRATCH_BYTES.  Calls
+    that overlap on one GPU race on its scratch (see include/gdn.h)."""
+    torch = _torch()
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    packed = cu_seqlens is not None
+    N = cu_seqlens.numel() - 1 if packed else B
+    dims = _Dims(B, T, H, HV, K, V, q.dtype, N, packed)
+    named = _check_forward_inputs(dims, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                                  initial_state)
+    _check_tensor("o", o, (B, T, HV, V), q.dtype)
+    _check_tensor("final_state", final_state, (N, HV, K, V), torch.float32, required=False)
+    _check_placement(named + [("o", o), ("final_state", final_state)], q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    params = make_params(B, T, H, HV, K, V, _dtype_code(q.dtype), N if packed else 0, scale)
+    st = load_library().gdn_fwd_noalloc(
+        ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta), _ptr(A_log),
+        _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state),
+        ctypes.c_void_p(stream.cuda_stream))
+    if st:
+        raise GdnError(st, "gdn_fwd_noalloc")
+    return o, final_state
 
 
 def fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None, initial_state=None,

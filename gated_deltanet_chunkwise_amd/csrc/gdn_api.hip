@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -669,6 +670,67 @@ gdn_status_t gdn_fwd(const gdn_params_t* p, const void* q, const void* k, const 
                        final_state, workspace, workspace_bytes, stream, nullptr);
 }
 
+}  // extern "C"
+
+// Workspace of gdn_fwd_noalloc: one static array per device, loaded with the
+// code object and held until the process ends.  Host code must never pass the
+// name `scratch` itself to a kernel or a copy (in host code it is only a
+// stand-in, not a device address): it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[GDN_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The device address of the current device's scratch array, looked up once
+// per device (with that device current) and cached; nullptr on failure.
+void* current_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  ptr = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  scratch_addr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_fwd_noalloc(const gdn_params_t* p, const void* q, const void* k, const void* v,
+                             const float* g_raw, const float* beta, const float* A_log,
+                             const float* dt_bias, const int64_t* cu_seqlens,
+                             const float* initial_state, void* o, float* final_state,
+                             void* stream) {
+  Plan pl;
+  if (!p) return GDN_ERR_NULL;
+  gdn_status_t st = make_plan(p, cu_seqlens != nullptr, &pl);
+  if (st != GDN_OK) return st;
+  if (pl.lay.total > (size_t)GDN_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+  // the remaining argument checks, with a stand-in for the workspace (aligned,
+  // large enough; never dereferenced) so that nothing touches the GPU before
+  // every argument has passed
+  st = check_all(p, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                 final_state, reinterpret_cast<const void*>(uintptr_t{kWsAlign}),
+                 GDN_SCRATCH_BYTES, &pl);
+  if (st != GDN_OK) return st;
+  void* ws = current_scratch();
+  if (!ws) return GDN_ERR_LAUNCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == GDN_BF16)
+    return run_e<gdn::bf16>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                            final_state, ws, s, nullptr, GDN_STAGE_ALL);
+  return run_e<float>(pl, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, o,
+                      final_state, ws, s, nullptr, GDN_STAGE_ALL);
+}
+
 gdn_status_t gdn_decode(const gdn_params_t* p, const void* q, const void* k, const void* v,
                         const float* g_raw, const float* beta, const float* A_log,
                         const float* dt_bias, float* state, void* o, void* stream) {
@@ -779,6 +841,7 @@ const char* gdn_status_string(gdn_status_t s) {
     case GDN_ERR_ALIGN: return "misaligned pointer";
     case GDN_ERR_WORKSPACE: return "workspace too small";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_SCRATCH: return "problem too large for the static scratch (GDN_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -99,7 +99,8 @@ typedef enum {
   GDN_ERR_UNSUPPORTED = 4, /* K or V not in {64, 128}, or a size beyond the int32 index range */
   GDN_ERR_ALIGN = 5,       /* a pointer is not aligned as required below */
   GDN_ERR_WORKSPACE = 6,   /* workspace smaller than gdn_fwd_workspace_size() */
-  GDN_ERR_LAUNCH = 7       /* a kernel launch failed */
+  GDN_ERR_LAUNCH = 7,      /* a kernel launch failed */
+  GDN_ERR_SCRATCH = 8      /* gdn_fwd_noalloc: workspace beyond GDN_SCRATCH_BYTES */
 } gdn_status_t;
 
 /* Element types.  gdn_fwd takes GDN_F32 or GDN_BF16; the KDA gate takes all three. */
@@ -176,6 +177,35 @@ gdn_status_t gdn_fwd(const gdn_params_t *p, const void *q, const void *k, const 
                      const float *dt_bias, const int64_t *cu_seqlens,
                      const float *initial_state, void *o, float *final_state,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- Forward pass without any allocation -------------------------------------
+ * For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gdn_fwd with
+ * the same arguments and results (the same kernels, bit for bit), but without
+ * a workspace argument.  Its intermediates live in a static device array of
+ * GDN_SCRATCH_BYTES per GPU, part of the library's code object: every GPU the
+ * library runs on holds it until the process ends.  Its device address is
+ * looked up on the first call on each device (hipGetSymbolAddress, with that
+ * device current); the call itself allocates and frees nothing.
+ *   Limit: gdn_fwd_workspace_size(p, cu_seqlens != NULL) <= GDN_SCRATCH_BYTES
+ *   (64 MiB: e.g. B=2, T=2048, H=HV=8, K=V=128 bf16 needs 52.25 MiB); a larger
+ *   problem returns GDN_ERR_SCRATCH and enqueues nothing.
+ *   Sharing: all calls on one GPU use that GPU's one array, and each call
+ *   leaves its intermediates there.  No part of it needs to start zeroed (each
+ *   call writes every intermediate before reading it).  Calls that overlap in
+ *   time on one GPU (on different streams, or from different host threads
+ *   without ordering) race on it and give undefined results; serialize them,
+ *   e.g. on one stream.
+ * Errors: those of gdn_fwd (checked before anything is enqueued), plus
+ * GDN_ERR_SCRATCH, and GDN_ERR_LAUNCH when the array's address cannot be
+ * obtained. */
+#define GDN_SCRATCH_BYTES (64u << 20)
+
+gdn_status_t gdn_fwd_noalloc(const gdn_params_t *p, const void *q, const void *k,
+                             const void *v, const float *g_raw, const float *beta,
+                             const float *A_log, const float *dt_bias,
+                             const int64_t *cu_seqlens, const float *initial_state, void *o,
+                             float *final_state, void *stream);
 
 /* Whether gdn_fwd, for these parameters on the current device, runs the output
  * stage fused into the state pass (one kernel) instead of as a kernel of its

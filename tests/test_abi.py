@@ -13,7 +13,7 @@ from gated_deltanet_chunkwise_amd import _binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EWS, ELAUNCH = range(8)
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EWS, ELAUNCH, ESCRATCH = range(9)
 
 
 def declared_functions():
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     seen = set()
-    for s in range(8):
+    for s in range(9):
         msg = gdn.status_string(s)
         assert msg and msg not in seen
         seen.add(msg)
@@ -293,3 +293,23 @@ def test_packed_call_without_sequences():
     assert gdn.check(empty, ptrs(cu_seqlens=0x90000, **null), ws) == OK
     # the same sizes without cu_seqlens are a fixed-length call (N = B = 1)
     assert gdn.check(bad, ptrs(), 1 << 40) == OK
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    """gdn_fwd_noalloc checks its arguments, and that the problem's workspace
+    fits GDN_SCRATCH_BYTES, before it looks up the scratch address or enqueues
+    anything (so these calls never touch a GPU)."""
+    lib = gdn.load_library()
+    vp = lambda **kw: [ctypes.c_void_p(a) if a else None for a in ptrs(**kw)[:11]]  # noqa: E731
+    # B=4, T=8192, H=HV=16, K=V=128 bf16: 836 MiB of workspace
+    big = P(B=4, T=8192, H=16, HV=16, K=128, V=128)
+    assert gdn.workspace_size(big) > gdn.GDN_SCRATCH_BYTES
+    assert lib.gdn_fwd_noalloc(ctypes.byref(big), *vp(), None) == ESCRATCH
+    # argument errors are reported like gdn_fwd's
+    small = P(B=2, T=2048, H=8, HV=8, K=128, V=128)
+    assert gdn.workspace_size(small) <= gdn.GDN_SCRATCH_BYTES
+    assert lib.gdn_fwd_noalloc(ctypes.byref(small), *vp(q=None), None) == ENULL
+    assert lib.gdn_fwd_noalloc(ctypes.byref(small), *vp(o=0x10004), None) == EALIGN
+    assert lib.gdn_fwd_noalloc(ctypes.byref(P(K=96)), *vp(), None) == EUNSUP
+    assert lib.gdn_fwd_noalloc(None, *vp(), None) == ENULL
+    assert "scratch" in gdn.status_string(ESCRATCH)
