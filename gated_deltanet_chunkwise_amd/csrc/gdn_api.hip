@@ -222,6 +222,19 @@ bool fuses_output(const Plan& pl) {
   }
 }
 
+// Value heads per output workgroup: 2 (sharing the key head's Q and K loads
+// and its Q K^T product) when an even number of value heads read each key
+// head and the per-(chunk, value head) workgroups would fill the device at
+// least eight times over; at fewer, the longer per-workgroup chain adds
+// latency that the shared work does not repay.  Measured on MI355X at B=1,
+// T=65536, H=16, HV=32: output 567 -> 499 us.  The same sharing in WY (K K^T
+// once per key head) needs ~210 VGPRs, which halves its occupancy: 737 ->
+// 1089 us, so WY stays one workgroup per (chunk, value head).
+int heads_per_workgroup(const Plan& pl) {
+  const int64_t wgs = (int64_t)pl.geo.slots * pl.geo.HV;
+  return (pl.geo.G % 2 == 0 && wgs >= 8 * (int64_t)device_cus()) ? 2 : 1;
+}
+
 template <typename E, int K, int V, bool VARLEN>
 gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, const float* g_raw,
                  const float* beta, const float* A_log, const float* dt_bias,
@@ -260,6 +273,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
               geo.slots, cmap, seq_slot));
   mark(1);
   const bool fused = fuses_output<E, K, V>(pl);
+  const int gs = fused ? 1 : heads_per_workgroup(pl);
   Frag<E>* pmf = reinterpret_cast<Frag<E>*>(w + L.pm);
   if (work && geo.slots > 0 && (mask & GDN_STAGE_WY)) {
     bool done = false;
@@ -318,9 +332,14 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
     }
   }
   mark(3);
-  if (work && geo.slots > 0 && (mask & GDN_STAGE_OUTPUT))
-    ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo,
-              qe, ke, cmap, gam, hcf, vnf, oe));
+  if (work && geo.slots > 0 && (mask & GDN_STAGE_OUTPUT)) {
+    if (gs == 2)
+      ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN, 2>, dim3(geo.slots * geo.HV / 2), dim3(256), s,
+                geo, qe, ke, cmap, gam, hcf, vnf, oe));
+    else
+      ok(launch(gdn::gdn_output_kernel<E, K, V, VARLEN>, dim3(geo.slots * geo.HV), dim3(256), s, geo,
+                qe, ke, cmap, gam, hcf, vnf, oe));
+  }
   mark(4);
   return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

@@ -450,7 +450,8 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   // output tiles.  Their k32 fragments of T diag(beta e^G) and T diag(beta)
   // over the chunk index (row 16w + lane%16, columns 32cb + kslot(g, i)) are
   // formed from T in registers.
-  const int ct = wave & 3, half = wave >> 2;
+  // wave-uniform (scalar) values, so the zero-block test below is a scalar branch
+  const int ct = __builtin_amdgcn_readfirstlane(wave & 3), half = __builtin_amdgcn_readfirstlane(wave >> 2);
   Frag<E> bw[2], bu[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -481,8 +482,11 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
     for (int m = 0; m < MTH; ++m) {
       const int mt = half * MTH + m;
       acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // T's column block cb is zero for the rows of tile ct < 2cb (right of
+      // the diagonal block): that product is skipped, not multiplied by zero
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mma_k32(acc[m], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
+      for (int cb = 0; cb < 2; ++cb)
+        if (2 * cb <= ct) mma_k32(acc[m], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
     }
     Frag<E>* dst = wf + (hs * 4 + ct) * (K / 32) * 64;
 #pragma unroll
@@ -498,7 +502,8 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       const int vt = half * (V / 32) + m;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CS, 32 * cb));
+      for (int cb = 0; cb < 2; ++cb)
+        if (2 * cb <= ct) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CS, 32 * cb));
       dst[((vt * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)] = make_quad<E>(acc);
     }
   }
@@ -1650,12 +1655,15 @@ __global__ __launch_bounds__(64) void gdn_segment_combine_kernel(Geo geo,
 }
 
 // ---------------------------------------------------------------------------
-// Output.  One workgroup (4 waves) per (chunk slot, value head), computing
-// o^T (V x 64) so that the state and v_new fragments written by the chain are
-// the A operands and rows of Q / P^T are the B operands:
-//   P^T = K Q^T * [j <= i] * e^{G_i - G_j}   (wave w: token tile i = w)
+// Output.  One workgroup (4 waves) per (chunk slot, GS value heads of one key
+// head), computing o^T (V x 64) so that the state and v_new fragments written
+// by the chain are the A operands and rows of Q / P^T are the B operands:
+//   S^T = K Q^T                               (wave w: token tile i = w; once)
+//   P^T = S^T * [j <= i] * e^{G_i - G_j}      (per value head: its own G)
 //   o^T = e^{G_i} (H_c^T Q^T) + v_new^T P^T, times scale  (wave w: value tiles w, w+4)
-template <typename E, int K, int V, bool VARLEN>
+// With GS > 1 the Q and K rows are read and S formed once for the value heads
+// hv0 .. hv0+GS-1 that share the key head (GS divides G).
+template <typename E, int K, int V, bool VARLEN, int GS = 1>
 __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __restrict__ qg,
                                                          const E* __restrict__ kg,
                                                          const int4* __restrict__ cmap,
@@ -1664,35 +1672,44 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
                                                          const Frag<E>* __restrict__ vnf,
                                                          E* __restrict__ og) {
   constexpr int P = 16 / sizeof(E), KS = K + P, NV = V / 16, KB = K / 32;
+  static_assert(GS >= 1 && GS <= 4, "value heads per workgroup");
   __shared__ __align__(16) E Qs[kChunk * KS];
   __shared__ __align__(16) E Ks[kChunk * KS];
-  __shared__ __align__(16) Frag<E> Pb[4][2][64];
-  __shared__ float sg[kChunk];
+  __shared__ __align__(16) Frag<E> Pb[GS][4][2][64];
+  __shared__ float sg[GS][kChunk];
 
-  int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  int hg, slot;
+  head_major_block(blockIdx.x, geo.HV / GS, geo.slots, hg, slot);
+  const int hv0 = hg * GS;
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
-  const int h = hv / geo.G;
+  const int h = hv0 / geo.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
-  const size_t hs = (size_t)hv * geo.slots + slot;
 
   // All global loads first: this wave's H_c and v_new fragments (value tiles
-  // wave, wave+4, ...), the gate row, and the Q and K rows of the chunk.
+  // wave, wave+4, ..., of every value head), the gate rows, and the Q and K
+  // rows of the chunk.
   constexpr int NVW = (NV + 3) / 4;  // value tiles per wave
-  Frag<E> hc[NVW][KB], vn[NVW][2];
+  Frag<E> hc[GS][NVW][KB], vn[GS][NVW][2];
 #pragma unroll
-  for (int a = 0; a < NVW; ++a) {
-    const int vt = wave + 4 * a;
-    if (vt < NV) {
+  for (int gi = 0; gi < GS; ++gi) {
+    const size_t hs = (size_t)(hv0 + gi) * geo.slots + slot;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) hc[a][kb] = hcf[((hs * NV + vt) * KB + kb) * 64 + lane];
+    for (int a = 0; a < NVW; ++a) {
+      const int vt = wave + 4 * a;
+      if (vt < NV) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) vn[a][jb] = vnf[((hs * NV + vt) * 2 + jb) * 64 + lane];
+        for (int kb = 0; kb < KB; ++kb) hc[gi][a][kb] = hcf[((hs * NV + vt) * KB + kb) * 64 + lane];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) vn[gi][a][jb] = vnf[((hs * NV + vt) * 2 + jb) * 64 + lane];
+      }
     }
   }
-  if (tid < kChunk) sg[tid] = gam[hs * kChunk + tid];
+  if (tid < kChunk * GS) {
+    const int gi = tid / kChunk, c = tid - gi * kChunk;
+    sg[gi][c] = gam[((size_t)(hv0 + gi) * geo.slots + slot) * kChunk + c];
+  }
   constexpr int NIT = kChunk * (K / 8) / 256;  // 8-element pieces per thread
   float eq[NIT][8], ek[NIT][8];
 #pragma unroll
@@ -1716,45 +1733,57 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
 
   {
     const int it = wave;
-    f32x4 pt[4];
+    f32x4 st[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-      pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (jt <= it) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          mma_k32(pt[jt], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
+          mma_k32(st[jt], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
                   frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
-        const int i = 16 * it + lc;
+      }
+    }
+    const int i = 16 * it + lc;
+#pragma unroll
+    for (int gi = 0; gi < GS; ++gi) {
+      f32x4 pt[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * g + r;
-          pt[jt][r] = j <= i ? pt[jt][r] * fast_exp2(sg[i] - sg[j]) : 0.f;
+          pt[jt][r] = (jt <= it && j <= i) ? st[jt][r] * fast_exp2(sg[gi][i] - sg[gi][j]) : 0.f;
         }
       }
-    }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) Pb[it][jb][lane] = frag_from_tiles<E>(pt[2 * jb], pt[2 * jb + 1]);
+      for (int jb = 0; jb < 2; ++jb) Pb[gi][it][jb][lane] = frag_from_tiles<E>(pt[2 * jb], pt[2 * jb + 1]);
+    }
   }
   __syncthreads();
 
 #pragma unroll
-  for (int a = 0; a < NVW; ++a) {
-    const int vt = wave + 4 * a;
-    if (vt >= NV) break;
+  for (int gi = 0; gi < GS; ++gi) {
+    const int hv = hv0 + gi;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < NVW; ++a) {
+      const int vt = wave + 4 * a;
+      if (vt >= NV) break;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[a][kb], frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
-      acc *= fast_exp2(sg[16 * it + lc]);
+      for (int it = 0; it < 4; ++it) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jb = 0; jb <= (it >> 1); ++jb) mma_k32(acc, vn[a][jb], Pb[it][jb][lane]);
-      acc *= geo.scale;
-      const int i = 16 * it + lc;
-      if (i < len) {
-        E* dst = og + ((t0 + i) * geo.HV + hv) * V + 16 * vt + 4 * g;
-        st4(dst, acc[0], acc[1], acc[2], acc[3]);
+        for (int kb = 0; kb < KB; ++kb)
+          mma_k32(acc, hc[gi][a][kb], frag_from_row(Qs + (16 * it + lc) * KS + 32 * kb));
+        acc *= fast_exp2(sg[gi][16 * it + lc]);
+#pragma unroll
+        for (int jb = 0; jb <= (it >> 1); ++jb) mma_k32(acc, vn[gi][a][jb], Pb[gi][it][jb][lane]);
+        acc *= geo.scale;
+        const int i = 16 * it + lc;
+        if (i < len) {
+          E* dst = og + ((t0 + i) * geo.HV + hv) * V + 16 * vt + 4 * g;
+          st4(dst, acc[0], acc[1], acc[2], acc[3]);
+        }
       }
     }
   }

@@ -38,6 +38,9 @@ WORKLOADS = {
     # one long sequence with few heads: 32 (sequence, head, 16-column) units, so
     # the plain state pass leaves most CUs idle (the segment-parallel case)
     "long_single_bf16": dict(B=1, T=65536, H=4, HV=4, K=128, V=128, dtype="bf16"),
+    # the same sequence with 16 and 64 units (segment-parallel cost model)
+    "long_h2_bf16": dict(B=1, T=65536, H=2, HV=2, K=128, V=128, dtype="bf16"),
+    "long_h8_bf16": dict(B=1, T=65536, H=8, HV=8, K=128, V=128, dtype="bf16"),
 }
 # Seeds per workload (20260 + index in the order above).
 SEEDS = {name: 20260 + i for i, name in enumerate(WORKLOADS)}
