@@ -78,7 +78,8 @@ def parse():
                     help="forward: also time this many steps each after touching 1 GiB on the "
                          "stream (inputs and intermediates out of the 256 MB last-level cache)")
     ap.add_argument("--seg-chunks", type=int, default=0,
-                    help="segment-parallel state pass with segments of this many chunks (0: off)")
+                    help="segment-parallel state pass with segments of this many chunks (0: off, "
+                         "-1: the library's automatic choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -835,7 +836,8 @@ def main():
         "config": {"workload": wl, "B": s["B"], "T": s["T"], "H": s["H"], "HV": s["HV"],
                    "K": s["K"], "V": s["V"], "chunk": CHUNK, "packed_seqs": s["N"] if packed
                    else None, "initial_state": inp.h0 is not None,
-                   "seg_chunks": args.seg_chunks},
+                   "seg_chunks": args.seg_chunks,
+                   "seg_chunks_used": gdn.seg_chunks(plan.params, packed)},
         "output_fused": fused,
         "roofline": roof,
         "path_roofline": {"bytes": path["bytes"], "flops": path["flops"],

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     GDN_F16,
     GDN_F32,
     GDN_SCRATCH_BYTES,
+    GDN_SEG_AUTO,
     GdnBackward,
     GdnError,
     GdnForward,
@@ -34,6 +35,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     load_library,
     make_params,
+    seg_chunks,
     status_string,
     workspace_layout,
     workspace_size,
@@ -41,7 +43,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "BWD_NUM_STAGES", "BWD_STAGES", "GdnBackward", "bwd",
-    "GDN_BF16", "GDN_F16", "GDN_F32", "GDN_SCRATCH_BYTES", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
-    "check", "decode", "decode_launcher", "fuses_output", "fwd", "fwd_noalloc", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "status_string",
+    "GDN_BF16", "GDN_F16", "GDN_F32", "GDN_SCRATCH_BYTES", "GDN_SEG_AUTO", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
+    "check", "decode", "decode_launcher", "fuses_output", "fwd", "fwd_noalloc", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "seg_chunks", "status_string",
     "workspace_layout", "workspace_size",
 ]

@@ -17,7 +17,8 @@ GDN_F16 = 2  # KDA gate only
 SYMBOLS = ("gdn_fwd_workspace_size", "gdn_fwd_workspace_layout", "gdn_fwd_check",
            "gdn_fwd", "gdn_fwd_timed", "gdn_fwd_stages", "gdn_decode", "gdn_kda_gate",
            "gdn_bwd_workspace_size", "gdn_bwd", "gdn_bwd_timed", "gdn_status_string",
-           "gdn_fwd_fuses_output", "gdn_fwd_noalloc")
+           "gdn_fwd_fuses_output", "gdn_fwd_noalloc", "gdn_fwd_seg_chunks")
+GDN_SEG_AUTO = -1  # include/gdn.h: seg_chunks chosen per call
 GDN_SCRATCH_BYTES = 64 << 20  # include/gdn.h: the static workspace of gdn_fwd_noalloc
 NUM_STAGES = 4
 STAGES = ("chunk_map", "wy", "chain", "output")
@@ -96,6 +97,8 @@ def _declare(lib):
     lib.gdn_bwd_timed.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, fp, ctypes.c_void_p]
     lib.gdn_fwd_fuses_output.restype = ctypes.c_int
     lib.gdn_fwd_fuses_output.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
+    lib.gdn_fwd_seg_chunks.restype = ctypes.c_int
+    lib.gdn_fwd_seg_chunks.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
     lib.gdn_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_fwd_noalloc.argtypes = [P] + [vp] * 11 + [fp]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -134,6 +137,17 @@ def fuses_output(params, packed=False):
     if st:
         raise GdnError(st, "gdn_fwd_fuses_output")
     return bool(f.value)
+
+
+def seg_chunks(params, packed=False):
+    """gdn_fwd_seg_chunks: the segment length gdn_fwd uses for these parameters
+    on the current device (0 = the plain state pass)."""
+    L = ctypes.c_int32(0)
+    st = load_library().gdn_fwd_seg_chunks(ctypes.byref(params), int(bool(packed)),
+                                           ctypes.byref(L))
+    if st:
+        raise GdnError(st, "gdn_fwd_seg_chunks")
+    return int(L.value)
 
 
 def check(params, ptrs, workspace_bytes):

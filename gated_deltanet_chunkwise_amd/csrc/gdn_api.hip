@@ -27,8 +27,33 @@ struct Plan {
   gdn_workspace_layout_t lay;
   bool varlen;
   int64_t ntok;    // tokens in q/k/v/o
-  int seg_chunks;  // chunks per segment of the segment-parallel state pass (0: off)
+  int seg_chunks;  // chunks per segment of the segment-parallel state pass (0: off,
+                   // GDN_SEG_AUTO: chosen at launch, see auto_seg_chunks)
 };
+
+// Smallest segment the automatic choice takes; the workspace of a
+// GDN_SEG_AUTO call is sized for it, so it holds whatever the choice is.
+constexpr int kAutoSegMin = 16;
+
+// The automatic segment length for B fixed-length sequences of NT chunks and
+// `units` (sequence, value head, 16-column) state-pass units on a device with
+// `cus` compute units; 0 = the plain pass.  Cost model, measured on MI355X
+// (256 CUs, bf16, K = V = 128, T = 65536): the segmented pass costs about
+// three passes of L chunk steps at units * NS units (NS = NT / L segments) plus
+// NS combine steps, the plain pass NT steps at `units` units; a step is
+// cheapest at up to two units per CU.  The best L measured puts units * NS at
+// two per CU: 16 units L = 32 (state pass 530 -> 225 us), 32 units L = 64
+// (722 -> 326 us), 64 units L = 128 (772 -> 387 us).  With fewer than 8
+// segments the three passes cost more than the one they replace (256 units,
+// NS = 2: 1062 -> 1730 us at the best L), and below 16 chunks a segment is
+// too short to amortise its start.
+int auto_seg_chunks(int64_t units, int NT, int cus) {
+  if (units <= 0 || cus <= 0) return 0;
+  const int64_t ns = 2 * (int64_t)cus / units;
+  if (ns < 8) return 0;
+  const int64_t L = std::max<int64_t>((NT + ns - 1) / ns, kAutoSegMin);
+  return NT / L >= 8 ? (int)L : 0;
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -70,7 +95,7 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   // tokens but no sequence: cu_seqlens = {0} cannot end at T > 0, and every
   // per-chunk launch would read a chunk map that nothing wrote
   if (varlen && p->num_seqs == 0 && p->T > 0) return GDN_ERR_SHAPE;
-  if (p->seg_chunks < 0) return GDN_ERR_SHAPE;
+  if (p->seg_chunks < 0 && p->seg_chunks != GDN_SEG_AUTO) return GDN_ERR_SHAPE;
   const int64_t N = varlen ? p->num_seqs : p->B;
   const int64_t NT = ((int64_t)p->T + gdn::kChunk - 1) / gdn::kChunk;
   const int64_t slots = varlen ? (int64_t)p->T / gdn::kChunk + N : (int64_t)p->B * NT;
@@ -83,7 +108,9 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   Plan pl{};
   pl.varlen = varlen;
   pl.ntok = ntok;
-  pl.seg_chunks = p->seg_chunks;
+  // packed input: the sequence lengths are on the device, so the automatic
+  // choice is the plain pass
+  pl.seg_chunks = (p->seg_chunks == GDN_SEG_AUTO && varlen) ? 0 : p->seg_chunks;
   gdn::Geo& g = pl.geo;
   g.B = p->B; g.T = p->T; g.H = p->H; g.HV = p->HV; g.K = p->K; g.V = p->V;
   g.N = (int)N; g.G = p->HV / p->H; g.NT = (int)NT; g.slots = (int)slots; g.scale = p->scale;
@@ -104,8 +131,9 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   L.seq_slot = off;  off = align_up(off + (varlen ? (size_t)(N + 1) * 4 : 0));
   // segments: at most ceil(c_n / L) per sequence, summing to <= slots / L + N
   int64_t nseg = 0;
-  if (p->seg_chunks > 0) {
-    nseg = varlen ? slots / p->seg_chunks + N : N * ((NT + p->seg_chunks - 1) / p->seg_chunks);
+  if (pl.seg_chunks != 0) {
+    const int Lmin = pl.seg_chunks > 0 ? pl.seg_chunks : kAutoSegMin;  // GDN_SEG_AUTO: the bound
+    nseg = varlen ? slots / Lmin + N : N * ((NT + Lmin - 1) / Lmin);
     if (nseg * p->HV * (p->V / 16) > INT32_MAX || nseg + 1 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     const size_t per = (size_t)nseg * p->HV * p->K;
     L.seg_slot = off; off = align_up(off + (size_t)(nseg + 1) * 4);
@@ -202,6 +230,20 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
                 ktf, uf, gam, seq_slot, h0, fin, hcf, vnf);
 }
 
+// The segment length a call uses on the current device (0: the plain state
+// pass) and its segment count: seg_chunks as given, or the automatic choice.
+struct SegRun {
+  int L, nseg;
+};
+SegRun seg_run(const Plan& pl) {
+  if (pl.seg_chunks > 0) return {pl.seg_chunks, pl.lay.num_segs};
+  if (pl.seg_chunks != GDN_SEG_AUTO) return {0, 0};
+  const gdn::Geo& g = pl.geo;
+  const int L = auto_seg_chunks((int64_t)g.N * g.HV * (g.V / 16), g.NT, device_cus());
+  if (L == 0) return {0, 0};
+  return {L, g.N * ((g.NT + L - 1) / L)};  // at most the workspace's bound (L >= kAutoSegMin)
+}
+
 // Whether the output stage runs fused into the state pass (see
 // gdn_fwd_fuses_output): bf16, no segments, and the units of the state pass
 // filling the compute units once over but not twice, so that the ring form
@@ -218,7 +260,7 @@ bool fuses_output(const Plan& pl) {
   } else {
     const int64_t units = (int64_t)pl.geo.N * pl.geo.HV * (V / 16);
     const int64_t cus = device_cus();
-    return pl.lay.num_segs == 0 && pl.seg_chunks == 0 && units > cus && units <= 2 * cus;
+    return seg_run(pl).L == 0 && units > cus && units <= 2 * cus;
   }
 }
 
@@ -306,7 +348,8 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
     return err == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
   }
   if (work && (mask & GDN_STAGE_STATE)) {
-    if (L.num_segs > 0) {
+    const SegRun seg = seg_run(pl);
+    if (seg.L > 0) {
       // segment-parallel: E_s and M_s per segment, start states in order, then
       // the full pass per segment from its start state
       int* seg_slot = reinterpret_cast<int*>(w + L.seg_slot);
@@ -315,15 +358,15 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
       float* seg_m = reinterpret_cast<float*>(w + L.seg_m);
       float* seg_h = reinterpret_cast<float*>(w + L.seg_h);
       ok(launch(gdn::gdn_segment_map_kernel<VARLEN>, dim3(1), dim3(256), s, seq_slot, geo.N,
-                geo.NT, pl.seg_chunks, L.num_segs, seg_slot, seq_seg));
+                geo.NT, seg.L, seg.nseg, seg_slot, seq_seg));
       gdn::Geo gs = geo;
-      gs.N = L.num_segs;
+      gs.N = seg.nseg;
       ok(launch_chain<E, K, V, true, gdn::CHAIN_END>(gs, s, wf, ktf, uf, gam, seg_slot, nullptr,
                                                      seg_e, hcf, vnf));
       ok(launch_chain<E, K, K, true, gdn::CHAIN_MAP>(gs, s, wf, ktf, uf, gam, seg_slot, nullptr,
                                                      seg_m, hcf, vnf));
       ok(launch(gdn::gdn_segment_combine_kernel<E, K, V>, dim3(geo.N * geo.HV * (V / 16)),
-                dim3(64), s, geo, seq_seg, seg_m, seg_e, h0, fin, seg_h));
+                dim3(64 * (K / 32)), s, geo, seq_seg, seg_m, seg_e, h0, fin, seg_h));
       ok(launch_chain<E, K, V, true, gdn::CHAIN_FULL>(gs, s, wf, ktf, uf, gam, seg_slot, seg_h,
                                                       nullptr, hcf, vnf));
     } else {
@@ -627,6 +670,15 @@ gdn_status_t gdn_fwd_fuses_output(const gdn_params_t* p, int packed, int32_t* fu
   else if (p->K == 64 && p->V == 128) f = bf ? fuses_output<gdn::bf16, 64, 128>(pl) : fuses_output<float, 64, 128>(pl);
   else f = bf ? fuses_output<gdn::bf16, 64, 64>(pl) : fuses_output<float, 64, 64>(pl);
   *fused = f ? 1 : 0;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_fwd_seg_chunks(const gdn_params_t* p, int packed, int32_t* seg_chunks) {
+  if (!p || !seg_chunks) return GDN_ERR_NULL;
+  Plan pl;
+  gdn_status_t st = make_plan(p, packed != 0, &pl);
+  if (st != GDN_OK) return st;
+  *seg_chunks = seg_run(pl).L;
   return GDN_OK;
 }
 

@@ -1589,68 +1589,148 @@ __global__ __launch_bounds__(256) void gdn_segment_map_kernel(const int* __restr
   for (int j = used + tid; j <= nseg_max; j += 256) seg_slot[j] = end;
 }
 
-// Level 2 of the segment-parallel state pass.  One wave per (sequence, value
-// head, 16 value columns) walks its sequence's segments in order:
+// Level 2 of the segment-parallel state pass.  One workgroup of K/32 waves per
+// (sequence, value head, 16 value columns) walks its sequence's segments in
+// order:
 //     seg_h[s] = H;   H <- M_s H + E_s,
-// starting from h0 (or zero); the last H is the final state.  M_s H runs on
-// the MFMA with operands in E: M_s's rows as A fragments (converted from
-// fp32), H's columns as B fragments, accumulating onto E_s's tile in fp32.
+// starting from h0 (or zero); the last H is the final state.  Wave q holds
+// rows 32q .. 32q+31 of H (two fp32 D tiles) and forms those rows of M_s H on
+// the MFMA: its rows of M_s as A fragments (converted from fp32), all of H as
+// B fragments in the call's dtype, accumulating onto E_s's tiles in fp32.  H's
+// k blocks pass between the waves through LDS (two buffers by segment parity,
+// one barrier per segment).  Each wave loads its rows of M_s and E_s D
+// segments ahead into registers, so a step costs the products and the
+// exchange, not a memory round trip.
 template <typename E>
-__device__ __forceinline__ Frag<E> frag_from_f32_row(const float* row);
+__device__ __forceinline__ Frag<E> frag_from_f32_pieces(const f32x4& a, const f32x4& b);
 template <>
-__device__ __forceinline__ Frag<bf16> frag_from_f32_row<bf16>(const float* row) {
-  const int g = lane_id() >> 4;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * g);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * g);
+__device__ __forceinline__ Frag<bf16> frag_from_f32_pieces<bf16>(const f32x4& a, const f32x4& b) {
   return frag_from_tiles<bf16>(a, b);
 }
 template <>
-__device__ __forceinline__ Frag<float> frag_from_f32_row<float>(const float* row) {
-  return frag_from_row(row);
+__device__ __forceinline__ Frag<float> frag_from_f32_pieces<float>(const f32x4& a, const f32x4& b) {
+  return {a, b};
 }
 
-template <typename E, int K, int V>
-__global__ __launch_bounds__(64) void gdn_segment_combine_kernel(Geo geo,
-                                                                 const int* __restrict__ seq_seg,
-                                                                 const float* __restrict__ seg_m,
-                                                                 const float* __restrict__ seg_e,
-                                                                 const float* __restrict__ h0,
-                                                                 float* __restrict__ fin,
-                                                                 float* __restrict__ seg_h) {
-  constexpr int NV = V / 16, KB = K / 32, KT = K / 16;
-  const int b = blockIdx.x;
-  const int vt = b % NV, hv = (b / NV) % geo.HV, n = b / (NV * geo.HV);
-  const int lane = lane_id(), g = lane >> 4, lc = lane & 15, v = 16 * vt + lc;
-  f32x4 Hs[KT];
-  load_state<K, V>(Hs, h0, ((size_t)n * geo.HV + hv) * K * V, v, g);
-  const int j0 = seq_seg[n], j1 = seq_seg[n + 1];
-  for (int j = j0; j < j1; ++j) {
-    const size_t sb = ((size_t)j * geo.HV + hv) * K * V;
-    const float* M = seg_m + ((size_t)j * geo.HV + hv) * K * K;
-    Frag<E> hb[KB];
+template <int K>
+struct CombineStep {
+  static constexpr int KB = K / 32;
+  f32x4 m[2][KB][2];  // rows of M_s: row tile 2q + t, k block kb, the two 4-column pieces
+  f32x4 e[2];         // E_s tiles (rows 32q + 16t + 4g + r, column v)
+
+  __device__ __forceinline__ void load(const float* __restrict__ M, const float* __restrict__ Es,
+                                       int q, int lane, int v, int V) {
+    const int g = lane >> 4, lc = lane & 15;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hb[kb] = frag_from_tiles<E>(Hs[2 * kb], Hs[2 * kb + 1]);
+    for (int t = 0; t < 2; ++t) {
+      const float* row = M + (size_t)(32 * q + 16 * t + lc) * K;
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt) {
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t at = sb + (size_t)(16 * mt + 4 * g + r) * V + v;
-        seg_h[at] = Hs[mt][r];
-        acc[r] = seg_e[at];
+      for (int kb = 0; kb < KB; ++kb) {
+        m[t][kb][0] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 4 * g);
+        m[t][kb][1] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16 + 4 * g);
       }
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        mma_k32(acc, frag_from_f32_row<E>(M + (size_t)(16 * mt + lc) * K + 32 * kb), hb[kb]);
-      Hs[mt] = acc;
+      for (int r = 0; r < 4; ++r) e[t][r] = Es[(size_t)(32 * q + 16 * t + 4 * g + r) * V + v];
     }
   }
+};
+
+template <typename E, int K, int V, int D, int Q>
+__device__ __forceinline__ void combine_wave(Frag<E> (&xb)[2][K / 32][64], const Geo& geo, int n,
+                                             int hv, int vt, const int* __restrict__ seq_seg,
+                                             const float* __restrict__ seg_m,
+                                             const float* __restrict__ seg_e,
+                                             const float* __restrict__ h0, float* __restrict__ fin,
+                                             float* __restrict__ seg_h) {
+  constexpr int KB = K / 32;
+  const int lane = lane_id(), g = lane >> 4, v = 16 * vt + (lane & 15);
+  f32x4 Hs[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Hs[t][r] = h0 ? h0[((size_t)n * geo.HV + hv) * K * V + (size_t)(32 * Q + 16 * t + 4 * g + r) * V + v]
+                    : 0.f;
+  const int j0 = seq_seg[n], j1 = seq_seg[n + 1];
+  auto mat = [&](int j) { return seg_m + ((size_t)j * geo.HV + hv) * K * K; };
+  auto est = [&](int j) { return seg_e + ((size_t)j * geo.HV + hv) * K * V; };
+  auto step = [&](const CombineStep<K>& S, int j, int par) {
+    // this segment's start state: stored, and its k block shared
+    float* hst = seg_h + ((size_t)j * geo.HV + hv) * K * V;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hst[(size_t)(32 * Q + 16 * t + 4 * g + r) * V + v] = Hs[t][r];
+    const Frag<E> own = frag_from_tiles<E>(Hs[0], Hs[1]);
+    xb[par][Q][lane] = own;
+    wait_lgkm0();
+    ring_barrier();
+    Frag<E> hb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[kb] = kb == Q ? own : xb[par][kb][lane];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = S.e[t];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int kb = (Q + i) % KB;  // the wave's own block first: no LDS wait
+        mma_k32(acc, frag_from_f32_pieces<E>(S.m[t][kb][0], S.m[t][kb][1]), hb[kb]);
+      }
+      Hs[t] = acc;
+    }
+  };
+  if (j0 < j1) {
+    // loads issued unconditionally (clamped to the last segment, in bounds), so
+    // the compiler's wait counts stay exact around the loop
+    CombineStep<K> buf[D];
+    const int last = j1 - 1;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int jj = min(j0 + d, last);
+      buf[d].load(mat(jj), est(jj), Q, lane, v, V);
+    }
+    for (int j = j0;; j += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (j + d >= j1) goto done;
+        step(buf[d], j + d, (j + d - j0) & 1);
+        const int jj = min(j + d + D, last);
+        buf[d].load(mat(jj), est(jj), Q, lane, v, V);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+done:
   if (fin) {
     const size_t sbase = ((size_t)n * geo.HV + hv) * K * V;
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
+      for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(32 * Q + 16 * t + 4 * g + r) * V + v] = Hs[t][r];
+  }
+}
+
+// Grid: one workgroup of K/32 waves per (sequence, value head, 16 value columns).
+template <typename E, int K, int V>
+__global__ __launch_bounds__(64 * (K / 32)) void gdn_segment_combine_kernel(
+    Geo geo, const int* __restrict__ seq_seg, const float* __restrict__ seg_m,
+    const float* __restrict__ seg_e, const float* __restrict__ h0, float* __restrict__ fin,
+    float* __restrict__ seg_h) {
+  static_assert(K == 64 || K == 128, "two or four waves");
+  constexpr int NV = V / 16, D = 2;
+  __shared__ Frag<E> xb[2][K / 32][64];
+  const int b = blockIdx.x;
+  const int vt = b % NV, hv = (b / NV) % geo.HV, n = b / (NV * geo.HV);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 0)
+    combine_wave<E, K, V, D, 0>(xb, geo, n, hv, vt, seq_seg, seg_m, seg_e, h0, fin, seg_h);
+  else if (wave == 1)
+    combine_wave<E, K, V, D, 1>(xb, geo, n, hv, vt, seq_seg, seg_m, seg_e, h0, fin, seg_h);
+  if constexpr (K == 128) {
+    if (wave == 2)
+      combine_wave<E, K, V, D, 2>(xb, geo, n, hv, vt, seq_seg, seg_m, seg_e, h0, fin, seg_h);
+    else if (wave == 3)
+      combine_wave<E, K, V, D, 3>(xb, geo, n, hv, vt, seq_seg, seg_m, seg_e, h0, fin, seg_h);
   }
 }
 

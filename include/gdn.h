@@ -41,11 +41,20 @@
  *      states the output kernel reads.
  * It does about three times the state-pass work, in sequential runs L chunks
  * long instead of a whole sequence: worth it only when a few long sequences
- * leave most CUs idle.  Measured on MI355X at B=1, T=65536, HV=4 (32 units of
- * 16 value columns): L = 64 takes the state pass from 726 to 438 us.  At 256
- * units (T=65536, HV=32) and at B=2, T=2048, HV=8 it is slower than the plain
- * pass.  Same results as the plain pass up to rounding; M_s H is evaluated
- * with operands in the call's dtype (bf16 for bf16 calls).
+ * leave most CUs idle.  Measured on MI355X at B=1, T=65536, K=V=128 bf16, with
+ * U (sequence, value head, 16-column) units: U = 16, L = 32: state pass 530 ->
+ * 225 us; U = 32, L = 64: 722 -> 326 us; U = 64, L = 128: 772 -> 387 us.  At
+ * U = 256 (HV = 32) and at B=2, T=2048, HV=8 it is slower than the plain pass.
+ * Same results as the plain pass up to rounding; M_s H is evaluated with
+ * operands in the call's dtype (bf16 for bf16 calls).
+ *
+ * seg_chunks = GDN_SEG_AUTO chooses per call, from the shape and the current
+ * device's compute-unit count (CUs): with NS = floor(2 CUs / U) (two units per
+ * CU in the segment passes), segments of L = max(ceil(NT / NS), 16) chunks
+ * (NT = chunks per sequence) when NS >= 8 and NT / L >= 8, else the plain pass
+ * (also for packed sequences, whose lengths are not known on the host).  The
+ * workspace is sized for the shortest segment it may choose (16 chunks);
+ * gdn_fwd_seg_chunks reports the choice.
  *
  * Layouts (all contiguous, row-major, device memory):
  *   q, k           [B][T][H][K]   dtype (GDN_BF16 or GDN_F32)
@@ -116,8 +125,12 @@ typedef struct {
   int32_t num_seqs; /* N with cu_seqlens; ignored (N = B) without */
   int32_t dtype;    /* gdn_dtype_t of q, k, v and o */
   float scale;      /* multiplies every o_t; 1.0 gives o_t = S_t q_t */
-  int32_t seg_chunks; /* 0: plain state pass; L > 0: segments of L chunks (see above) */
+  int32_t seg_chunks; /* 0: plain state pass; L > 0: segments of L chunks;
+                         GDN_SEG_AUTO: chosen per call (see above) */
 } gdn_params_t;
+
+/* seg_chunks value: let the library choose the segment length (see above). */
+#define GDN_SEG_AUTO (-1)
 
 /* Byte offsets of the intermediates inside the workspace, for inspection.
  * Every per-chunk buffer is indexed by a chunk slot: slot = n*ceil(T/64) + c
@@ -206,6 +219,12 @@ gdn_status_t gdn_fwd_noalloc(const gdn_params_t *p, const void *q, const void *k
                              const float *A_log, const float *dt_bias,
                              const int64_t *cu_seqlens, const float *initial_state, void *o,
                              float *final_state, void *stream);
+
+/* The segment length gdn_fwd uses for these parameters on the current device:
+ * p->seg_chunks itself, or with GDN_SEG_AUTO the automatic choice (0 = the
+ * plain state pass).  *seg_chunks is set.  Queries the device's compute-unit
+ * count (no GPU work); GDN_ERR_NULL / the gdn_fwd_check shape errors. */
+gdn_status_t gdn_fwd_seg_chunks(const gdn_params_t *p, int packed, int32_t *seg_chunks);
 
 /* Whether gdn_fwd, for these parameters on the current device, runs the output
  * stage fused into the state pass (one kernel) instead of as a kernel of its

@@ -213,7 +213,7 @@ def test_decode_validation():
 
 
 def test_segment_layout():
-    """seg_chunks > 0 adds the segment tables and buffers; negative is an error."""
+    """seg_chunks > 0 adds the segment tables and buffers."""
     p0 = P(B=2, T=700, H=2, HV=4, K=128, V=64)
     p2 = P(B=2, T=700, H=2, HV=4, K=128, V=64, seg_chunks=3)
     l0, l2 = gdn.workspace_layout(p0), gdn.workspace_layout(p2)
@@ -228,7 +228,8 @@ def test_segment_layout():
     # packed: an upper bound of slots / L + N segments
     lp = gdn.workspace_layout(P(B=1, T=1000, num_seqs=3, seg_chunks=2), packed=True)
     assert lp.num_segs == (1000 // 64 + 3) // 2 + 3
-    assert gdn.check(P(seg_chunks=-1), ptrs(), 1 << 40) == ESHAPE
+    # negative values other than GDN_SEG_AUTO (-1) are errors
+    assert gdn.check(P(seg_chunks=-3), ptrs(), 1 << 40) == ESHAPE
 
 
 def _bwd_call(lib, p, ws_bytes, **over):
@@ -313,3 +314,20 @@ def test_noalloc_rejects_problems_beyond_the_scratch():
     assert lib.gdn_fwd_noalloc(ctypes.byref(P(K=96)), *vp(), None) == EUNSUP
     assert lib.gdn_fwd_noalloc(None, *vp(), None) == ENULL
     assert "scratch" in gdn.status_string(ESCRATCH)
+
+
+def test_automatic_segments_layout():
+    """seg_chunks = GDN_SEG_AUTO: the workspace holds the shortest segments the
+    choice may take (16 chunks) for fixed-length input; packed input keeps the
+    plain pass (no segment buffers).  Other negative values are rejected."""
+    auto = P(B=1, T=65536, H=2, HV=2, K=128, V=128, seg_chunks=gdn.GDN_SEG_AUTO)
+    assert gdn.workspace_size(auto) == gdn.workspace_size(
+        P(B=1, T=65536, H=2, HV=2, K=128, V=128, seg_chunks=16))
+    assert gdn.workspace_layout(auto).num_segs == 65536 // 64 // 16
+    packed = P(B=1, T=65536, H=2, HV=2, K=128, V=128, num_seqs=3, seg_chunks=gdn.GDN_SEG_AUTO)
+    assert gdn.workspace_size(packed, packed=True) == gdn.workspace_size(
+        P(B=1, T=65536, H=2, HV=2, K=128, V=128, num_seqs=3), packed=True)
+    assert gdn.workspace_size(P(seg_chunks=-2)) == 0
+    assert gdn.check(P(seg_chunks=-2), ptrs(), 1 << 40) == ESHAPE
+    # an explicit length is reported as given (no device query needed)
+    assert gdn.seg_chunks(P(seg_chunks=5)) == 5 and gdn.seg_chunks(P()) == 0

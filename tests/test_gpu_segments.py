@@ -98,3 +98,38 @@ def test_stages_with_segments():
     assert np.array_equal(f64(plan.o), o_ref) and np.array_equal(f64(plan.final_state), f_ref)
     lay = plan.layout
     assert lay.num_segs == 2 * 3 and lay.seg_m > 0
+
+
+def _auto_rule(units, NT, cus):
+    """The documented automatic choice (include/gdn.h, GDN_SEG_AUTO)."""
+    ns = 2 * cus // units
+    if ns < 8:
+        return 0
+    L = max(-(-NT // ns), 16)
+    return L if NT // L >= 8 else 0
+
+
+@pytest.mark.parametrize("B,T,H,HV,packed", [(1, 16384, 2, 2, False), (2, 4100, 2, 2, False),
+                                             (2, 300, 8, 8, False), (1, 5000, 2, 2, True)])
+def test_automatic_segment_length(B, T, H, HV, packed):
+    """GDN_SEG_AUTO picks the documented length on this device, and the call
+    gives the same bits as one with that length set explicitly (or with the
+    plain pass when it picks none), within the oracle's tolerance."""
+    if packed:
+        inp = make_inputs(B=1, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16", seed=430,
+                          lengths=[3000, 0, 2000], h0=True, A_log_range=(-5.0, -3.0))
+    else:
+        inp = make_inputs(B=B, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16", seed=431 + T,
+                          h0=True, A_log_range=(-5.0, -3.0))
+    s = inp.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = gdn.make_params(s["B"], s["T"], s["H"], s["HV"], 128, 128, gdn.GDN_BF16,
+                        s["N"] if packed else 0, 1.0, gdn.GDN_SEG_AUTO)
+    L = gdn.seg_chunks(p, packed)
+    units = s["N"] * s["HV"] * 8
+    expect = 0 if packed else _auto_rule(units, -(-s["T"] // 64), cus)
+    say("case auto segments", s, "units", units, "cus", cus, "L", L)
+    assert L == expect
+    o, fin = check(inp, gdn.GDN_SEG_AUTO, "bf16", "auto L=%d" % L)
+    o2, fin2 = run_seg(inp, L)
+    assert np.array_equal(o, o2) and np.array_equal(fin, fin2)
