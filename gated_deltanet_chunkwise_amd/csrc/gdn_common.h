@@ -177,4 +177,27 @@ __device__ __forceinline__ void head_major_block(int b, int HV, int per_head, in
   }
 }
 
+// Block id -> (value head, chunk slot) for the per-(chunk, value head) WY
+// kernel.  With H a multiple of 8, key head h's value heads go to XCD h % 8,
+// and on each XCD the blocks run slot-major over its value heads, so one
+// chunk's workgroups for all of an XCD's value heads are dispatched together:
+// they read the same K rows (the value heads of a key head) and the same gate
+// and beta lines (the [T][HV] rows hold every head), which then come from that
+// XCD's L2 once instead of once per value head.  Otherwise slot-major over all
+// value heads.  A bijection of [0, HV * slots) in both branches; with one value
+// head per key head and HV = 8 it is head_major_block's mapping.
+__device__ __forceinline__ void xcd_slot_block(int b, int H, int G, int slots, int& hv, int& slot) {
+  if ((H & 7) == 0) {
+    const int x = b & 7, j = b >> 3;
+    const int nh = (H >> 3) * G;  // value heads per XCD
+    slot = j / nh;
+    const int r = j - slot * nh;
+    hv = (x + 8 * (r / G)) * G + r % G;
+  } else {
+    const int HV = H * G;
+    slot = b / HV;
+    hv = b - slot * HV;
+  }
+}
+
 }  // namespace gdn

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   E* const Qs = reinterpret_cast<E*>(Ts);  // EMIT_P: Q natural [64][KS], until T is formed
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
