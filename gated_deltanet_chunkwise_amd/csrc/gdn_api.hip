@@ -425,6 +425,8 @@ gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayo
   q.seg_chunks = 0;
   gdn_status_t st = make_plan(&q, varlen, pl);
   if (st != GDN_OK) return st;
+  // the key-head sum's grid: one workgroup per (slot, key head, 256 pieces)
+  if ((int64_t)pl->geo.slots * p->H * (gdn::kChunk * p->K / 1024) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   const size_t hsl = (size_t)p->HV * (size_t)pl->geo.slots, C = gdn::kChunk, K = p->K, V = p->V;
   size_t off = pl->lay.total;
   auto take = [&](size_t& field, size_t floats) {
@@ -578,9 +580,9 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   }
   mark(5);
   if (geo.slots > 0 && geo.G > 1)
-    ok(launch(gdn::gdn_bwd_qk_sum_kernel<E, K, VARLEN>, dim3((unsigned)geo.slots * geo.H),
-              dim3(256), s, geo, cmap, F(bl.dqp), F(bl.dkp), static_cast<E*>(a.dq),
-              static_cast<E*>(a.dk)));
+    ok(launch(gdn::gdn_bwd_qk_sum_kernel<E, K, VARLEN>,
+              dim3((unsigned)geo.slots * geo.H * gdn::qk_sum_parts<K>()), dim3(256), s, geo, cmap,
+              F(bl.dqp), F(bl.dkp), static_cast<E*>(a.dq), static_cast<E*>(a.dk)));
   ok(launch(gdn::gdn_bwd_param_kernel, dim3(geo.HV), dim3(256), s, geo, F(bl.dAp), F(bl.dbp),
             a.dA_log, a.ddt_bias));
   mark(6);

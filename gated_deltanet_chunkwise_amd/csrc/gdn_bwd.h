@@ -1968,29 +1968,36 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
 
 // ---------------------------------------------------------------------------
 // dq, dk of key head h: the sum of its G value heads' terms, in head order,
-// rounded to the dtype.  One workgroup per (chunk slot, key head).
+// rounded to the dtype.  A pure stream (2 G fp32 reads, 2 dtype writes per
+// element), so every thread takes one 4-element piece of one chunk's rows and
+// issues all of its loads at once: workgroup (slot, h, p) covers pieces
+// 256 p .. 256 p + 255 of the chunk's 64 x K elements / 4.
+template <int K>
+constexpr int qk_sum_parts() { return kChunk * K / 4 / 256; }
+
 template <typename E, int K, bool VARLEN>
 __global__ __launch_bounds__(256) void gdn_bwd_qk_sum_kernel(Geo geo, const int4* __restrict__ cmap,
                                                              const float* __restrict__ dqp,
                                                              const float* __restrict__ dkp,
                                                              E* __restrict__ dqg, E* __restrict__ dkg) {
-  const int slot = blockIdx.x % geo.slots, h = blockIdx.x / geo.slots;
+  constexpr int PARTS = qk_sum_parts<K>();
+  const int part = blockIdx.x % PARTS, rest = blockIdx.x / PARTS;
+  const int slot = rest % geo.slots, h = rest / geo.slots;
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
-  // four consecutive k per thread: 16-byte loads, one 8- or 16-byte store
-  for (int e = 4 * threadIdx.x; e < len * K; e += 4 * 256) {
-    const int c = e / K, kk = e - c * K;
-    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < geo.G; ++r) {
-      const size_t o = (((size_t)(h * geo.G + r) * geo.slots + slot) * kChunk + c) * K + kk;
-      sq += *reinterpret_cast<const f32x4*>(dqp + o);
-      sk += *reinterpret_cast<const f32x4*>(dkp + o);
-    }
-    const size_t d = ((t0 + c) * geo.H + h) * K + kk;
-    st4(dqg + d, sq[0], sq[1], sq[2], sq[3]);
-    st4(dkg + d, sk[0], sk[1], sk[2], sk[3]);
+  const int e = 4 * (threadIdx.x + 256 * part);
+  const int c = e / K, kk = e - c * K;
+  if (c >= len) return;
+  f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < geo.G; ++r) {
+    const size_t o = (((size_t)(h * geo.G + r) * geo.slots + slot) * kChunk + c) * K + kk;
+    sq += *reinterpret_cast<const f32x4*>(dqp + o);
+    sk += *reinterpret_cast<const f32x4*>(dkp + o);
   }
+  const size_t d = ((t0 + c) * geo.H + h) * K + kk;
+  st4(dqg + d, sq[0], sq[1], sq[2], sq[3]);
+  st4(dkg + d, sk[0], sk[1], sk[2], sk[3]);
 }
 
 // dA_log[hv], ddt_bias[hv]: sums of the per-chunk terms over the slots in slot
