@@ -262,8 +262,10 @@ def test_many_units_fp32_state_pass(K, V):
     check_full(inp, "fp32_many_units_K%d_V%d" % (K, V))
 
 
-@pytest.mark.parametrize("K,V,packed", [(128, 128, False), (64, 128, True), (128, 64, True)])
-def test_shared_key_head_workgroups(K, V, packed):
+@pytest.mark.parametrize("K,V,packed,dtype", [(128, 128, False, BF), (64, 128, True, BF),
+                                               (128, 64, True, BF), (64, 64, False, F32),
+                                               (128, 128, True, F32)])
+def test_shared_key_head_workgroups(K, V, packed, dtype):
     """Two value heads per key head and enough (chunk, value head) workgroups
     to fill the 256-CU device eight times over: the output stage runs one
     workgroup per (chunk, key head) for both of its value heads (the key
@@ -271,15 +273,15 @@ def test_shared_key_head_workgroups(K, V, packed):
     sequence and one shorter than a chunk."""
     if packed:
         lengths = [4100, 1, 0, 64, 3999, 129]
-        inp = make_inputs(B=1, T=sum(lengths), H=8, HV=16, K=K, V=V, dtype=BF, seed=91 + K + V,
+        inp = make_inputs(B=1, T=sum(lengths), H=8, HV=16, K=K, V=V, dtype=dtype, seed=91 + K + V,
                           lengths=lengths, h0=True, scale=0.7)
     else:
-        inp = make_inputs(B=2, T=8229, H=4, HV=8, K=K, V=V, dtype=BF, seed=92, h0=True)
+        inp = make_inputs(B=2, T=8229, H=4, HV=8, K=K, V=V, dtype=dtype, seed=92, h0=True)
     s = inp.shape
-    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], torch.bfloat16, "cuda",
+    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], inp.q.dtype, "cuda",
                           num_seqs=s["N"] if packed else None)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs = plan.layout.num_slots * s["HV"]
     say("case shared_key_head", s, "workgroups", wgs, "cus", cus)
     assert wgs >= 8 * cus or cus != 256
-    check_full(inp, "shared_kh_K%d_V%d%s" % (K, V, "_packed" if packed else ""))
+    check_full(inp, "shared_kh_%s_K%d_V%d%s" % (dtype, K, V, "_packed" if packed else ""))
