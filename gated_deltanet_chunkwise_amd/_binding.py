@@ -57,8 +57,14 @@ def lib_path():
 
 
 def load_library(path=None):
-    """Load libgdn.so (raises OSError if it has not been built)."""
+    """Load libgdn.so (raises OSError if it has not been built).
+
+    torch is imported first: torch ships its own HIP runtime, and libgdn.so
+    loaded before it would bind to the system's copy instead, leaving two
+    runtimes in the process, so that torch's device pointers and streams
+    are not valid in the library (every launch then fails)."""
     global _LIB
+    _torch()
     if path is not None:
         return _declare(ctypes.CDLL(path))
     if _LIB is None:

@@ -142,3 +142,24 @@ def test_backward_gradient_seeds_checked():
             call_bwd(bwd_plan(), d, d_o, dht)
     with pytest.raises(ValueError, match="GPU tensor"):
         call_bwd(bwd_plan(), d, good_do, torch.zeros(B, HV, K, V))
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch is imported must still leave one HIP
+    runtime in the process (torch's): the binding imports torch first."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from gated_deltanet_chunkwise_amd import _binding\n"
+            "assert 'torch' not in sys.modules\n"
+            "_binding.load_library()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n" % root)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=300, cwd=root)
+    assert out.returncode == 0, out.stderr[-2000:]
+    runtimes = eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
