@@ -245,14 +245,19 @@ SegRun seg_run(const Plan& pl) {
 }
 
 // Whether the output stage runs fused into the state pass (see
-// gdn_fwd_fuses_output): bf16, no segments, and the units of the state pass
-// filling the compute units once over but not twice, so that the ring form
-// runs two compute waves per workgroup.  Measured on MI355X: with two value
-// tiles per workgroup the fused kernel beats the state pass and output kernel
-// together (B=4, T=8192, H=16: 0.50 against 0.58 ms per forward step); with
-// one, the output waves' operand loads (Q rows and P^T, ~20 KB per chunk and
-// workgroup, mostly from the last-level cache) outlast the ~0.66 us chunk step
-// and hold up the state pass (B=2, T=2048, H=8: 45 us against 33 us).
+// gdn_fwd_fuses_output): bf16, no segments, and more units of the state pass
+// than compute units, so that each fused workgroup holds two value tiles
+// (beyond two units per CU its workgroups run in several rounds, one per CU at
+// a time).  Measured on MI355X, ms per forward step, fused against the state
+// pass and output kernels: B=4, T=8192, H=16 (512 units) 0.50 against 0.58;
+// B=8, T=4096, H=16 (1024 units) 0.51 against 0.57; 12 packed sequences,
+// T=32768, H=16 (1536 units) 0.56 against 0.61.  The fused kernel drops the
+// chunk states' and v_new's round trip through memory; at these shapes the
+// separate state pass is bound by that traffic (~5 TB/s).  With one value
+// tile per workgroup (at most one unit per CU) the output waves' operand loads
+// (Q rows and P^T, ~20 KB per chunk and workgroup, mostly from the last-level
+// cache) outlast the ~0.66 us chunk step and hold up the state pass (B=2,
+// T=2048, H=8: 45 us against 33 us), so those shapes keep the two kernels.
 template <typename E, int K, int V>
 bool fuses_output(const Plan& pl) {
   if constexpr (!gdn::ChainOutCfg<E, K, V, 2>::FITS || sizeof(E) != 2) {
@@ -260,7 +265,7 @@ bool fuses_output(const Plan& pl) {
   } else {
     const int64_t units = (int64_t)pl.geo.N * pl.geo.HV * (V / 16);
     const int64_t cus = device_cus();
-    return seg_run(pl).L == 0 && units > cus && units <= 2 * cus;
+    return seg_run(pl).L == 0 && units > cus;
   }
 }
 

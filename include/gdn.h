@@ -229,8 +229,9 @@ gdn_status_t gdn_fwd_seg_chunks(const gdn_params_t *p, int packed, int32_t *seg_
 /* Whether gdn_fwd, for these parameters on the current device, runs the output
  * stage fused into the state pass (one kernel) instead of as a kernel of its
  * own.  It does so for bf16 without segments when the state pass has more
- * (sequence, value head, 16-column) units than the device has compute units but
- * at most twice as many, so that each state-pass workgroup holds two of them:
+ * (sequence, value head, 16-column) units than the device has compute units,
+ * so that each state-pass workgroup holds two of them (beyond twice the
+ * compute units the workgroups run in several rounds):
  * each chunk's start state and v_new then pass from the state-pass waves to
  * two output waves of the same workgroup through LDS instead of memory, and WY
  * also emits the chunk's masked, decayed Q K^T (the intra-chunk term of the

@@ -155,7 +155,7 @@ def test_fused_output_path(packed):
     units = s["N"] * s["HV"] * (s["V"] // 16)
     say("case fused_output", "packed" if packed else "fixed", s, "units", units, "cus", cus,
         "fused", fused)
-    assert fused == (cus < units <= 2 * cus)
+    assert fused == (units > cus)
     check_full(inp, "fused_output_%s" % ("packed" if packed else "fixed"))
     o_ref, f_ref = run_gpu(inp)
     plan.o.fill_(float("nan"))
@@ -182,7 +182,7 @@ def test_fused_output_head_sizes(K, V, B, T, HV, h0):
     units = s["N"] * s["HV"] * (s["V"] // 16)
     path = gdn.fuses_output(plan.params, False)
     say("case fused_heads", s, "units", units, "path", path)
-    assert path == (cus < units <= 2 * cus)
+    assert path == (units > cus)
     check_full(inp, "fused_heads_K%d_V%d_T%d" % (K, V, T))
 
 
@@ -190,7 +190,10 @@ def test_fused_output_head_sizes(K, V, B, T, HV, h0):
                                            (128, 64, 16, True)])
 def test_many_units_two_tile_state_pass(K, V, HV, packed):
     """More (sequence, head, 16-column) units than two per compute unit on the
-    256-CU device: the bf16 state pass runs one wave per two value tiles."""
+    256-CU device.  A whole call runs the state pass and the output fused, the
+    fused workgroups in several rounds; the stages one at a time run the bf16
+    state pass with one wave per two value tiles and the output kernel.  Both
+    against the oracle."""
     if packed:
         lengths = [130, 0, 64, 1, 65, 200, 7, 128, 63, 90]   # 10 sequences
         inp = make_inputs(B=1, T=sum(lengths), H=HV // 2, HV=HV, K=K, V=V, dtype=BF, seed=50,
@@ -203,7 +206,21 @@ def test_many_units_two_tile_state_pass(K, V, HV, packed):
     units = s["N"] * s["HV"] * (s["V"] // 16)
     say("case two_tile_state_pass", s, "units", units, "cus", cus)
     assert units > 2 * cus or cus != 256
-    check_full(inp, "two_tile_K%d_V%d%s" % (K, V, "_packed" if packed else ""))
+    tag = "two_tile_K%d_V%d%s" % (K, V, "_packed" if packed else "")
+    check_full(inp, tag)
+    d = inp.to("cuda")
+    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
+                          num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale)
+    assert gdn.fuses_output(plan.params, plan.packed) == (cus == 256)
+    plan.o.fill_(float("nan"))
+    plan.final_state.fill_(float("nan"))
+    args = (d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
+    for name in gdn.STAGES:
+        plan.bind(*args, stage_mask=gdn.STAGE_BITS[name])()
+    torch.cuda.synchronize()
+    o_r, fin_r = run_oracle(inp)
+    assert_close(f64(plan.o), o_r, inp.q.dtype, tag + " stages o")
+    assert_close(f64(plan.final_state), fin_r, inp.q.dtype, tag + " stages final")
 
 
 def test_split_and_resume_matches_one_call():
