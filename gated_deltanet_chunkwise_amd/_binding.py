@@ -41,6 +41,7 @@ class WorkspaceLayout(ctypes.Structure):
     """gdn_workspace_layout_t."""
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("gamma", "beta", "w", "kt", "u", "hc", "vn", "pm", "chunk_map", "seq_slot",
+                 "seq_order",
                  "seg_slot", "seq_seg", "seg_e", "seg_m", "seg_h", "total")] + [
                     ("num_slots", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                     ("num_segs", ctypes.c_int32)]

@@ -129,6 +129,7 @@ gdn_status_t make_plan(const gdn_params_t* p, bool varlen, Plan* out) {
   L.pm = off;    off = align_up(off + hsl * gdn::kChunk * gdn::kChunk * esz);  // [4][2] k32 fragments
   L.chunk_map = off; off = align_up(off + (varlen ? (size_t)slots * 16 : 0));
   L.seq_slot = off;  off = align_up(off + (varlen ? (size_t)(N + 1) * 4 : 0));
+  L.seq_order = off; off = align_up(off + (varlen ? (size_t)N * 4 : 0));
   // segments: at most ceil(c_n / L) per sequence, summing to <= slots / L + N
   int64_t nseg = 0;
   if (pl.seg_chunks != 0) {
@@ -301,6 +302,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   Frag<E>* vnf = reinterpret_cast<Frag<E>*>(w + L.vn);
   int4* cmap = VARLEN ? reinterpret_cast<int4*>(w + L.chunk_map) : nullptr;
   int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
+  int* seq_order = VARLEN ? reinterpret_cast<int*>(w + L.seq_order) : nullptr;
   const E* qe = static_cast<const E*>(q);
   const E* ke = static_cast<const E*>(k);
   const E* ve = static_cast<const E*>(v);
@@ -317,7 +319,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   const bool work = geo.N > 0;
   if (VARLEN && work && (mask & GDN_STAGE_CHUNK_MAP))
     ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, cu_seqlens, geo.N, geo.T,
-              geo.slots, cmap, seq_slot));
+              geo.slots, cmap, seq_slot, seq_order));
   mark(1);
   const bool fused = fuses_output<E, K, V>(pl);
   const int gs = fused ? 1 : heads_per_workgroup(pl);
@@ -346,7 +348,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
       if (work && units > 0)
         ok(launch(gdn::gdn_chain_out_kernel<E, K, V, VARLEN, 2>, dim3(units / 2),
                   dim3(64 * gdn::ChainOutCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam,
-                  seq_slot, cmap, h0, fin, qe, pmf, oe));
+                  seq_slot, seq_order, cmap, h0, fin, qe, pmf, oe));
     }
     mark(3);
     mark(4);
@@ -507,6 +509,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   Quad<E>* uf = reinterpret_cast<Quad<E>*>(w + L.u);
   int4* cmap = VARLEN ? reinterpret_cast<int4*>(w + L.chunk_map) : nullptr;
   int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
+  int* seq_order = VARLEN ? reinterpret_cast<int*>(w + L.seq_order) : nullptr;
   auto FE = [&](size_t off) { return reinterpret_cast<Frag<E>*>(w + off); };
   const E* qe = static_cast<const E*>(a.q);
   const E* ke = static_cast<const E*>(a.k);
@@ -525,7 +528,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   mark(0);
   if (VARLEN && geo.N > 0)
     ok(launch(gdn::gdn_chunk_map_kernel, dim3(1), dim3(256), s, a.cu, geo.N, geo.T, geo.slots,
-              cmap, seq_slot));
+              cmap, seq_slot, seq_order));
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(gdn::kWyThreads), s, geo, ke, ve,
               a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat),

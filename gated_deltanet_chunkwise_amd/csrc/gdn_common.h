@@ -177,6 +177,29 @@ __device__ __forceinline__ void head_major_block(int b, int HV, int per_head, in
   }
 }
 
+// Block id -> (value head, sequence rank r, group of value tiles vp) for a
+// state pass over packed sequences whose workgroups do not all fit on the
+// device at once: rank-major, so the workgroups of the sequence of rank 0 (the
+// longest, in the chunk map's order) are dispatched first, then rank 1, and so
+// on.  With HV a multiple of 8 a value head keeps the XCD head_major_block
+// gives it (hv % 8), so the workgroups of one (sequence, head) share that
+// XCD's L2.  A bijection of [0, nseq * HV * groups).
+__device__ __forceinline__ void rank_major_block(int b, int HV, int groups, int& hv, int& r,
+                                                 int& vp) {
+  if ((HV & 7) == 0) {
+    const int x = b & 7, j = b >> 3, hl8 = HV >> 3;
+    vp = j % groups;
+    const int t = j / groups;
+    r = t / hl8;
+    hv = x + 8 * (t - r * hl8);
+  } else {
+    vp = b % groups;
+    const int t = b / groups;
+    r = t / HV;
+    hv = t - r * HV;
+  }
+}
+
 // Block id -> (value head, chunk slot) for the per-(chunk, value head) WY
 // kernel.  With H a multiple of 8, key head h's value heads go to XCD h % 8,
 // and on each XCD the blocks run slot-major over its value heads, so one

@@ -86,12 +86,26 @@ __device__ __forceinline__ int kslot(int g, int i) { return i < 4 ? 4 * g + i : 
 // for valid input this is the identity.  Writes cmap[slot] = (seq, first
 // token, length, 0) for used slots, (-1, 0, 0, 0) for the rest, and
 // seq_slot[n] = first slot of sequence n, seq_slot[N] = slots used.
+//
+// It also writes seq_order, a permutation of the sequences by decreasing chunk
+// count: a counting sort over min(count, kOrderBuckets - 1), so sequences of
+// that many chunks or more share the first bucket, and the order inside a
+// bucket is whatever the LDS atomics give (it decides only which workgroups
+// start first, never a result).
+constexpr int kOrderBuckets = 1024;
+
+__device__ __forceinline__ int order_bucket(int nch) {
+  return (kOrderBuckets - 1) - min(nch, kOrderBuckets - 1);
+}
+
 __global__ __launch_bounds__(256) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu, int N,
                                                             int T, int slots,
                                                             int4* __restrict__ cmap,
-                                                            int* __restrict__ seq_slot) {
+                                                            int* __restrict__ seq_slot,
+                                                            int* __restrict__ seq_order) {
   __shared__ int64_t smax[256];
   __shared__ int ssum[256];
+  __shared__ int hist[kOrderBuckets];
   __shared__ int64_t carry_b;
   __shared__ int carry_s;
   const int tid = threadIdx.x;
@@ -141,6 +155,36 @@ __global__ __launch_bounds__(256) void gdn_chunk_map_kernel(const int64_t* __res
   const int used = min(carry_s, slots);
   for (int s = used + tid; s < slots; s += 256) cmap[s] = make_int4(-1, 0, 0, 0);
   if (tid == 0) seq_slot[N] = used;
+
+  // seq_order: bucket counts, their exclusive scan (thread t owns buckets
+  // 4t .. 4t+3), then each sequence placed at its bucket's next position
+  constexpr int PER = kOrderBuckets / 256;
+  static_assert(kOrderBuckets % 256 == 0, "buckets split evenly over the threads");
+  for (int i = tid; i < kOrderBuckets; i += 256) hist[i] = 0;
+  __syncthreads();  // also makes every seq_slot entry visible to the workgroup
+  for (int n = tid; n < N; n += 256) atomicAdd(&hist[order_bucket(seq_slot[n + 1] - seq_slot[n])], 1);
+  __syncthreads();
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += hist[PER * tid + i];
+  ssum[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int y = tid >= off ? ssum[tid - off] : 0;
+    __syncthreads();
+    ssum[tid] += y;
+    __syncthreads();
+  }
+  int run = ssum[tid] - mine;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = hist[PER * tid + i];
+    hist[PER * tid + i] = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += 256)
+    seq_order[atomicAdd(&hist[order_bucket(seq_slot[n + 1] - seq_slot[n])], 1)] = n;
 }
 
 // Transposed K / V tiles in LDS ([K or V][64] rows, chunk index along a row)
@@ -1373,18 +1417,29 @@ template <typename E, int K, int V, bool VARLEN, int NC>
 __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_chain_out_kernel(
     Geo geo, const Frag<E>* __restrict__ wf, const Frag<E>* __restrict__ ktf,
     const Quad<E>* __restrict__ uf, const float* __restrict__ gam,
-    const int* __restrict__ seq_slot, const int4* __restrict__ cmap,
-    const float* __restrict__ h0, float* __restrict__ fin, const E* __restrict__ qg,
-    const Frag<E>* __restrict__ pf, E* __restrict__ og) {
+    const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
+    const int4* __restrict__ cmap, const float* __restrict__ h0, float* __restrict__ fin,
+    const E* __restrict__ qg, const Frag<E>* __restrict__ pf, E* __restrict__ og) {
   using C = ChainOutCfg<E, K, V, NC>;
   using R = typename C::R;
   using Step = ChainStep<E, K, V, CHAIN_FULL>;
   constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D, XF = C::XF;
   __shared__ __align__(16) char ring[R::LDS];
   __shared__ __align__(16) Frag<E> xch[2][NC][XF][64];
-  int hv, rest;
-  head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
-  const int n = rest / (NV / NC), vp = rest - n * (NV / NC);
+  // Beyond one workgroup per CU the workgroups run in rounds; packed
+  // sequences are then taken longest first (seq_order), so that the longest
+  // chains start in the first round.
+  int hv, n, vp;
+  if constexpr (VARLEN) {
+    int r;
+    rank_major_block(blockIdx.x, geo.HV, NV / NC, hv, r, vp);
+    n = seq_order[r];
+  } else {
+    int rest;
+    head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
+    n = rest / (NV / NC);
+    vp = rest - n * (NV / NC);
+  }
   int s0, s1;
   if constexpr (VARLEN) {
     s0 = seq_slot[n];

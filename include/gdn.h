@@ -144,7 +144,10 @@ typedef struct {
  *                                    chunk, written only when the output stage is
  *                                    fused into the state pass (below), which then
  *                                    leaves hc and vn unwritten
- *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32 (cu_seqlens only)
+ *   chunk_map [num_slots] int32x4, seq_slot [N+1] int32, seq_order [N] int32
+ *                                    (cu_seqlens only; seq_order: the sequences
+ *                                    by decreasing chunk count, the order in
+ *                                    which the fused state pass starts them)
  * With seg_chunks > 0 (num_segs = an upper bound on the segment count):
  *   seg_slot [num_segs+1] int32    first slot of each segment, sequence order
  *   seq_seg  [N+1] int32           first segment of each sequence
@@ -152,7 +155,7 @@ typedef struct {
  *   seg_m    [num_segs][HV][K][K] fp32        M_s
  * (their offsets are 0 and num_segs is 0 without segments). */
 typedef struct {
-  size_t gamma, beta, w, kt, u, hc, vn, pm, chunk_map, seq_slot;
+  size_t gamma, beta, w, kt, u, hc, vn, pm, chunk_map, seq_slot, seq_order;
   size_t seg_slot, seq_seg, seg_e, seg_m, seg_h, total;
   int32_t num_slots;
   int32_t num_seqs;

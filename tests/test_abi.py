@@ -142,7 +142,7 @@ def test_workspace_layout():
             HV, K, V = 8, 128, 64
             hsl = HV * slots
             offs = [lay.gamma, lay.beta, lay.w, lay.kt, lay.u, lay.hc, lay.vn, lay.pm,
-                    lay.chunk_map, lay.seq_slot, lay.total]
+                    lay.chunk_map, lay.seq_slot, lay.seq_order, lay.total]
             assert all(o % 256 == 0 for o in offs)
             assert offs == sorted(offs)
             assert lay.beta - lay.gamma >= hsl * 64 * 4
@@ -155,7 +155,8 @@ def test_workspace_layout():
             assert lay.chunk_map - lay.pm >= hsl * 4 * 2 * 64 * 8 * esz
             if packed:
                 assert lay.seq_slot - lay.chunk_map >= slots * 16
-                assert lay.total - lay.seq_slot >= (5 + 1) * 4
+                assert lay.seq_order - lay.seq_slot >= (5 + 1) * 4
+                assert lay.total - lay.seq_order >= 5 * 4
             assert lay.total == gdn.workspace_size(p, packed)
 
 

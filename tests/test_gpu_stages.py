@@ -187,3 +187,28 @@ def test_intermediates(dtype, tol, packed):
                 for name, arr in (("w", w), ("u", u), ("kd", kd), ("vn", vn)):
                     assert not np.any(arr[hv, slot, L:]), tag + " %s rows past the end" % name
             slot += 1
+
+
+def test_sequence_order_longest_first():
+    """The chunk map's seq_order: a permutation of the packed sequences by
+    decreasing chunk count (counts of 1023 chunks and more share the first
+    bucket, in any order), and seq_slot's prefix of the chunk counts."""
+    lengths = [1, 300, 0, 64, 65, 129, 70000, 200, 5000, 65500, 63, 640, 0, 3]
+    inp = make_inputs(B=1, T=sum(lengths), H=1, HV=1, K=64, V=64, dtype="bf16", seed=80,
+                      lengths=lengths)
+    s = inp.shape
+    say("case seq_order", s)
+    plan_out = []
+    run_gpu(inp, plan_out=plan_out)
+    plan = plan_out[0]
+    lay = gdn.workspace_layout(plan.params, plan.packed)
+    N = len(lengths)
+    ws = plan.workspace
+    order = ws[lay.seq_order:lay.seq_order + 4 * N].view(torch.int32).cpu().numpy()
+    first = ws[lay.seq_slot:lay.seq_slot + 4 * (N + 1)].view(torch.int32).cpu().numpy()
+    nch = np.array([(n + 63) // 64 for n in lengths])
+    assert np.array_equal(first, np.concatenate([[0], np.cumsum(nch)]))
+    assert sorted(order.tolist()) == list(range(N))
+    keys = np.minimum(nch[order], 1023)
+    assert np.all(np.diff(keys) <= 0), (order, nch[order])
+    assert set(order[:2].tolist()) == {6, 9}          # the two sequences past the last bucket
