@@ -293,7 +293,8 @@ class GdnForward:
         zero-argument callable that launches the pass (for hot loops: no
         per-call Python checks).  `stage_mask` (STAGE_BITS values) restricts it
         to those stages, through gdn_fwd_stages: meaningful once a full call
-        has filled the workspace."""
+        has filled the workspace, and with cu_seqlens a mask without the
+        chunk-map stage requires it (its index tables become addresses)."""
         args = self._args(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state, stream)
         keep = (q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state)
         if stage_mask is None:

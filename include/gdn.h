@@ -283,7 +283,12 @@ gdn_status_t gdn_fwd_timed(const gdn_params_t *p, const void *q, const void *k,
  * either bit alone runs the unfused kernel of that stage (the state pass then
  * writes the chunk states hc and v_new vn, which the unfused output reads).
  * Same validation and errors as gdn_fwd, plus GDN_ERR_UNSUPPORTED for bits
- * outside GDN_STAGE_ALL. */
+ * outside GDN_STAGE_ALL.  Precondition with cu_seqlens: a mask without
+ * GDN_STAGE_CHUNK_MAP takes the chunk map, seq_slot and seq_order from the
+ * workspace as addresses, so the workspace must hold those a call with the
+ * same cu_seqlens wrote; on any other workspace the kernels can read and
+ * write outside the buffers.  (gdn_fwd, gdn_fwd_noalloc and gdn_bwd always
+ * write them first.) */
 gdn_status_t gdn_fwd_stages(const gdn_params_t *p, const void *q, const void *k,
                             const void *v, const float *g_raw, const float *beta,
                             const float *A_log, const float *dt_bias,
