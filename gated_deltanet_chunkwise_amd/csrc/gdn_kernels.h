@@ -1396,7 +1396,10 @@ __global__ __launch_bounds__(64 * (K / 32)) void gdn_chain_ks_kernel(Geo geo, co
 //                       tiles and the workgroup's NC value tiles,
 //                         o^T = scale (e^{G_i} (H_c^T Q^T) + v_new^T P^T)
 //                       with Q rows read from q and P^T from the WY stage
-//                       (pf), both loaded two chunks ahead into registers;
+//                       (pf), both loaded into registers before the chunk's
+//                       barrier (one register set: a second one, loading the
+//                       next chunk during this one's products, measured
+//                       slower);
 //   two loader waves -- as in gdn_chain_ring_kernel.
 // Exchange timing: compute writes buffer i%2 before B_i (its LDS writes have
 // completed when it reaches the barrier); the output waves read it between B_i
