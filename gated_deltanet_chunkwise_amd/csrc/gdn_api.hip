@@ -189,12 +189,14 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, 
 // columns) per workgroup when the units fit, two sharing the ring otherwise;
 // beyond that many units share a CU and the register-buffered variant is used
 // (also for fp32 at K = 128, whose pipelined operands do not fit the ring
-// variant's registers).
+// variant's registers), except in CHAIN_PLAIN mode, which keeps the two-wave
+// ring.  seq_order (packed input, not segments): the ring's workgroups take
+// the sequences longest first.
 template <typename E, int K, int V, bool VARLEN, int MODE>
 hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* wf,
                         const gdn::Frag<E>* ktf, const gdn::Quad<E>* uf, const float* gam,
                         const int* seq_slot, const float* h0, float* fin, gdn::Frag<E>* hcf,
-                        gdn::Frag<E>* vnf) {
+                        gdn::Frag<E>* vnf, const int* seq_order = nullptr) {
   const int units = geo.N * geo.HV * (V / 16);
   if (units == 0) return hipSuccess;
   const int cus = device_cus();
@@ -214,11 +216,15 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
     if (units <= cus)
       return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1, MODE>, dim3(units),
                     dim3(64 * gdn::RingCfg<E, K, V, 1>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
-                    h0, fin, hcf, vnf);
-    if (units <= 2 * cus)
+                    seq_order, h0, fin, hcf, vnf);
+    // CHAIN_PLAIN (the backward's recompute, fp32 stores) keeps the ring at
+    // any unit count, its workgroups then in rounds.  Measured on MI355X at
+    // 12 packed sequences, T=32768, H=16 (1536 units): recompute 616 -> 535 us
+    // against the register variant.
+    if (units <= 2 * cus || MODE == gdn::CHAIN_PLAIN)
       return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 2, MODE>, dim3(units / 2),
                     dim3(64 * gdn::RingCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
-                    h0, fin, hcf, vnf);
+                    seq_order, h0, fin, hcf, vnf);
   }
   // bf16, beyond the ring variant: two value tiles per wave while the waves
   // (one per SIMD) are all resident at once
@@ -378,7 +384,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
                                                       nullptr, hcf, vnf));
     } else {
       ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_FULL>(geo, s, wf, ktf, uf, gam, seq_slot, h0,
-                                                        fin, hcf, vnf));
+                                                        fin, hcf, vnf, seq_order));
     }
   }
   mark(3);
@@ -536,7 +542,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   if (units > 0 && geo.slots > 0)
     ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_PLAIN>(
         geo, s, wf, ktf, uf, gam, seq_slot, a.h0, nullptr, reinterpret_cast<Frag<E>*>(F(bl.hcp)),
-        reinterpret_cast<Frag<E>*>(F(bl.vnp))));
+        reinterpret_cast<Frag<E>*>(F(bl.vnp)), seq_order));
   mark(1);
   if (chunk_wgs > 0)
     {

@@ -1118,15 +1118,26 @@ template <typename E, int K, int V, bool VARLEN, int NC, int MODE = CHAIN_FULL>
 __global__ __launch_bounds__((64 * RingCfg<E, K, V, NC>::WAVES)) void gdn_chain_ring_kernel(
     Geo geo, const Frag<E>* __restrict__ wf, const Frag<E>* __restrict__ ktf,
     const Quad<E>* __restrict__ uf, const float* __restrict__ gam,
-    const int* __restrict__ seq_slot, const float* __restrict__ h0, float* __restrict__ fin,
-    Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf) {
+    const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
+    const float* __restrict__ h0, float* __restrict__ fin, Frag<E>* __restrict__ hcf,
+    Frag<E>* __restrict__ vnf) {
   using R = RingCfg<E, K, V, NC, MODE != CHAIN_MAP>;
   using Step = ChainStep<E, K, V, MODE>;
   constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D;
   __shared__ __align__(16) char ring[R::LDS];
-  int hv, rest;
-  head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
-  const int n = rest / (NV / NC), vp = rest - n * (NV / NC);
+  // packed sequences with an order (the chunk map's seq_order): longest
+  // first, for launches whose workgroups run in several rounds
+  int hv, n, vp;
+  if (VARLEN && seq_order != nullptr) {
+    int r;
+    rank_major_block(blockIdx.x, geo.HV, NV / NC, hv, r, vp);
+    n = seq_order[r];
+  } else {
+    int rest;
+    head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
+    n = rest / (NV / NC);
+    vp = rest - n * (NV / NC);
+  }
   int s0, s1;
   if constexpr (VARLEN) {
     s0 = seq_slot[n];

@@ -204,3 +204,19 @@ def test_many_units_one_wave_state_pass(dtype):
     say("case bwd one_wave_state_pass", s, "units", units, "cus", cus)
     assert units > cus or cus != 256
     check_full(inp, "bwd many_units_%s" % dtype, 702)
+
+
+@pytest.mark.parametrize("dtype,K,V", [(BF, 128, 128), (F32, 64, 64)])
+def test_many_units_ring_recompute(dtype, K, V):
+    """Packed sequences with more (sequence, head, 16-column) units than two per
+    compute unit on the 256-CU device: the forward recompute's state pass keeps
+    the two-wave LDS ring, its workgroups in rounds, longest sequences first."""
+    lengths = [1, 63, 64, 65, 130, 0, 200, 3, 300, 129]
+    inp = make_inputs(B=1, T=sum(lengths), H=8, HV=16, K=K, V=V, dtype=dtype, seed=720 + K,
+                      lengths=lengths, h0=True)
+    s = inp.shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = s["N"] * s["HV"] * (s["V"] // 16)
+    say("case bwd ring_recompute", s, "units", units, "cus", cus)
+    assert units > 2 * cus or cus != 256
+    check_full(inp, "bwd ring_recompute_%s_K%d" % (dtype, K), 721)
