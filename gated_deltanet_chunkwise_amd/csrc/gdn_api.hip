@@ -556,11 +556,15 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
                   reinterpret_cast<gdn::f32x4*>(w + bl.dvl)));
     }
   mark(2);
-  if (units > 0 && units <= device_cus())
-    // one unit per CU or fewer: the K rows split over K/32 waves
+  if (units > 0 && (units <= device_cus() || sizeof(E) == 2))
+    // the K rows split over K/32 waves: one unit per CU or fewer, and bf16 at
+    // any unit count (about four workgroups per CU, in rounds beyond that,
+    // packed sequences longest first).  Measured on MI355X beyond one unit
+    // per CU against one wave per unit: 12 packed sequences, T=32768, H=16
+    // 553 -> 486 us (index order); B=4, T=8192, H=16 428 -> 409 us.
     ok(launch(gdn::gdn_bwd_chain_ks_kernel<E, K, V, VARLEN, 2>, dim3(units), dim3(64 * (K / 32)), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
-              reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
+              reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, seq_order, a.dht, a.dh0,
               F(bl.dhn), F(bl.dvn)));
   else if (units > 0)
     ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,

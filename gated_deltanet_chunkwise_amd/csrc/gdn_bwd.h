@@ -564,14 +564,25 @@ template <typename E, int K, int V, bool VARLEN, int D>
 __global__ __launch_bounds__(64 * (K / 32)) void gdn_bwd_chain_ks_kernel(
     Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
     const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
-    const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
-    float* __restrict__ dhn, float* __restrict__ dvn) {
+    const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
+    const float* __restrict__ dht, float* __restrict__ dh0, float* __restrict__ dhn,
+    float* __restrict__ dvn) {
   static_assert(K == 64 || K == 128, "two or four waves");
   constexpr int NV = V / 16;
   __shared__ ChainKsLds<E, K, V> sh;
-  int hv, rest;
-  head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
-  const int n = rest / NV, vt = rest - n * NV;
+  // packed sequences longest first (seq_order), for launches whose
+  // workgroups run in several rounds
+  int hv, n, vt;
+  if (VARLEN && seq_order != nullptr) {
+    int r;
+    rank_major_block(blockIdx.x, geo.HV, NV, hv, r, vt);
+    n = seq_order[r];
+  } else {
+    int rest;
+    head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
+    n = rest / NV;
+    vt = rest - n * NV;
+  }
   int s0, s1;
   if constexpr (VARLEN) {
     s0 = seq_slot[n];

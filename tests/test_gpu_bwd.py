@@ -195,8 +195,9 @@ def test_long_gqa_sampled_key_head():
 @pytest.mark.parametrize("dtype", [BF, F32])
 def test_many_units_one_wave_state_pass(dtype):
     """More (sequence, head, 16-column) units than compute units on the 256-CU
-    device: the backward state pass runs one wave per unit instead of splitting
-    the K rows over waves."""
+    device: the fp32 backward state pass runs one wave per unit; the bf16 one
+    keeps the K rows split over waves, its workgroups beyond the resident ones
+    in a second round."""
     inp = make_inputs(B=9, T=130, H=2, HV=4, K=128, V=128, dtype=dtype, seed=701, h0=True)
     s = inp.shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
