@@ -203,8 +203,9 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 // ---------------------------------------------------------------------------
 // WY representation.  One workgroup (4 waves) per (chunk slot, value head).
 //
-// LDS: K natural [64][K] (later reused for A), K^T [K][64], V^T [V][64], and
-// T (fp32 [64][64]).  Rows past the chunk end are zero.
+// LDS: K natural [64][K] (later reused for A, then for V^T), K^T [K][64], and
+// T (fp32 [64][64]); V^T [V][64] is staged once T is formed.  Rows past the
+// chunk end are zero.
 //
 // T = (I + A)^-1 is unit lower triangular.  Its 16x16 diagonal blocks are
 // found by forward substitution (one lane per column, the block held in
@@ -257,17 +258,21 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   static_assert(!EMIT_P || wy_q_fits<E, K>(), "Q rows must fit the LDS of T");
   constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
   constexpr int KS = K + P;          // K natural row stride
-  constexpr int CS = kChunk + P;     // K^T, V^T row stride
+  constexpr int CSK = kChunk + 4;    // K^T row stride
+  constexpr int CSV = kChunk + P;    // V^T row stride
   constexpr int FS = kChunk + 4;     // A, T row stride (fp32)
-  // Region 0 holds K natural until the products of A are formed, then A.
+  // Region 0 holds K natural until the products of A are formed, then A
+  // until T is formed, then V^T: V waits in registers meanwhile, so that
+  // three workgroups fit a CU's LDS (bf16 at K = V = 128: 53.8 KB each).
   constexpr int R0A = kChunk * KS * (int)sizeof(E), R0C = kChunk * FS * 4;
-  constexpr int R0 = R0A > R0C ? R0A : R0C;
+  constexpr int R0V = V * CSV * (int)sizeof(E);
+  constexpr int R0 = R0A > R0C ? (R0A > R0V ? R0A : R0V) : (R0C > R0V ? R0C : R0V);
   __shared__ __align__(16) char r0[R0];
-  __shared__ __align__(16) E Kt[K * CS];
-  __shared__ __align__(16) E Vt[V * CS];
+  __shared__ __align__(16) E Kt[K * CSK];
   __shared__ __align__(16) float Ts[kChunk * FS];
   __shared__ float sg[kChunk], sb[kChunk];
   E* const Ks = reinterpret_cast<E*>(r0);
+  E* const Vt = reinterpret_cast<E*>(r0);  // V^T, once T is formed
   float* const As = reinterpret_cast<float*>(r0);
   E* const Qs = reinterpret_cast<E*>(Ts);  // EMIT_P: Q natural [64][KS], until T is formed
 
@@ -317,15 +322,12 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       for (int j = 0; j < 8; ++j) eq[it][j] = 0.f;
     }
   }
-  if (owns) {
-    if (kside) {
+  if (owns && kside) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st8(Ks + (rb + r) * KS + c0, e[r]);
-    }
-    E* const tr = kside ? Kt : Vt;
+    for (int r = 0; r < 4; ++r) st8(Ks + (rb + r) * KS + c0, e[r]);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      st4(tr + (c0 + j) * CS + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
+      st4(Kt + (c0 + j) * CSK + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
   }
 #pragma unroll
   for (int it = 0; it < NQP; ++it) {
@@ -424,34 +426,41 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   }
   __syncthreads();
 
-  // Diagonal blocks of T by forward substitution (the block read into
-  // registers with 16-byte LDS loads, so the dependent chain runs on
-  // registers).  The blocks above them are never written: T is lower
-  // triangular, and the reads below take those blocks as zero.
+  // Diagonal blocks of T by forward substitution, lane j solving column j of
+  // the block: row i of T_bb is e_i - sum_{m<i} A_bb[i][m] T_bb[m], with
+  // A_bb's rows read from LDS (the same address in every lane: broadcast),
+  // a row ahead of its use, so that few registers are live.  The blocks
+  // above the diagonal are never written: T is lower triangular, and the
+  // reads below take those blocks as zero.
   {
     const int b = wave;
     if (b < 4 && lane < 16) {
-      float a[16][16];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        const f32x4* rowp = reinterpret_cast<const f32x4*>(As + (16 * b + i) * FS + 16 * b);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (4 * q < i) {
-            const f32x4 x = rowp[q];
-            a[i][4 * q] = x[0]; a[i][4 * q + 1] = x[1]; a[i][4 * q + 2] = x[2]; a[i][4 * q + 3] = x[3];
-          }
-        }
-      }
-      // Column sweep: once x[m] is final, subtract its contribution from every
-      // later row, so the dependent chain is 15 FMAs long, not 120.
+      const float* ab = As + 16 * b * FS + 16 * b;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+      f32x4 nxt[4];
 #pragma unroll
-      for (int m = 0; m < 15; ++m)
+      for (int q = 0; q < 4; ++q) nxt[q] = reinterpret_cast<const f32x4*>(ab + FS)[q];
 #pragma unroll
-        for (int i = m + 1; i < 16; ++i) x[i] -= a[i][m] * x[m];
+      for (int i = 1; i < 16; ++i) {
+        f32x4 row[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) row[q] = nxt[q];
+        if (i + 1 < 16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) nxt[q] = reinterpret_cast<const f32x4*>(ab + (i + 1) * FS)[q];
+        }
+        // A_bb[i][m] for m >= i is zero (strictly lower), so the later x[m]
+        // (still e_j's entries) add nothing
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; m += 2) {
+          if (m < i) s0 += row[m >> 2][m & 3] * x[m];
+          if (m + 1 < i) s1 += row[(m + 1) >> 2][(m + 1) & 3] * x[m + 1];
+        }
+        x[i] -= s0 + s1;
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ts[(16 * b + i) * FS + 16 * b + lane] = x[i];
     }
@@ -478,6 +487,13 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
     }
     __syncthreads();
   }
+  // A is no longer read: V^T takes region 0
+  if (owns && !kside) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      st4(Vt + (c0 + j) * CSV + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
+  }
+  __syncthreads();
 
   if constexpr (STORE_T) {
 #pragma unroll
@@ -530,7 +546,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       // the diagonal block): that product is skipped, not multiplied by zero
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        if (2 * cb <= ct) mma_k32(acc[m], frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), bw[cb]);
+        if (2 * cb <= ct) mma_k32(acc[m], frag_from_trow(Kt, 16 * mt + lc, CSK, 32 * cb), bw[cb]);
     }
     Frag<E>* dst = wf + (hs * 4 + ct) * (K / 32) * 64;
 #pragma unroll
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        if (2 * cb <= ct) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CS, 32 * cb));
+        if (2 * cb <= ct) mma_k32(acc, bu[cb], frag_from_trow(Vt, 16 * vt + lc, CSV, 32 * cb));
       dst[((vt * 2 + (ct >> 1)) * 64 + lane) * 2 + (ct & 1)] = make_quad<E>(acc);
     }
   }
@@ -560,7 +576,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) sc[i] = fast_exp2(gl - sg[32 * cb + kslot(g, i)]);
-      dst[f * 64 + lane] = frag_scale(frag_from_trow(Kt, 16 * mt + lc, CS, 32 * cb), sc);
+      dst[f * 64 + lane] = frag_scale(frag_from_trow(Kt, 16 * mt + lc, CSK, 32 * cb), sc);
     }
   }
 }
