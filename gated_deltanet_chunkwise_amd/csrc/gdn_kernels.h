@@ -1417,7 +1417,8 @@ __global__ __launch_bounds__(64 * (K / 32)) void gdn_chain_ks_kernel(Geo geo, co
 //   NC compute waves -- as in gdn_chain_ring_kernel, except that H_c and v_new
 //                       go to an LDS exchange (two buffers, by chunk parity)
 //                       instead of memory;
-//   two output waves -- output wave ow owns query tiles 2ow and 2ow+1 of every
+//   NOUT output waves -- output wave ow owns query tiles TPW*ow ..
+//                       TPW*ow + TPW-1 (TPW = 4 / NOUT) of every
 //                       chunk: after B_i it takes chunk i's H_c and v_new
 //                       fragments from the exchange and computes, for its
 //                       tiles and the workgroup's NC value tiles,
@@ -1438,7 +1439,9 @@ struct ChainOutCfg {
   static constexpr int XF = K / 32 + 2;                 // exchange fragments per compute wave
   static constexpr int XBYTES = 2 * NC * XF * 64 * FB;  // both buffers
   using R = RingCfg<E, K, V, NC, true, XBYTES>;
-  static constexpr int WAVES = NC + 4;                  // compute, two output, two loaders
+  static constexpr int NOUT = 4;                        // output waves
+  static constexpr int TPW = 4 / NOUT;                  // query tiles per output wave
+  static constexpr int WAVES = NC + NOUT + 2;           // compute, output, two loaders
   // the ring's registers hold bf16 fragments at any K, fp32 ones at K = 64
   static constexpr bool FITS = (FB == 16 || K <= 64) && wy_q_fits<E, K>();
 };
@@ -1450,6 +1453,7 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
     const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
     const int4* __restrict__ cmap, const float* __restrict__ h0, float* __restrict__ fin,
     const E* __restrict__ qg, const Frag<E>* __restrict__ pf, E* __restrict__ og) {
+  static_assert(sizeof(E) == 2, "the exchange layout assumes 2-byte elements");
   using C = ChainOutCfg<E, K, V, NC>;
   using R = typename C::R;
   using Step = ChainStep<E, K, V, CHAIN_FULL>;
@@ -1513,7 +1517,22 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
           st.kt[mt][cb] = ring_frag(stage, 4 * KB + 2 * mt + cb, lane, (E*)nullptr);
       Frag<E> vb[2];
       Frag<E>* x = &xch[i & 1][wave][0][lane];
-      st.vnew(Hs, vb, [&](int kb, const Frag<E>& f) { x[kb * 64] = f; },
+      // H_c goes to the exchange with k in natural order inside each k32
+      // block (lane group g' holds k = 8g' .. 8g'+7), so that the output
+      // waves' Q operands are single 16-byte runs of a q row.  The k order
+      // of one product only has to agree between its two operands.  The
+      // fragment's halves are the two D tiles (rows 4g .. 4g+3 of tiles 0
+      // and 1 of the block): tile t's four values are k = 16t + 4g + r, that
+      // is lane group 2t + g/2, elements 4(g%2) + r.
+      char* xh = reinterpret_cast<char*>(&xch[i & 1][wave][0][0]);
+      st.vnew(Hs, vb,
+              [&](int kb, const Frag<E>& f) {
+                // lane slot lc + 16 (2t + g/2), byte 8 (g % 2) of its 16
+                char* blk = xh + kb * 64 * 16 + (lc + 16 * (g >> 1)) * 16 + (g & 1) * 8;
+                *reinterpret_cast<Quad<E>*>(blk) = Quad<E>{__builtin_shufflevector(f.x, f.x, 0, 1, 2, 3)};
+                *reinterpret_cast<Quad<E>*>(blk + 32 * 16) =
+                    Quad<E>{__builtin_shufflevector(f.x, f.x, 4, 5, 6, 7)};
+              },
               [&](int cb, const Frag<E>& f) { x[(KB + cb) * 64] = f; }, none_t);
       const float dec = fast_exp2(glast);
 #pragma unroll
@@ -1532,11 +1551,13 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
 #pragma unroll
         for (int r = 0; r < 4; ++r) fin[sbase + (size_t)(16 * mt + 4 * g + r) * V + v] = Hs[mt][r];
     }
-  } else if (wave < NC + 2) {
-    // output wave OW (0 or 1) as a compile-time constant, so that every load
-    // count is fixed
+  } else if (wave < NC + C::NOUT) {
+    // output wave OW (0 .. NOUT-1, query tiles TPW*OW ..) as a compile-time
+    // constant, so that every load count is fixed
+    constexpr int TPW = C::TPW;
     auto role = [&](auto ow_c) {
       constexpr int OW = decltype(ow_c)::value;
+      constexpr int it0 = TPW * OW;
       const int h = hv / geo.G;
       // the sequence's token range: chunk c covers bos + 64c .. min(bos + 64c + 64, eos)
       int64_t bos = 0, eos = 0;
@@ -1551,9 +1572,9 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
         }
       }
       struct Ops {
-        Frag<E> q[2][KB];  // Q rows of query tiles 2OW, 2OW+1 (B operands over K)
-        Frag<E> p[2][2];   // P^T fragments (it, jb), jb <= it/2
-        float gq[2];       // cumulative gate (log2 units) of the lane's query in each tile
+        Frag<E> q[TPW][KB];  // Q rows of query tiles it0 + t (B operands over K)
+        Frag<E> p[TPW][2];   // P^T fragments (it, jb), jb <= it/2
+        float gq[TPW];       // cumulative gate (log2 units) of the lane's query in each tile
       };
       // Every load is unconditional (in bounds): a query row past the chunk's
       // end reads the chunk's last row instead; only output rows that are not
@@ -1563,15 +1584,15 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
         const int64_t t0 = bos + (int64_t)kChunk * c;
         const int len = (int)min((int64_t)kChunk, eos - t0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          constexpr int it0 = 2 * OW;
+        for (int t = 0; t < TPW; ++t) {
           const int it = it0 + t, row = 16 * it + lc;
-          const E* qr = qg + ((t0 + min(row, len - 1)) * geo.H + h) * K;
+          const E* qr = qg + ((t0 + min(row, len - 1)) * geo.H + h) * K + 8 * g;
+          // k in natural order (see the exchange): one 16-byte load each
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) o.q[t][kb] = frag_from_row(qr + 32 * kb);
+          for (int kb = 0; kb < KB; ++kb) o.q[t][kb] = *reinterpret_cast<const Frag<E>*>(qr + 32 * kb);
 #pragma unroll
-          for (int jb = 0; jb <= ((it0 + 1) >> 1); ++jb)
-            if (jb <= ((2 * OW + t) >> 1)) o.p[t][jb] = pf[(((hbase + c) * 4 + it) * 2 + jb) * 64 + lane];
+          for (int jb = 0; jb <= ((it0 + TPW - 1) >> 1); ++jb)
+            if (jb <= ((it0 + t) >> 1)) o.p[t][jb] = pf[(((hbase + c) * 4 + it) * 2 + jb) * 64 + lane];
           o.gq[t] = gam[(hbase + c) * kChunk + row];
         }
       };
@@ -1588,15 +1609,15 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
           for (int jb = 0; jb < 2; ++jb) vn[jb] = x[(KB + jb) * 64];
           const int vt = NC * vp + c;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int it = 2 * OW + t;
+          for (int t = 0; t < TPW; ++t) {
+            const int it = it0 + t;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) mma_k32(acc, hc[kb], o.q[t][kb]);
             acc *= fast_exp2(o.gq[t]);
 #pragma unroll
-            for (int jb = 0; jb <= ((2 * OW + 1) >> 1); ++jb)
-              if (jb <= ((2 * OW + t) >> 1)) mma_k32(acc, vn[jb], o.p[t][jb]);
+            for (int jb = 0; jb <= ((it0 + TPW - 1) >> 1); ++jb)
+              if (jb <= ((it0 + t) >> 1)) mma_k32(acc, vn[jb], o.p[t][jb]);
             acc *= geo.scale;
             const int row = 16 * it + lc;
             if (row < len)
@@ -1617,9 +1638,13 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
       }
     };
     if (wave == NC) role(std::integral_constant<int, 0>{});
-    else role(std::integral_constant<int, 1>{});
+    else if (C::NOUT == 2 || wave == NC + 1) role(std::integral_constant<int, 1>{});
+    else if constexpr (C::NOUT == 4) {
+      if (wave == NC + 2) role(std::integral_constant<int, 2>{});
+      else role(std::integral_constant<int, 3>{});
+    }
   } else {
-    ring_loader<R, E, K, V, NC>(ring, wave - NC - 2, geo, wf, ktf, uf, gam, hbase, vp, nsteps);
+    ring_loader<R, E, K, V, NC>(ring, wave - NC - C::NOUT, geo, wf, ktf, uf, gam, hbase, vp, nsteps);
   }
 }
 
