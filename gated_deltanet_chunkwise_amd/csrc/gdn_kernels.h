@@ -203,9 +203,11 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 // ---------------------------------------------------------------------------
 // WY representation.  One workgroup (4 waves) per (chunk slot, value head).
 //
-// LDS: K natural [64][K] (later reused for A, then for V^T), K^T [K][64], and
-// T (fp32 [64][64]); V^T [V][64] is staged once T is formed.  Rows past the
-// chunk end are zero.
+// LDS: K natural [64][K] (later reused for A, then for V^T) and T (fp32
+// [64][64]).  K and V wait in registers as loaded; once T has been read into
+// the w / u operands, V^T [V][64] takes the region of K / A and K^T [K][64]
+// (bf16; fp32 at K = 128 keeps an array of its own, staged at the start) the
+// region of T.  Rows past the chunk end are zero.
 //
 // T = (I + A)^-1 is unit lower triangular.  Its 16x16 diagonal blocks are
 // found by forward substitution (one lane per column, the block held in
@@ -234,6 +236,35 @@ constexpr int kWyThreads = 512;
 //                                     jb <= it/2 only; the rest is all zero)
 // Q is staged in the LDS of T, which is free until the diagonal blocks of T
 // are solved.
+// Eight consecutive elements of one row as loaded (16 bytes for bf16), and
+// column j of four such rows stored as four consecutive elements.
+template <typename E> struct Raw8;
+template <> struct Raw8<bf16> {
+  bf16x8 x;
+  __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() { x = bf16x8{}; }
+  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = x; }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const f32x4*>(p)[0];
+    b = reinterpret_cast<const f32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+  }
+};
+__device__ __forceinline__ void raw_column(const Raw8<bf16> (&e)[4], int j, bf16* p) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{e[0].x[j], e[1].x[j], e[2].x[j], e[3].x[j]};
+}
+__device__ __forceinline__ void raw_column(const Raw8<float> (&e)[4], int j, float* p) {
+  auto el = [&](int r) { return j < 4 ? e[r].a[j] : e[r].b[j - 4]; };
+  *reinterpret_cast<f32x4*>(p) = f32x4{el(0), el(1), el(2), el(3)};
+}
+
 template <typename E, int K>
 constexpr bool wy_q_fits() {
   return kChunk * (K + 16 / (int)sizeof(E)) * (int)sizeof(E) <= kChunk * (kChunk + 4) * 4;
@@ -262,14 +293,17 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   constexpr int CSV = kChunk + P;    // V^T row stride
   constexpr int FS = kChunk + 4;     // A, T row stride (fp32)
   // Region 0 holds K natural until the products of A are formed, then A
-  // until T is formed, then V^T: V waits in registers meanwhile, so that
-  // three workgroups fit a CU's LDS (bf16 at K = V = 128: 53.8 KB each).
+  // until T is formed, then V^T (bf16 at K = V = 128: 36.4 KB in all).
   constexpr int R0A = kChunk * KS * (int)sizeof(E), R0C = kChunk * FS * 4;
   constexpr int R0V = V * CSV * (int)sizeof(E);
   constexpr int R0 = R0A > R0C ? (R0A > R0V ? R0A : R0V) : (R0C > R0V ? R0C : R0V);
   __shared__ __align__(16) char r0[R0];
-  __shared__ __align__(16) E Kt[K * CSK];
+  // K^T too is staged late when it fits the LDS of T (bf16): T has then been
+  // read into the w / u operands
+  constexpr bool KT_LATE = K * CSK * (int)sizeof(E) <= kChunk * FS * 4;
+  __shared__ __align__(16) E Kt_sep[KT_LATE ? 8 : K * CSK];
   __shared__ __align__(16) float Ts[kChunk * FS];
+  E* const Kt = KT_LATE ? reinterpret_cast<E*>(Ts) : Kt_sep;
   __shared__ float sg[kChunk], sb[kChunk];
   E* const Ks = reinterpret_cast<E*>(r0);
   E* const Vt = reinterpret_cast<E*>(r0);  // V^T, once T is formed
@@ -298,15 +332,15 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   const int mtile = tid & 255, W8 = (kside ? K : V) / 8;
   const int rb = 4 * (mtile / W8), c0 = 8 * (mtile % W8);
   const bool owns = mtile < (kside ? NKM : NVM);
-  float e[4][8];
+  // the micro-tile as loaded (raw elements: few registers while it waits)
+  Raw8<E> e[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (owns && rb + r < len) {
-      if (kside) ld8(kg + ((t0 + rb + r) * geo.H + h) * K + c0, e[r]);
-      else ld8(vg + ((t0 + rb + r) * geo.HV + hv) * V + c0, e[r]);
+      if (kside) e[r].load(kg + ((t0 + rb + r) * geo.H + h) * K + c0);
+      else e[r].load(vg + ((t0 + rb + r) * geo.HV + hv) * V + c0);
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[r][j] = 0.f;
+      e[r].zero();
     }
   }
   // EMIT_P: thread t also loads 8-element pieces t and t + 512 of Q's rows.
@@ -324,10 +358,11 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   }
   if (owns && kside) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st8(Ks + (rb + r) * KS + c0, e[r]);
+    for (int r = 0; r < 4; ++r) e[r].store(Ks + (rb + r) * KS + c0);
+    if constexpr (!KT_LATE) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st4(Kt + (c0 + j) * CSK + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
+      for (int j = 0; j < 8; ++j) raw_column(e, j, Kt + (c0 + j) * CSK + (rb ^ tswz(c0 + j)));
+    }
   }
 #pragma unroll
   for (int it = 0; it < NQP; ++it) {
@@ -487,13 +522,6 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
     }
     __syncthreads();
   }
-  // A is no longer read: V^T takes region 0
-  if (owns && !kside) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st4(Vt + (c0 + j) * CSV + (rb ^ tswz(c0 + j)), e[0][j], e[1][j], e[2][j], e[3][j]);
-  }
-  __syncthreads();
 
   if constexpr (STORE_T) {
 #pragma unroll
@@ -532,6 +560,17 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
     bw[cb] = to_frag<E>(frag_scale(tf, sw));
     bu[cb] = to_frag<E>(frag_scale(tf, su));
   }
+
+  // T has been read (w / u operands in registers): V^T takes region 0 (A is
+  // no longer read either), K^T the LDS of T
+  __syncthreads();
+  if (owns && (!kside || KT_LATE)) {
+    E* const tr = kside ? Kt : Vt;
+    const int cs = kside ? CSK : CSV;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) raw_column(e, j, tr + (c0 + j) * cs + (rb ^ tswz(c0 + j)));
+  }
+  __syncthreads();
 
   // w^T = K^T T_w^T: D tile (mt) holds w[16ct + lane%16][16mt + 4g + r], so
   // tile pairs are the state pass's A fragments.
