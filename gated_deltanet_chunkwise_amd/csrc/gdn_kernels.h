@@ -1940,23 +1940,23 @@ __global__ __launch_bounds__(256) void gdn_output_kernel(Geo geo, const E* __res
     sg[gi][c] = gam[((size_t)(hv0 + gi) * geo.slots + slot) * kChunk + c];
   }
   constexpr int NIT = kChunk * (K / 8) / 256;  // 8-element pieces per thread
-  float eq[NIT][8], ek[NIT][8];
+  Raw8<E> eq[NIT], ek[NIT];                      // as loaded
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int m = tid + 256 * it, row = m / (K / 8), c0 = 8 * (m % (K / 8));
     if (row < len) {
-      ld8(qg + ((t0 + row) * geo.H + h) * K + c0, eq[it]);
-      ld8(kg + ((t0 + row) * geo.H + h) * K + c0, ek[it]);
+      eq[it].load(qg + ((t0 + row) * geo.H + h) * K + c0);
+      ek[it].load(kg + ((t0 + row) * geo.H + h) * K + c0);
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) eq[it][j] = ek[it][j] = 0.f;
+      eq[it].zero();
+      ek[it].zero();
     }
   }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int m = tid + 256 * it, row = m / (K / 8), c0 = 8 * (m % (K / 8));
-    st8(Qs + row * KS + c0, eq[it]);
-    st8(Ks + row * KS + c0, ek[it]);
+    eq[it].store(Qs + row * KS + c0);
+    ek[it].store(Ks + row * KS + c0);
   }
   __syncthreads();
 
