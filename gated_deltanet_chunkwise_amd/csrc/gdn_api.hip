@@ -252,27 +252,26 @@ SegRun seg_run(const Plan& pl) {
 }
 
 // Whether the output stage runs fused into the state pass (see
-// gdn_fwd_fuses_output): bf16, no segments, and more units of the state pass
-// than compute units, so that each fused workgroup holds two value tiles
-// (beyond two units per CU its workgroups run in several rounds, one per CU at
-// a time).  Measured on MI355X, ms per forward step, fused against the state
-// pass and output kernels: B=4, T=8192, H=16 (512 units) 0.50 against 0.58;
-// B=8, T=4096, H=16 (1024 units) 0.51 against 0.57; 12 packed sequences,
-// T=32768, H=16 (1536 units) 0.56 against 0.61.  The fused kernel drops the
-// chunk states' and v_new's round trip through memory; at these shapes the
-// separate state pass is bound by that traffic (~5 TB/s).  With one value
-// tile per workgroup (at most one unit per CU) the output waves' operand loads
-// (Q rows and P^T, ~20 KB per chunk and workgroup, mostly from the last-level
-// cache) outlast the ~0.66 us chunk step and hold up the state pass (B=2,
-// T=2048, H=8: 45 us against 33 us), so those shapes keep the two kernels.
+// gdn_fwd_fuses_output): bf16 without segments.  The fused workgroup holds
+// one value tile when the units fit one per CU, two beyond that (in several
+// rounds beyond two per CU).  Measured on MI355X, ms per forward step, fused
+// against the state pass and output kernels: B=1, T=65536, H=16, HV=32 (256
+// units) 1.86 against 2.09; B=2, T=2048, H=8 (128 units) 0.0489 against
+// 0.0492; B=4, T=8192, H=16 (512 units) 0.50 against 0.58; B=8, T=4096,
+// H=16 (1024 units) 0.51 against 0.57; 12 packed sequences, T=32768, H=16
+// (1536 units) 0.56 against 0.61.  The fused kernel drops the chunk states'
+// and v_new's round trip through memory.  With one value tile per workgroup
+// it lost while the output waves' Q operands were two 8-byte pieces in the
+// kslot order (B=2, T=2048, H=8: 45 us against 33 us for the state pass and
+// output); since H_c reaches them with k in natural order, each is one
+// 16-byte load.
 template <typename E, int K, int V>
 bool fuses_output(const Plan& pl) {
   if constexpr (!gdn::ChainOutCfg<E, K, V, 2>::FITS || sizeof(E) != 2) {
     return false;
   } else {
     const int64_t units = (int64_t)pl.geo.N * pl.geo.HV * (V / 16);
-    const int64_t cus = device_cus();
-    return seg_run(pl).L == 0 && units > cus;
+    return seg_run(pl).L == 0 && units > 0;
   }
 }
 
@@ -351,7 +350,11 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
     // the state pass with the output stage in the same workgroups
     if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS && sizeof(E) == 2) {
       const int units = geo.N * geo.HV * (V / 16);
-      if (work && units > 0)
+      if (work && units > 0 && units <= device_cus())
+        ok(launch(gdn::gdn_chain_out_kernel<E, K, V, VARLEN, 1>, dim3(units),
+                  dim3(64 * gdn::ChainOutCfg<E, K, V, 1>::WAVES), s, geo, wf, ktf, uf, gam,
+                  seq_slot, seq_order, cmap, h0, fin, qe, pmf, oe));
+      else if (work && units > 0)
         ok(launch(gdn::gdn_chain_out_kernel<E, K, V, VARLEN, 2>, dim3(units / 2),
                   dim3(64 * gdn::ChainOutCfg<E, K, V, 2>::WAVES), s, geo, wf, ktf, uf, gam,
                   seq_slot, seq_order, cmap, h0, fin, qe, pmf, oe));

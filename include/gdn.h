@@ -231,17 +231,17 @@ gdn_status_t gdn_fwd_seg_chunks(const gdn_params_t *p, int packed, int32_t *seg_
 
 /* Whether gdn_fwd, for these parameters on the current device, runs the output
  * stage fused into the state pass (one kernel) instead of as a kernel of its
- * own.  It does so for bf16 without segments when the state pass has more
- * (sequence, value head, 16-column) units than the device has compute units,
- * so that each state-pass workgroup holds two of them (beyond twice the
- * compute units the workgroups run in several rounds):
- * each chunk's start state and v_new then pass from the state-pass waves to
- * two output waves of the same workgroup through LDS instead of memory, and WY
+ * own.  It does so for bf16 without segments: each state-pass workgroup
+ * holds one (sequence, value head, 16-column) unit when they fit one per
+ * compute unit, two beyond that (beyond twice the compute units its
+ * workgroups run in several rounds).  Each chunk's start state and v_new
+ * then pass from the state-pass waves to
+ * the output waves of the same workgroup through LDS instead of memory, and WY
  * also emits the chunk's masked, decayed Q K^T (the intra-chunk term of the
  * output).  The results are bit-identical either way: the same products in the
- * same order and rounding.  *fused is set to 1 or 0.  Queries the device's
- * compute-unit count (no GPU work); GDN_ERR_NULL / the gdn_fwd_check shape
- * errors. */
+ * same order and rounding.  *fused is set to 1 or 0.  No GPU work (with
+ * seg_chunks = GDN_SEG_AUTO it queries the device's compute-unit count, as
+ * gdn_fwd_seg_chunks does); GDN_ERR_NULL / the gdn_fwd_check shape errors. */
 gdn_status_t gdn_fwd_fuses_output(const gdn_params_t *p, int packed, int32_t *fused);
 
 /* Number of stages gdn_fwd_timed brackets with events: chunk map, WY (with

@@ -155,7 +155,7 @@ def test_fused_output_path(packed):
     units = s["N"] * s["HV"] * (s["V"] // 16)
     say("case fused_output", "packed" if packed else "fixed", s, "units", units, "cus", cus,
         "fused", fused)
-    assert fused == (units > cus)
+    assert fused  # bf16 without segments
     check_full(inp, "fused_output_%s" % ("packed" if packed else "fixed"))
     o_ref, f_ref = run_gpu(inp)
     plan.o.fill_(float("nan"))
@@ -182,7 +182,7 @@ def test_fused_output_head_sizes(K, V, B, T, HV, h0):
     units = s["N"] * s["HV"] * (s["V"] // 16)
     path = gdn.fuses_output(plan.params, False)
     say("case fused_heads", s, "units", units, "path", path)
-    assert path == (units > cus)
+    assert path  # bf16 without segments
     check_full(inp, "fused_heads_K%d_V%d_T%d" % (K, V, T))
 
 
@@ -211,7 +211,7 @@ def test_many_units_two_tile_state_pass(K, V, HV, packed):
     d = inp.to("cuda")
     plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
                           num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale)
-    assert gdn.fuses_output(plan.params, plan.packed) == (cus == 256)
+    assert gdn.fuses_output(plan.params, plan.packed)
     plan.o.fill_(float("nan"))
     plan.final_state.fill_(float("nan"))
     args = (d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
