@@ -345,16 +345,12 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   }
   // EMIT_P: thread t also loads 8-element pieces t and t + 512 of Q's rows.
   constexpr int NQP = EMIT_P ? (kChunk * (K / 8) + kWyThreads - 1) / kWyThreads : 0;
-  float eq[NQP > 0 ? NQP : 1][8];
+  Raw8<E> eq[NQP > 0 ? NQP : 1];  // as loaded
 #pragma unroll
   for (int it = 0; it < NQP; ++it) {
     const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
-    if (row < kChunk && row < len) {
-      ld8(qg + ((t0 + row) * geo.H + h) * K + qc, eq[it]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) eq[it][j] = 0.f;
-    }
+    if (row < kChunk && row < len) eq[it].load(qg + ((t0 + row) * geo.H + h) * K + qc);
+    else eq[it].zero();
   }
   if (owns && kside) {
 #pragma unroll
@@ -367,7 +363,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
 #pragma unroll
   for (int it = 0; it < NQP; ++it) {
     const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
-    if (row < kChunk) st8(Qs + row * KS + qc, eq[it]);
+    if (row < kChunk) eq[it].store(Qs + row * KS + qc);
   }
   // Gate prologue (wave 0, lane = token): g in fp32 with the softplus
   // threshold of the KDA gate guide ("core computation logic"), the chunk-local
