@@ -312,13 +312,15 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
 
   int hv, slot;
   xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
-  // fixed-length sequences: blocks in descending chunk order (every sequence's
-  // last chunk first), so the first chunks, which the state pass reads first,
-  // are the most recently written when it starts (still in the last-level
-  // cache when a step's intermediates exceed it)
+  // Blocks in descending chunk order (fixed length: every sequence's last
+  // chunk first; packed: the slots reversed), so the first chunks, which the
+  // state pass reads first, are the most recently written when it starts
+  // (still in the last-level cache when a step's intermediates exceed it).
   if constexpr (!VARLEN) {
     const int c = geo.NT - 1 - slot / geo.N, n = slot % geo.N;
     slot = n * geo.NT + c;
+  } else {
+    slot = geo.slots - 1 - slot;
   }
   int n, len;
   int64_t t0;
