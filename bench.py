@@ -15,6 +15,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -102,13 +103,24 @@ OP_SOURCES = {
 }
 
 
+_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(text):
+    """C++ source with its comments removed and whitespace collapsed (string and
+    character literals kept as written): what the compiler sees."""
+    kept = _TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return " ".join(kept.split())
+
+
 def source_hash(op="gdn_fwd"):
-    """Hash of the sources of one op (traffic counters are only valid for this code)."""
+    """Hash of the code of one op (traffic counters are only valid for this code;
+    comments and layout do not enter it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_chunkwise_amd", "csrc")
     for f in OP_SOURCES[op]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -201,7 +201,7 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 }
 
 // ---------------------------------------------------------------------------
-// WY representation.  One workgroup (4 waves) per (chunk slot, value head).
+// WY representation.  One workgroup (8 waves) per (chunk slot, value head).
 //
 // LDS: K natural [64][K] (later reused for A, then for V^T) and T (fp32
 // [64][64]).  K and V wait in registers as loaded; once T has been read into
@@ -210,8 +210,8 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 // region of T.  Rows past the chunk end are zero.
 //
 // T = (I + A)^-1 is unit lower triangular.  Its 16x16 diagonal blocks are
-// found by forward substitution (one lane per column, the block held in
-// registers), the off-diagonal blocks block-row by block-row:
+// found by forward substitution (one lane per column, the rows of A read from
+// LDS one ahead of their use), the off-diagonal blocks block-row by block-row:
 // T_rc = -T_rr sum_{m=c}^{r-1} A_rm T_mc, on fp32 MFMAs.  The scaled factors
 // T diag(beta e^G) and T diag(beta) are never stored: each wave builds its
 // operand fragments for w and u from its own rows of T, scaled in registers.

@@ -83,6 +83,27 @@ def test_write_traffic_scales_counters_and_reads_mfma_passes(tmp_path, monkeypat
     assert bench.kernel_counters(ent["chain"]) == {"mfma_util": 0.025, "mfma_flops": 512}
 
 
+def test_code_text_drops_comments_and_layout_only():
+    src = 'int a; // note\nasm("s_waitcnt // kept");  /* block\n comment */ char c = \'/\';\n'
+    assert bench.code_text(src) == 'int a; asm("s_waitcnt // kept"); char c = \'/\';'
+    assert bench.code_text("x  =\n  y; // z") == bench.code_text("x = y;")
+    assert bench.code_text("x = y;") != bench.code_text("x = z;")
+
+
+def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    import shutil
+    csrc = os.path.join(str(tmp_path), "gated_deltanet_chunkwise_amd", "csrc")
+    shutil.copytree(os.path.join(ROOT, "gated_deltanet_chunkwise_amd", "csrc"), csrc)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.source_hash("decode")
+    path = os.path.join(csrc, "gdn_decode.h")
+    text = open(path).read()
+    open(path, "w").write("// an added comment\n" + text.replace(";", "; /* c */", 1))
+    assert bench.source_hash("decode") == base
+    open(path, "w").write(text + "\nstatic int extra_symbol;\n")
+    assert bench.source_hash("decode") != base
+
+
 def test_source_hash_covers_each_op_only_with_its_sources():
     ops = ("gdn_fwd", "gdn_bwd", "kda_gate", "decode")
     hashes = {op: bench.source_hash(op) for op in ops}
