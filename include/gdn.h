@@ -25,8 +25,10 @@
  * the gate prologue and chunk-local cumsum and writes them stride-1 along T
  * (the layout fix of the G_T_CONTIG page, "fix: host transpose + stride-1
  * pointer", done inside the kernel instead of on the host), the sequential
- * inter-chunk state pass, and the chunk output.  A fourth kernel builds the
- * chunk map when cu_seqlens is given.
+ * inter-chunk state pass, and the chunk output.  For bf16 without segments
+ * the output runs inside the state-pass kernel (gdn_fwd_fuses_output), so a
+ * call is two kernels.  One more kernel builds the chunk map when cu_seqlens
+ * is given.
  *
  * Segment-parallel state pass (seg_chunks > 0).  The chunk update is affine in
  * the state, H_next = M_c H + B_c (M_c = e^{G_last} I - kd^T w), so a run of
