@@ -252,7 +252,8 @@ SegRun seg_run(const Plan& pl) {
 }
 
 // Whether the output stage runs fused into the state pass (see
-// gdn_fwd_fuses_output): bf16 without segments.  The fused workgroup holds
+// gdn_fwd_fuses_output): bf16 without segments, and fp32 at K = 64 beyond one
+// unit per CU.  The fused workgroup holds
 // one value tile when the units fit one per CU, two beyond that (in several
 // rounds beyond two per CU).  Measured on MI355X, ms per forward step, fused
 // against the state pass and output kernels: B=1, T=65536, H=16, HV=32 (256
@@ -267,11 +268,16 @@ SegRun seg_run(const Plan& pl) {
 // 16-byte load.
 template <typename E, int K, int V>
 bool fuses_output(const Plan& pl) {
-  if constexpr (!gdn::ChainOutCfg<E, K, V, 2>::FITS || sizeof(E) != 2) {
+  if constexpr (!gdn::ChainOutCfg<E, K, V, 2>::FITS) {
     return false;
   } else {
     const int64_t units = (int64_t)pl.geo.N * pl.geo.HV * (V / 16);
-    return seg_run(pl).L == 0 && units > 0;
+    if (seg_run(pl).L != 0 || units <= 0) return false;
+    // fp32 (K = 64): fused only beyond one unit per CU, where the two-tile
+    // workgroups share the chunk operands.  Measured: B=4, T=2048, H=HV=32,
+    // K=V=64 (512 units) 0.277 -> 0.252 ms; B=2, T=4096 (256 units) 0.286 ->
+    // 0.296 ms fused (not used); B=1, T=256, H=2 (8 units) 24.6 -> 24.5 us.
+    return sizeof(E) == 2 || units > device_cus();
   }
 }
 
@@ -331,7 +337,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   Frag<E>* pmf = reinterpret_cast<Frag<E>*>(w + L.pm);
   if (work && geo.slots > 0 && (mask & GDN_STAGE_WY)) {
     bool done = false;
-    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS && sizeof(E) == 2) {
+    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS) {
       if (fused) {
         ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, false, true>, dim3(geo.slots * geo.HV),
                   dim3(gdn::kWyThreads), s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam,
@@ -348,7 +354,7 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
   const unsigned so = GDN_STAGE_STATE | GDN_STAGE_OUTPUT;
   if (fused && (mask & so) == so) {
     // the state pass with the output stage in the same workgroups
-    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS && sizeof(E) == 2) {
+    if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS) {
       const int units = geo.N * geo.HV * (V / 16);
       if (work && units > 0 && units <= device_cus())
         ok(launch(gdn::gdn_chain_out_kernel<E, K, V, VARLEN, 1>, dim3(units),

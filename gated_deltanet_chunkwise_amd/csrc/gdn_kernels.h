@@ -1498,8 +1498,8 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
     const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
     const int4* __restrict__ cmap, const float* __restrict__ h0, float* __restrict__ fin,
     const E* __restrict__ qg, const Frag<E>* __restrict__ pf, E* __restrict__ og) {
-  static_assert(sizeof(E) == 2, "the exchange layout assumes 2-byte elements");
   using C = ChainOutCfg<E, K, V, NC>;
+  static_assert(C::FITS, "fragments fit the ring's registers");
   using R = typename C::R;
   using Step = ChainStep<E, K, V, CHAIN_FULL>;
   constexpr int NV = V / 16, KB = K / 32, KT = K / 16, D = R::D, XF = C::XF;
@@ -1572,11 +1572,13 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
       char* xh = reinterpret_cast<char*>(&xch[i & 1][wave][0][0]);
       st.vnew(Hs, vb,
               [&](int kb, const Frag<E>& f) {
-                // lane slot lc + 16 (2t + g/2), byte 8 (g % 2) of its 16
-                char* blk = xh + kb * 64 * 16 + (lc + 16 * (g >> 1)) * 16 + (g & 1) * 8;
-                *reinterpret_cast<Quad<E>*>(blk) = Quad<E>{__builtin_shufflevector(f.x, f.x, 0, 1, 2, 3)};
-                *reinterpret_cast<Quad<E>*>(blk + 32 * 16) =
-                    Quad<E>{__builtin_shufflevector(f.x, f.x, 4, 5, 6, 7)};
+                // lane slot lc + 16 (2t + g/2), half g % 2 of its FB bytes
+                constexpr int FB = C::FB;
+                char* blk = xh + kb * 64 * FB + (lc + 16 * (g >> 1)) * FB + (g & 1) * (FB / 2);
+                Quad<E> t0, t1;
+                split_pair(f, t0, t1);
+                *reinterpret_cast<Quad<E>*>(blk) = t0;
+                *reinterpret_cast<Quad<E>*>(blk + 32 * FB) = t1;
               },
               [&](int cb, const Frag<E>& f) { x[(KB + cb) * 64] = f; }, none_t);
       const float dec = fast_exp2(glast);
@@ -1632,7 +1634,7 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
         for (int t = 0; t < TPW; ++t) {
           const int it = it0 + t, row = 16 * it + lc;
           const E* qr = qg + ((t0 + min(row, len - 1)) * geo.H + h) * K + 8 * g;
-          // k in natural order (see the exchange): one 16-byte load each
+          // k in natural order (see the exchange): one run of 8 elements each
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) o.q[t][kb] = *reinterpret_cast<const Frag<E>*>(qr + 32 * kb);
 #pragma unroll

@@ -26,8 +26,8 @@
  * (the layout fix of the G_T_CONTIG page, "fix: host transpose + stride-1
  * pointer", done inside the kernel instead of on the host), the sequential
  * inter-chunk state pass, and the chunk output.  For bf16 without segments
- * the output runs inside the state-pass kernel (gdn_fwd_fuses_output), so a
- * call is two kernels.  One more kernel builds the chunk map when cu_seqlens
+ * (and fp32 at K = 64 with many units) the output runs inside the state-pass
+ * kernel (gdn_fwd_fuses_output), so a call is two kernels.  One more kernel builds the chunk map when cu_seqlens
  * is given.
  *
  * Segment-parallel state pass (seg_chunks > 0).  The chunk update is affine in
@@ -233,17 +233,22 @@ gdn_status_t gdn_fwd_seg_chunks(const gdn_params_t *p, int packed, int32_t *seg_
 
 /* Whether gdn_fwd, for these parameters on the current device, runs the output
  * stage fused into the state pass (one kernel) instead of as a kernel of its
- * own.  It does so for bf16 without segments: each state-pass workgroup
+ * own.  It does so for bf16 without segments, and for fp32 with K = 64 and
+ * more units than compute units (below that, separate kernels measured
+ * faster in fp32): each state-pass workgroup
  * holds one (sequence, value head, 16-column) unit when they fit one per
  * compute unit, two beyond that (beyond twice the compute units its
  * workgroups run in several rounds).  Each chunk's start state and v_new
  * then pass from the state-pass waves to
  * the output waves of the same workgroup through LDS instead of memory, and WY
  * also emits the chunk's masked, decayed Q K^T (the intra-chunk term of the
- * output).  The results are bit-identical either way: the same products in the
- * same order and rounding.  *fused is set to 1 or 0.  No GPU work (with
- * seg_chunks = GDN_SEG_AUTO it queries the device's compute-unit count, as
- * gdn_fwd_seg_chunks does); GDN_ERR_NULL / the gdn_fwd_check shape errors. */
+ * output).  For bf16 the results are bit-identical either way: the same
+ * products in the same order and rounding.  For fp32 the final state is, while
+ * o's fp32 MFMA sums group the reduction index differently (four at a time),
+ * so o agrees up to fp32 rounding.  *fused is set to 1 or 0.  No GPU work (for fp32,
+ * and with seg_chunks = GDN_SEG_AUTO, it queries the device's compute-unit
+ * count, as gdn_fwd_seg_chunks does); GDN_ERR_NULL / the gdn_fwd_check shape
+ * errors. */
 gdn_status_t gdn_fwd_fuses_output(const gdn_params_t *p, int packed, int32_t *fused);
 
 /* Number of stages gdn_fwd_timed brackets with events: chunk map, WY (with

@@ -265,18 +265,47 @@ def test_full_size_workload(name):
     assert_metrics(m["final"], dt, "%s final (all elements)" % name)
 
 
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
-def test_many_units_fp32_state_pass(K, V):
+@pytest.mark.parametrize("K,V,packed", [(128, 128, False), (64, 128, False), (64, 64, True)])
+def test_many_units_fp32_state_pass(K, V, packed):
     """fp32 with more (sequence, head, 16-column) units than compute units on
-    the 256-CU device: not the K-split state pass, but one wave per unit (the
-    register variant at K = 128, the two-wave LDS ring at K = 64)."""
-    inp = make_inputs(B=9, T=130, H=2, HV=4, K=K, V=V, dtype=F32, seed=61 + K, h0=True)
+    the 256-CU device: not the K-split state pass.  At K = 128 one wave per
+    unit (the register variant) and the output kernel; at K = 64 a whole call
+    runs the state pass and the output fused (two value tiles per workgroup),
+    and the stages one at a time the two-wave LDS ring and the output kernel,
+    both against the oracle and each other."""
+    if packed:
+        lengths = [130, 0, 64, 1, 65, 200, 7, 128, 63, 90]   # 10 sequences
+        inp = make_inputs(B=1, T=sum(lengths), H=8, HV=16, K=K, V=V, dtype=F32, seed=62,
+                          lengths=lengths, h0=True)
+    else:
+        inp = make_inputs(B=9, T=130, H=2, HV=4, K=K, V=V, dtype=F32, seed=61 + K, h0=True)
     s = inp.shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     units = s["N"] * s["HV"] * (s["V"] // 16)
     say("case fp32_many_units", s, "units", units, "cus", cus)
     assert units > cus or cus != 256
-    check_full(inp, "fp32_many_units_K%d_V%d" % (K, V))
+    tag = "fp32_many_units_K%d_V%d%s" % (K, V, "_packed" if packed else "")
+    check_full(inp, tag)
+    d = inp.to("cuda")
+    plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
+                          num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale)
+    fused = gdn.fuses_output(plan.params, plan.packed)
+    say("  output fused into the state pass:", fused)
+    assert fused == (K == 64 and units > cus)
+    o_ref, f_ref = run_gpu(inp)
+    plan.o.fill_(float("nan"))
+    plan.final_state.fill_(float("nan"))
+    args = (d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
+    for name in gdn.STAGES:
+        plan.bind(*args, stage_mask=gdn.STAGE_BITS[name])()
+    torch.cuda.synchronize()
+    o_r, fin_r = run_oracle(inp)
+    assert_close(f64(plan.o), o_r, inp.q.dtype, tag + " stages o")
+    assert_close(f64(plan.final_state), fin_r, inp.q.dtype, tag + " stages final")
+    # the state pass is the same either way; o's fp32 MFMA sums group the
+    # reduction index differently when fused, so o agrees to fp32 rounding
+    assert np.array_equal(f64(plan.final_state), f_ref)
+    assert np.allclose(f64(plan.o), o_ref, rtol=1e-5, atol=1e-5)
 
 
 @pytest.mark.parametrize("K,V,packed,dtype", [(128, 128, False, BF), (64, 128, True, BF),
