@@ -585,8 +585,9 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
     // bf16 calls take the bf16-MFMA variant, fp32 calls the fp32 one
     if constexpr (std::is_same<E, gdn::bf16>::value)
       ok(launch(gdn::gdn_bwd_dqk_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo,
-                qe, ke, doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp),
-                F(bl.dkp), F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
+                qe, ke, doe, cmap, gam, reinterpret_cast<const gdn::bf16*>(w + bl.vnp), F(bl.dvn),
+                reinterpret_cast<const gdn::bf16*>(w + bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
+                F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
     else
       ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe,
                 ke, doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),

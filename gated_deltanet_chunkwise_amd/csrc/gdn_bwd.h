@@ -47,8 +47,10 @@
 // backward (gdn_bwd_wy_bf16_kernel: k, v exact; dw, dv_new, T, dT, Y and dS
 // rounded to bf16 once each).  The gate backward, the chunk-local reductions
 // and the sums are fp32 VALU work.  q, k, v, do are read, and dq, dk, dv
-// written, in the call's dtype.  Workspace intermediates: T, H_c, v_new and
-// the gradients below are fp32 row-major; the state pass's operands (wtf, kdf)
+// written, in the call's dtype.  Workspace intermediates: H_c and v_new are
+// row-major in the call's dtype (the recompute rounds them once; the bf16
+// MFMAs take them as stored, the dot of H_c with dH widens them to fp32); T
+// and the gradients below are fp32 row-major; the state pass's operands (wtf, kdf)
 // and the dO term bq are fragments in the call's dtype (bq is rounded to it
 // once per chunk, before the state pass adds it to the fp32 dH):
 //   hcp, dhn [hv][slot][V][K]          H_c^T, (dL/dH_{c+1})^T
@@ -851,6 +853,26 @@ __device__ __forceinline__ void stage_t(bf16* dst, const float* src) {
   }
 }
 
+// The same from a bf16 source.
+template <int SR, int SC, int DS, int THREADS>
+__device__ __forceinline__ void stage_t(bf16* dst, const bf16* src) {
+  constexpr int BC = SC / 4, NB = (SR / 4) * BC, PER = (NB + THREADS - 1) / THREADS;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int b = threadIdx.x + THREADS * it;
+    if (NB % THREADS == 0 || b < NB) {
+      const int r0 = 4 * (b / BC), c0 = 4 * (b % BC);
+      bf16x4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const bf16x4*>(src + (size_t)(r0 + j) * SC + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<bf16x4*>(dst + (c0 + j) * DS + (r0 ^ tswz(c0 + j))) =
+            bf16x4{x[0][j], x[1][j], x[2][j], x[3][j]};
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The prep kernel for bf16 calls: the products of gdn_bwd_prep_kernel on the
 // bf16 MFMA (fp32 accumulation).  q, k and do are staged exactly; P (for
@@ -1024,7 +1046,7 @@ template <int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_dqk_bf16_kernel(
     Geo geo, const bf16* __restrict__ qg, const bf16* __restrict__ kg,
     const bf16* __restrict__ dog, const int4* __restrict__ cmap, const float* __restrict__ gam,
-    const float* __restrict__ vnp, const float* __restrict__ dvn, const float* __restrict__ hcp,
+    const bf16* __restrict__ vnp, const float* __restrict__ dvn, const bf16* __restrict__ hcp,
     const float* __restrict__ dhn, float* __restrict__ dqp, float* __restrict__ dkp,
     float* __restrict__ dwp, float* __restrict__ dgp, bf16* __restrict__ dqg) {
   constexpr int SK = PadB<K>::v, SV = PadB<V>::v, SC = PadB<kChunk>::v;
@@ -1053,10 +1075,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   const size_t hs = (size_t)hv * geo.slots + slot;
   const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4);  // 64 x K ownership
   const int pit = wave >> 1, pj0 = 2 * (wave & 1);               // 64 x 64 ownership
-  const float* Hc = hcp + hs * K * V;
+  const bf16* Hc = hcp + hs * K * V;
   const float* dHn = dhn + hs * K * V;
 
-  // H_c^T and dH_{c+1}^T ([V][K] fp32) in 4 x 4 blocks: their dot in fp32;
+  // H_c^T ([V][K] bf16) and dH_{c+1}^T ([V][K] fp32) in 4 x 4 blocks: their
+  // dot in fp32;
   // H_c goes to LDS now, dH_{c+1} stays in registers (already rounded to bf16,
   // transposed) until the second staging.
   constexpr int HBC = K / 4, HNB = (V / 4) * HBC, HPER = (HNB + TH - 1) / TH;
@@ -1071,7 +1094,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
         f32x4 hc[4], dh[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          hc[j] = *reinterpret_cast<const f32x4*>(Hc + (size_t)(r0 + j) * K + c0);
+          hc[j] = to_f32x4(*reinterpret_cast<const bf16x4*>(Hc + (size_t)(r0 + j) * K + c0));
           dh[j] = *reinterpret_cast<const f32x4*>(dHn + (size_t)(r0 + j) * K + c0);
         }
 #pragma unroll

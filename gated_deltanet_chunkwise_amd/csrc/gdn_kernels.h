@@ -645,7 +645,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
 // kept).  CHAIN_MAP: u taken as 0 and no stores; started from the identity
 // (with V = K), the end state is the chunks' composed linear map M.
 // CHAIN_PLAIN: the CHAIN_FULL arithmetic, storing H_c and v_new transposed in
-// fp32 row-major layouts instead (hcf, vnf then point at float arrays
+// row-major layouts of the call's dtype instead (hcf, vnf then point at arrays
 // [hv][slot][V][K] = H_c^T and [hv][slot][V][64] = v_new^T); the backward pass
 // reads them.
 enum { CHAIN_FULL = 0, CHAIN_END = 1, CHAIN_MAP = 2, CHAIN_PLAIN = 3 };
@@ -714,7 +714,7 @@ struct ChainStep {
   }
 
   // vnew with H_c and v_new stored straight to their fragment-major arrays
-  // (CHAIN_FULL), in fp32 plain layouts (CHAIN_PLAIN), or not stored at all
+  // (CHAIN_FULL), in plain layouts (CHAIN_PLAIN), or not stored at all
   // (the other modes).
   __device__ __forceinline__ void vnew_global(const f32x4 (&Hs)[KT], Frag<E> (&vb)[2],
                                               Frag<E>* __restrict__ hcf, Frag<E>* __restrict__ vnf,
@@ -730,13 +730,13 @@ struct ChainStep {
       // D tile element r of lane (lc, g) is row 4g + r of the tile, column lc:
       // four consecutive elements of row v of the transposed layouts.
       const int g = lane >> 4, v = 16 * vt + (lane & 15);
-      f32x4* hp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hcf) + hs * K * V + (size_t)v * K + 4 * g);
+      Quad<E>* hp = reinterpret_cast<Quad<E>*>(reinterpret_cast<E*>(hcf) + hs * K * V + (size_t)v * K + 4 * g);
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = Hs[mt];
-      f32x4* vp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(vnf) + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
+      for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = make_quad<E>(Hs[mt]);
+      Quad<E>* vp = reinterpret_cast<Quad<E>*>(reinterpret_cast<E*>(vnf) + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
       vnew(Hs, vb, none_f, none_f, [&](int cb, const f32x4& d0, const f32x4& d1) {
-        vp[8 * cb] = d0;
-        vp[8 * cb + 4] = d1;
+        vp[8 * cb] = make_quad<E>(d0);
+        vp[8 * cb + 4] = make_quad<E>(d1);
       });
     } else {
       vnew(Hs, vb, none_f, none_f, none_t);
