@@ -526,6 +526,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   int* seq_slot = VARLEN ? reinterpret_cast<int*>(w + L.seq_slot) : nullptr;
   int* seq_order = VARLEN ? reinterpret_cast<int*>(w + L.seq_order) : nullptr;
   auto FE = [&](size_t off) { return reinterpret_cast<Frag<E>*>(w + off); };
+  auto EP = [&](size_t off) { return reinterpret_cast<E*>(w + off); };
   const E* qe = static_cast<const E*>(a.q);
   const E* ke = static_cast<const E*>(a.k);
   const E* ve = static_cast<const E*>(a.v);
@@ -546,7 +547,7 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
               cmap, seq_slot, seq_order));
   if (chunk_wgs > 0)
     ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, true>, dim3(chunk_wgs), dim3(gdn::kWyThreads), s, geo, ke, ve,
-              a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, F(bl.tmat),
+              a.g_raw, a.beta, a.A_log, a.dt_bias, cmap, gam, bet, wf, ktf, uf, EP(bl.tmat),
               nullptr, nullptr));
   if (units > 0 && geo.slots > 0)
     ok(launch_chain<E, K, V, VARLEN, gdn::CHAIN_PLAIN>(
@@ -574,20 +575,19 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
     ok(launch(gdn::gdn_bwd_chain_ks_kernel<E, K, V, VARLEN, 2>, dim3(units), dim3(64 * (K / 32)), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
               reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, seq_order, a.dht, a.dh0,
-              F(bl.dhn), F(bl.dvn)));
+              EP(bl.dhn), EP(bl.dvn)));
   else if (units > 0)
     ok(launch(gdn::gdn_bwd_chain_kernel<E, K, V, VARLEN>, dim3(units), dim3(64), s, geo,
               FE(bl.kdf), reinterpret_cast<const gdn::f32x4*>(w + bl.dvl), FE(bl.wtf),
               reinterpret_cast<const gdn::Quad<E>*>(w + bl.bq), gam, seq_slot, a.dht, a.dh0,
-              F(bl.dhn), F(bl.dvn)));
+              EP(bl.dhn), EP(bl.dvn)));
   mark(3);
   if (chunk_wgs > 0) {
     // bf16 calls take the bf16-MFMA variant, fp32 calls the fp32 one
     if constexpr (std::is_same<E, gdn::bf16>::value)
       ok(launch(gdn::gdn_bwd_dqk_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo,
-                qe, ke, doe, cmap, gam, reinterpret_cast<const gdn::bf16*>(w + bl.vnp), F(bl.dvn),
-                reinterpret_cast<const gdn::bf16*>(w + bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
-                F(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
+                qe, ke, doe, cmap, gam, EP(bl.vnp), EP(bl.dvn), EP(bl.hcp), EP(bl.dhn), F(bl.dqp),
+                F(bl.dkp), EP(bl.dwp), F(bl.dgp), static_cast<E*>(a.dq)));
     else
       ok(launch(gdn::gdn_bwd_dqk_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, qe,
                 ke, doe, cmap, gam, F(bl.vnp), F(bl.dvn), F(bl.hcp), F(bl.dhn), F(bl.dqp), F(bl.dkp),
@@ -597,8 +597,8 @@ gdn_status_t run_bwd(const Plan& pl, const BwdLayout& bl, const BwdArgs& a, void
   if (chunk_wgs > 0) {
     if constexpr (std::is_same<E, gdn::bf16>::value)
       ok(launch(gdn::gdn_bwd_wy_bf16_kernel<K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s,
-                geo, ke, ve, a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, F(bl.tmat), F(bl.dwp),
-                F(bl.dvn), F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw,
+                geo, ke, ve, a.g_raw, a.A_log, a.dt_bias, cmap, gam, bet, EP(bl.tmat), EP(bl.dwp),
+                EP(bl.dvn), F(bl.dgp), F(bl.dkp), static_cast<E*>(a.dv), a.dbeta, a.dg_raw,
                 F(bl.dAp), F(bl.dbp), static_cast<E*>(a.dk)));
     else
       ok(launch(gdn::gdn_bwd_wy_kernel<E, K, V, VARLEN>, dim3(chunk_wgs), dim3(gdn::kBwdThreads), s, geo, ke,

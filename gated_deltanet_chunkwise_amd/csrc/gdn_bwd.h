@@ -47,10 +47,11 @@
 // backward (gdn_bwd_wy_bf16_kernel: k, v exact; dw, dv_new, T, dT, Y and dS
 // rounded to bf16 once each).  The gate backward, the chunk-local reductions
 // and the sums are fp32 VALU work.  q, k, v, do are read, and dq, dk, dv
-// written, in the call's dtype.  Workspace intermediates: H_c and v_new are
-// row-major in the call's dtype (the recompute rounds them once; the bf16
-// MFMAs take them as stored, the dot of H_c with dH widens them to fp32); T
-// and the gradients below are fp32 row-major; the state pass's operands (wtf, kdf)
+// written, in the call's dtype.  Workspace intermediates: T, H_c, v_new, dH,
+// dv_new and dw are row-major in the call's dtype (rounded once when stored;
+// the bf16 MFMAs take them as stored, the dot of H_c with dH widens them to
+// fp32); dq, dk partials and the per-chunk sums are fp32 row-major; the state
+// pass's operands (wtf, kdf)
 // and the dO term bq are fragments in the call's dtype (bq is rounded to it
 // once per chunk, before the state pass adds it to the fp32 dH):
 //   hcp, dhn [hv][slot][V][K]          H_c^T, (dL/dH_{c+1})^T
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
     Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
     const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const float* __restrict__ dht, float* __restrict__ dh0,
-    float* __restrict__ dhn, float* __restrict__ dvn) {
+    E* __restrict__ dhn, E* __restrict__ dvn) {
   constexpr int NV = V / 16, KT = K / 16, KB = K / 32;
   int hv, rest;
   head_major_block(blockIdx.x, geo.HV, geo.N * NV, hv, rest);
@@ -393,9 +394,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
   for (int s = s1 - 1; s >= s0; --s) {
     const size_t hs = hbase + s, nxt = hbase + (s > s0 ? s - 1 : s0);  // in bounds
     // transposed: lane (v, g) holds rows 4g..4g+3 of each tile, contiguous in dH^T
-    f32x4* hp = reinterpret_cast<f32x4*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
+    Quad<E>* hp = reinterpret_cast<Quad<E>*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = dH[mt];
+    for (int mt = 0; mt < KT; ++mt) hp[4 * mt] = make_quad<E>(dH[mt]);
     Frag<E> hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) hb[kb] = frag_from_tiles<E>(dH[2 * kb], dH[2 * kb + 1]);
@@ -409,9 +410,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_chain_kernel(
     asm volatile("" ::: "memory");
     load_a(nxt);
     asm volatile("" ::: "memory");
-    f32x4* vp = reinterpret_cast<f32x4*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
+    Quad<E>* vp = reinterpret_cast<Quad<E>*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) vp[4 * ct] = dv[ct];
+    for (int ct = 0; ct < 4; ++ct) vp[4 * ct] = make_quad<E>(dv[ct]);
     const Frag<E> nb[2] = {frag_from_tiles<E>(-dv[0], -dv[1]), frag_from_tiles<E>(-dv[2], -dv[3])};
     const float dec = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kChunk - 1)));
 #pragma unroll
@@ -478,7 +479,7 @@ __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const
                                                   const Frag<E>* __restrict__ wtf,
                                                   const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
                                                   const float* __restrict__ dht, float* __restrict__ dh0,
-                                                  float* __restrict__ dhn, float* __restrict__ dvn, int s0,
+                                                  E* __restrict__ dhn, E* __restrict__ dvn, int s0,
                                                   int s1, size_t hbase, size_t sbase, int vt) {
   using Step = BwdKsStep<E, K, V>;
   constexpr int KB = Step::KB, OWN = Step::OWN;
@@ -492,9 +493,9 @@ __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const
 
   auto chunk = [&](const Step& S, size_t hs) {
     // transposed: lane (v, g) holds rows 4g..4g+3 of each tile, contiguous in dH^T
-    f32x4* hp = reinterpret_cast<f32x4*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
-    hp[4 * (2 * Q)] = dH[0];
-    hp[4 * (2 * Q + 1)] = dH[1];
+    Quad<E>* hp = reinterpret_cast<Quad<E>*>(dhn + hs * K * V + (size_t)v * K + 4 * g);
+    hp[4 * (2 * Q)] = make_quad<E>(dH[0]);
+    hp[4 * (2 * Q + 1)] = make_quad<E>(dH[1]);
     const Frag<E> hb = frag_from_tiles<E>(dH[0], dH[1]);
     f32x4 p[4];
 #pragma unroll
@@ -508,7 +509,7 @@ __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const
     wait_lgkm0();
     ring_barrier();
     Quad<E> own[OWN];
-    f32x4* vp = reinterpret_cast<f32x4*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
+    Quad<E>* vp = reinterpret_cast<Quad<E>*>(dvn + hs * kChunk * V + (size_t)v * kChunk + 4 * g);
 #pragma unroll
     for (int j = 0; j < OWN; ++j) {
       const int ct = Q + KB * j;
@@ -516,7 +517,7 @@ __device__ __forceinline__ void bwd_chain_ks_wave(ChainKsLds<E, K, V>& sh, const
 #pragma unroll
       for (int w2 = 1; w2 < KB; ++w2) acc += (w2 == Q ? p[ct] : sh.part[w2][ct][lane]);
       const f32x4 dv = S.dl[j] + acc;
-      vp[4 * ct] = dv;
+      vp[4 * ct] = make_quad<E>(dv);
       own[j] = make_quad<E>(-dv);
       sh.vx[ct][lane] = own[j];
     }
@@ -567,8 +568,8 @@ __global__ __launch_bounds__(64 * (K / 32)) void gdn_bwd_chain_ks_kernel(
     Geo geo, const Frag<E>* __restrict__ kdf, const f32x4* __restrict__ dvl,
     const Frag<E>* __restrict__ wtf, const Quad<E>* __restrict__ bq, const float* __restrict__ gam,
     const int* __restrict__ seq_slot, const int* __restrict__ seq_order,
-    const float* __restrict__ dht, float* __restrict__ dh0, float* __restrict__ dhn,
-    float* __restrict__ dvn) {
+    const float* __restrict__ dht, float* __restrict__ dh0, E* __restrict__ dhn,
+    E* __restrict__ dvn) {
   static_assert(K == 64 || K == 128, "two or four waves");
   constexpr int NV = V / 16;
   __shared__ ChainKsLds<E, K, V> sh;
@@ -1046,9 +1047,9 @@ template <int K, int V, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_bwd_dqk_bf16_kernel(
     Geo geo, const bf16* __restrict__ qg, const bf16* __restrict__ kg,
     const bf16* __restrict__ dog, const int4* __restrict__ cmap, const float* __restrict__ gam,
-    const bf16* __restrict__ vnp, const float* __restrict__ dvn, const bf16* __restrict__ hcp,
-    const float* __restrict__ dhn, float* __restrict__ dqp, float* __restrict__ dkp,
-    float* __restrict__ dwp, float* __restrict__ dgp, bf16* __restrict__ dqg) {
+    const bf16* __restrict__ vnp, const bf16* __restrict__ dvn, const bf16* __restrict__ hcp,
+    const bf16* __restrict__ dhn, float* __restrict__ dqp, float* __restrict__ dkp,
+    bf16* __restrict__ dwp, float* __restrict__ dgp, bf16* __restrict__ dqg) {
   constexpr int SK = PadB<K>::v, SV = PadB<V>::v, SC = PadB<kChunk>::v;
   constexpr int NKT = K / 64, TH = kBwdThreads;
   constexpr int P12 = 2 * kChunk * SV + K * SV, P3 = 2 * kChunk * SK + 2 * K * SC;
@@ -1076,10 +1077,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4);  // 64 x K ownership
   const int pit = wave >> 1, pj0 = 2 * (wave & 1);               // 64 x 64 ownership
   const bf16* Hc = hcp + hs * K * V;
-  const float* dHn = dhn + hs * K * V;
+  const bf16* dHn = dhn + hs * K * V;
 
-  // H_c^T ([V][K] bf16) and dH_{c+1}^T ([V][K] fp32) in 4 x 4 blocks: their
-  // dot in fp32;
+  // H_c^T and dH_{c+1}^T ([V][K] bf16) in 4 x 4 blocks: their dot in fp32;
   // H_c goes to LDS now, dH_{c+1} stays in registers (already rounded to bf16,
   // transposed) until the second staging.
   constexpr int HBC = K / 4, HNB = (V / 4) * HBC, HPER = (HNB + TH - 1) / TH;
@@ -1095,7 +1095,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           hc[j] = to_f32x4(*reinterpret_cast<const bf16x4*>(Hc + (size_t)(r0 + j) * K + c0));
-          dh[j] = *reinterpret_cast<const f32x4*>(dHn + (size_t)(r0 + j) * K + c0);
+          dh[j] = to_f32x4(*reinterpret_cast<const bf16x4*>(dHn + (size_t)(r0 + j) * K + c0));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1152,7 +1152,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
     // (lane base + constant offsets: no per-store 64-bit address arithmetic)
-    float* const dwl = dwp + (hs * kChunk + 16 * rt0 + 4 * g) * K + kc0 + lc;
+    bf16* const dwl = dwp + (hs * kChunk + 16 * rt0 + 4 * g) * K + kc0 + lc;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -1161,7 +1161,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int nt = 0; nt < NKT; ++nt) {
           dq[a][nt][r] *= e;
-          dwl[(16 * a + r) * K + 16 * nt] = -dw[a][nt][r];
+          dwl[(16 * a + r) * K + 16 * nt] = (bf16)(-dw[a][nt][r]);
         }
       }
     // scaled here, not deferred to the end (which would keep the factors live)
@@ -1619,8 +1619,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
     Geo geo, const bf16* __restrict__ kg, const bf16* __restrict__ vg,
     const float* __restrict__ g_raw, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const int4* __restrict__ cmap,
-    const float* __restrict__ gam, const float* __restrict__ bet, const float* __restrict__ tmat,
-    const float* __restrict__ dwp, const float* __restrict__ dvn, const float* __restrict__ dgp,
+    const float* __restrict__ gam, const float* __restrict__ bet, const bf16* __restrict__ tmat,
+    const bf16* __restrict__ dwp, const bf16* __restrict__ dvn, const float* __restrict__ dgp,
     float* __restrict__ dkp, bf16* __restrict__ dvg, float* __restrict__ dbeta,
     float* __restrict__ dg_raw, float* __restrict__ dAp, float* __restrict__ dbp,
     bf16* __restrict__ dkg) {
@@ -1667,13 +1667,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4), vc0 = (wave & 3) * (V / 4);
   const int pit = wave >> 1, pj0 = 2 * (wave & 1);
 
-  // dw [64][K], dv_new^T [V][64] and T [64][64] (fp32) into registers as bf16,
+  // dw [64][K], dv_new^T [V][64] and T [64][64] (bf16) into registers,
   // 4 x 4 blocks per thread: row j of block b is w[b][j].
   using BW = Blk4<kChunk, K>;
   using BD = Blk4<V, kChunk>;
   using BT = Blk4<kChunk, kChunk>;
   bf16x4 wr[BW::PER][4], dr[BD::PER][4], tr[BT::PER][4];
-  auto fetch = [&](auto B, bf16x4 (&dst)[decltype(B)::PER][4], const float* src, int C) {
+  auto fetch = [&](auto B, bf16x4 (&dst)[decltype(B)::PER][4], const bf16* src, int C) {
     using Bk = decltype(B);
 #pragma unroll
     for (int it = 0; it < Bk::PER; ++it) {
@@ -1682,7 +1682,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
         const int r0 = 4 * (b / Bk::BC), c0 = 4 * (b % Bk::BC);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          dst[it][j] = to_bf16x4(*reinterpret_cast<const f32x4*>(src + (size_t)(r0 + j) * C + c0));
+          dst[it][j] = *reinterpret_cast<const bf16x4*>(src + (size_t)(r0 + j) * C + c0);
       }
     }
   };

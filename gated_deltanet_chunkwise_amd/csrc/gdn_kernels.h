@@ -224,8 +224,8 @@ __device__ __forceinline__ Frag<E> frag_from_trow(const E* tile, int row, int st
 // Eight waves per WY workgroup.
 constexpr int kWyThreads = 512;
 
-// With STORE_T, T itself (lower triangular, fp32, [hv][slot][64][64] row-major,
-// zeros above the diagonal) is also written to tmat, for the backward pass.
+// With STORE_T, T itself (lower triangular, in the call's dtype, [hv][slot][64][64]
+// row-major, zeros above the diagonal) is also written to tmat, for the backward pass.
 //
 // With EMIT_P the workgroup also forms the chunk's intra-chunk output matrix
 // P^T = (K Q^T) * [j <= i] * e^{G_i - G_j} (rows j: keys, columns i: queries;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
                                                      Frag<E>* __restrict__ wf,
                                                      Frag<E>* __restrict__ ktf,
                                                      Quad<E>* __restrict__ uf,
-                                                     float* __restrict__ tmat,
+                                                     E* __restrict__ tmat,
                                                      const E* __restrict__ qg,
                                                      Frag<E>* __restrict__ pf) {
   static_assert(!EMIT_P || wy_q_fits<E, K>(), "Q rows must fit the LDS of T");
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       // blocks right of the diagonal block were never written
       const f32x4 x = (j >> 4) <= (i >> 4) ? *reinterpret_cast<const f32x4*>(Ts + i * FS + j) : zero;
-      *reinterpret_cast<f32x4*>(tmat + hs * kChunk * kChunk + i * kChunk + j) = x;
+      *reinterpret_cast<Quad<E>*>(tmat + hs * kChunk * kChunk + i * kChunk + j) = make_quad<E>(x);
     }
   }
 
