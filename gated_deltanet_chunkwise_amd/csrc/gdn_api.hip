@@ -436,7 +436,7 @@ gdn_status_t run_e(const Plan& pl, const void* q, const void* k, const void* v, 
 namespace {
 
 // Workspace of the backward pass: the forward layout (without segments), then
-// the backward's fp32 intermediates (see gdn_bwd.h).
+// the backward's intermediates (see gdn_bwd.h for each one's type).
 struct BwdLayout {
   size_t tmat, hcp, vnp, wtf, kdf, bq, dvl, dhn, dvn, dqp, dkp, dwp, dgp, dAp, dbp, total;
 };
@@ -451,22 +451,26 @@ gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayo
   if ((int64_t)pl->geo.slots * p->H * (gdn::kChunk * p->K / 1024) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   const size_t hsl = (size_t)p->HV * (size_t)pl->geo.slots, C = gdn::kChunk, K = p->K, V = p->V;
   size_t off = pl->lay.total;
-  auto take = [&](size_t& field, size_t floats) {
+  const size_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+  auto take_n = [&](size_t& field, size_t n, size_t bytes) {
     field = off;
-    off = align_up(off + hsl * floats * 4);
+    off = align_up(off + hsl * n * bytes);
   };
-  take(bl->tmat, C * C);
-  take(bl->hcp, K * V);
-  take(bl->vnp, C * V);
+  auto take = [&](size_t& field, size_t floats) { take_n(field, floats, 4); };
+  // in the call's dtype: T, H_c, v_new, dH, dv_new, dw (see gdn_bwd.h)
+  auto take_e = [&](size_t& field, size_t elems) { take_n(field, elems, esz); };
+  take_e(bl->tmat, C * C);
+  take_e(bl->hcp, K * V);
+  take_e(bl->vnp, C * V);
   take(bl->wtf, K * C);  // fp32 size: also holds the dtype's fragments
   take(bl->kdf, C * K);
   take(bl->bq, K * V);
   take(bl->dvl, C * V);
-  take(bl->dhn, K * V);
-  take(bl->dvn, C * V);
+  take_e(bl->dhn, K * V);
+  take_e(bl->dvn, C * V);
   take(bl->dqp, C * K);
   take(bl->dkp, C * K);
-  take(bl->dwp, C * K);
+  take_e(bl->dwp, C * K);
   take(bl->dgp, C);
   take(bl->dAp, 1);
   take(bl->dbp, 1);
