@@ -170,7 +170,9 @@ def algorithmic(shape, esz, has_h0, used_slots, fused=False):
 def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
     """Algorithmic bytes and flops per launch of each backward stage (the
     forward-recompute stage is two kernels, WY and the state pass), and of the
-    whole pass.  fp32 intermediates count at 4 bytes; triangular products by
+    whole pass.  Each intermediate counts at its stored width: T, H_c, v_new,
+    dH, dv_new, dw and the dO term bq in the call's dtype (esz), dv_local, the
+    dq / dk partials and the per-chunk sums in fp32; triangular products by
     their nonzero half."""
     B, T, H, HV, K, V, N = (shape[k] for k in ("B", "T", "H", "HV", "K", "V", "N"))
     ntok = T if shape.get("packed") else B * T
@@ -179,25 +181,33 @@ def algorithmic_bwd(shape, esz, has_h0, has_dht, used_slots):
     state = N * HV * K * V * 4
     C = CHUNK
     k_in = ntok * H * K * esz
+    kv = Ck * K * V * esz          # one K x V per chunk and value head (H_c, dH, bq)
+    tv = U * V * esz               # one V per token and value head (v_new, dv_new)
     fwd, _, _ = algorithmic(shape, esz, has_h0, used_slots)
+    dq_out = U * K * (esz if HV == H else 4)  # dq (or dk): dtype, else fp32 partials
     kern = {
+        # WY storing T, then the state pass storing H_c and v_new
         "recompute": dict(
-            bytes=fwd["wy"]["bytes"] + Ck * C * C * 4 + U * (2 * K + V) * esz + Ck * 4
-            + (state if has_h0 else 0) + Ck * K * V * 4 + U * V * 4,
+            bytes=fwd["wy"]["bytes"] + Ck * C * C * esz + U * (2 * K + V) * esz + Ck * 4
+            + (state if has_h0 else 0) + kv + tv,
             flops=fwd["wy"]["flops"] + U * 4 * K * V),
+        # q, k, do, gates, w in; kd, w^T fragments, bq and dv_local (fp32) out
         "prep": dict(bytes=2 * k_in + U * V * esz + U * 4 + U * K * esz + 2 * U * K * esz
-                     + Ck * K * V * 4 + U * V * 4,
+                     + kv + U * V * 4,
                      flops=U * C * (K + V) + U * 2 * K * V),
-        "bwd_chain": dict(bytes=2 * U * K * esz + Ck * K * V * 4 + U * V * 4 + Ck * 4
-                          + (state if has_dht else 0) + Ck * K * V * 4 + U * V * 4 + state,
+        # kd, w^T, bq, dv_local, gates in; dH, dv_new and dh0 out
+        "bwd_chain": dict(bytes=2 * U * K * esz + kv + U * V * 4 + Ck * 4
+                          + (state if has_dht else 0) + kv + tv + state,
                           flops=U * 4 * K * V),
-        # with one value head per key head dq and dk are written at the dtype by
-        # these two kernels, else as fp32 partials per value head
-        "dqk": dict(bytes=2 * k_in + U * V * esz + 2 * U * V * 4 + 2 * Ck * K * V * 4 + U * 4
-                    + U * K * (esz if HV == H else 4) + 2 * U * K * 4 + U * 4,
+        # q, k, do, v_new, dv_new, H_c, dH, gates in; dq, dk partial (fp32),
+        # dw, dG out
+        "dqk": dict(bytes=2 * k_in + U * V * esz + 2 * tv + 2 * kv + U * 4
+                    + dq_out + U * K * 4 + U * K * esz + U * 4,
                     flops=U * (6 * K * V + C * V + 3 * C * K)),
-        "bwd_wy": dict(bytes=k_in + U * V * esz + 2 * U * K * 4 + U * V * 4 + Ck * C * C * 4
-                       + 4 * U * 4 + U * K * (esz if HV == H else 4) + U * V * esz + 2 * U * 4
+        # k, v, dw, dk partial, dv_new, T, gates in; dk, dv, dbeta, dg_raw and
+        # the per-chunk sums out
+        "bwd_wy": dict(bytes=k_in + U * V * esz + U * K * esz + U * K * 4 + tv + Ck * C * C * esz
+                       + 4 * U * 4 + dq_out + U * V * esz + 2 * U * 4
                        + 2 * Ck * 4,
                        flops=U * (2 * C * (K + V) + 2 * C * C // 3 + 3 * C * K)),
         # per-head parameter sums, plus the key-head dq/dk sums when value heads
