@@ -217,7 +217,7 @@ hipError_t launch_chain(const gdn::Geo& geo, hipStream_t s, const gdn::Frag<E>* 
       return launch(gdn::gdn_chain_ring_kernel<E, K, V, VARLEN, 1, MODE>, dim3(units),
                     dim3(64 * gdn::RingCfg<E, K, V, 1>::WAVES), s, geo, wf, ktf, uf, gam, seq_slot,
                     seq_order, h0, fin, hcf, vnf);
-    // CHAIN_PLAIN (the backward's recompute, fp32 stores) keeps the ring at
+    // CHAIN_PLAIN (the backward's recompute, row-major stores) keeps the ring at
     // any unit count, its workgroups then in rounds.  Measured on MI355X at
     // 12 packed sequences, T=32768, H=16 (1536 units): recompute 616 -> 535 us
     // against the register variant.
