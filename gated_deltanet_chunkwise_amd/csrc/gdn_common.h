@@ -177,6 +177,25 @@ __device__ __forceinline__ void head_major_block(int b, int HV, int per_head, in
   }
 }
 
+// Block id -> (value head, index within the head) like head_major_block, but
+// with the XCD chosen by key head: with H a multiple of 8, key head h's value
+// heads (hv = h G .. h G + G - 1) all go to XCD h % 8, so the query rows they
+// share come through one L2.  With one value head per key head it is
+// head_major_block's mapping.  A bijection of [0, H G per_head).
+__device__ __forceinline__ void key_head_major_block(int b, int H, int G, int per_head, int& hv,
+                                                     int& rest) {
+  if ((H & 7) == 0) {
+    const int x = b & 7, j = b >> 3;
+    const int kl = j / (G * per_head), r2 = j - kl * (G * per_head);
+    const int r = r2 / per_head;
+    rest = r2 - r * per_head;
+    hv = (x + 8 * kl) * G + r;
+  } else {
+    hv = b / per_head;
+    rest = b - hv * per_head;
+  }
+}
+
 // Block id -> (value head, sequence rank r, group of value tiles vp) for a
 // state pass over packed sequences whose workgroups do not all fit on the
 // device at once: rank-major, so the workgroups of the sequence of rank 0 (the

@@ -1514,8 +1514,9 @@ __global__ __launch_bounds__((64 * ChainOutCfg<E, K, V, NC>::WAVES)) void gdn_ch
     rank_major_block(blockIdx.x, geo.HV, NV / NC, hv, r, vp);
     n = seq_order[r];
   } else {
+    // a key head's value heads on one XCD: their output waves read the same q rows
     int rest;
-    head_major_block(blockIdx.x, geo.HV, geo.N * (NV / NC), hv, rest);
+    key_head_major_block(blockIdx.x, geo.H, geo.G, geo.N * (NV / NC), hv, rest);
     n = rest / (NV / NC);
     vp = rest - n * (NV / NC);
   }
