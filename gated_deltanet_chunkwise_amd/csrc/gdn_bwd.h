@@ -79,6 +79,10 @@ namespace gdn {
 template <int N> struct Pad { static constexpr int v = N + 4; };
 constexpr int kCP = kChunk + 4;  // stride of 64-column fp32 tiles
 
+// The per-chunk backward kernels (prep, dq/dk, WY backward) map block ids to
+// (value head, chunk slot) as WY does (xcd_slot_block): a key head's value
+// heads on one XCD, slot-major there, so the q / k rows they share come
+// through one L2 at about the same time.
 // The per-chunk backward kernels run eight waves per workgroup (two per SIMD,
 // so one wave's LDS waits overlap the other's MFMAs).  A 64 x N result (N = K
 // or V) is split in row halves x column quarters: wave w owns row tiles
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_prep_kernel(
   __shared__ float sg[kChunk];
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
@@ -633,7 +637,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_dqk_kernel(
   float* const Pd = lds + 2 * kChunk * KP;
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
@@ -905,7 +909,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   bf16* const Dst = Dt + V * SC;
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
@@ -1067,7 +1071,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   bf16* const Pt = Ks;
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   int n, len;
   int64_t t0;
   if (!chunk_of_slot<VARLEN>(geo, cmap, slot, n, t0, len)) return;
@@ -1377,7 +1381,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_wy_kernel(
   float* const Ys = Dv;
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   const size_t hs = (size_t)hv * geo.slots + slot;
   int n, len;
   int64_t t0;
@@ -1651,7 +1655,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   bf16* const St = Sn + kChunk * SC;        // 5: dS^T (t-w)
 
   int hv, slot;
-  head_major_block(blockIdx.x, geo.HV, geo.slots, hv, slot);
+  xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
   const size_t hs = (size_t)hv * geo.slots + slot;
   int n, len;
   int64_t t0;
