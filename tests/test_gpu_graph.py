@@ -50,7 +50,7 @@ def refill(dst, src):
 
 
 FWD = {
-    # ring state pass and separate output kernel, h0, GQA
+    # output inside the state pass, one value tile per workgroup, h0, GQA
     "fixed_bf16": dict(B=2, T=300, H=2, HV=4, K=128, V=128, dtype="bf16", h0=True),
     # K split over waves, fp32
     "fixed_fp32_k64": dict(B=1, T=200, H=2, HV=2, K=64, V=64, dtype="fp32", h0=True),
@@ -59,8 +59,11 @@ FWD = {
                         lengths=[1, 63, 64, 65, 130, 0, 200, 3]),
     # output inside the state pass (units between one and two per CU)
     "fused_bf16": dict(B=5, T=300, H=4, HV=8, K=128, V=128, dtype="bf16", h0=True),
-    # one output workgroup for both value heads of a key head (2048 workgroups)
-    "shared_key_head_bf16": dict(B=1, T=8192, H=8, HV=16, K=128, V=128, dtype="bf16"),
+    # fp32 at K = 128 (never fused): the state pass, then one output workgroup
+    # for both value heads of a key head (2048 workgroups)
+    "shared_key_head_fp32": dict(B=1, T=8192, H=8, HV=16, K=128, V=128, dtype="fp32"),
+    # fp32 at K = 64 beyond one unit per CU: output inside the state pass
+    "fused_fp32_k64": dict(B=3, T=300, H=16, HV=32, K=64, V=64, dtype="fp32", h0=True),
 }
 
 
@@ -85,6 +88,12 @@ def _check_forward_replays(case, seg_chunks=0):
     say("case graph fwd", case, s, "seg_chunks", seg_chunks)
     g_plan = _fwd_plan(s, d.q.dtype, packed, d.scale, seg_chunks)
     e_plan = _fwd_plan(s, d.q.dtype, packed, d.scale, seg_chunks)
+    fused = gdn.fuses_output(g_plan.params, packed)
+    say("  output fused into the state pass:", fused)
+    if case.startswith("fused") and seg_chunks == 0:
+        assert fused
+    if case == "shared_key_head_fp32":
+        assert not fused
     args = (d.q, d.k, d.v, d.g_raw, d.beta, d.A_log, d.dt_bias, d.cu_seqlens, d.h0)
     graph = capture(lambda st: g_plan.bind(*args, stream=st))
     for r in range(REPLAYS):

@@ -65,6 +65,8 @@ CASES = {
                             lengths=[70, 0, 129, 64]),
     # output fused into the state pass (units between one and two per CU)
     "fused_bf16": dict(B=5, T=300, H=4, HV=8, K=128, V=128, dtype="bf16", seed=73, h0=True),
+    # fp32 fused (K = 64, beyond one unit per CU)
+    "fused_fp32_k64": dict(B=3, T=300, H=16, HV=32, K=64, V=64, dtype="fp32", seed=74, h0=True),
 }
 
 
