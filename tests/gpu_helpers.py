@@ -23,13 +23,14 @@ def f64(t):
     return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, plan_out=None, ws_fill=None):
+def run_gpu(inp, plan_out=None, ws_fill=None, seg_chunks=0):
     """Run the library on `inp` (CPU GdnInputs); returns (o, final) as fp64 numpy.
     ws_fill: a byte value the workspace is filled with first."""
     d = inp.to("cuda")
     s = inp.shape
     plan = gdn.GdnForward(s["B"], s["T"], s["H"], s["HV"], s["K"], s["V"], d.q.dtype, d.q.device,
-                          num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale)
+                          num_seqs=None if d.cu_seqlens is None else s["N"], scale=d.scale,
+                          seg_chunks=seg_chunks)
     # NaN-fill the outputs so that any element the kernels fail to write shows up
     plan.o.fill_(float("nan"))
     plan.final_state.fill_(float("nan"))

@@ -313,10 +313,12 @@ def test_many_units_fp32_state_pass(K, V, packed):
                                                (128, 128, True, F32)])
 def test_shared_key_head_workgroups(K, V, packed, dtype):
     """Two value heads per key head and enough (chunk, value head) workgroups
-    to fill the 256-CU device eight times over: the output stage runs one
-    workgroup per (chunk, key head) for both of its value heads (the key
-    head's Q and K loads and its Q K^T shared).  Ragged tails, an empty
-    sequence and one shorter than a chunk."""
+    to fill the 256-CU device eight times over: where the output stage runs as
+    a kernel of its own (these fp32 shapes; bf16 with segments, since a whole
+    bf16 call fuses it into the state pass) it runs one workgroup per (chunk,
+    key head) for both of its value heads (the key head's Q and K loads and
+    its Q K^T shared).  Ragged tails, an empty sequence and one shorter than a
+    chunk."""
     if packed:
         lengths = [4100, 1, 0, 64, 3999, 129]
         inp = make_inputs(B=1, T=sum(lengths), H=8, HV=16, K=K, V=V, dtype=dtype, seed=91 + K + V,
@@ -330,4 +332,14 @@ def test_shared_key_head_workgroups(K, V, packed, dtype):
     wgs = plan.layout.num_slots * s["HV"]
     say("case shared_key_head", s, "workgroups", wgs, "cus", cus)
     assert wgs >= 8 * cus or cus != 256
-    check_full(inp, "shared_kh_%s_K%d_V%d%s" % (dtype, K, V, "_packed" if packed else ""))
+    tag = "shared_kh_%s_K%d_V%d%s" % (dtype, K, V, "_packed" if packed else "")
+    o_r, fin_r = run_oracle(inp)
+    o, fin = run_gpu(inp)
+    assert_close(o, o_r, inp.q.dtype, tag + " o")
+    assert_close(fin, fin_r, inp.q.dtype, tag + " final")
+    if gdn.fuses_output(plan.params, packed):
+        # the whole call fuses the output into the state pass; with segments
+        # the separate output kernel runs, a workgroup per (chunk, key head)
+        o, fin = run_gpu(inp, seg_chunks=16)
+        assert_close(o, o_r, inp.q.dtype, tag + " segments o")
+        assert_close(fin, fin_r, inp.q.dtype, tag + " segments final")
