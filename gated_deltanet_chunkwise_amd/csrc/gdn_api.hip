@@ -339,9 +339,15 @@ gdn_status_t run(const Plan& pl, const void* q, const void* k, const void* v, co
     bool done = false;
     if constexpr (gdn::ChainOutCfg<E, K, V, 2>::FITS) {
       if (fused) {
-        ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, false, true>, dim3(geo.slots * geo.HV),
-                  dim3(gdn::kWyThreads), s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam,
-                  bet, wf, ktf, uf, nullptr, qe, pmf));
+        // all workgroups resident at two per CU: the LDS-rich split variant
+        if ((int64_t)geo.slots * geo.HV <= 2 * (int64_t)device_cus())
+          ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, false, true, true>, dim3(geo.slots * geo.HV),
+                    dim3(gdn::kWyThreads), s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam,
+                    bet, wf, ktf, uf, nullptr, qe, pmf));
+        else
+          ok(launch(gdn::gdn_wy_kernel<E, K, V, VARLEN, false, true>, dim3(geo.slots * geo.HV),
+                    dim3(gdn::kWyThreads), s, geo, ke, ve, g_raw, beta, A_log, dt_bias, cmap, gam,
+                    bet, wf, ktf, uf, nullptr, qe, pmf));
         done = true;
       }
     }

@@ -270,7 +270,13 @@ constexpr bool wy_q_fits() {
   return kChunk * (K + 16 / (int)sizeof(E)) * (int)sizeof(E) <= kChunk * (kChunk + 4) * 4;
 }
 
-template <typename E, int K, int V, bool VARLEN, bool STORE_T = false, bool EMIT_P = false>
+// SPLIT (with EMIT_P, for grids that run in one round at two workgroups per
+// CU): K and Q natural get LDS of their own (71 KB in all at K = V = 128), so
+// that Q's loads go out after the first barrier, while K K^T is formed, and
+// waves 4-7 form P^T while waves 0-3 solve the diagonal blocks of T, instead
+// of both lengthening the phases before.
+template <typename E, int K, int V, bool VARLEN, bool STORE_T = false, bool EMIT_P = false,
+          bool SPLIT = false>
 __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __restrict__ kg,
                                                      const E* __restrict__ vg,
                                                      const float* __restrict__ g_raw,
@@ -287,6 +293,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
                                                      const E* __restrict__ qg,
                                                      Frag<E>* __restrict__ pf) {
   static_assert(!EMIT_P || wy_q_fits<E, K>(), "Q rows must fit the LDS of T");
+  static_assert(!SPLIT || EMIT_P, "the split only moves the P^T work");
   constexpr int P = 16 / sizeof(E);  // 16 bytes of row padding
   constexpr int KS = K + P;          // K natural row stride
   constexpr int CSK = kChunk + 4;    // K^T row stride
@@ -305,10 +312,12 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   __shared__ __align__(16) float Ts[kChunk * FS];
   E* const Kt = KT_LATE ? reinterpret_cast<E*>(Ts) : Kt_sep;
   __shared__ float sg[kChunk], sb[kChunk];
-  E* const Ks = reinterpret_cast<E*>(r0);
+  __shared__ __align__(16) E KQ_sep[SPLIT ? 2 * kChunk * KS : 8];  // SPLIT: K, Q natural
+  E* const Ks = SPLIT ? KQ_sep : reinterpret_cast<E*>(r0);
   E* const Vt = reinterpret_cast<E*>(r0);  // V^T, once T is formed
   float* const As = reinterpret_cast<float*>(r0);
-  E* const Qs = reinterpret_cast<E*>(Ts);  // EMIT_P: Q natural [64][KS], until T is formed
+  // EMIT_P: Q natural [64][KS], until T is formed (SPLIT: for the whole kernel)
+  E* const Qs = SPLIT ? KQ_sep + kChunk * KS : reinterpret_cast<E*>(Ts);
 
   int hv, slot;
   xcd_slot_block(blockIdx.x, geo.H, geo.G, geo.slots, hv, slot);
@@ -353,15 +362,26 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       e[r].zero();
     }
   }
-  // EMIT_P: thread t also loads 8-element pieces t and t + 512 of Q's rows.
+  // EMIT_P: thread t also loads 8-element pieces t and t + 512 of Q's rows
+  // (SPLIT: after the first barrier).
   constexpr int NQP = EMIT_P ? (kChunk * (K / 8) + kWyThreads - 1) / kWyThreads : 0;
   Raw8<E> eq[NQP > 0 ? NQP : 1];  // as loaded
+  auto load_q = [&]() {
 #pragma unroll
-  for (int it = 0; it < NQP; ++it) {
-    const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
-    if (row < kChunk && row < len) eq[it].load(qg + ((t0 + row) * geo.H + h) * K + qc);
-    else eq[it].zero();
-  }
+    for (int it = 0; it < NQP; ++it) {
+      const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
+      if (row < kChunk && row < len) eq[it].load(qg + ((t0 + row) * geo.H + h) * K + qc);
+      else eq[it].zero();
+    }
+  };
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int it = 0; it < NQP; ++it) {
+      const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
+      if (row < kChunk) eq[it].store(Qs + row * KS + qc);
+    }
+  };
+  if constexpr (!SPLIT) load_q();
   if (owns && kside) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) e[r].store(Ks + (rb + r) * KS + c0);
@@ -370,11 +390,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       for (int j = 0; j < 8; ++j) raw_column(e, j, Kt + (c0 + j) * CSK + (rb ^ tswz(c0 + j)));
     }
   }
-#pragma unroll
-  for (int it = 0; it < NQP; ++it) {
-    const int m = tid + kWyThreads * it, row = m / (K / 8), qc = 8 * (m % (K / 8));
-    if (row < kChunk) eq[it].store(Qs + row * KS + qc);
-  }
+  if constexpr (!SPLIT) stage_q();
   // Gate prologue (wave 0, lane = token): g in fp32 with the softplus
   // threshold of the KDA gate guide ("core computation logic"), the chunk-local
   // scan, and this head's stride-1 rows of the cumulative gate (times log2 e)
@@ -398,6 +414,44 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
     bet[hs * kChunk + lane] = braw;
   }
   __syncthreads();
+  if constexpr (SPLIT) load_q();  // in flight while K K^T is formed
+
+  // EMIT_P: P^T fragment job j (0..5): query tile it, key rows 32jb..32jb+31
+  // (key tiles 2jb, 2jb+1; a key tile past it is 0).  p_products forms it
+  // from K and Q natural; p_store masks and decays it (sg) and stores it.
+  auto p_tile = [](int j, int& pit, int& pjb) {
+    pit = j < 1 ? 0 : j < 2 ? 1 : j < 4 ? 2 : 3;
+    pjb = (j == 3 || j == 5) ? 1 : 0;
+  };
+  auto p_products = [&](int j, f32x4 (&pt)[2]) {
+    int pit, pjb;
+    p_tile(j, pit, pjb);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int jt = 2 * pjb + q;
+      pt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt <= pit) {
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb)
+          mma_k32(pt[q], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
+                  frag_from_row(Qs + (16 * pit + lc) * KS + 32 * kb));
+      }
+    }
+  };
+  auto p_store = [&](int j, f32x4 (&pt)[2]) {
+    int pit, pjb;
+    p_tile(j, pit, pjb);
+    const int i = 16 * pit + lc;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jj = 16 * (2 * pjb + q) + 4 * g + r;
+        pt[q][r] = jj <= i ? pt[q][r] * fast_exp2(sg[i] - sg[jj]) : 0.f;
+      }
+    }
+    pf[((hs * 4 + pit) * 2 + pjb) * 64 + lane] = frag_from_tiles<E>(pt[0], pt[1]);
+  };
 
   // A = strictly_lower(beta_i (K K^T)_ij exp(G_i - G_j)).  The 10 tiles on or
   // below the diagonal go 2/2/1/1/1/1/1/1 to the waves; the products finish
@@ -419,40 +473,15 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
                   frag_from_row(Ks + (16 * tj[q] + lc) * KS + 32 * kb));
       }
     }
-    // EMIT_P: fragment job j = wave - 2 (waves 2..7) of P^T: query tile it,
-    // key rows 32jb..32jb+31 (key tiles 2jb, 2jb+1; a key tile past it is 0).
+    // EMIT_P without SPLIT: fragment job j = wave - 2 (waves 2..7) of P^T
+    // (p_products / p_store below), formed here next to K K^T.
     f32x4 pt[2];
-    int pit = 0, pjb = 0;
-    if constexpr (EMIT_P) {
-      const int j = wave - 2;
-      pit = j < 1 ? 0 : j < 2 ? 1 : j < 4 ? 2 : 3;
-      pjb = (j == 3 || j == 5) ? 1 : 0;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int jt = 2 * pjb + q;
-        pt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (wave >= 2 && jt <= pit) {
-#pragma unroll
-          for (int kb = 0; kb < K / 32; ++kb)
-            mma_k32(pt[q], frag_from_row(Ks + (16 * jt + lc) * KS + 32 * kb),
-                    frag_from_row(Qs + (16 * pit + lc) * KS + 32 * kb));
-        }
-      }
+    if constexpr (EMIT_P && !SPLIT) {
+      if (wave >= 2) p_products(wave - 2, pt);
     }
     __syncthreads();
-    if constexpr (EMIT_P) {
-      if (wave >= 2) {
-        const int i = 16 * pit + lc;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * (2 * pjb + q) + 4 * g + r;
-            pt[q][r] = j <= i ? pt[q][r] * fast_exp2(sg[i] - sg[j]) : 0.f;
-          }
-        }
-        pf[((hs * 4 + pit) * 2 + pjb) * 64 + lane] = frag_from_tiles<E>(pt[0], pt[1]);
-      }
+    if constexpr (EMIT_P && !SPLIT) {
+      if (wave >= 2) p_store(wave - 2, pt);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -465,6 +494,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
       }
     }
   }
+  if constexpr (SPLIT) stage_q();
   __syncthreads();
 
   // Diagonal blocks of T by forward substitution, lane j solving column j of
@@ -475,6 +505,18 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(Geo geo, const E* __
   // reads below take those blocks as zero.
   {
     const int b = wave;
+    if constexpr (SPLIT) {
+      // waves 4-7: the P^T jobs (4, 5 two each; 6, 7 one each)
+      if (b >= 4) {
+        f32x4 pt[2];
+        p_products(b - 4, pt);
+        p_store(b - 4, pt);
+        if (b < 6) {
+          p_products(b, pt);
+          p_store(b, pt);
+        }
+      }
+    }
     if (b < 4 && lane < 16) {
       const float* ab = As + 16 * b * FS + 16 * b;
       float x[16];
