@@ -27,8 +27,8 @@
  * pointer", done inside the kernel instead of on the host), the sequential
  * inter-chunk state pass, and the chunk output.  For bf16 without segments
  * (and fp32 at K = 64 with many units) the output runs inside the state-pass
- * kernel (gdn_fwd_fuses_output), so a call is two kernels.  One more kernel builds the chunk map when cu_seqlens
- * is given.
+ * kernel (gdn_fwd_fuses_output), so a call is two kernels.  One more kernel
+ * builds the chunk map when cu_seqlens is given.
  *
  * Segment-parallel state pass (seg_chunks > 0).  The chunk update is affine in
  * the state, H_next = M_c H + B_c (M_c = e^{G_last} I - kd^T w), so a run of
