@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     fuses_output,
     fwd,
     fwd_noalloc,
+    gated_delta_rule,
     kda_gate,
     kda_gate_launcher,
     lib_path,
@@ -44,6 +45,6 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "BWD_NUM_STAGES", "BWD_STAGES", "GdnBackward", "bwd",
     "GDN_BF16", "GDN_F16", "GDN_F32", "GDN_SCRATCH_BYTES", "GDN_SEG_AUTO", "GdnError", "GdnForward", "NUM_STAGES", "Params", "STAGES", "STAGE_ALL", "STAGE_BITS", "WorkspaceLayout",
-    "check", "decode", "decode_launcher", "fuses_output", "fwd", "fwd_noalloc", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "seg_chunks", "status_string",
+    "check", "decode", "decode_launcher", "fuses_output", "fwd", "fwd_noalloc", "gated_delta_rule", "kda_gate", "kda_gate_launcher", "lib_path", "load_library", "make_params", "seg_chunks", "status_string",
     "workspace_layout", "workspace_size",
 ]

@@ -566,6 +566,59 @@ class GdnBackward:
         return launch
 
 
+_GATED_DELTA_RULE = None
+
+
+def _gated_delta_rule_fn():
+    """The torch.autograd.Function behind gated_delta_rule (defined on first use,
+    since torch is imported lazily)."""
+    global _GATED_DELTA_RULE
+    if _GATED_DELTA_RULE is None:
+        torch = _torch()
+
+        class GatedDeltaRule(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
+                        scale):
+                o, fin = fwd(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, initial_state,
+                             scale=scale)
+                ctx.save_for_backward(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                                      initial_state)
+                ctx.scale = scale
+                return o, fin
+
+            @staticmethod
+            def backward(ctx, d_o, d_fin):
+                q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens, h0 = ctx.saved_tensors
+                B, T = q.shape[0], q.shape[1]
+                HV, V = v.shape[2], v.shape[3]
+                # torch may hand over expanded or strided gradients; the library
+                # takes dense row-major buffers
+                if d_o is None:
+                    d_o = torch.zeros((B, T, HV, V), dtype=q.dtype, device=q.device)
+                d_o = d_o.to(q.dtype).contiguous()
+                if d_fin is not None:
+                    d_fin = d_fin.to(torch.float32).contiguous()
+                gr = bwd(q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_fin,
+                         cu_seqlens=cu_seqlens, initial_state=h0, scale=ctx.scale)
+                return (gr["dq"], gr["dk"], gr["dv"], gr["dg_raw"], gr["dbeta"], gr["dA_log"],
+                        gr["ddt_bias"] if dt_bias is not None else None, None,
+                        gr["dh0"] if h0 is not None else None, None)
+
+        _GATED_DELTA_RULE = GatedDeltaRule
+    return _GATED_DELTA_RULE
+
+
+def gated_delta_rule(q, k, v, g_raw, beta, A_log, dt_bias=None, cu_seqlens=None,
+                     initial_state=None, scale=1.0):
+    """fwd() as a differentiable torch op: returns (o, final_state) like fwd();
+    their gradients run gdn_bwd (which recomputes the forward's intermediates)
+    and reach q, k, v, g_raw, beta, A_log, dt_bias and initial_state.  Inputs
+    as for fwd(): contiguous GPU tensors of the documented shapes and dtypes."""
+    return _gated_delta_rule_fn().apply(q, k, v, g_raw, beta, A_log, dt_bias, cu_seqlens,
+                                        initial_state, scale)
+
+
 def bwd(q, k, v, g_raw, beta, A_log, dt_bias, d_o, d_final_state=None, cu_seqlens=None,
         initial_state=None, scale=1.0):
     """One backward pass (allocates outputs and workspace with torch); returns

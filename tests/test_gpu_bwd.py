@@ -221,3 +221,53 @@ def test_many_units_ring_recompute(dtype, K, V):
     say("case bwd ring_recompute", s, "units", units, "cus", cus)
     assert units > 2 * cus or cus != 256
     check_full(inp, "bwd ring_recompute_%s_K%d" % (dtype, K), 721)
+
+
+@pytest.mark.parametrize("dtype,packed", [(BF, False), (F32, True)])
+def test_autograd_op(dtype, packed):
+    """gated_delta_rule as a torch op: the gradients loss.backward() leaves on
+    every input, for loss = <d_o, o> + <d_final, final state>, against the
+    oracle's reverse sweep (the same tolerances as a direct gdn_bwd call)."""
+    if packed:
+        inp = make_inputs(B=1, T=333, H=2, HV=4, K=64, V=128, dtype=dtype, seed=651, h0=True,
+                          lengths=[100, 0, 64, 169])
+    else:
+        inp = make_inputs(B=2, T=150, H=2, HV=4, K=128, V=128, dtype=dtype, seed=652, h0=True,
+                          scale=0.8)
+    say("case autograd_op", dtype, "packed" if packed else "fixed", inp.shape)
+    d_o, dht = make_grads(inp, 653)
+    d = inp.to("cuda")
+    leaves = {n: getattr(d, n).detach().clone().requires_grad_(True)
+              for n in ("q", "k", "v", "g_raw", "beta", "A_log", "dt_bias", "h0")}
+    o, fin = gdn.gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g_raw"],
+                                  leaves["beta"], leaves["A_log"], leaves["dt_bias"],
+                                  cu_seqlens=d.cu_seqlens, initial_state=leaves["h0"],
+                                  scale=d.scale)
+    loss = (o.float() * d_o.cuda().float()).sum() + (fin * dht.cuda()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    got = dict(dq=leaves["q"].grad, dk=leaves["k"].grad, dv=leaves["v"].grad,
+               dg_raw=leaves["g_raw"].grad, dbeta=leaves["beta"].grad,
+               dA_log=leaves["A_log"].grad, ddt_bias=leaves["dt_bias"].grad,
+               dh0=leaves["h0"].grad)
+    got = {n: f64(t) for n, t in got.items()}
+    ref = run_oracle_bwd(inp, d_o, dht)
+    compare(got, ref, inp.q.dtype, "autograd %s" % dtype, term_scale=param_term_scale(inp, ref))
+
+
+def test_autograd_op_output_only():
+    """Only o enters the loss (no final-state gradient) and the inputs take no
+    dt_bias or initial state: those gradients are None, the rest match a
+    direct call with d_final_state = NULL."""
+    inp = make_inputs(B=1, T=200, H=1, HV=2, K=64, V=64, dtype=BF, seed=661)
+    inp.dt_bias = None
+    d_o, _ = make_grads(inp, 662, final_state_grad=False)
+    d = inp.to("cuda")
+    q = d.q.detach().clone().requires_grad_(True)
+    g_raw = d.g_raw.detach().clone().requires_grad_(True)
+    o, _ = gdn.gated_delta_rule(q, d.k, d.v, g_raw, d.beta, d.A_log, scale=d.scale)
+    (o.float() * d_o.cuda().float()).sum().backward()
+    torch.cuda.synchronize()
+    ref = run_oracle_bwd(inp, d_o, None)
+    compare(dict(dq=f64(q.grad), dg_raw=f64(g_raw.grad)), ref, inp.q.dtype,
+            "autograd o only", names=("dq", "dg_raw"))
