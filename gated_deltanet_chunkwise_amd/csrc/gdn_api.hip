@@ -455,6 +455,9 @@ gdn_status_t make_bwd_plan(const gdn_params_t* p, bool varlen, Plan* pl, BwdLayo
   if (st != GDN_OK) return st;
   // the key-head sum's grid: one workgroup per (slot, key head, 256 pieces)
   if ((int64_t)pl->geo.slots * p->H * (gdn::kChunk * p->K / 1024) > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  // the WY backward addresses a chunk's token rows with 32-bit offsets
+  if ((int64_t)gdn::kChunk * p->HV * p->V > INT32_MAX || (int64_t)gdn::kChunk * p->H * p->K > INT32_MAX)
+    return GDN_ERR_UNSUPPORTED;
   const size_t hsl = (size_t)p->HV * (size_t)pl->geo.slots, C = gdn::kChunk, K = p->K, V = p->V;
   size_t off = pl->lay.total;
   const size_t esz = p->dtype == GDN_BF16 ? 2 : 4;

@@ -1669,6 +1669,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int h = hv / geo.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, lc = lane & 15;
   const int rt0 = 2 * (wave >> 2), kc0 = (wave & 3) * (K / 4), vc0 = (wave & 3) * (V / 4);
+  // The chunk's rows as wave-uniform base pointers with 32-bit offsets (the
+  // host rejects 64 H K or 64 HV V beyond int32): per-element 64-bit addresses
+  // kept from here to the stores spilled to scratch memory.
+  const int kstride = geo.H * K, vstride = geo.HV * V;
+  const bf16* const vrow = vg + (t0 * geo.HV + hv) * V;
+  bf16* const dvrow = dvg + (t0 * geo.HV + hv) * V;
+  bf16* const dkrow = dkg + (t0 * geo.H + h) * K;
+  float* const dkpc = dkp + hs * kChunk * K;
   const int pit = wave >> 1, pj0 = 2 * (wave & 1);
 
   // dw [64][K], dv_new^T [V][64] and T [64][64] (bf16) into registers,
@@ -1816,8 +1824,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
       for (int nv = 0; nv < NVT; ++nv) {
         const int vv = vc0 + 16 * nv + lc;
         if (j < len) {
-          vx += (float)vg[((t0 + j) * geo.HV + hv) * V + vv] * xu[a][nv][r];
-          dvg[((t0 + j) * geo.HV + hv) * V + vv] = (bf16)(sb[j] * xu[a][nv][r]);
+          vx += (float)vrow[j * vstride + vv] * xu[a][nv][r];
+          dvrow[j * vstride + vv] = (bf16)(sb[j] * xu[a][nv][r]);
         }
       }
       kx = sum16(kx);
@@ -1911,7 +1919,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
     for (int nt = 0; nt < NKT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dk0[a][nt][r] = dkp[(hs * kChunk + 16 * (rt0 + a) + 4 * g + r) * K + kc0 + 16 * nt + lc];
+        dk0[a][nt][r] = dkpc[(16 * (rt0 + a) + 4 * g + r) * K + kc0 + 16 * nt + lc];
   // 5. dk += (dS + dS^T) K.  K^T from the natural rows (4 rows x 8 columns per thread).
   {
     constexpr int CB = K / 8, NB = (kChunk / 4) * CB;
@@ -1963,12 +1971,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * jt + 4 * g + r;
-        const size_t o = (hs * kChunk + j) * K + kc + lc;
+        const int o = j * K + kc + lc;
         // one value head per key head: dk is final here
         if (geo.G == 1) {
-          if (j < len) dkg[((t0 + j) * geo.H + h) * K + kc + lc] = (bf16)(dk0[a][nt][r] + dk[a][nt][r]);
+          if (j < len) dkrow[j * kstride + kc + lc] = (bf16)(dk0[a][nt][r] + dk[a][nt][r]);
         } else {
-          dkp[o] = dk0[a][nt][r] + dk[a][nt][r];
+          dkpc[o] = dk0[a][nt][r] + dk[a][nt][r];
         }
       }
     }

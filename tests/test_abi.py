@@ -263,6 +263,12 @@ def test_bwd_validation():
     assert lib.gdn_bwd_workspace_size(ctypes.byref(bad), 0) == 0
     assert _bwd_call(lib, bad, ws) == EUNSUP
     assert _bwd_call(lib, P(HV=3, H=2), ws) == ESHAPE
+    # the WY backward's 32-bit row offsets: 64 HV V beyond int32 is rejected
+    # by the backward only (the forward takes it)
+    wide = P(B=1, T=64, H=1, HV=262144, K=128, V=128)
+    assert gdn.workspace_size(wide) > 0
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(wide), 0) == 0
+    assert _bwd_call(lib, wide, ws) == EUNSUP
     assert _bwd_call(lib, P(num_seqs=2), ws, cu_seqlens=0x90000) == ESHAPE  # packed needs B == 1
     # no tokens: token pointers may be NULL (dA_log is still required)
     e = P(T=0)
