@@ -34,8 +34,8 @@
 //   * dq, dk of a key head sum its value heads (a key-head sum kernel; with one
 //     value head per key head the dq/dk and WY kernels write them directly).
 // The forward intermediates are recomputed first by the forward kernels: WY
-// (also storing T) and the state pass in its CHAIN_PLAIN mode (fp32 H_c and
-// v_new).
+// (also storing T) and the state pass in its CHAIN_PLAIN mode (H_c and v_new
+// row-major, in the call's dtype like T).
 //
 // Arithmetic.  fp32 calls run every product on the fp32 MFMA
 // (v_mfma_f32_16x16x4f32, operands staged as fp32 in LDS).  bf16 calls run
