@@ -163,3 +163,15 @@ def test_library_shares_torchs_hip_runtime():
     assert out.returncode == 0, out.stderr[-2000:]
     runtimes = eval(out.stdout.strip().splitlines()[-1])
     assert len(runtimes) == 1, runtimes
+
+
+def test_autograd_op_checks_placement_before_any_launch():
+    """gated_delta_rule has no CPU path: host tensors are refused by the same
+    checks as fwd(), before anything is launched."""
+    d = inputs()
+    leaves = {n: t.clone().requires_grad_(True) for n, t in d.items()
+              if t is not None and t.dtype != torch.int64}
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g_raw"],
+                             leaves["beta"], leaves["A_log"], leaves["dt_bias"],
+                             initial_state=leaves["initial_state"])
