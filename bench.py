@@ -665,12 +665,23 @@ def bench_bwd(args):
 SEEDS_BWD = 20290  # output-gradient seed of the backward benchmark
 
 
+def traffic_key(workload, op="gdn_fwd", seg_chunks=0):
+    """traffic.json key of one measured configuration: the workload, then
+    ':bwd' for the backward, or ':seg=L' (':seg=auto') for a forward with the
+    segment-parallel state pass, whose kernels differ from the plain pass's."""
+    if op == "gdn_bwd":
+        return workload + ":bwd"
+    if seg_chunks:
+        return workload + (":seg=auto" if seg_chunks < 0 else ":seg=%d" % seg_chunks)
+    return workload
+
+
 def main():
     args = parse()
     if args.write_traffic:
-        key = args.workload + (":bwd" if args.op == "gdn_bwd" else "")
         op = {"kda_gate": "kda_gate", "decode": "decode"}.get(
             args.workload, "gdn_bwd" if args.op == "gdn_bwd" else "gdn_fwd")
+        key = traffic_key(args.workload, op, args.seg_chunks if op == "gdn_fwd" else 0)
         write_traffic(args.write_traffic, key, args.copy_mib << 20, op)
         return
     if args.gpus != 1:
@@ -827,13 +838,14 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
-        ent = tr.get(wl, {}).get(dom)
+        tk = traffic_key(wl, "gdn_fwd", args.seg_chunks)
+        ent = tr.get(tk, {}).get(dom)
         if ent and ent.get("source_hash") == src:
             roof["traffic"] = ent["bytes_per_launch"]
             roof.update(kernel_counters(ent))
         # counter-measured MFMA utilisation and matrix flops of every kernel
         for name, k in kernels.items():
-            e = tr.get(wl, {}).get(name)
+            e = tr.get(tk, {}).get(name)
             if e and e.get("source_hash") == src:
                 k.update({"counters_" + a: b for a, b in kernel_counters(e).items()})
     sec = ms / 1e3

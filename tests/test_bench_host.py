@@ -163,3 +163,14 @@ def test_every_kernel_is_rated_against_its_own_dtype_peak(dtype, peak):
     for name in ("wy", "chain", "output"):
         assert bench.kernel_figures(fwd[name], 0.01, dtype)["mfma_frac"] == round(
             fwd[name]["flops"] / 1e-5 / peak, 4)
+
+
+def test_traffic_keys_separate_configurations():
+    """Counters of a run with segments, or of the backward, never stand in for
+    the plain forward of the same workload (their kernels differ)."""
+    assert bench.traffic_key("pages_bf16") == "pages_bf16"
+    assert bench.traffic_key("pages_bf16", "gdn_bwd") == "pages_bf16:bwd"
+    assert bench.traffic_key("pages_bf16", "gdn_bwd", -1) == "pages_bf16:bwd"
+    assert bench.traffic_key("long_h2_bf16", "gdn_fwd", -1) == "long_h2_bf16:seg=auto"
+    assert bench.traffic_key("long_h2_bf16", "gdn_fwd", 32) == "long_h2_bf16:seg=32"
+    assert bench.traffic_key("decode", "decode") == "decode"
