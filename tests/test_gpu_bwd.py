@@ -271,3 +271,15 @@ def test_autograd_op_output_only():
     ref = run_oracle_bwd(inp, d_o, None)
     compare(dict(dq=f64(q.grad), dg_raw=f64(g_raw.grad)), ref, inp.q.dtype,
             "autograd o only", names=("dq", "dg_raw"))
+
+
+@pytest.mark.parametrize("H,HV,packed", [(8, 32, False), (1, 8, True)])
+def test_wide_gqa_groups(H, HV, packed):
+    """Four and eight value heads per key head: the backward's block-to-head
+    maps and the key-head sums of dq and dk over the group."""
+    if packed:
+        inp = make_inputs(B=1, T=300, H=H, HV=HV, K=64, V=64, dtype=BF, seed=681, h0=True,
+                          lengths=[130, 0, 64, 106])
+    else:
+        inp = make_inputs(B=1, T=200, H=H, HV=HV, K=64, V=64, dtype=BF, seed=682, h0=True)
+    check_full(inp, "bwd gqa_groups_H%d_HV%d%s" % (H, HV, "_packed" if packed else ""), 683)

@@ -343,3 +343,26 @@ def test_shared_key_head_workgroups(K, V, packed, dtype):
         o, fin = run_gpu(inp, seg_chunks=16)
         assert_close(o, o_r, inp.q.dtype, tag + " segments o")
         assert_close(fin, fin_r, inp.q.dtype, tag + " segments final")
+
+
+@pytest.mark.parametrize("H,HV,T,packed,dtype", [
+    (8, 32, 200, False, BF),     # four value heads per key head, key heads on every XCD, split WY
+    (8, 32, 2100, False, BF),    # the same beyond one dispatch round (non-split WY)
+    (8, 64, 700, True, BF),      # eight per key head, packed
+    (1, 8, 300, False, BF),      # eight per key head, fewer key heads than XCDs
+    (8, 32, 300, True, F32),     # fp32, four per key head, packed
+])
+def test_wide_gqa_groups(H, HV, T, packed, dtype):
+    """GQA groups of four and eight value heads per key head: the block-to-head
+    maps of WY, the fused state pass and the output (a key head's value heads
+    on one XCD when H is a multiple of 8) at group sizes above two, every
+    element against the oracle."""
+    K, V = 64, 64
+    if packed:
+        lengths = [T - 170, 0, 64, 106]
+        inp = make_inputs(B=1, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype, seed=71 + HV,
+                          lengths=lengths, h0=True)
+    else:
+        inp = make_inputs(B=1, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype, seed=72 + HV + T, h0=True)
+    check_full(inp, "gqa_groups_H%d_HV%d_T%d%s_%s" % (H, HV, T, "_packed" if packed else "",
+                                                     dtype))
