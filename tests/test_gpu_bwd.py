@@ -283,3 +283,29 @@ def test_wide_gqa_groups(H, HV, packed):
     else:
         inp = make_inputs(B=1, T=200, H=H, HV=HV, K=64, V=64, dtype=BF, seed=682, h0=True)
     check_full(inp, "bwd gqa_groups_H%d_HV%d%s" % (H, HV, "_packed" if packed else ""), 683)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF])
+def test_extreme_decay(dtype):
+    """The backward at A_log in [4, 5] (gates of about -100 per token): every
+    gradient finite, and q, k, v, beta and initial-state gradients within the
+    usual bounds.  The gate gradients are not held to them here: the chunk form
+    gets a token's dg as the reversed in-chunk sum of the cumulative-gate
+    gradients, whose O(1) terms cancel to ~0 for a token that cuts the state
+    (e^g ~ 1e-44), leaving an fp32 rounding floor (measured ~5e-6 in dg_raw
+    against true values below 1e-38) that the per-head sums dA_log and ddt_bias
+    gather over the chunk."""
+    inp = make_inputs(B=1, T=150, H=2, HV=4, K=64, V=64, dtype=dtype, seed=691, h0=True,
+                      A_log_range=(4.0, 5.0))
+    d_o, dht = make_grads(inp, 692)
+    got = run_gpu_bwd(inp, d_o, dht)
+    for n in NAMES:
+        assert np.all(np.isfinite(got[n])), n
+    ref = run_oracle_bwd(inp, d_o, dht)
+    compare(got, ref, inp.q.dtype, "bwd extreme_decay_%s" % dtype,
+            names=("dq", "dk", "dv", "dbeta", "dh0"))
+    # the floor is small against the largest gate gradient: within the bf16
+    # max-abs bound (2e-2) of it for bf16 calls, 1e-3 of it for fp32 calls
+    err = np.max(np.abs(got["dg_raw"] - ref["dg_raw"]))
+    say("  dg_raw max |err| / max |ref| = %.3e" % (err / np.max(np.abs(ref["dg_raw"]))))
+    assert err <= (2e-2 if dtype == BF else 1e-3) * np.max(np.abs(ref["dg_raw"]))

@@ -366,3 +366,14 @@ def test_wide_gqa_groups(H, HV, T, packed, dtype):
         inp = make_inputs(B=1, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype, seed=72 + HV + T, h0=True)
     check_full(inp, "gqa_groups_H%d_HV%d_T%d%s_%s" % (H, HV, T, "_packed" if packed else "",
                                                      dtype))
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+def test_extreme_decay(dtype):
+    """A_log in [4, 5]: every token's gate is about -100, so the state is all
+    but reset at every token, cumulative gates reach thousands within a chunk
+    and their forward-in-time differences would overflow exp: the masked
+    entries must be selected away, never multiplied by zero (no inf or NaN)."""
+    inp = make_inputs(B=2, T=150, H=2, HV=4, K=128, V=128, dtype=dtype, seed=75, h0=True,
+                      A_log_range=(4.0, 5.0))
+    check_full(inp, "extreme_decay_%s" % dtype)
